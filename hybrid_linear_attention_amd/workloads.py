@@ -1,0 +1,273 @@
+"""Seeded synthetic inputs for the GDN mixer core.
+
+This module only draws random numbers and rounds them to the storage dtype; it
+holds none of the method's arithmetic.  Both the GPU path and the CPU oracle are
+fed the tensors it returns (CPU torch tensors; the oracle widens them exactly to
+fp64, the GPU path copies them to the device).
+
+Generator: ``numpy.random.Generator(PCG64(seed))`` (seed 1234 + workload id for
+the five named workloads).  Normal draws are float32 from that generator, scaled
+by the standard deviation in float32 and rounded to bf16 round-to-nearest-even
+by torch on the CPU where the storage dtype is bf16.  Draw order is fixed and
+documented in ``make_gdn_case``.
+
+Shapes follow the tutorial page's data-structure table (section 01): q/k
+[T,16,128], v/z [T,48,128], a/b [T,48], state [R,48,128,128] fp32, conv history
+[R,10240,3].
+"""
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+# Bit patterns written into slots no request uses, so that a stray write or
+# read is visible: a quiet-NaN payload in each storage format.
+STATE_SENTINEL_BITS = 0x7FC0DEAD  # float32
+HIST_SENTINEL_BITS_F32 = 0x7FC0BEEF
+HIST_SENTINEL_BITS_BF16 = 0x7FDE
+
+
+@dataclass
+class GdnDims:
+    num_k_heads: int
+    num_v_heads: int
+    head_dim_k: int
+    head_dim_v: int
+    conv_taps: int = 4
+
+    @property
+    def conv_channels(self) -> int:
+        return 2 * self.num_k_heads * self.head_dim_k + self.num_v_heads * self.head_dim_v
+
+
+FULL_DIMS = GdnDims(16, 48, 128, 128, 4)
+TINY_DIMS = GdnDims(2, 6, 16, 16, 4)
+
+
+@dataclass
+class GdnCase:
+    dims: GdnDims
+    x_qkv: torch.Tensor          # [T, Cqkv]  conv input (pre-conv q|k|v)
+    z: torch.Tensor              # [T, Hv, dv]
+    a: torch.Tensor              # [T, Hv]    raw decay projection
+    b: torch.Tensor              # [T, Hv]    raw write-strength projection
+    conv_w: torch.Tensor         # [Cqkv, taps], conv_w[c, i] multiplies x[t-i]
+    gamma: torch.Tensor          # [dv] gated-norm gain
+    conv_pool: torch.Tensor      # [num_slots, Cqkv, taps-1] oldest -> newest
+    state_pool: torch.Tensor     # [num_slots, Hv, dv, dk] fp32
+    qsl: torch.Tensor            # [N+1] int32 query_start_loc
+    slot_ids: torch.Tensor       # [N] int32
+    has_initial: torch.Tensor    # [N] uint8
+    used_slots: List[int] = field(default_factory=list)
+    meta: Dict = field(default_factory=dict)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.x_qkv.shape[0])
+
+    @property
+    def num_reqs(self) -> int:
+        return int(self.slot_ids.shape[0])
+
+    @property
+    def num_slots(self) -> int:
+        return int(self.state_pool.shape[0])
+
+
+def _normal(rng, shape, std, dtype):
+    """float32 normal draws scaled by std, stored as ``dtype`` (RNE for bf16)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = torch.empty(n, dtype=dtype)
+    step = 1 << 24  # bounded temporaries for the multi-GB workloads
+    for s in range(0, n, step):
+        e = min(n, s + step)
+        blk = rng.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            blk *= np.float32(std)
+        out[s:e] = torch.from_numpy(blk).to(dtype)
+    return out.reshape(shape)
+
+
+def _fill_bits(t: torch.Tensor, bits: int):
+    if t.dtype == torch.float32:
+        t.view(torch.int32).fill_(np.int32(np.uint32(bits).view(np.int32)))
+    elif t.dtype == torch.bfloat16:
+        t.view(torch.int16).fill_(np.int16(np.uint16(bits).view(np.int16)))
+    else:
+        raise TypeError(t.dtype)
+
+
+def make_gdn_case(seed: int, dims: GdnDims, lengths: Optional[List[int]] = None,
+                  *, random_lengths=None, num_slots: Optional[int] = None,
+                  permute_slots: bool = False, act_dtype=torch.bfloat16,
+                  pool_dtype=None, weight_dtype=None, state_std: float = 0.0,
+                  hist_std: float = 0.0, has_initial: Optional[bool] = None,
+                  conv_w_std: float = 0.5, gamma_std: float = 0.0) -> GdnCase:
+    """Build one seeded GDN-core workload.
+
+    Draw order from one PCG64 stream:
+      1. request lengths (only if ``random_lengths=(n, lo, hi)``: integers in
+         [lo, hi] inclusive),
+      2. slot permutation of range(num_slots) (only if ``permute_slots``),
+      3. initial state of each used slot, in request order (if state_std > 0),
+      4. conv history of each used slot, in request order (if hist_std > 0),
+      5. x_qkv [T, Cqkv], 6. z [T, Hv, dv], 7. a [T, Hv], 8. b [T, Hv] ~ N(0,1),
+      9. conv_w [Cqkv, taps] ~ N(0, conv_w_std),
+     10. gamma = 1 + N(0, gamma_std) (only if gamma_std > 0, else exactly 1).
+    Unused slots carry a NaN sentinel bit pattern.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if random_lengths is not None:
+        n, lo, hi = random_lengths
+        lengths = [int(x) for x in rng.integers(lo, hi + 1, n)]
+    assert lengths is not None
+    nreq = len(lengths)
+    if num_slots is None:
+        num_slots = nreq
+    if permute_slots:
+        perm = rng.permutation(num_slots)
+        slot_ids = [int(x) for x in perm[:nreq]]
+    else:
+        slot_ids = list(range(nreq))
+    pool_dtype = pool_dtype or act_dtype
+    weight_dtype = weight_dtype or act_dtype
+    C = dims.conv_channels
+    nh = dims.conv_taps - 1
+    Hv, dv, dk = dims.num_v_heads, dims.head_dim_v, dims.head_dim_k
+    T = int(sum(lengths))
+    if has_initial is None:
+        has_initial = state_std > 0 or hist_std > 0
+
+    state_pool = torch.empty((num_slots, Hv, dv, dk), dtype=torch.float32)
+    _fill_bits(state_pool, STATE_SENTINEL_BITS)
+    conv_pool = torch.empty((num_slots, C, nh), dtype=pool_dtype)
+    _fill_bits(conv_pool, HIST_SENTINEL_BITS_BF16 if pool_dtype == torch.bfloat16
+               else HIST_SENTINEL_BITS_F32)
+    for s in slot_ids:
+        if state_std > 0:
+            state_pool[s] = _normal(rng, (Hv, dv, dk), state_std, torch.float32)
+        else:
+            state_pool[s].zero_()
+    for s in slot_ids:
+        if hist_std > 0:
+            conv_pool[s] = _normal(rng, (C, nh), hist_std, pool_dtype)
+        else:
+            conv_pool[s].zero_()
+
+    x_qkv = _normal(rng, (T, C), 1.0, act_dtype)
+    z = _normal(rng, (T, Hv, dv), 1.0, act_dtype)
+    a = _normal(rng, (T, Hv), 1.0, act_dtype)
+    b = _normal(rng, (T, Hv), 1.0, act_dtype)
+    conv_w = _normal(rng, (C, dims.conv_taps), conv_w_std, weight_dtype)
+    if gamma_std > 0:
+        gamma = (1.0 + _normal(rng, (dv,), gamma_std, torch.float32)).to(weight_dtype)
+    else:
+        gamma = torch.ones(dv, dtype=weight_dtype)
+
+    qsl = torch.zeros(nreq + 1, dtype=torch.int32)
+    qsl[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return GdnCase(dims=dims, x_qkv=x_qkv, z=z, a=a, b=b, conv_w=conv_w,
+                   gamma=gamma, conv_pool=conv_pool, state_pool=state_pool, qsl=qsl,
+                   slot_ids=torch.tensor(slot_ids, dtype=torch.int32),
+                   has_initial=torch.full((nreq,), 1 if has_initial else 0,
+                                          dtype=torch.uint8),
+                   used_slots=slot_ids, meta=dict(seed=seed, lengths=lengths))
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads
+# ---------------------------------------------------------------------------
+def tiny_core(seed: int = 1234) -> GdnCase:
+    """Tiny GDN core, fp32 throughout: one sequence of 64 tokens, 2 key heads,
+    6 value heads, d_k = d_v = 16, 4-tap conv, zero history and state."""
+    return make_gdn_case(seed, TINY_DIMS, [64], act_dtype=torch.float32,
+                         pool_dtype=torch.float32, weight_dtype=torch.float32)
+
+
+def decode_r64(seed: int = 1235) -> GdnCase:
+    """Decode step at full shapes: 64 requests x 1 token, 16/48 heads, d = 128,
+    state [64,48,128,128] ~ N(0, 0.02) fp32, conv history [64,10240,3] ~ N(0,1)
+    bf16, slot r = request r."""
+    return make_gdn_case(seed, FULL_DIMS, [1] * 64, state_std=0.02, hist_std=1.0)
+
+
+def prefill_4096(seed: int = 1236) -> GdnCase:
+    """Single-sequence prefill at full shapes: T = 4096, zero state and history."""
+    return make_gdn_case(seed, FULL_DIMS, [4096])
+
+
+def prefill_varlen16(seed: int = 1237) -> GdnCase:
+    """Packed varlen prefill: 16 requests of lengths uniform in [256, 8192],
+    slots a seeded permutation of a 64-slot pool, nonzero initial state
+    ~ N(0, 0.02) and conv history ~ N(0, 1) per used slot."""
+    return make_gdn_case(seed, FULL_DIMS, random_lengths=(16, 256, 8192),
+                         num_slots=64, permute_slots=True, state_std=0.02,
+                         hist_std=1.0)
+
+
+@dataclass
+class LayerCase:
+    core: GdnCase                 # GDN-core tensors (x_qkv/z/a/b unused: made by the projection)
+    X: torch.Tensor               # [T, hidden] bf16
+    gamma_in: torch.Tensor        # [hidden]
+    W_qkvz: torch.Tensor          # [hidden, 2*Hk*dk + 2*Hv*dv]
+    W_ba: torch.Tensor            # [hidden, 2*Hv]  (b columns then a columns)
+    W_o: torch.Tensor             # [Hv*dv, hidden]
+    num_prefill: int = 0
+    prefill_len: int = 0
+    num_decode: int = 0
+
+
+def layer_mixed(seed: int = 1238, hidden: int = 5120, num_prefill: int = 8,
+                prefill_len: int = 2048, num_decode: int = 256,
+                dims: GdnDims = FULL_DIMS) -> LayerCase:
+    """Full GDN layer block at hidden 5120, mixed batch: 8 prefill requests of
+    2048 tokens (zero state and history) then 256 decode requests of 1 token
+    (state ~ N(0, 0.02), history ~ N(0, 1)).  Weights ~ N(0, 0.02), X ~ N(0, 1),
+    norm gains 1 + N(0, 0.02), conv taps ~ N(0, 0.5).
+
+    Draw order: decode-slot states, decode-slot histories, X, W_qkvz, W_ba, W_o,
+    conv_w, gamma_in, gamma_out.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    C = dims.conv_channels
+    nh = dims.conv_taps - 1
+    Hv, dv, dk = dims.num_v_heads, dims.head_dim_v, dims.head_dim_k
+    nreq = num_prefill + num_decode
+    lengths = [prefill_len] * num_prefill + [1] * num_decode
+    T = sum(lengths)
+    state_pool = torch.zeros((nreq, Hv, dv, dk), dtype=torch.float32)
+    conv_pool = torch.zeros((nreq, C, nh), dtype=torch.bfloat16)
+    for s in range(num_prefill, nreq):
+        state_pool[s] = _normal(rng, (Hv, dv, dk), 0.02, torch.float32)
+    for s in range(num_prefill, nreq):
+        conv_pool[s] = _normal(rng, (C, nh), 1.0, torch.bfloat16)
+    X = _normal(rng, (T, hidden), 1.0, torch.bfloat16)
+    W_qkvz = _normal(rng, (hidden, C + Hv * dv), 0.02, torch.bfloat16)
+    W_ba = _normal(rng, (hidden, 2 * Hv), 0.02, torch.bfloat16)
+    W_o = _normal(rng, (Hv * dv, hidden), 0.02, torch.bfloat16)
+    conv_w = _normal(rng, (C, dims.conv_taps), 0.5, torch.bfloat16)
+    gamma_in = (1.0 + _normal(rng, (hidden,), 0.02, torch.float32)).to(torch.bfloat16)
+    gamma_out = (1.0 + _normal(rng, (dv,), 0.02, torch.float32)).to(torch.bfloat16)
+    qsl = torch.zeros(nreq + 1, dtype=torch.int32)
+    qsl[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    has_initial = torch.tensor([0] * num_prefill + [1] * num_decode, dtype=torch.uint8)
+    empty = torch.empty(0)
+    core = GdnCase(dims=dims, x_qkv=empty, z=empty, a=empty, b=empty, conv_w=conv_w,
+                   gamma=gamma_out, conv_pool=conv_pool, state_pool=state_pool,
+                   qsl=qsl, slot_ids=torch.arange(nreq, dtype=torch.int32),
+                   has_initial=has_initial, used_slots=list(range(nreq)),
+                   meta=dict(seed=seed, lengths=lengths))
+    return LayerCase(core=core, X=X, gamma_in=gamma_in, W_qkvz=W_qkvz, W_ba=W_ba,
+                     W_o=W_o, num_prefill=num_prefill, prefill_len=prefill_len,
+                     num_decode=num_decode)
+
+
+WORKLOADS = {
+    "tiny_core": tiny_core,
+    "decode_r64": decode_r64,
+    "prefill_4096": prefill_4096,
+    "prefill_varlen16": prefill_varlen16,
+    "layer_mixed": layer_mixed,
+}
