@@ -1,0 +1,225 @@
+// C-ABI layer of libgdn: argument validation (pure host code, runs before any
+// HIP call) and dispatch to the kernel launchers.  See include/gdn.h for the
+// contract of every entry point.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gdn_launch.h"
+
+namespace {
+
+bool valid_dtype(gdn_dtype d) { return d == GDN_F32 || d == GDN_BF16; }
+size_t dt_size(gdn_dtype d) { return d == GDN_F32 ? 4 : 2; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gdn_status check_dims(const gdn_dims *d) {
+    if (!d) return GDN_ERR_NULL;
+    if (d->num_k_heads <= 0 || d->num_v_heads <= 0 || d->num_v_heads % d->num_k_heads != 0)
+        return GDN_ERR_DIMS;
+    if (d->head_dim_k != d->head_dim_v) return GDN_ERR_DIMS;
+    const int D = d->head_dim_k;
+    if (D != 16 && D != 32 && D != 64 && D != 128) return GDN_ERR_DIMS;
+    if (d->conv_taps != 4) return GDN_ERR_DIMS;
+    if ((int64_t)d->num_v_heads * D > (1 << 20)) return GDN_ERR_DIMS;
+    return GDN_OK;
+}
+
+gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL: required pointer is NULL";
+        case GDN_ERR_DIMS: return "GDN_ERR_DIMS: unsupported head geometry";
+        case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unsupported dtype";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: inconsistent counts or strides";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer misaligned";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP launch error";
+        case GDN_ERR_METADATA: return "GDN_ERR_METADATA: bad query_start_loc or slot ids";
+    }
+    return "GDN_ERR_UNKNOWN";
+}
+
+const char *gdn_version(void) { return "libgdn 0.1 (gfx950)"; }
+
+gdn_status gdn_conv1d_update(const gdn_dims *dims, const void *x, gdn_dtype x_dt,
+                             int64_t x_ld, const void *conv_w, gdn_dtype w_dt,
+                             void *conv_pool, gdn_dtype pool_dt,
+                             const int32_t *query_start_loc, const int32_t *slot_ids,
+                             const uint8_t *has_initial, int32_t num_reqs,
+                             int32_t num_tokens, int32_t num_slots, float l2_eps, void *q,
+                             void *k, void *v, gdn_dtype act_dt, void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    if (!valid_dtype(x_dt) || !valid_dtype(w_dt) || !valid_dtype(pool_dt) || !valid_dtype(act_dt))
+        return GDN_ERR_DTYPE;
+    if (pool_dt != x_dt) return GDN_ERR_DTYPE;
+    const int D = dims->head_dim_k;
+    const int32_t nq = dims->num_k_heads * D;
+    const int32_t C = 2 * nq + dims->num_v_heads * D;
+    if (num_reqs < 0 || num_tokens < 0 || num_slots < 0) return GDN_ERR_SHAPE;
+    if (num_reqs > num_slots) return GDN_ERR_SHAPE;
+    if (num_tokens > 0 && num_reqs == 0) return GDN_ERR_SHAPE;
+    if (x_ld < C) return GDN_ERR_SHAPE;
+    if (num_tokens == 0 || num_reqs == 0) return GDN_OK;
+    if (!x || !conv_w || !conv_pool || !query_start_loc || !slot_ids || !q || !k || !v)
+        return GDN_ERR_NULL;
+    if (!(l2_eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if (x_ld % 2 != 0 || !aligned(x, 2 * dt_size(x_dt)) || !aligned(conv_w, dt_size(w_dt)) ||
+        !aligned(conv_pool, dt_size(pool_dt)) || !aligned(q, 2 * dt_size(act_dt)) ||
+        !aligned(k, 2 * dt_size(act_dt)) || !aligned(v, 2 * dt_size(act_dt)) ||
+        !aligned(query_start_loc, 4) || !aligned(slot_ids, 4))
+        return GDN_ERR_ALIGN;
+    gdn::ConvArgs a{D, x, x_ld, x_dt == GDN_BF16, conv_w, w_dt == GDN_BF16, conv_pool,
+                    query_start_loc, slot_ids, has_initial, num_reqs, num_tokens, C, nq,
+                    l2_eps, q, k, v, act_dt == GDN_BF16};
+    return hip_status(gdn::launch_conv1d(a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, const void *v,
+                           gdn_dtype act_dt, const void *a, const void *b, gdn_dtype gate_dt,
+                           int64_t gate_ld, float *state_pool, const int32_t *slot_ids,
+                           int32_t num_reqs, int32_t num_slots, void *o, gdn_dtype o_dt,
+                           void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    if (!valid_dtype(act_dt) || !valid_dtype(gate_dt) || !valid_dtype(o_dt)) return GDN_ERR_DTYPE;
+    if (num_reqs < 0 || num_slots < 0 || num_reqs > num_slots) return GDN_ERR_SHAPE;
+    if (gate_ld < dims->num_v_heads) return GDN_ERR_SHAPE;
+    if (num_reqs == 0) return GDN_OK;
+    if (!q || !k || !v || !a || !b || !state_pool || !slot_ids || !o) return GDN_ERR_NULL;
+    const size_t qk_align = act_dt == GDN_F32 ? 16 : 8;
+    if (!aligned(state_pool, 16) || !aligned(q, qk_align) || !aligned(k, qk_align) ||
+        !aligned(v, dt_size(act_dt)) || !aligned(a, dt_size(gate_dt)) ||
+        !aligned(b, dt_size(gate_dt)) || !aligned(o, dt_size(o_dt)) || !aligned(slot_ids, 4))
+        return GDN_ERR_ALIGN;
+    gdn::DecodeArgs da{dims->head_dim_k, q, k, v, act_dt == GDN_BF16, a, b, gate_ld,
+                       gate_dt == GDN_BF16, state_pool, slot_ids, num_reqs,
+                       dims->num_k_heads, dims->num_v_heads, o, o_dt == GDN_BF16};
+    return hip_status(gdn::launch_decode(da, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_tokens, int32_t num_reqs) {
+    if (check_dims(dims) != GDN_OK || num_tokens < 0 || num_reqs < 0) return 0;
+    return gdn::prefill_workspace_bytes(dims->head_dim_k, dims->num_k_heads, dims->num_v_heads,
+                                        num_tokens, num_reqs);
+}
+
+gdn_status gdn_prefill_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v,
+                              gdn_dtype act_dt, const void *a, const void *b, gdn_dtype gate_dt,
+                              int64_t gate_ld, float *state_pool,
+                              const int32_t *query_start_loc, const int32_t *slot_ids,
+                              const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
+                              int32_t num_slots, void *o, gdn_dtype o_dt, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    if (!valid_dtype(act_dt) || !valid_dtype(gate_dt) || !valid_dtype(o_dt)) return GDN_ERR_DTYPE;
+    if (num_reqs < 0 || num_tokens < 0 || num_slots < 0 || num_reqs > num_slots)
+        return GDN_ERR_SHAPE;
+    if (num_tokens > 0 && num_reqs == 0) return GDN_ERR_SHAPE;
+    if (gate_ld < dims->num_v_heads) return GDN_ERR_SHAPE;
+    if (num_tokens == 0 || num_reqs == 0) return GDN_OK;
+    if (!q || !k || !v || !a || !b || !state_pool || !query_start_loc || !slot_ids || !o)
+        return GDN_ERR_NULL;
+    const size_t need = gdn::prefill_workspace_bytes(dims->head_dim_k, dims->num_k_heads,
+                                                     dims->num_v_heads, num_tokens, num_reqs);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    const size_t qk_align = act_dt == GDN_F32 ? 16 : 8;
+    if (!aligned(state_pool, 16) || !aligned(q, qk_align) || !aligned(k, qk_align) ||
+        !aligned(v, qk_align) || !aligned(a, dt_size(gate_dt)) || !aligned(b, dt_size(gate_dt)) ||
+        !aligned(o, dt_size(o_dt)) || !aligned(query_start_loc, 4) || !aligned(slot_ids, 4) ||
+        (workspace && !aligned(workspace, 256)))
+        return GDN_ERR_ALIGN;
+    gdn::PrefillArgs pa{dims->head_dim_k, q, k, v, act_dt == GDN_BF16, a, b, gate_ld,
+                        gate_dt == GDN_BF16, state_pool, query_start_loc, slot_ids, has_initial,
+                        num_reqs, num_tokens, dims->num_k_heads, dims->num_v_heads, o,
+                        o_dt == GDN_BF16, workspace, workspace_bytes};
+    return hip_status(gdn::launch_prefill(pa, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_gated_norm(const gdn_dims *dims, const void *o, gdn_dtype o_dt, const void *z,
+                          gdn_dtype z_dt, int64_t z_ld, const void *gamma, gdn_dtype gamma_dt,
+                          float eps, int32_t num_tokens, void *y, gdn_dtype y_dt, void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    if (!valid_dtype(o_dt) || !valid_dtype(z_dt) || !valid_dtype(gamma_dt) || !valid_dtype(y_dt))
+        return GDN_ERR_DTYPE;
+    const int D = dims->head_dim_v;
+    if (num_tokens < 0 || z_ld < (int64_t)dims->num_v_heads * D || !(eps >= 0.0f))
+        return GDN_ERR_SHAPE;
+    if (num_tokens == 0) return GDN_OK;
+    if (!o || !z || !gamma || !y) return GDN_ERR_NULL;
+    if (z_ld % 2 != 0 || !aligned(o, 2 * dt_size(o_dt)) || !aligned(z, 2 * dt_size(z_dt)) ||
+        !aligned(gamma, 2 * dt_size(gamma_dt)) || !aligned(y, 2 * dt_size(y_dt)))
+        return GDN_ERR_ALIGN;
+    gdn::GatedNormArgs ga{D, o, o_dt == GDN_BF16, z, z_ld, z_dt == GDN_BF16, gamma,
+                          gamma_dt == GDN_BF16, eps, num_tokens, dims->num_v_heads, y,
+                          y_dt == GDN_BF16};
+    return hip_status(gdn::launch_gated_norm(ga, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_rmsnorm(const void *x, gdn_dtype x_dt, const void *gamma, gdn_dtype gamma_dt,
+                       float eps, int32_t rows, int32_t cols, void *y, gdn_dtype y_dt,
+                       void *stream) {
+    if (!valid_dtype(x_dt) || !valid_dtype(gamma_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    if (rows < 0 || cols <= 0 || cols % 8 != 0 || cols > 16384 || !(eps >= 0.0f))
+        return GDN_ERR_SHAPE;
+    if (rows == 0) return GDN_OK;
+    if (!x || !gamma || !y) return GDN_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(y, 16)) return GDN_ERR_ALIGN;
+    gdn::RmsNormArgs ra{x, x_dt == GDN_BF16, gamma, gamma_dt == GDN_BF16, eps, rows, cols,
+                        y, y_dt == GDN_BF16};
+    return hip_status(gdn::launch_rmsnorm(ra, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                         int64_t ldc, gdn_dtype c_dt, const void *residual, int64_t ldr,
+                         int32_t M, int32_t N, int32_t K, void *stream) {
+    if (!valid_dtype(c_dt)) return GDN_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || N % 8 != 0 || K % 8 != 0) return GDN_ERR_SHAPE;
+    if (lda < K || ldb < N || ldc < N || (residual && ldr < N)) return GDN_ERR_SHAPE;
+    if (lda % 8 || ldb % 8 || ldc % 8 || (residual && ldr % 8)) return GDN_ERR_SHAPE;
+    if (M == 0 || N == 0) return GDN_OK;
+    if (!A || !B || !C) return GDN_ERR_NULL;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || (residual && !aligned(residual, 16)))
+        return GDN_ERR_ALIGN;
+    gdn::GemmArgs g{A, lda, B, ldb, C, ldc, c_dt == GDN_BF16, residual, ldr, M, N, K};
+    return hip_status(gdn::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_validate_metadata(const int32_t *qsl, const int32_t *slots, int32_t num_reqs,
+                                 int32_t num_tokens, int32_t num_slots) {
+    if (num_reqs < 0 || num_tokens < 0 || num_slots < 0) return GDN_ERR_SHAPE;
+    if (!qsl || (num_reqs > 0 && !slots)) return GDN_ERR_NULL;
+    if (qsl[0] != 0 || qsl[num_reqs] != num_tokens) return GDN_ERR_METADATA;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        if (qsl[r + 1] < qsl[r]) return GDN_ERR_METADATA;
+        if (slots[r] < 0 || slots[r] >= num_slots) return GDN_ERR_METADATA;
+    }
+    // distinctness: O(n log n) without allocation is awkward in C; use a
+    // bitmap on the stack for small pools and a quadratic scan otherwise.
+    if (num_slots <= 65536) {
+        uint64_t seen[1024] = {0};
+        for (int32_t r = 0; r < num_reqs; ++r) {
+            const uint32_t s = (uint32_t)slots[r];
+            if (seen[s >> 6] & (1ull << (s & 63))) return GDN_ERR_METADATA;
+            seen[s >> 6] |= 1ull << (s & 63);
+        }
+    } else {
+        for (int32_t r = 0; r < num_reqs; ++r)
+            for (int32_t u = r + 1; u < num_reqs; ++u)
+                if (slots[r] == slots[u]) return GDN_ERR_METADATA;
+    }
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal device helpers shared by the gfx950 kernels of libgdn.
+// (Not part of the ABI; include/gdn.h is the public interface.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Native 4-float vector (usable with the nontemporal builtins, unlike float4).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its raw 16-bit pattern; conversions are explicit.
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16 to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{uint16_t((u >> 16) | 0x40u)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16{uint16_t(u >> 16)};
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { return to_bf16(f); }
+
+template <typename T> __device__ __forceinline__ float ld(const T *p) { return to_f32(*p); }
+template <typename T> __device__ __forceinline__ void st(T *p, float f) { *p = from_f32<T>(f); }
+
+// Two consecutive elements (p must be aligned to two elements).
+__device__ __forceinline__ float2 ld2(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+__device__ __forceinline__ float2 ld2(const bf16 *p) {
+    uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+__device__ __forceinline__ void st2(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+}
+__device__ __forceinline__ void st2(bf16 *p, float a, float b) {
+    uint32_t u = uint32_t(to_bf16(a).bits) | (uint32_t(to_bf16(b).bits) << 16);
+    *reinterpret_cast<uint32_t *>(p) = u;
+}
+
+// Four consecutive elements (p aligned to four elements).
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 ld4(const bf16 *p) {
+    uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Butterfly sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int WIDTH> __device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < WIDTH; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float silu_f(float y) { return y / (1.0f + __expf(-y)); }
+
+// alpha = exp(-softplus(a)) = 1 / (1 + e^a); beta = sigmoid(b) = 1 / (1 + e^-b).
+// Written in the forms that stay finite for any |a|, |b|.
+__device__ __forceinline__ float gate_alpha(float a) {
+    float sp = fmaxf(a, 0.0f) + log1pf(expf(-fabsf(a)));
+    return expf(-sp);
+}
+__device__ __forceinline__ float gate_log_alpha(float a) {
+    return -(fmaxf(a, 0.0f) + log1pf(expf(-fabsf(a))));
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+
+// First index r in [0, n) with qsl[r] <= t < qsl[r + 1] (qsl non-decreasing,
+// qsl[0] = 0 <= t < qsl[n]); empty requests are skipped.
+__device__ __forceinline__ int find_request(const int32_t *__restrict__ qsl, int n, int t) {
+    int lo = 0, hi = n;  // invariant: qsl[lo] <= t < qsl[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (qsl[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace gdn

@@ -1,0 +1,75 @@
+// Internal launcher interface between the C-ABI layer (gdn_api.cpp) and the
+// kernel translation units.  Host-side structs only; validated before use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct ConvArgs {
+    int D;  // d_k == d_v
+    const void *x; int64_t x_ld; bool x_bf16;
+    const void *w; bool w_bf16;
+    void *pool;
+    const int32_t *qsl; const int32_t *slots; const uint8_t *has_init;
+    int32_t nreq, T, C, nq;
+    float l2_eps;
+    void *q, *k, *v; bool act_bf16;
+};
+hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+    int D;
+    const void *q, *k, *v; bool act_bf16;
+    const void *a, *b; int64_t gate_ld; bool gate_bf16;
+    float *state; const int32_t *slots;
+    int32_t R, Hk, Hv;
+    void *o; bool o_bf16;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+struct GatedNormArgs {
+    int D;
+    const void *o; bool o_bf16;
+    const void *z; int64_t z_ld; bool z_bf16;
+    const void *gamma; bool gamma_bf16;
+    float eps;
+    int32_t T, Hv;
+    void *y; bool y_bf16;
+};
+hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s);
+
+struct RmsNormArgs {
+    const void *x; bool x_bf16;
+    const void *gamma; bool gamma_bf16;
+    float eps;
+    int32_t rows, cols;
+    void *y; bool y_bf16;
+};
+hipError_t launch_rmsnorm(const RmsNormArgs &a, hipStream_t s);
+
+struct PrefillArgs {
+    int D;
+    const void *q, *k, *v; bool act_bf16;
+    const void *a, *b; int64_t gate_ld; bool gate_bf16;
+    float *state;
+    const int32_t *qsl, *slots; const uint8_t *has_init;
+    int32_t nreq, T, Hk, Hv;
+    void *o; bool o_bf16;
+    void *ws; size_t ws_bytes;
+};
+size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+struct GemmArgs {
+    const void *A; int64_t lda;
+    const void *B; int64_t ldb;
+    void *C; int64_t ldc; bool c_bf16;
+    const void *R; int64_t ldr;
+    int32_t M, N, K;
+};
+hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s);
+
+}  // namespace gdn

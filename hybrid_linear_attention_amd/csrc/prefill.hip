@@ -1,0 +1,18 @@
+// Prefill dispatch: picks the kernel for the head geometry.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+hipError_t launch_prefill_seq(const PrefillArgs &a, hipStream_t s);
+
+size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq) {
+    (void)D; (void)Hk; (void)Hv; (void)T; (void)nreq;
+    return 0;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
+    return launch_prefill_seq(a, s);
+}
+
+}  // namespace gdn

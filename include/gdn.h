@@ -1,0 +1,238 @@
+/*
+ * gdn.h — C ABI of the MI355X (gfx950) Gated DeltaNet mixer-core library.
+ *
+ * The method ("Qwen3.8-27B: from model structure to the vLLM inference
+ * dataflow", section 01 LAYER-BY-LAYER, per-layer operator table, GDN layer):
+ *
+ *   [Q0,K0,V0,Z] = U Wqkvz; a = U Wa; b = U Wb
+ *   c_t = SiLU(sum_{i=0..3} w_i * QKV0_{t-i});  q = normalize(q); k = normalize(k)
+ *   Sbar = alpha S_prev;  e = v - Sbar k;  S = Sbar + beta e k^T;  o = S q / sqrt(d_k)
+ *   Ogate = RMSNorm(o) * SiLU(Z);  Delta_mix = Ogate Wo;  Y = X + Delta_mix
+ *
+ * with the data structures of that section's data-structure table: q/k
+ * [T,16,128], v/z [T,48,128], a/b [T,48], recurrent state [R,48,128,128] fp32
+ * (3 MiB per sequence per layer), conv history [R,10240,3] (three past inputs;
+ * the 4-tap window includes the current one).  A packed batch of requests is
+ * delimited by query_start_loc; requests never mix (same table, engine note).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees, or keeps them.  Every call is asynchronous: work
+ *    is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *    call returns without synchronising.
+ *  - Tensors are dense row-major in the shapes given, except where a leading
+ *    dimension (`*_ld`, in elements, >= the row width) lets rows be strided.
+ *  - Value head h reads key head h / (Hv / Hk): contiguous groups, the layout
+ *    the page's 4-way tensor-parallel table implies (key heads 0-3 travel with
+ *    value heads 0-11).
+ *  - Recurrent state is fp32 [num_slots, Hv, d_v, d_k], d_k contiguous.
+ *    Conv history is [num_slots, Cqkv, taps-1], oldest -> newest, where
+ *    Cqkv = 2*Hk*d_k + Hv*d_v and channels are ordered q | k | v.
+ *  - Slots named in one call must be distinct (a duplicate is a data race).
+ *    query_start_loc must be non-decreasing, start at 0 and end at num_tokens,
+ *    and slot ids must lie in [0, num_slots): these device-resident contents are
+ *    a caller contract (gdn_validate_metadata checks host copies of them).
+ *  - Host-checkable faults (null pointers, unsupported dims or dtypes,
+ *    negative or inconsistent counts, short workspace, misalignment) return a
+ *    status BEFORE anything is enqueued.  A launch failure returns GDN_ERR_HIP.
+ *  - Supported dims on the GPU: d_k == d_v in {16, 32, 64, 128},
+ *    Hv % Hk == 0, conv_taps == 4.
+ *  - Outputs never alias inputs; the state and history pools are updated in
+ *    place.  A request of length 0 leaves its slots untouched.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head geometry: mirrors the inputs of the page's state-shape calculator
+ * ("How the 64 layers of Qwen3.8-27B are dispatched in vLLM", step 5:
+ * key heads, value heads, key dim, value dim, conv kernel size). */
+typedef struct gdn_dims {
+    int32_t num_k_heads; /* Hk: 16 (tiny workload: 2)   */
+    int32_t num_v_heads; /* Hv: 48 (tiny workload: 6)   */
+    int32_t head_dim_k;  /* d_k: 128 (tiny workload: 16) */
+    int32_t head_dim_v;  /* d_v: 128 (tiny workload: 16) */
+    int32_t conv_taps;   /* 4 */
+} gdn_dims;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,
+    GDN_BF16 = 1
+} gdn_dtype;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,      /* a required pointer is NULL                     */
+    GDN_ERR_DIMS = 2,      /* unsupported or inconsistent head geometry      */
+    GDN_ERR_DTYPE = 3,     /* unsupported dtype combination                  */
+    GDN_ERR_SHAPE = 4,     /* negative or inconsistent counts / strides      */
+    GDN_ERR_WORKSPACE = 5, /* workspace missing or too small                 */
+    GDN_ERR_ALIGN = 6,     /* pointer not aligned as documented              */
+    GDN_ERR_HIP = 7,       /* the HIP runtime reported an error on launch    */
+    GDN_ERR_METADATA = 8   /* gdn_validate_metadata: bad qsl or slot ids     */
+} gdn_status;
+
+/* Human-readable name of a status code (static storage). */
+const char *gdn_status_string(gdn_status s);
+
+/* Library version string (static storage). */
+const char *gdn_version(void);
+
+/*
+ * gdn_conv1d_update — causal depthwise conv1d + SiLU + L2 norm of q and k,
+ * over a packed batch, with the per-request conv history read and written in
+ * place (operator table, conv row; data-structure table, conv-history row).
+ *
+ *   x          [num_tokens, x_ld] in x_dt; row t holds the Cqkv conv inputs
+ *              q | k | v of token t in its first Cqkv entries.
+ *   conv_w     [Cqkv, taps] in w_dt; conv_w[c][i] multiplies x[t - i][c].
+ *              No bias.
+ *   conv_pool  [num_slots, Cqkv, taps-1] in pool_dt (== x_dt); read for the
+ *              first taps-1 tokens of each request (zeros if has_initial[r] is
+ *              0), then overwritten with the last taps-1 entries of the window
+ *              [history, request rows] — a bit-exact copy of inputs.
+ *   query_start_loc [num_reqs + 1] int32 (device), slot_ids [num_reqs] int32
+ *              (device), has_initial [num_reqs] uint8 (device; NULL = all 1).
+ *   l2_eps     q = q~ / sqrt(|q~|^2 + l2_eps) per (token, key head); same for k.
+ *   q, k       [num_tokens, Hk, d_k] in act_dt (outputs, normalised).
+ *   v          [num_tokens, Hv, d_v] in act_dt (output, SiLU'd conv output).
+ * num_tokens == 0 or num_reqs == 0 enqueues nothing.
+ * Alignment: x and conv_w 4-byte aligned, x_ld even; outputs 8-byte aligned.
+ */
+gdn_status gdn_conv1d_update(const gdn_dims *dims, const void *x, gdn_dtype x_dt,
+                             int64_t x_ld, const void *conv_w, gdn_dtype w_dt,
+                             void *conv_pool, gdn_dtype pool_dt,
+                             const int32_t *query_start_loc,
+                             const int32_t *slot_ids, const uint8_t *has_initial,
+                             int32_t num_reqs, int32_t num_tokens,
+                             int32_t num_slots, float l2_eps, void *q, void *k,
+                             void *v, gdn_dtype act_dt, void *stream);
+
+/*
+ * gdn_decode_step — one token per request of the gated delta rule, in place
+ * on the request's state slot (operator table, GDN row; the error is read from
+ * the decayed state, evidence-matrix row citing the Gated DeltaNet paper,
+ * eq. 10; decode cost O(Hv d_v d_k) independent of history length, section 01
+ * "why compress most layers").
+ *
+ *   q, k   [num_reqs, Hk, d_k] in act_dt (L2-normalised by the caller's conv).
+ *   v      [num_reqs, Hv, d_v] in act_dt.
+ *   a, b   [num_reqs, gate_ld] in gate_dt; entries [r][h] for h < Hv are the raw
+ *          projections: alpha = exp(-softplus(a)), beta = sigmoid(b).
+ *   state_pool [num_slots, Hv, d_v, d_k] fp32, slot slot_ids[r] read once and
+ *          written once: S' = alpha S + beta (v - alpha S k) k^T.
+ *   o      [num_reqs, Hv, d_v] in o_dt: o = S' q / sqrt(d_k).
+ * Alignment: state_pool 16-byte aligned; q, k 16-byte aligned when fp32,
+ * 8-byte when bf16.
+ */
+gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k,
+                           const void *v, gdn_dtype act_dt, const void *a,
+                           const void *b, gdn_dtype gate_dt, int64_t gate_ld,
+                           float *state_pool, const int32_t *slot_ids,
+                           int32_t num_reqs, int32_t num_slots, void *o,
+                           gdn_dtype o_dt, void *stream);
+
+/*
+ * gdn_prefill_workspace_bytes — device workspace gdn_prefill_varlen needs for
+ * a batch of at most num_tokens tokens in at most num_reqs requests.
+ * Returns 0 for unsupported dims.
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_tokens,
+                                   int32_t num_reqs);
+
+/*
+ * gdn_prefill_varlen — the gated delta rule over a packed batch of requests,
+ * computed chunkwise in parallel (section 01, LM-head worked example notes:
+ * the GDN block recurrence is parallelised through its associative
+ * structure).  Exactly the sequential recurrence of gdn_decode_step applied to
+ * every token of each request in order, up to rounding.
+ *
+ *   q, k   [num_tokens, Hk, d_k], v [num_tokens, Hv, d_v] in act_dt.
+ *   a, b   [num_tokens, gate_ld] raw gates in gate_dt (as gdn_decode_step).
+ *   state_pool [num_slots, Hv, d_v, d_k] fp32: request r starts from slot
+ *          slot_ids[r] (or from zero if has_initial[r] == 0; has_initial NULL
+ *          = all 1) and its final state is written back to the same slot.
+ *   query_start_loc [num_reqs+1], slot_ids [num_reqs] int32, has_initial
+ *          [num_reqs] uint8 — device.
+ *   o      [num_tokens, Hv, d_v] in o_dt.
+ *   workspace  device scratch of at least
+ *          gdn_prefill_workspace_bytes(dims, num_tokens, num_reqs) bytes,
+ *          256-byte aligned; contents on entry are ignored.
+ */
+gdn_status gdn_prefill_varlen(const gdn_dims *dims, const void *q,
+                              const void *k, const void *v, gdn_dtype act_dt,
+                              const void *a, const void *b, gdn_dtype gate_dt,
+                              int64_t gate_ld, float *state_pool,
+                              const int32_t *query_start_loc,
+                              const int32_t *slot_ids,
+                              const uint8_t *has_initial, int32_t num_reqs,
+                              int32_t num_tokens, int32_t num_slots, void *o,
+                              gdn_dtype o_dt, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_gated_norm — Ogate = RMSNorm(o) * SiLU(Z) (operator table, gated-output
+ * row: [T,48,128] -> [T,6144]; the GDN output gate is SiLU after RMSNorm,
+ * evidence-matrix row on output gates).  Per (token, value head) over d_v:
+ *   y[t][h*d_v + j] = o[t][h][j] / sqrt(mean_j o[t][h][j]^2 + eps) * gamma[j]
+ *                     * SiLU(z[t][h][j])
+ *   o      [num_tokens, Hv, d_v] in o_dt.
+ *   z      [num_tokens, z_ld] in z_dt; head h at columns h*d_v .. h*d_v+d_v-1.
+ *   gamma  [d_v] in gamma_dt, shared by all heads.
+ *   y      [num_tokens, Hv*d_v] in y_dt.
+ */
+gdn_status gdn_gated_norm(const gdn_dims *dims, const void *o, gdn_dtype o_dt,
+                          const void *z, gdn_dtype z_dt, int64_t z_ld,
+                          const void *gamma, gdn_dtype gamma_dt, float eps,
+                          int32_t num_tokens, void *y, gdn_dtype y_dt,
+                          void *stream);
+
+/*
+ * gdn_rmsnorm — U = X / sqrt(mean(X^2) + eps) * gamma per row (operator table,
+ * first row, [T,5120] -> [T,5120]).
+ *   x [rows, cols] in x_dt, gamma [cols] in gamma_dt, y [rows, cols] in y_dt.
+ *   cols must be a multiple of 8 and at most 16384.
+ */
+gdn_status gdn_rmsnorm(const void *x, gdn_dtype x_dt, const void *gamma,
+                       gdn_dtype gamma_dt, float eps, int32_t rows, int32_t cols,
+                       void *y, gdn_dtype y_dt, void *stream);
+
+/*
+ * gdn_gemm_bf16 — C[M,N] = A[M,K] * B[N,K]^T (+ R[M,N]) on bf16 operands with
+ * fp32 accumulation, rounded once to c_dt (operator table: the in-projection
+ * [Q0,K0,V0,Z] = U Wqkvz and a, b = U Wa, U Wb; and Delta_mix = Ogate Wo
+ * followed by the residual Y = X + Delta_mix when `residual` is non-NULL).
+ *   A [M, lda] bf16 row-major (activations).
+ *   B [N, ldb] bf16 row-major: the weight stored output-major (row n holds the
+ *     K inputs of output n), so both operands are contiguous along K.
+ *   C [M, ldc] in c_dt; residual [M, ldr] bf16 or NULL (C may not alias it).
+ *   K and N multiples of 8; lda, ldb, ldc, ldr multiples of 8 elements;
+ *   pointers 16-byte aligned.
+ */
+gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb,
+                         void *C, int64_t ldc, gdn_dtype c_dt,
+                         const void *residual, int64_t ldr, int32_t M,
+                         int32_t N, int32_t K, void *stream);
+
+/*
+ * gdn_validate_metadata — HOST-side check of host copies of the varlen
+ * metadata: qsl[0] == 0, qsl non-decreasing, qsl[num_reqs] == num_tokens,
+ * slot ids in range and distinct.  Enqueues nothing; GDN_ERR_METADATA on
+ * violation.
+ */
+gdn_status gdn_validate_metadata(const int32_t *query_start_loc_host,
+                                 const int32_t *slot_ids_host, int32_t num_reqs,
+                                 int32_t num_tokens, int32_t num_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/gdn.h, and rejects bad arguments on the host before any HIP
+call (every call here fails validation, so nothing is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_attention_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gdn.LIB_PATH),
+                                reason="libgdn.so not built (run __graft_entry__.build())")
+
+FULL = gdn.GdnDimsC(16, 48, 128, 128, 4)
+FAKE = 0x10000  # 64 KiB-aligned non-null address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = gdn.lib()
+    names = declared_functions()
+    assert "gdn_decode_step" in names and "gdn_prefill_varlen" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) <= set(gdn._SIGS), "binding is missing a declared entry point"
+
+
+def test_status_strings_and_version():
+    lib = gdn.lib()
+    for code in range(9):
+        assert lib.gdn_status_string(code).decode().startswith(gdn.STATUS[code])
+    assert b"gfx950" in lib.gdn_version()
+
+
+def dims(*v):
+    return gdn.GdnDimsC(*v)
+
+
+def decode_call(d, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, act=0, a=FAKE, b=FAKE, gdt=1, gld=48, state=FAKE,
+                slots=FAKE, R=4, nslots=8, o=FAKE, odt=0)
+    args.update(kw)
+    return gdn.lib().gdn_decode_step(
+        None if d is None else ctypes.byref(d), args["q"], args["k"], args["v"], args["act"],
+        args["a"], args["b"], args["gdt"], args["gld"], args["state"], args["slots"], args["R"],
+        args["nslots"], args["o"], args["odt"], None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (None, 1),
+    ((16, 48, 128, 128, 3), 2),     # conv taps
+    ((16, 40, 128, 128, 4), 2),     # Hv % Hk
+    ((16, 48, 128, 64, 4), 2),      # dk != dv
+    ((16, 48, 96, 96, 4), 2),       # unsupported head dim
+    ((0, 48, 128, 128, 4), 2),
+])
+def test_decode_rejects_bad_dims(bad, status):
+    d = None if bad is None else dims(*bad)
+    assert decode_call(d) == status
+
+
+def test_decode_rejects_bad_args():
+    assert decode_call(FULL, act=2) == 3
+    assert decode_call(FULL, R=-1) == 4
+    assert decode_call(FULL, R=9, nslots=8) == 4
+    assert decode_call(FULL, gld=47) == 4
+    assert decode_call(FULL, q=None) == 1
+    assert decode_call(FULL, state=None) == 1
+    assert decode_call(FULL, state=FAKE + 4) == 6
+    assert decode_call(FULL, q=FAKE + 8, act=0) == 6  # fp32 q needs 16 bytes
+    assert decode_call(FULL, R=0, q=None) == 0        # nothing to do, nothing enqueued
+
+
+def test_prefill_and_conv_reject_bad_args():
+    lib = gdn.lib()
+    P = FAKE
+
+    def prefill(**kw):
+        a = dict(T=10, R=2, nslots=4, qsl=P, ws=None, wsb=0, gld=48, act=1)
+        a.update(kw)
+        return lib.gdn_prefill_varlen(ctypes.byref(FULL), P, P, P, a["act"], P, P, 1, a["gld"], P,
+                                      a["qsl"], P, None, a["R"], a["T"], a["nslots"], P, 0, a["ws"],
+                                      a["wsb"], None)
+    assert prefill(T=10, R=0) == 4
+    assert prefill(R=5) == 4
+    assert prefill(qsl=None) == 1
+    assert prefill(gld=10) == 4
+    assert prefill(act=7) == 3
+    assert prefill(T=0) == 0
+
+    def conv(**kw):
+        a = dict(x=P, xdt=1, xld=10240, pdt=1, T=16, R=2, nslots=2, eps=1e-6, out=P)
+        a.update(kw)
+        return lib.gdn_conv1d_update(ctypes.byref(FULL), a["x"], a["xdt"], a["xld"], P, 1, P,
+                                     a["pdt"], P, P, None, a["R"], a["T"], a["nslots"], a["eps"],
+                                     a["out"], P, P, 0, None)
+    assert conv(pdt=0) == 3               # pool dtype must equal x dtype
+    assert conv(xld=10000) == 4           # row stride shorter than Cqkv
+    assert conv(R=3) == 4                 # more requests than slots
+    assert conv(x=None) == 1
+    assert conv(x=P + 2) == 6             # bf16 pairs need 4-byte alignment
+    assert conv(xld=10241) == 6           # odd row stride breaks pair alignment
+    assert conv(eps=float("nan")) == 4
+    assert conv(T=0) == 0
+
+
+def test_norm_and_gemm_reject_bad_args():
+    lib = gdn.lib()
+    P = FAKE
+    assert lib.gdn_gated_norm(ctypes.byref(FULL), P, 0, P, 1, 6000, P, 1, 1e-6, 4, P, 1, None) == 4
+    assert lib.gdn_gated_norm(ctypes.byref(FULL), P, 0, P, 1, 6144, P, 1, 1e-6, 4, None, 1, None) == 1
+    assert lib.gdn_rmsnorm(P, 1, P, 1, 1e-6, 4, 5121, P, 1, None) == 4
+    assert lib.gdn_rmsnorm(P, 1, P, 1, 1e-6, 4, 5120, P + 8, 1, None) == 6
+    assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 64, 0, None, 0, 10, 64, 60, None) == 4   # K % 8
+    assert lib.gdn_gemm_bf16(P, 32, P, 64, P, 64, 0, None, 0, 10, 64, 64, None) == 4   # lda < K
+    assert lib.gdn_gemm_bf16(None, 64, P, 64, P, 64, 0, None, 0, 10, 64, 64, None) == 1
+    assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 64, 0, None, 0, 0, 64, 64, None) == 0
+
+
+def test_workspace_query():
+    assert gdn.gdn_prefill_workspace_bytes((16, 48, 128, 128, 3), 100, 2) == 0
+    n = gdn.gdn_prefill_workspace_bytes(FULL, 70000, 16)
+    assert n >= 0
+
+
+def test_validate_metadata_host():
+    ok = gdn.gdn_validate_metadata(torch.tensor([0, 3, 3, 7]), torch.tensor([5, 0, 2]), 7, 6)
+    assert ok == 0
+    assert gdn.gdn_validate_metadata(torch.tensor([1, 3, 7]), torch.tensor([0, 1]), 7, 6) == 8
+    assert gdn.gdn_validate_metadata(torch.tensor([0, 4, 3]), torch.tensor([0, 1]), 3, 6) == 8
+    assert gdn.gdn_validate_metadata(torch.tensor([0, 3, 7]), torch.tensor([0, 0]), 7, 6) == 8
+    assert gdn.gdn_validate_metadata(torch.tensor([0, 3, 7]), torch.tensor([0, 6]), 7, 6) == 8
+    assert gdn.gdn_validate_metadata(torch.tensor([0, 3, 6]), torch.tensor([0, 1]), 7, 6) == 8
+    assert gdn.gdn_validate_metadata(torch.tensor([0]), torch.tensor([], dtype=torch.int32), 0, 0) == 0
+    rng = np.random.default_rng(0)
+    perm = torch.from_numpy(rng.permutation(100000)[:50].astype(np.int32))
+    qsl = torch.arange(51, dtype=torch.int32)
+    assert gdn.gdn_validate_metadata(qsl, perm, 50, 100000) == 0
+    perm[7] = perm[3]
+    assert gdn.gdn_validate_metadata(qsl, perm, 50, 100000) == 8
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        gdn.gdn_rmsnorm(torch.zeros(4, 8), torch.ones(8), x.new_zeros(4, 8))

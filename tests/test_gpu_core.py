@@ -1,0 +1,326 @@
+"""GPU parity of the conv, decode, gated-norm and prefill entry points against
+the fp64 oracle, called through the C ABI on seeded inputs.
+
+Per-call parity feeds each oracle stage the exact values the GPU stage
+received; chained runs feed the oracle the original inputs and compare the
+end of the chain.  Conv history and slot placement are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import FP32_TOL, OUT_TOL, STATE_TOL, bf16_ulp_ok, bits, dev, f64, rel_l2
+from hybrid_linear_attention_amd import gdn
+from hybrid_linear_attention_amd.workloads import (FULL_DIMS, TINY_DIMS, GdnDims, decode_r64,
+                                                   make_gdn_case, tiny_core)
+
+pytestmark = pytest.mark.gpu
+
+L2_EPS = 1e-6
+NORM_EPS = 1e-6
+
+
+def dims_t(d):
+    return (d.num_k_heads, d.num_v_heads, d.head_dim_k, d.head_dim_v, d.conv_taps)
+
+
+def run_conv_gpu(case, act_dtype=torch.float32):
+    d = case.dims
+    T = case.num_tokens
+    q = torch.empty((T, d.num_k_heads, d.head_dim_k), dtype=act_dtype, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, d.num_v_heads, d.head_dim_v), dtype=act_dtype, device="cuda")
+    pool = dev(case.conv_pool)
+    gdn.gdn_conv1d_update(d, dev(case.x_qkv), dev(case.conv_w), pool, dev(case.qsl),
+                          dev(case.slot_ids), dev(case.has_initial), q, k, v, l2_eps=L2_EPS)
+    return q, k, v, pool
+
+
+def oracle_conv(case):
+    d = case.dims
+    return oracle.conv1d_update(f64(case.x_qkv), f64(case.conv_w), f64(case.conv_pool),
+                                case.qsl.numpy(), case.slot_ids.numpy(), case.has_initial.numpy(),
+                                d.num_k_heads, d.num_v_heads, d.head_dim_k, d.head_dim_v, L2_EPS)
+
+
+def check_pool(case, got_pool, ref_pool):
+    """Used slots: bit-exact against the oracle's history; unused: bits unchanged."""
+    gb = bits(got_pool)
+    ib = bits(case.conv_pool)
+    used = set(int(s) for s in case.slot_ids)
+    for s in range(case.num_slots):
+        if s in used:
+            ref = torch.from_numpy(ref_pool[s]).to(case.conv_pool.dtype)
+            np.testing.assert_array_equal(gb[s], bits(ref), err_msg=f"history slot {s}")
+        else:
+            np.testing.assert_array_equal(gb[s], ib[s], err_msg=f"unused slot {s} touched")
+
+
+def varlen_case(seed, D=128, Hk=2, Hv=6, lengths=(1, 2, 5, 37, 0, 130, 3), num_slots=10,
+                dtype=torch.bfloat16, state_std=0.02, hist_std=1.0, mixed_init=True):
+    c = make_gdn_case(seed, GdnDims(Hk, Hv, D, D, 4), list(lengths), num_slots=num_slots,
+                      permute_slots=True, act_dtype=dtype, state_std=state_std,
+                      hist_std=hist_std)
+    if mixed_init:
+        c.has_initial = torch.tensor([(r % 3) != 1 for r in range(c.num_reqs)], dtype=torch.uint8)
+    return c
+
+
+# ---------------------------------------------------------------------------
+# conv1d + SiLU + L2 norm
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("which", ["tiny", "varlen_bf16", "varlen_f32_d16", "decode_r64"])
+def test_conv_parity(which):
+    if which == "tiny":
+        case = tiny_core()
+    elif which == "varlen_bf16":
+        case = varlen_case(11)
+    elif which == "varlen_f32_d16":
+        case = varlen_case(12, D=16, Hk=3, Hv=6, dtype=torch.float32)
+    else:
+        case = decode_r64()
+    q, k, v, pool = run_conv_gpu(case)
+    qr, kr, vr, pr = oracle_conv(case)
+    for name, got, ref in (("q", q, qr), ("k", k, kr), ("v", v, vr)):
+        err = rel_l2(f64(got), ref)
+        assert err <= FP32_TOL, f"{which} {name} rel-L2 {err:.3e}"
+    check_pool(case, pool, pr)
+
+
+def test_conv_bf16_outputs_round_once():
+    case = varlen_case(13)
+    q, k, v, _ = run_conv_gpu(case, act_dtype=torch.bfloat16)
+    qr, kr, vr, _ = oracle_conv(case)
+    for got, ref in ((q, qr), (k, kr), (v, vr)):
+        assert bf16_ulp_ok(got, ref, ulps=1)
+
+
+def test_conv_strided_input_rows():
+    """x as a column slice of a wider row (the in-projection's q|k|v|z output)."""
+    case = varlen_case(14, lengths=(3, 9, 1))
+    d = case.dims
+    C = d.conv_channels
+    wide = torch.randn(case.num_tokens, C + 40, dtype=case.x_qkv.dtype)
+    wide[:, :C] = case.x_qkv
+    T = case.num_tokens
+    q = torch.empty((T, d.num_k_heads, d.head_dim_k), device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, d.num_v_heads, d.head_dim_v), device="cuda")
+    pool = dev(case.conv_pool)
+    gdn.gdn_conv1d_update(d, dev(wide)[:, :C], dev(case.conv_w), pool, dev(case.qsl),
+                          dev(case.slot_ids), dev(case.has_initial), q, k, v, l2_eps=L2_EPS)
+    qr, kr, vr, pr = oracle_conv(case)
+    assert rel_l2(f64(v), vr) <= FP32_TOL and rel_l2(f64(q), qr) <= FP32_TOL
+    check_pool(case, pool, pr)
+
+
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+def run_decode_gpu(d, q, k, v, a, b, state_pool, slot_ids, o_dtype=torch.float32):
+    o = torch.empty((q.shape[0], d.num_v_heads, d.head_dim_v), dtype=o_dtype, device="cuda")
+    gdn.gdn_decode_step(d, q, k, v, a, b, state_pool, slot_ids, o)
+    return o
+
+
+@pytest.mark.parametrize("D,Hk,Hv,R,nslots", [(128, 16, 48, 64, 64), (128, 2, 6, 5, 9),
+                                              (16, 2, 6, 7, 7), (32, 1, 2, 3, 8),
+                                              (64, 4, 4, 33, 40)])
+def test_decode_step_parity(D, Hk, Hv, R, nslots):
+    """Per-call parity: the oracle gets the exact q/k/v/a/b the kernel got."""
+    rng = np.random.default_rng(D * 1000 + R)
+    d = GdnDims(Hk, Hv, D, D, 4)
+    q = torch.from_numpy(oracle.l2norm(rng.standard_normal((R, Hk, D)), 0)).float()
+    k = torch.from_numpy(oracle.l2norm(rng.standard_normal((R, Hk, D)), 0)).float()
+    v = torch.from_numpy(rng.standard_normal((R, Hv, D))).float()
+    a = torch.from_numpy(rng.standard_normal((R, Hv))).to(torch.bfloat16)
+    b = torch.from_numpy(rng.standard_normal((R, Hv))).to(torch.bfloat16)
+    pool = torch.from_numpy(rng.standard_normal((nslots, Hv, D, D)) * 0.02).float()
+    slots = torch.from_numpy(rng.permutation(nslots)[:R].astype(np.int32))
+    gpool = dev(pool)
+    o = run_decode_gpu(d, dev(q), dev(k), dev(v), dev(a), dev(b), gpool, dev(slots))
+    o_ref, pool_ref = oracle.decode_step(f64(q), f64(k), f64(v), f64(a), f64(b), f64(pool),
+                                         slots.numpy())
+    assert rel_l2(f64(o), o_ref) <= 1e-5
+    assert rel_l2(f64(gpool), pool_ref) <= 1e-6
+    unused = sorted(set(range(nslots)) - set(slots.tolist()))
+    if unused:
+        np.testing.assert_array_equal(bits(gpool)[unused], bits(pool)[unused])
+
+
+def test_decode_bf16_inputs_and_output():
+    rng = np.random.default_rng(5)
+    R, Hk, Hv, D = 8, 2, 6, 128
+    d = GdnDims(Hk, Hv, D, D, 4)
+    q = torch.from_numpy(oracle.l2norm(rng.standard_normal((R, Hk, D)), 0)).to(torch.bfloat16)
+    k = torch.from_numpy(oracle.l2norm(rng.standard_normal((R, Hk, D)), 0)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((R, Hv, D))).to(torch.bfloat16)
+    ab = torch.from_numpy(rng.standard_normal((R, 2 * Hv + 4))).float()
+    a, b = ab[:, :Hv], ab[:, Hv:2 * Hv]  # strided gate views (gate_ld = 2*Hv + 4)
+    pool = torch.from_numpy(rng.standard_normal((R, Hv, D, D)) * 0.02).float()
+    slots = torch.arange(R, dtype=torch.int32)
+    gab = dev(ab)
+    gpool = dev(pool)
+    o = run_decode_gpu(d, dev(q), dev(k), dev(v), gab[:, :Hv], gab[:, Hv:2 * Hv], gpool,
+                       dev(slots), o_dtype=torch.bfloat16)
+    o_ref, pool_ref = oracle.decode_step(f64(q), f64(k), f64(v), f64(a), f64(b), f64(pool),
+                                         slots.numpy())
+    assert bf16_ulp_ok(o, o_ref, ulps=1)
+    assert rel_l2(f64(gpool), pool_ref) <= 1e-6
+
+
+def test_decode_chain_full_size():
+    """Full-size decode step as a chain: conv1d_update -> decode_step -> gated_norm
+    on 64 requests x 48 value heads, against the oracle fed the original inputs."""
+    case = decode_r64()
+    d = case.dims
+    q, k, v, pool = run_conv_gpu(case)
+    state = dev(case.state_pool)
+    o = run_decode_gpu(d, q, k, v, dev(case.a), dev(case.b), state, dev(case.slot_ids))
+    y = torch.empty((case.num_tokens, d.num_v_heads * d.head_dim_v), dtype=torch.bfloat16,
+                    device="cuda")
+    gdn.gdn_gated_norm(d, o, dev(case.z), dev(case.gamma), y, eps=NORM_EPS)
+    qr, kr, vr, pr = oracle_conv(case)
+    o_ref, st_ref = oracle.decode_step(qr, kr, vr, f64(case.a), f64(case.b), f64(case.state_pool),
+                                       case.slot_ids.numpy())
+    y_ref = oracle.gated_norm(o_ref, f64(case.z), f64(case.gamma), NORM_EPS)
+    e_o, e_s, e_y = rel_l2(f64(o), o_ref), rel_l2(f64(state), st_ref), rel_l2(f64(y), y_ref)
+    print(f"decode chain rel-L2: o {e_o:.2e} state {e_s:.2e} y {e_y:.2e}")
+    assert e_o <= OUT_TOL and e_s <= STATE_TOL and e_y <= OUT_TOL
+    check_pool(case, pool, pr)
+
+
+def test_tiny_core_as_decode_steps():
+    """The tiny workload (T=64, fp32) run as 64 single-token steps (conv then decode)
+    against the oracle's whole-sequence result."""
+    case = tiny_core()
+    d = case.dims
+    pool = dev(case.conv_pool)
+    state = dev(case.state_pool)
+    x = dev(case.x_qkv)
+    a, b = dev(case.a), dev(case.b)
+    qsl1 = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    slot = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hi = torch.ones(1, dtype=torch.uint8, device="cuda")
+    outs = []
+    for t in range(case.num_tokens):
+        q = torch.empty((1, d.num_k_heads, d.head_dim_k), device="cuda")
+        k = torch.empty_like(q)
+        v = torch.empty((1, d.num_v_heads, d.head_dim_v), device="cuda")
+        gdn.gdn_conv1d_update(d, x[t:t + 1], dev(case.conv_w), pool, qsl1, slot, hi, q, k, v,
+                              l2_eps=L2_EPS)
+        outs.append(run_decode_gpu(d, q, k, v, a[t:t + 1], b[t:t + 1], state, slot))
+    o = torch.cat(outs)
+    qr, kr, vr, pr = oracle_conv(case)
+    o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
+                                            f64(case.state_pool), case.qsl.numpy(),
+                                            case.slot_ids.numpy(), case.has_initial.numpy())
+    assert rel_l2(f64(o), o_ref) <= 1e-5
+    assert rel_l2(f64(state), st_ref) <= 1e-5
+    check_pool(case, pool, pr)
+
+
+# ---------------------------------------------------------------------------
+# gated RMSNorm
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D,Hv,T,odt,ydt", [(128, 48, 37, torch.float32, torch.bfloat16),
+                                            (16, 6, 64, torch.float32, torch.float32),
+                                            (64, 5, 3, torch.bfloat16, torch.float32)])
+def test_gated_norm_parity(D, Hv, T, odt, ydt):
+    rng = np.random.default_rng(D + T)
+    d = GdnDims(1, Hv, D, D, 4)
+    o = torch.from_numpy(rng.standard_normal((T, Hv, D)) * rng.uniform(0.01, 3, (T, Hv, 1))).to(odt)
+    zw = torch.from_numpy(rng.standard_normal((T, Hv * D + 16))).to(torch.bfloat16)
+    z = zw[:, 8:8 + Hv * D]  # strided view, z_ld = Hv*D + 16
+    g = torch.from_numpy(1 + 0.1 * rng.standard_normal(D)).to(torch.bfloat16)
+    y = torch.empty((T, Hv * D), dtype=ydt, device="cuda")
+    gdn.gdn_gated_norm(d, dev(o), dev(zw)[:, 8:8 + Hv * D], dev(g), y, eps=NORM_EPS)
+    y_ref = oracle.gated_norm(f64(o), f64(z).reshape(T, Hv, D), f64(g), NORM_EPS)
+    if ydt == torch.bfloat16:
+        assert bf16_ulp_ok(y, y_ref, ulps=1)
+    else:
+        assert rel_l2(f64(y), y_ref) <= FP32_TOL
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def run_prefill_gpu(case, q, k, v, state, o_dtype=torch.float32):
+    d = case.dims
+    o = torch.empty((case.num_tokens, d.num_v_heads, d.head_dim_v), dtype=o_dtype, device="cuda")
+    nbytes = gdn.gdn_prefill_workspace_bytes(d, case.num_tokens, case.num_reqs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+    gdn.gdn_prefill_varlen(d, q, k, v, dev(case.a), dev(case.b), state, dev(case.qsl),
+                           dev(case.slot_ids), dev(case.has_initial), o, ws)
+    return o
+
+
+def check_states(case, got_state, ref_state, tol):
+    used = [int(s) for s, L in zip(case.slot_ids, np.diff(case.qsl.numpy()))]
+    touched = [int(s) for s, L in zip(case.slot_ids, np.diff(case.qsl.numpy())) if L > 0]
+    g = f64(got_state)
+    if touched:
+        err = rel_l2(g[touched], ref_state[touched])
+        assert err <= tol, f"state rel-L2 {err:.3e}"
+    untouched = sorted(set(range(case.num_slots)) - set(touched))
+    if untouched:
+        np.testing.assert_array_equal(bits(got_state)[untouched], bits(case.state_pool)[untouched])
+    return used
+
+
+@pytest.mark.parametrize("which", ["tiny", "varlen_d128", "varlen_d32"])
+def test_prefill_chain_parity(which):
+    if which == "tiny":
+        case = tiny_core()
+    elif which == "varlen_d128":
+        case = varlen_case(21, lengths=(1, 64, 65, 130, 0, 7, 200))
+    else:
+        case = varlen_case(22, D=32, Hk=2, Hv=4, lengths=(70, 1, 0, 129), num_slots=6)
+    q, k, v, pool = run_conv_gpu(case)
+    state = dev(case.state_pool)
+    o = run_prefill_gpu(case, q, k, v, state)
+    qr, kr, vr, pr = oracle_conv(case)
+    o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
+                                            f64(case.state_pool), case.qsl.numpy(),
+                                            case.slot_ids.numpy(), case.has_initial.numpy())
+    e_o = rel_l2(f64(o), o_ref)
+    print(f"{which}: o rel-L2 {e_o:.2e}")
+    assert e_o <= OUT_TOL
+    check_states(case, state, st_ref, STATE_TOL)
+    check_pool(case, pool, pr)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and GEMM (layer-block stages)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols,ydt", [(37, 5120, torch.bfloat16), (5, 136, torch.float32)])
+def test_rmsnorm_parity(rows, cols, ydt):
+    rng = np.random.default_rng(cols)
+    x = torch.from_numpy(rng.standard_normal((rows, cols))).to(torch.bfloat16)
+    g = torch.from_numpy(1 + 0.02 * rng.standard_normal(cols)).to(torch.bfloat16)
+    y = torch.empty((rows, cols), dtype=ydt, device="cuda")
+    gdn.gdn_rmsnorm(dev(x), dev(g), y, eps=NORM_EPS)
+    ref = oracle.rmsnorm(f64(x), f64(g), NORM_EPS)
+    if ydt == torch.bfloat16:
+        assert bf16_ulp_ok(y, ref, ulps=1)
+    else:
+        assert rel_l2(f64(y), ref) <= FP32_TOL
+
+
+@pytest.mark.parametrize("M,N,K,res", [(300, 200, 5120, False), (129, 136, 264, True),
+                                       (1, 8, 8, False), (256, 96, 5120, True)])
+def test_gemm_parity(M, N, K, res):
+    rng = np.random.default_rng(M + N + K)
+    A = torch.from_numpy(rng.standard_normal((M, K))).to(torch.bfloat16)
+    B = torch.from_numpy(rng.standard_normal((N, K)) * 0.02).to(torch.bfloat16)
+    R = torch.from_numpy(rng.standard_normal((M, N))).to(torch.bfloat16) if res else None
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    gdn.gdn_gemm_bf16(dev(A), dev(B), C, residual=dev(R) if res else None)
+    ref = oracle.linear(f64(A), f64(B).T)
+    if res:
+        ref = oracle.residual_add(f64(R), ref)
+    assert rel_l2(f64(C), ref) <= FP32_TOL
+    Cb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_gemm_bf16(dev(A), dev(B), Cb, residual=dev(R) if res else None)
+    assert bf16_ulp_ok(Cb, ref, ulps=1)
