@@ -1,0 +1,315 @@
+"""Benchmark of the GDN mixer core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+
+Headline workload (N=1): one decode step of 64 requests at full shapes (16 key /
+48 value heads, d = 128, fp32 state [64,48,128,128]): conv1d_update ->
+decode_step -> gated_norm, with every input already resident in HBM.  `value`
+is the state bytes each step reads and writes (2 x 64 x 3 MiB) divided by the
+measured step time.  A prefill leg (single 4096-token sequence; 16-request
+packed varlen batch) reports tokens/s in the same run, and the fp64 CPU oracle
+is timed on a bounded sample on the host cores.
+
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("GDN prefill tokens/s + decode state GB/s vs HBM peak "
+          "(48×128×128 fp32 state)")
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+NORM_EPS = 1e-6
+L2_EPS = 1e-6
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-varlen", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-ref-mib", type=int, default=0,
+                   help="after the benchmark, run plain device copies of this many MiB "
+                        "(a known-size reference for the HBM byte counters)")
+    return p.parse_args()
+
+
+def decode_bytes(d, R, act_bytes=4, o_bytes=4):
+    """Algorithmic HBM bytes of one decode_step launch: the state read and
+    written once, q/k/v/a/b read once, o written once."""
+    D = d.head_dim_k
+    state = 2 * R * d.num_v_heads * D * D * 4
+    qkv = R * (2 * d.num_k_heads + d.num_v_heads) * D * act_bytes
+    gates = 2 * R * d.num_v_heads * 2
+    o = R * d.num_v_heads * D * o_bytes
+    return state, state + qkv + gates + o
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from hybrid_linear_attention_amd import gdn
+    from hybrid_linear_attention_amd.workloads import decode_r64, prefill_4096, prefill_varlen16
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gdn.lib()
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ decode
+    case = decode_r64()
+    d = case.dims
+    R = case.num_reqs
+    D = d.head_dim_k
+    x = case.x_qkv.to(dev)
+    conv_w = case.conv_w.to(dev)
+    # Three layers' worth of caches, used in turn: a model's GDN layers each own
+    # a state pool, so a layer's state is never still resident in the 256 MB
+    # memory-side cache when its next decode step comes round.
+    n_rot = 3
+    conv_pools = [case.conv_pool.to(dev) for _ in range(n_rot)]
+    states = [case.state_pool.to(dev) for _ in range(n_rot)]
+    qsl = case.qsl.to(dev)
+    slots = case.slot_ids.to(dev)
+    hinit = case.has_initial.to(dev)
+    a, b, z, gamma = case.a.to(dev), case.b.to(dev), case.z.to(dev), case.gamma.to(dev)
+    q = torch.empty((R, d.num_k_heads, D), device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((R, d.num_v_heads, D), device=dev)
+    o = torch.empty((R, d.num_v_heads, D), device=dev)
+    y = torch.empty((R, d.num_v_heads * D), dtype=torch.bfloat16, device=dev)
+
+    ev = {n: [] for n in ("conv", "decode", "norm")}
+
+    it_count = [0]
+
+    def decode_step(record):
+        conv_pool = conv_pools[it_count[0] % n_rot]
+        state = states[it_count[0] % n_rot]
+        it_count[0] += 1
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        gdn.gdn_conv1d_update(d, x, conv_w, conv_pool, qsl, slots, hinit, q, k, v, l2_eps=L2_EPS)
+        if record:
+            e[1].record(stream)
+        gdn.gdn_decode_step(d, q, k, v, a, b, state, slots, o)
+        if record:
+            e[2].record(stream)
+        gdn.gdn_gated_norm(d, o, z, gamma, y, eps=NORM_EPS)
+        if record:
+            e[3].record(stream)
+            ev["conv"].append((e[0], e[1]))
+            ev["decode"].append((e[1], e[2]))
+            ev["norm"].append((e[2], e[3]))
+
+    for _ in range(args.warmup):
+        decode_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        decode_step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = {n: float(np.mean([s.elapsed_time(e) for s, e in ev[n]])) for n in ev}
+    state_bytes, dec_bytes = decode_bytes(d, R)
+    value = state_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (kern_ms["decode"] * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_r64: 64 requests x 1 token; 16 key / 48 value heads; "
+                        "d_k = d_v = 128; fp32 state [64,48,128,128]; bf16 inputs",
+            "step": "gdn_conv1d_update + gdn_decode_step + gdn_gated_norm",
+            "state_bytes_per_step": state_bytes,
+            "state_pools_rotated": n_rot,
+        },
+        "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "roofline": {
+            "kernel": "decode_kernel (gdn_decode_step)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": dec_bytes,
+            "traffic": None,
+        },
+    }
+    del states, conv_pools
+    torch.cuda.empty_cache()
+
+    # ----------------------------------------------------------------- prefill
+    if not args.no_prefill:
+        legs = [("prefill_4096", prefill_4096)]
+        if not args.no_varlen:
+            legs.append(("prefill_varlen16", prefill_varlen16))
+        pre = {}
+        for name, make in legs:
+            c = make()
+            pre[name] = bench_prefill(c, args.prefill_steps, dev, stream, torch, gdn, np)
+            del c
+            torch.cuda.empty_cache()
+        result["prefill"] = pre
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+
+    if args.copy_ref_mib > 0:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_ref_bytes"] = {"read": n * 4, "write": n * 4, "launches": 3}
+
+    print(json.dumps(result), flush=True)
+
+
+def prefill_flops(d, T, chunk=64):
+    """Algorithmic flops of the chunkwise gated delta rule over T tokens at
+    chunk length C: per token and value head 6 d_k d_v (K S0^T, Q S0^T and the
+    state update) + C (2 d_k + 4 d_v) (the triangular solve applied to V and K,
+    and P Delta) + C^2 / 3 (forming T), plus per key head 4 C d_k (K K^T and
+    Q K^T).  7.67 MFLOP per token at 16/48 heads, d = 128, C = 64."""
+    Dk, Dv = d.head_dim_k, d.head_dim_v
+    per_tok = (d.num_v_heads * (6 * Dk * Dv + chunk * (2 * Dk + 4 * Dv) + chunk * chunk / 3)
+               + d.num_k_heads * 4 * chunk * Dk)
+    return float(per_tok * T)
+
+
+def bench_prefill(c, steps, dev, stream, torch, gdn, np):
+    """conv1d_update -> prefill_varlen -> gated_norm over one packed batch.
+    State and history are re-seeded from device copies before every step (the
+    copies run outside the timed events)."""
+    d = c.dims
+    T = c.num_tokens
+    D = d.head_dim_k
+    x = c.x_qkv.to(dev)
+    conv_w = c.conv_w.to(dev)
+    pool0 = c.conv_pool.to(dev)
+    state0 = c.state_pool.to(dev)
+    pool = pool0.clone()
+    state = state0.clone()
+    qsl, slots, hinit = c.qsl.to(dev), c.slot_ids.to(dev), c.has_initial.to(dev)
+    a, b, z, gamma = c.a.to(dev), c.b.to(dev), c.z.to(dev), c.gamma.to(dev)
+    q = torch.empty((T, d.num_k_heads, D), device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((T, d.num_v_heads, D), device=dev)
+    o = torch.empty((T, d.num_v_heads, D), device=dev)
+    y = torch.empty((T, d.num_v_heads * D), dtype=torch.bfloat16, device=dev)
+    nbytes = gdn.gdn_prefill_workspace_bytes(d, T, c.num_reqs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    times, ktimes = [], []
+    for it in range(steps + 1):
+        pool.copy_(pool0)
+        state.copy_(state0)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        gdn.gdn_conv1d_update(d, x, conv_w, pool, qsl, slots, hinit, q, k, v, l2_eps=L2_EPS)
+        e[1].record(stream)
+        gdn.gdn_prefill_varlen(d, q, k, v, a, b, state, qsl, slots, hinit, o, ws)
+        e[2].record(stream)
+        gdn.gdn_gated_norm(d, o, z, gamma, y, eps=NORM_EPS)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if it > 0:  # first pass is warm-up
+            times.append(e[0].elapsed_time(e[3]))
+            ktimes.append(e[1].elapsed_time(e[2]))
+    ms = float(np.median(times))
+    kms = float(np.median(ktimes))
+    flops = prefill_flops(d, T)
+    return {
+        "roofline": {
+            "kernel": "prefill_chunk_kernel (gdn_prefill_varlen)",
+            "bound": "mfma",
+            "achieved": round(flops / (kms * 1e-3) / 1e12, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops,
+            "traffic": None,
+        },
+        "tokens": T,
+        "requests": c.num_reqs,
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "prefill_kernel_ms": round(kms, 4),
+        "prefill_kernel_tokens_per_s": round(T / (kms * 1e-3), 1),
+    }
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle (conv1d_update -> decode_step -> gated_norm) on the same
+    decode workload, repeated until ~`seconds` of CPU time have passed."""
+    import oracle
+    import numpy as np
+
+    d = case.dims
+
+    def f64(t):
+        return t.double().numpy()
+
+    x, w, hist = f64(case.x_qkv), f64(case.conv_w), f64(case.conv_pool)
+    st = f64(case.state_pool)
+    a, b, z, g = f64(case.a), f64(case.b), f64(case.z), f64(case.gamma)
+    qsl, slots, hi = case.qsl.numpy(), case.slot_ids.numpy(), case.has_initial.numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        qq, kk, vv, hist = oracle.conv1d_update(x, w, hist, qsl, slots, hi, d.num_k_heads,
+                                                d.num_v_heads, d.head_dim_k, d.head_dim_v, L2_EPS)
+        o, st = oracle.decode_step(qq, kk, vv, a, b, st, slots)
+        oracle.gated_norm(o, z, g, NORM_EPS)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    state_bytes = 2 * case.num_reqs * d.num_v_heads * d.head_dim_k * d.head_dim_v * 4
+    return {
+        "value": round(state_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{reps} full decode steps of the same 64-request workload "
+                  f"(conv + recurrence + gated norm, fp64) in {el:.1f} s; "
+                  f"state bytes counted as fp32, as on the GPU",
+        "ms_per_step": round(el * 1e3 / reps, 2),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -12,9 +12,12 @@
 //     read as 4-byte pairs and a 128-wide head is one wave-local reduction);
 //   * a block of 4 waves owns 512 channels for a tile of consecutive tokens,
 //     sliding the 3-entry window in registers across the tile;
-//   * the first tokens of each request read that request's history slot; the
-//     history write-back is a second, stream-ordered kernel, so no thread can
-//     overwrite a slot another thread has yet to read.
+//   * only a request's first three tokens read its history slot, so those three
+//     tokens always belong to the block whose tile holds the request's first
+//     token (a tile may run up to two tokens past its end to keep them).  That
+//     block, after its tokens, writes the request's new history: the thread that
+//     read a history entry is the only one that ever writes it, so one launch
+//     is race-free without any grid-wide ordering.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -24,19 +27,25 @@ constexpr int CONV_WAVES = 4;
 constexpr int CONV_CH_PER_WAVE = 128;
 constexpr int CONV_CH_PER_BLOCK = CONV_WAVES * CONV_CH_PER_WAVE;
 
+// Request holding token t: a direct guess (decode batches have request t at
+// token t), else a binary search.
+__device__ __forceinline__ int locate_request(const int32_t *__restrict__ qsl, int n, int t) {
+    if (t < n && qsl[t] <= t && t < qsl[t + 1]) return t;
+    return find_request(qsl, n, t);
+}
+
 template <int D, typename TX, typename TW, typename TO>
 __global__ __launch_bounds__(256) void conv1d_silu_l2_kernel(
-    const TX *__restrict__ x, int64_t x_ld, const TW *__restrict__ w,
-    const TX *__restrict__ pool, const int32_t *__restrict__ qsl,
-    const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
-    int32_t nreq, int32_t T, int32_t C, int32_t nq, int32_t tile, float l2_eps,
-    TO *__restrict__ q, TO *__restrict__ k, TO *__restrict__ v) {
+    const TX *__restrict__ x, int64_t x_ld, const TW *__restrict__ w, TX *__restrict__ pool,
+    const int32_t *__restrict__ qsl, const int32_t *__restrict__ slots,
+    const uint8_t *__restrict__ has_init, int32_t nreq, int32_t T, int32_t C, int32_t nq,
+    int32_t tile, float l2_eps, TO *__restrict__ q, TO *__restrict__ k, TO *__restrict__ v) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = (blockIdx.y * CONV_WAVES + wave) * CONV_CH_PER_WAVE + 2 * lane;
     const bool active = c < C;  // C is a multiple of D >= 16, so pairs never straddle C
     const int t_begin = blockIdx.x * tile;
-    const int t_end = min(T, t_begin + tile);
+    const int t_nom_end = min(T, t_begin + tile);
     const int nqk = 2 * nq;
     const int nv = C - nqk;
 
@@ -48,13 +57,20 @@ __global__ __launch_bounds__(256) void conv1d_silu_l2_kernel(
         w1[i] = active ? ld(w + (int64_t)(c + 1) * 4 + i) : 0.f;
     }
 
+    const int r_first = locate_request(qsl, nreq, t_begin);
     float2 h3 = make_float2(0.f, 0.f), h2 = h3, h1 = h3;  // x_{t-3}, x_{t-2}, x_{t-1}
-    int r = -1;
-    for (int t = t_begin; t < t_end; ++t) {
-        if (r < 0 || t >= qsl[r + 1]) r = find_request(qsl, nreq, t);
+    bool have_window = false;
+    int r = r_first;
+    for (int t = t_begin; t < T; ++t) {
+        while (t >= qsl[r + 1]) ++r;  // skips empty requests too
         const int p = t - qsl[r];
+        if (t >= t_nom_end && (p == 0 || p >= 3)) break;          // past the tile
+        if (p >= 1 && p <= 2 && t - p < t_begin) {                // owned by an earlier tile
+            have_window = false;
+            continue;
+        }
         float2 x0 = active ? ld2(x + (int64_t)t * x_ld + c) : make_float2(0.f, 0.f);
-        if (t == t_begin || p == 0) {
+        if (!have_window || p == 0) {
             // (re)build the window from the request's own rows and history
             const bool hi = has_init == nullptr || has_init[r] != 0;
             const int64_t hbase = ((int64_t)slots[r] * C + c) * 3;
@@ -73,13 +89,14 @@ __global__ __launch_bounds__(256) void conv1d_silu_l2_kernel(
                 hw[3 - lag] = val;
             }
             h3 = hw[0]; h2 = hw[1]; h1 = hw[2];
+            have_window = true;
         }
         float y0 = w0[0] * x0.x + w0[1] * h1.x + w0[2] * h2.x + w0[3] * h3.x;
         float y1 = w1[0] * x0.y + w1[1] * h1.y + w1[2] * h2.y + w1[3] * h3.y;
         y0 = silu_f(y0);
         y1 = silu_f(y1);
         // per-head L2 norm (heads are D channels = D/2 lanes, aligned)
-        float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
+        const float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
         if (active) {
             if (c < nqk) {
                 const float inv = 1.0f / sqrtf(ss + l2_eps);
@@ -91,32 +108,40 @@ __global__ __launch_bounds__(256) void conv1d_silu_l2_kernel(
         }
         h3 = h2; h2 = h1; h1 = x0;
     }
-}
 
-// New history of request r = last 3 entries of [old history | request rows].
-template <typename TX>
-__global__ __launch_bounds__(256) void conv_history_kernel(
-    const TX *__restrict__ x, int64_t x_ld, TX *__restrict__ pool,
-    const int32_t *__restrict__ qsl, const int32_t *__restrict__ slots,
-    const uint8_t *__restrict__ has_init, int32_t C) {
-    const int r = blockIdx.y;
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= C) return;
-    const int t0 = qsl[r];
-    const int L = qsl[r + 1] - t0;
-    if (L <= 0) return;  // empty request: slot untouched
-    const bool hi = has_init == nullptr || has_init[r] != 0;
-    TX *hp = pool + ((int64_t)slots[r] * C + c) * 3;
-    TX nv[3];
+    // New history of every request whose first token lies in this tile: the
+    // last three entries of [old history | request rows].  This thread alone
+    // read the old entries above.
+    if (!active) return;
+    for (int rr = (qsl[r_first] == t_begin ? r_first : r_first + 1);
+         rr < nreq && qsl[rr] < t_nom_end; ++rr) {
+        const int t0 = qsl[rr];
+        const int L = qsl[rr + 1] - t0;
+        if (L <= 0) continue;  // empty request: slot untouched
+        const bool hi = has_init == nullptr || has_init[rr] != 0;
+        TX *hp = pool + ((int64_t)slots[rr] * C + c) * 3;
+        TX nv0[3], nv1[3];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int m = L + j;  // index into [h0, h1, h2, x0 .. x_{L-1}]
-        if (m >= 3) nv[j] = x[(int64_t)(t0 + m - 3) * x_ld + c];
-        else if (hi) nv[j] = hp[m];
-        else nv[j] = from_f32<TX>(0.0f);
+        for (int j = 0; j < 3; ++j) {
+            const int m = L + j;  // index into [h0, h1, h2, x0 .. x_{L-1}]
+            if (m >= 3) {
+                const TX *xp = x + (int64_t)(t0 + m - 3) * x_ld + c;
+                nv0[j] = xp[0];
+                nv1[j] = xp[1];
+            } else if (hi) {
+                nv0[j] = hp[m];
+                nv1[j] = hp[3 + m];
+            } else {
+                nv0[j] = from_f32<TX>(0.0f);
+                nv1[j] = from_f32<TX>(0.0f);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            hp[j] = nv0[j];
+            hp[3 + j] = nv1[j];
+        }
     }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) hp[j] = nv[j];
 }
 
 template <int D, typename TX, typename TW, typename TO>
@@ -125,14 +150,9 @@ static hipError_t launch_conv_t(const ConvArgs &a, hipStream_t s) {
     const int tile = a.T <= 1024 ? 1 : (a.T <= 16384 ? 8 : 16);
     dim3 grid((a.T + tile - 1) / tile, (a.C + CONV_CH_PER_BLOCK - 1) / CONV_CH_PER_BLOCK);
     hipLaunchKernelGGL((conv1d_silu_l2_kernel<D, TX, TW, TO>), grid, dim3(256), 0, s,
-                       (const TX *)a.x, a.x_ld, (const TW *)a.w, (const TX *)a.pool, a.qsl,
-                       a.slots, a.has_init, a.nreq, a.T, a.C, a.nq, tile, a.l2_eps,
-                       (TO *)a.q, (TO *)a.k, (TO *)a.v);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 g2((a.C + 255) / 256, a.nreq);
-    hipLaunchKernelGGL((conv_history_kernel<TX>), g2, dim3(256), 0, s, (const TX *)a.x, a.x_ld,
-                       (TX *)a.pool, a.qsl, a.slots, a.has_init, a.C);
+                       (const TX *)a.x, a.x_ld, (const TW *)a.w, (TX *)a.pool, a.qsl, a.slots,
+                       a.has_init, a.nreq, a.T, a.C, a.nq, tile, a.l2_eps, (TO *)a.q, (TO *)a.k,
+                       (TO *)a.v);
     return hipGetLastError();
 }
 

@@ -20,22 +20,22 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(
     constexpr int LPR = D / 2;
     constexpr int ROWS = 256 / LPR;
     const int l = threadIdx.x % LPR;
-    const int64_t row = (int64_t)blockIdx.x * ROWS + threadIdx.x / LPR;
-    const bool valid = row < (int64_t)T * Hv;
-    const int64_t rr = valid ? row : 0;
-    const int64_t t = rr / Hv;
-    const int h = (int)(rr % Hv);
+    const int row = blockIdx.x * ROWS + threadIdx.x / LPR;  // T * Hv < 2^31
+    const bool valid = row < T * Hv;
+    const int rr = valid ? row : 0;
+    const int t = rr / Hv;
+    const int h = rr - t * Hv;
     const int j = 2 * l;
     float2 ov = make_float2(0.f, 0.f), zv = ov;
     if (valid) {
-        ov = ld2(o + rr * D + j);
-        zv = ld2(z + t * z_ld + (int64_t)h * D + j);
+        ov = ld2(o + (int64_t)rr * D + j);
+        zv = ld2(z + (int64_t)t * z_ld + h * D + j);
     }
     const float ss = group_sum<LPR>(ov.x * ov.x + ov.y * ov.y);
     const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
     if (valid) {
         const float2 g = ld2(gamma + j);
-        st2(y + rr * D + j, ov.x * inv * g.x * silu_f(zv.x), ov.y * inv * g.y * silu_f(zv.y));
+        st2(y + (int64_t)rr * D + j, ov.x * inv * g.x * silu_f(zv.x), ov.y * inv * g.y * silu_f(zv.y));
     }
 }
 

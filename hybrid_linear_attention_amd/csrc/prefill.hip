@@ -5,13 +5,16 @@
 namespace gdn {
 
 hipError_t launch_prefill_seq(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t s);
 
 size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq) {
     (void)D; (void)Hk; (void)Hv; (void)T; (void)nreq;
     return 0;
 }
 
+// d = 128 runs the chunkwise MFMA kernel; smaller heads the sequential one.
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
+    if (a.D == 128) return launch_prefill_chunk(a, s);
     return launch_prefill_seq(a, s);
 }
 
