@@ -198,12 +198,13 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def prefill_flops(d, T, chunk=64):
+def prefill_flops(d, T, chunk=32):
     """Algorithmic flops of the chunkwise gated delta rule over T tokens at
     chunk length C: per token and value head 6 d_k d_v (K S0^T, Q S0^T and the
     state update) + C (2 d_k + 4 d_v) (the triangular solve applied to V and K,
     and P Delta) + C^2 / 3 (forming T), plus per key head 4 C d_k (K K^T and
-    Q K^T).  7.67 MFLOP per token at 16/48 heads, d = 128, C = 64."""
+    Q K^T).  6.16 MFLOP per token at 16/48 heads, d = 128, C = 32 (the
+    chunk length the prefill kernels use)."""
     Dk, Dv = d.head_dim_k, d.head_dim_v
     per_tok = (d.num_v_heads * (6 * Dk * Dv + chunk * (2 * Dk + 4 * Dv) + chunk * chunk / 3)
                + d.num_k_heads * 4 * chunk * Dk)

@@ -36,13 +36,24 @@ __global__ __launch_bounds__(256) void decode_kernel(
     constexpr int LPR = D / 8;             // lanes per state row
     constexpr int NF = 2;                  // float4 per lane per row
     constexpr int ROWS = 256 / LPR;        // rows per block
+    // When d is a multiple of the rows per block, every row of a block belongs
+    // to one (request, head) unit: derive it from blockIdx alone so the slot and
+    // gate lookups are uniform (scalar) loads that issue before the state loads.
+    constexpr bool UNIFORM = (D % ROWS) == 0;
     const int l = threadIdx.x % LPR;
     const int64_t g = (int64_t)blockIdx.x * ROWS + threadIdx.x / LPR;  // global row
     const int64_t total_rows = (int64_t)R * Hv * D;
-    const bool valid = g < total_rows;
-    const int64_t gg = valid ? g : 0;  // keep every lane in the reductions
-    const int u = (int)(gg / D);       // (request, head) unit; R * Hv < 2^31
-    const int i = (int)(gg % D);
+    const bool valid = UNIFORM || g < total_rows;
+    int u, i;  // (request, head) unit (R * Hv < 2^31) and row within it
+    if constexpr (UNIFORM) {
+        const int64_t g0 = (int64_t)blockIdx.x * ROWS;
+        u = (int)(g0 / D);
+        i = (int)(g0 % D) + threadIdx.x / LPR;
+    } else {
+        const int64_t gg = valid ? g : 0;  // keep every lane in the reductions
+        u = (int)(gg / D);
+        i = (int)(gg % D);
+    }
     const int r = u / Hv;
     const int h = u - r * Hv;
     const int kh = h / (Hv / Hk);
