@@ -45,6 +45,32 @@ def parse():
     return p.parse_args()
 
 
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/<kernel>_traffic.txt: FETCH_SIZE and WRITE_SIZE scaled by
+    a plain copy's reading), or None when that summary is missing or was taken
+    on a different version of the kernel's source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", vals.get("source", ""))
+    if not os.path.exists(src) or source_digest(src) != vals.get("source_sha256_16"):
+        return None
+    return int(float(vals["hbm_bytes_per_launch"]))
+
+
 def decode_bytes(d, R, act_bytes=4, o_bytes=4):
     """Algorithmic HBM bytes of one decode_step launch: the state read and
     written once, q/k/v/a/b read once, o written once."""
@@ -163,7 +189,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "bytes_per_launch": dec_bytes,
-            "traffic": None,
+            "traffic": measured_traffic("decode_kernel"),
         },
     }
     del states, conv_pools
@@ -187,11 +213,12 @@ def main():
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
 
     if args.copy_ref_mib > 0:
+        # a plain elementwise kernel of known size: reads n*4 bytes, writes n*4
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         result["copy_ref_bytes"] = {"read": n * 4, "write": n * 4, "launches": 3}
 
