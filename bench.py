@@ -1,14 +1,16 @@
 """Benchmark of the GDN mixer core on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-layer]
+                    [--no-cpu]
 
 Headline workload (N=1): one decode step of 64 requests at full shapes (16 key /
 48 value heads, d = 128, fp32 state [64,48,128,128]): conv1d_update ->
 decode_step -> gated_norm, with every input already resident in HBM.  `value`
 is the state bytes each step reads and writes (2 x 64 x 3 MiB) divided by the
 measured step time.  A prefill leg (single 4096-token sequence; 16-request
-packed varlen batch) reports tokens/s in the same run, and the fp64 CPU oracle
-is timed on a bounded sample on the host cores.
+packed varlen batch) reports tokens/s in the same run, a layer leg times the
+whole layer block on the mixed 8 x 2048 + 256 batch at hidden 5120, and the
+fp64 CPU oracle is timed on a bounded sample on the host cores.
 
 Prints ONE JSON line.
 """
@@ -37,6 +39,8 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=5)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-varlen", action="store_true")
+    p.add_argument("--no-layer", action="store_true")
+    p.add_argument("--layer-steps", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-ref-mib", type=int, default=0,
@@ -208,6 +212,11 @@ def main():
             torch.cuda.empty_cache()
         result["prefill"] = pre
 
+    # ------------------------------------------------------------- layer block
+    if not args.no_layer:
+        result["layer"] = bench_layer(args.layer_steps, dev, stream, torch, np)
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
@@ -236,6 +245,69 @@ def prefill_flops(d, T, chunk=32):
     per_tok = (d.num_v_heads * (6 * Dk * Dv + chunk * (2 * Dk + 4 * Dv) + chunk * chunk / 3)
                + d.num_k_heads * 4 * chunk * Dk)
     return float(per_tok * T)
+
+
+def prefill_bytes(d, T, nreq, n_init, act_bytes=4, gate_bytes=2, o_bytes=4):
+    """Algorithmic HBM bytes of one gdn_prefill_varlen launch: q, k, v and the
+    two gate rows read once, o written once, each request's state written once
+    (and read once where it has an initial state)."""
+    per_tok = (act_bytes * (2 * d.num_k_heads * d.head_dim_k + d.num_v_heads * d.head_dim_v)
+               + 2 * gate_bytes * d.num_v_heads + o_bytes * d.num_v_heads * d.head_dim_v)
+    state = d.num_v_heads * d.head_dim_v * d.head_dim_k * 4
+    return per_tok * T + state * (nreq + n_init)
+
+
+def bench_layer(steps, dev, stream, torch, np):
+    """The full layer block on the mixed batch (8 x 2048 prefill tokens + 256
+    decode tokens, hidden 5120): RMSNorm -> in-projection -> conv1d_update ->
+    prefill_varlen + decode_step -> gated_norm -> out-projection + residual, with
+    every launch timed by events on the stream."""
+    from hybrid_linear_attention_amd.layer import GdnLayer, stack_weights
+    from hybrid_linear_attention_amd.workloads import layer_mixed
+
+    case = layer_mixed()
+    core = case.core
+    d = core.dims
+    T = int(core.qsl[-1])
+    T_pf = case.num_prefill * case.prefill_len
+    w = stack_weights(d, case.W_qkvz, case.W_ba, case.W_o, core.conv_w, case.gamma_in,
+                      core.gamma, device=dev)
+    layer = GdnLayer(d, w, T, case.num_prefill, T_pf, case.num_decode, NORM_EPS, L2_EPS,
+                     device=dev)
+    X = case.X.to(dev)
+    pool, state = core.conv_pool.to(dev), core.state_pool.to(dev)
+    qsl, slots, hinit = core.qsl.to(dev), core.slot_ids.to(dev), core.has_initial.to(dev)
+    del case
+    stages = layer.stages(X, pool, state, qsl, slots, hinit)
+    names = [n for n, _ in stages]
+    per, tot = {n: [] for n in names}, []
+    for it in range(steps + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        ev[0].record(stream)
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        if it > 0:
+            for i, n in enumerate(names):
+                per[n].append(ev[i].elapsed_time(ev[i + 1]))
+            tot.append(ev[0].elapsed_time(ev[-1]))
+    med = {n: float(np.median(v)) for n, v in per.items()}
+    ms = float(np.median(tot))
+    hidden = X.shape[1]
+    n_in = w.W_in.shape[0]
+    f_in = 2.0 * T * hidden * n_in
+    f_out = 2.0 * T * w.W_out.shape[1] * hidden
+    out = {
+        "workload": f"layer_mixed: {T} tokens = 8 x 2048 prefill + 256 decode, hidden {hidden}",
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "stage_ms": {n: round(v, 4) for n, v in med.items()},
+        "in_proj_tflops": round(f_in / (med["in_proj"] * 1e-3) / 1e12, 1),
+        "out_proj_tflops": round(f_out / (med["out_proj"] * 1e-3) / 1e12, 1),
+    }
+    del layer, w, X, pool, state
+    return out
 
 
 def bench_prefill(c, steps, dev, stream, torch, gdn, np):
@@ -279,17 +351,23 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np):
     ms = float(np.median(times))
     kms = float(np.median(ktimes))
     flops = prefill_flops(d, T)
+    nbytes = prefill_bytes(d, T, c.num_reqs, int(c.has_initial.sum()))
+    tflops = flops / (kms * 1e-3) / 1e12
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    # the binding resource is the one whose peak needs longer for this work
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12)
+    roof = {"kernel": "prefill plan + prep + chain kernels (gdn_prefill_varlen)"}
+    if hbm_bound:
+        roof.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        roof.update(bound="mfma", achieved=round(tflops, 2), peak=BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(tflops / BF16_PEAK_TFLOPS, 4))
+    roof.update(bytes_per_launch=nbytes, flops_per_launch=flops, traffic=None,
+                mfma_tflops=round(tflops, 2),
+                mfma_util=round(tflops / BF16_PEAK_TFLOPS, 4))
     return {
-        "roofline": {
-            "kernel": "prefill_chunk_kernel (gdn_prefill_varlen)",
-            "bound": "mfma",
-            "achieved": round(flops / (kms * 1e-3) / 1e12, 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(flops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "flops_per_launch": flops,
-            "traffic": None,
-        },
+        "roofline": roof,
         "tokens": T,
         "requests": c.num_reqs,
         "ms_per_step": round(ms, 4),

@@ -186,7 +186,7 @@ gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb,
                          int32_t M, int32_t N, int32_t K, void *stream) {
     if (!valid_dtype(c_dt)) return GDN_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || N % 8 != 0 || K % 8 != 0) return GDN_ERR_SHAPE;
-    if (lda < K || ldb < N || ldc < N || (residual && ldr < N)) return GDN_ERR_SHAPE;
+    if (lda < K || ldb < K || ldc < N || (residual && ldr < N)) return GDN_ERR_SHAPE;
     if (lda % 8 || ldb % 8 || ldc % 8 || (residual && ldr % 8)) return GDN_ERR_SHAPE;
     if (M == 0 || N == 0) return GDN_OK;
     if (!A || !B || !C) return GDN_ERR_NULL;

@@ -124,6 +124,9 @@ def test_norm_and_gemm_reject_bad_args():
     assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 64, 0, None, 0, 10, 64, 60, None) == 4   # K % 8
     assert lib.gdn_gemm_bf16(P, 32, P, 64, P, 64, 0, None, 0, 10, 64, 64, None) == 4   # lda < K
     assert lib.gdn_gemm_bf16(None, 64, P, 64, P, 64, 0, None, 0, 10, 64, 64, None) == 1
+    # B is [N, ldb] with ldb >= K (not N): a wide projection, N > K, is valid
+    assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 128, 0, None, 0, 0, 128, 64, None) == 0
+    assert lib.gdn_gemm_bf16(P, 64, P, 32, P, 128, 0, None, 0, 0, 128, 64, None) == 4
     assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 64, 0, None, 0, 0, 64, 64, None) == 0
 
 
