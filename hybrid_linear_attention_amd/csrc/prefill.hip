@@ -6,12 +6,12 @@ namespace gdn {
 
 hipError_t launch_prefill_seq(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t s);
-size_t prefill_chunk_workspace_bytes(int32_t Hv, int32_t T, int32_t nreq);
+size_t prefill_chunk_workspace_bytes(int32_t Hk, int32_t Hv, int32_t T, int32_t nreq);
 
-// d = 128: chunk offsets + one record of T, P and gates per (chunk, value head).
+// d = 128: chunk offsets and request order, a K image per (chunk, key head)
+// and a T image per (chunk, value head).
 size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq) {
-    (void)Hk;
-    if (D == 128) return prefill_chunk_workspace_bytes(Hv, T, nreq);
+    if (D == 128) return prefill_chunk_workspace_bytes(Hk, Hv, T, nreq);
     return 0;
 }
 

@@ -23,21 +23,27 @@
 // operand, which keeps the final state well inside a 1e-3 relative error even
 // when the decay is weak.  A single bf16 rounding of k or of Delta would not.
 //
-// Chunks are C = 32 tokens: one MFMA k-step spans a chunk, the triangular
-// inverse is 32x32, and a chain block's LDS (~68 KB) leaves room for two
-// blocks per CU, so one block's waits overlap the other's work.
+// Chunks are C = 32 tokens: one MFMA k-step spans a chunk and the triangular
+// inverse is 32x32.
 //
 // Three launches:
-//   plan   one block: chunk offsets per request (prefix sum of ceil(L/C)), on
-//          the device so the host never waits for query_start_loc.
-//   prep   one block per (chunk, key head), fully parallel: K K^T and Q K^T once
-//          for the key head, then one wave per value head reading it: the
-//          gates' cumulative decay, T = (I + A)^-1 and P, written to the
-//          workspace as bf16 hi/lo planes (8,448 bytes per chunk and value head).
-//   chain  one block per (request, value head, block of 32 or 64 state rows),
-//          sequential over the request's chunks: only the state-dependent
-//          products.  State rows evolve independently given (k, beta, alpha),
-//          so the row blocks of a head never communicate.
+//   plan   one block: chunk offsets per request (prefix sum of ceil(L/C)) and
+//          the requests in order of decreasing length, on the device so the
+//          host never waits for query_start_loc.
+//   prep   one block per (chunk, key head), fully parallel: splits K and Q into
+//          hi/lo planes, K K^T and Q K^T on MFMA, then one wave per value head:
+//          the gates' cumulative decay, T = (I + A)^-1 and P.  It writes every
+//          MFMA A operand the chain needs, already split and in the exact
+//          per-lane fragment order, as "images": a 48 KiB K image per (chunk,
+//          key head) holding K, Q and K^T, and a 9 KiB T image per (chunk, value
+//          head) holding T, P and the per-token gamma, e^{G_C-G_t} and beta.
+//   chain  one block per (request, value head, block of state rows), sequential
+//          over the request's chunks: only the state-dependent products.  Each
+//          chunk's images are copied global -> LDS with direct-to-LDS loads
+//          (global_load_lds_dwordx4) into a two-stage ring while the previous
+//          chunk computes; every operand fragment is then one conflict-free
+//          16-byte LDS read.  State rows evolve independently given
+//          (k, beta, alpha), so the row blocks of a head never communicate.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -50,15 +56,23 @@ namespace chunk {
 
 constexpr int D = 128;      // d_k == d_v
 constexpr int CH = 32;      // tokens per chunk
-constexpr int KP = D + 8;   // padded bf16 row of 128-wide planes (272 B)
-constexpr int TP = CH + 8;  // padded bf16 row of 32-wide T/P planes (80 B)
-constexpr int KTP = CH + 4; // padded bf16 row of the K^T planes (72 B; conflict-free transpose writes)
+constexpr int KP = D + 8;   // padded bf16 row of the prep kernel's 128-wide planes (272 B)
 constexpr int AP = CH + 4;  // padded fp32 row of 32x32 work matrices
 
-// workspace record of one (chunk, value head): T and P as bf16 hi/lo planes
-// [32][32], then the cumulative log-decay G and beta of the chunk's tokens
-constexpr size_t REC_TH = 0, REC_TL = 2048, REC_PH = 4096, REC_PL = 6144;
-constexpr size_t REC_G = 8192, REC_B = REC_G + 128, REC_BYTES = REC_B + 128;  // 8,448
+// An image is a sequence of fragment blocks: 64 lanes x 16 bytes, lane l at
+// byte 16 l, holding the eight bf16 values of one MFMA A operand in k-slot
+// order (see the chain kernel's layout note).
+constexpr int FRAG = 1024;
+// K image: K and Q as (plane hi/lo, row tile tau, k-step ks), K^T as (plane, jt)
+constexpr int FK = 0, FQ = 16, FKT = 32, KIMG_FRAGS = 48;
+// T image: T and P as (plane, tau), then three float[32] token vectors
+constexpr int FT = 0, FP = 4, TIMG_FRAGS = 9;
+constexpr int T_GAM = 8 * FRAG, T_REV = T_GAM + 128, T_BETA = T_REV + 128;
+constexpr size_t KIMG = (size_t)KIMG_FRAGS * FRAG;  // 49,152 bytes
+constexpr size_t TIMG = (size_t)TIMG_FRAGS * FRAG;  //  9,216 bytes
+constexpr size_t STAGE = KIMG + TIMG;               // LDS per chunk in the chain
+
+constexpr int PLAN_SORT_MAX = 4096;  // longest-first order for up to this many requests
 
 __device__ __forceinline__ uint16_t bits_of(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
@@ -93,16 +107,17 @@ __device__ __forceinline__ void split_vals(const float (&x)[8], bf16x8_t &hi, bf
     }
 }
 
-__device__ __forceinline__ bf16x8_t frag(const uint16_t *p) {
-    return *reinterpret_cast<const bf16x8_t *>(p);
+// eight values -> two 16-byte hi/lo fragment pieces
+__device__ __forceinline__ void split_pack(const float (&x)[8], uint4 &hi, uint4 &lo) {
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split(x[e], h[e], l[e]);
+    hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+    lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
 }
 
-// A operand in k-slot order from a bf16 plane row: columns c0 .. c0+3 and
-// c0+16 .. c0+19 with c0 = 32 ks + 4 lg (see the chain kernel's layout note)
-__device__ __forceinline__ bf16x8_t frag_slots(const uint16_t *row, int c0) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(row + c0);
-    const uint2 b = *reinterpret_cast<const uint2 *>(row + c0 + 16);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+__device__ __forceinline__ bf16x8_t frag(const uint8_t *p) {
+    return *reinterpret_cast<const bf16x8_t *>(p);
 }
 
 // acc += a * b with a = ah + al, b = bh + bl (the lo*lo term is below fp32 noise).
@@ -113,34 +128,41 @@ __device__ __forceinline__ void mma3(floatx4_t &acc, const bf16x8_t &ah, const b
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
 }
 
-// Raw 4-element loads, converted to fp32 only at use, so a prefetch never
-// waits on its own load.
-template <typename T> struct Raw4;
-template <> struct Raw4<float> {
-    f32x4 v;
-    __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const f32x4 *>(p); }
-    __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
-    __device__ __forceinline__ float4 get() const { return make_float4(v.x, v.y, v.z, v.w); }
+// A scalar load kept in its storage format until use, so that issuing it never
+// waits for its own data.
+template <typename T> struct Raw1;
+template <> struct Raw1<float> {
+    float v;
+    __device__ __forceinline__ void load(const float *p) { v = *p; }
+    __device__ __forceinline__ void zero() { v = 0.f; }
+    __device__ __forceinline__ float get() const { return v; }
 };
-template <> struct Raw4<bf16> {
-    uint2 v;
-    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const uint2 *>(p); }
-    __device__ __forceinline__ void zero() { v = make_uint2(0, 0); }
-    __device__ __forceinline__ float4 get() const {
-        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-    }
+template <> struct Raw1<bf16> {
+    uint16_t v;
+    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const uint16_t *>(p); }
+    __device__ __forceinline__ void zero() { v = 0; }
+    __device__ __forceinline__ float get() const { return __uint_as_float(uint32_t(v) << 16); }
 };
+
+// One 16-byte direct-to-LDS copy per lane: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void copy_frag(const uint8_t *src_frag, uint8_t *dst_frag, int lane) {
+    __builtin_amdgcn_global_load_lds(
+        static_cast<const void *>(src_frag + 16 * lane),
+        (__attribute__((address_space(3))) void *)(dst_frag), 16, 0, 0);
+}
 
 }  // namespace chunk
 
 // ---------------------------------------------------------------------------
-// plan: chunk_off[r] = sum_{r' < r} ceil(L_r' / C)
+// plan: chunk_off[r] = sum_{r' < r} ceil(L_r' / C); order = requests by
+// decreasing length (ties by index) so the longest chains start first
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__restrict__ qsl,
                                                             int32_t nreq,
-                                                            int32_t *__restrict__ chunk_off) {
+                                                            int32_t *__restrict__ chunk_off,
+                                                            int32_t *__restrict__ order) {
     __shared__ int32_t part[1024];
+    __shared__ int32_t lens[chunk::PLAN_SORT_MAX];
     const int tid = threadIdx.x;
     const int per = (nreq + 1023) / 1024;
     const int r0 = min(nreq, tid * per), r1 = min(nreq, r0 + per);
@@ -160,10 +182,26 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
         run += (qsl[r + 1] - qsl[r] + chunk::CH - 1) / chunk::CH;
         chunk_off[r + 1] = run;
     }
+    if (nreq <= chunk::PLAN_SORT_MAX) {  // uniform over the block
+        for (int r = tid; r < nreq; r += 1024) lens[r] = qsl[r + 1] - qsl[r];
+        __syncthreads();
+        for (int r = tid; r < nreq; r += 1024) {
+            const int L = lens[r];
+            int rank = 0;
+            for (int r2 = 0; r2 < nreq; ++r2) {
+                const int L2 = lens[r2];
+                rank += (L2 > L) || (L2 == L && r2 < r);
+            }
+            order[rank] = r;
+        }
+    } else {
+        for (int r = tid; r < nreq; r += 1024) order[r] = r;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// prep: per (chunk, key head): K K^T and Q K^T, then one wave per value head
+// prep: per (chunk, key head): the K image, then one wave per value head for
+// its T image
 // ---------------------------------------------------------------------------
 namespace chunk {
 struct PrepSmem {
@@ -179,7 +217,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const TA *__restrict__ q, const TA *__restrict__ k, const TG *__restrict__ ga,
     const TG *__restrict__ gb, int64_t gate_ld, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ chunk_off, int32_t nreq, int32_t Hk, int32_t Hv,
-    uint8_t *__restrict__ records) {
+    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg) {
     using namespace chunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
@@ -193,6 +231,16 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const int tb = qsl[r] + CH * (c - chunk_off[r]);
     const int Lc = min(CH, qsl[r + 1] - tb);
     const int group = Hv / Hk;
+
+    // this wave's first value head: its gates load while K and Q are staged
+    Raw1<TG> ga0, gb0;
+    ga0.zero();
+    gb0.zero();
+    if (w < group && lane < Lc) {
+        const int64_t go = (int64_t)(tb + lane) * gate_ld + kh * group + w;
+        ga0.load(ga + go);
+        gb0.load(gb + go);
+    }
 
     // stage K and Q of the key head as hi/lo planes (1024 four-element slots each)
 #pragma unroll
@@ -211,6 +259,46 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     }
     __syncthreads();
 
+    // K image: 48 fragment blocks x 64 lanes = 12 pieces per thread, each a
+    // coalesced 16-byte store
+    {
+        uint8_t *kim = kimg + ((size_t)c * Hk + kh) * KIMG;
+#pragma unroll 4
+        for (int m = 0; m < 12; ++m) {
+            const int pi = tid + 256 * m;
+            const int f = pi >> 6;
+            const int l = pi & 63;
+            const int plr = l & 15, plg = l >> 4;
+            uint4 val;
+            if (f < FKT) {
+                // K or Q rows 16 tau + lr, channels 32 ks + 4 lg + {0..3, 16..19}
+                const int ff = f & 15;
+                const int plane = ff >> 3, tau = (ff >> 2) & 1, ks = ff & 3;
+                const bool isQ = f >= FQ;
+                const uint16_t *row = isQ ? (plane ? sm.Ql[16 * tau + plr] : sm.Qh[16 * tau + plr])
+                                          : (plane ? sm.Kl[16 * tau + plr] : sm.Kh[16 * tau + plr]);
+                const int c0 = 32 * ks + 4 * plg;
+                const uint2 a = *reinterpret_cast<const uint2 *>(row + c0);
+                const uint2 b = *reinterpret_cast<const uint2 *>(row + c0 + 16);
+                val = make_uint4(a.x, a.y, b.x, b.y);
+            } else {
+                // K^T row j = 16 jt + lr, tokens 4 lg + {0..3, 16..19}
+                const int ff = f - FKT;
+                const int plane = ff >> 3, jt = ff & 7;
+                const int j = 16 * jt + plr;
+                uint16_t e[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int t = 16 * (p >> 2) + 4 * plg + (p & 3);
+                    e[p] = plane ? sm.Kl[t][j] : sm.Kh[t][j];
+                }
+                val = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
+                                 pack2(e[6], e[7]));
+            }
+            *reinterpret_cast<uint4 *>(kim + (size_t)f * FRAG + 16 * l) = val;
+        }
+    }
+
     // K K^T and Q K^T on the three lower-triangular 16x16 tiles of each
     for (int item = w; item < 6; item += 4) {
         const bool isQ = item >= 3;
@@ -221,9 +309,13 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int off = 32 * ks + 8 * lg;
-            const bf16x8_t ah = isQ ? frag(&sm.Qh[16 * tm + lr][off]) : frag(&sm.Kh[16 * tm + lr][off]);
-            const bf16x8_t al = isQ ? frag(&sm.Ql[16 * tm + lr][off]) : frag(&sm.Kl[16 * tm + lr][off]);
-            mma3(acc, ah, al, frag(&sm.Kh[16 * tn + lr][off]), frag(&sm.Kl[16 * tn + lr][off]));
+            const uint16_t *arow_h = isQ ? sm.Qh[16 * tm + lr] : sm.Kh[16 * tm + lr];
+            const uint16_t *arow_l = isQ ? sm.Ql[16 * tm + lr] : sm.Kl[16 * tm + lr];
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(arow_h + off);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(arow_l + off);
+            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&sm.Kh[16 * tn + lr][off]);
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&sm.Kl[16 * tn + lr][off]);
+            mma3(acc, ah, al, bh, bl);
         }
         float(*dst)[AP] = isQ ? sm.QK : sm.KK;
 #pragma unroll
@@ -234,16 +326,21 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     // one wave per value head: nothing below crosses waves
     for (int hh = w; hh < group; hh += 4) {
         const int h = kh * group + hh;
-        uint8_t *rec = records + ((size_t)c * Hv + h) * REC_BYTES;
+        uint8_t *tim = timg + ((size_t)c * Hv + h) * TIMG;
         float(*A)[AP] = sm.A[w];
         float *Gw = sm.G[w];
         float *Bw = sm.Beta[w];
         {
             float g = 0.f, beta = 0.f;
             if (lane < Lc) {
-                const int64_t go = (int64_t)(tb + lane) * gate_ld + h;
-                g = gate_log_alpha(ld(ga + go));
-                beta = gate_beta(ld(gb + go));
+                if (hh == w) {
+                    g = gate_log_alpha(ga0.get());
+                    beta = gate_beta(gb0.get());
+                } else {
+                    const int64_t go = (int64_t)(tb + lane) * gate_ld + h;
+                    g = gate_log_alpha(ld(ga + go));
+                    beta = gate_beta(ld(gb + go));
+                }
             }
             float G = g;  // inclusive prefix sum over the chunk; padded rows add nothing
 #pragma unroll
@@ -251,31 +348,43 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 const float y = __shfl_up(G, off, 64);
                 if (lane >= off) G += y;
             }
+            const float Glast = __shfl(G, CH - 1, 64);
             if (lane < CH) {
                 Gw[lane] = G;
                 Bw[lane] = beta;
-                reinterpret_cast<float *>(rec + REC_G)[lane] = G;
-                reinterpret_cast<float *>(rec + REC_B)[lane] = beta;
+                reinterpret_cast<float *>(tim + T_GAM)[lane] = expf(G);
+                reinterpret_cast<float *>(tim + T_REV)[lane] = expf(Glast - G);
+                reinterpret_cast<float *>(tim + T_BETA)[lane] = beta;
             }
         }
         __builtin_amdgcn_wave_barrier();
-        // A = strict-lower(beta_t e^{G_t-G_s} KK), P = lower(e^{G_t-G_s} QK) -> record
+        // A = strict-lower(beta_t e^{G_t-G_s} KK) into the work matrix
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int idx = lane + 64 * m;  // 256 groups of 4 columns
             const int t = idx >> 3;
             const int s0 = (idx & 7) * 4;
-            float pv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = s0 + e;
-                const float dec = expf(fminf(Gw[t] - Gw[s], 0.f));
-                A[t][s] = s < t ? Bw[t] * dec * sm.KK[t][s] : 0.f;
-                pv[e] = s <= t ? dec * sm.QK[t][s] : 0.f;
+                A[t][s] = s < t ? Bw[t] * expf(fminf(Gw[t] - Gw[s], 0.f)) * sm.KK[t][s] : 0.f;
             }
-            split4_store(pv[0], pv[1], pv[2], pv[3],
-                         reinterpret_cast<uint16_t *>(rec + REC_PH) + t * CH + s0,
-                         reinterpret_cast<uint16_t *>(rec + REC_PL) + t * CH + s0);
+        }
+        // P = lower(e^{G_t-G_s} QK) straight into its fragments:
+        // row t = 16 tau + lr, columns s = 4 lg + {0..3, 16..19}
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const int t = 16 * tau + lr;
+            float pv[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int s = 16 * (p >> 2) + 4 * lg + (p & 3);
+                pv[p] = s <= t ? expf(fminf(Gw[t] - Gw[s], 0.f)) * sm.QK[t][s] : 0.f;
+            }
+            uint4 hi, lo;
+            split_pack(pv, hi, lo);
+            *reinterpret_cast<uint4 *>(tim + (size_t)(FP + tau) * FRAG + 16 * lane) = hi;
+            *reinterpret_cast<uint4 *>(tim + (size_t)(FP + 2 + tau) * FRAG + 16 * lane) = lo;
         }
         __builtin_amdgcn_wave_barrier();
         // T = (I + A)^-1: the two 16x16 diagonal blocks by substitution
@@ -323,15 +432,17 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
             for (int e = 0; e < 4; ++e) A[16 + lg + 4 * e][lr] = tv[e];
             __builtin_amdgcn_wave_barrier();
         }
-        // T (lower triangle, zeros above) -> record
+        // T (lower triangle, zeros above) into its fragments
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int idx = lane + 64 * m;
-            const int t = idx >> 3;
-            const int s0 = (idx & 7) * 4;
-            split4_store(A[t][s0], A[t][s0 + 1], A[t][s0 + 2], A[t][s0 + 3],
-                         reinterpret_cast<uint16_t *>(rec + REC_TH) + t * CH + s0,
-                         reinterpret_cast<uint16_t *>(rec + REC_TL) + t * CH + s0);
+        for (int tau = 0; tau < 2; ++tau) {
+            const int t = 16 * tau + lr;
+            float tv[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) tv[p] = A[t][16 * (p >> 2) + 4 * lg + (p & 3)];
+            uint4 hi, lo;
+            split_pack(tv, hi, lo);
+            *reinterpret_cast<uint4 *>(tim + (size_t)(FT + tau) * FRAG + 16 * lane) = hi;
+            *reinterpret_cast<uint4 *>(tim + (size_t)(FT + 2 + tau) * FRAG + 16 * lane) = lo;
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -339,329 +450,227 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 
 // ---------------------------------------------------------------------------
 // chain: sequential over a request's chunks, per (request, value head, block
-// of 16 NW state rows).  Wave w of the NW compute waves owns state rows
-// 16 w .. 16 w + 15 of the block for all 32 tokens of a chunk, so the error E,
-// the pseudo-values Delta and the state itself never leave its registers:
-//   X = K S0^T, OQ = Q S0^T        (A: K / Q rows from LDS, B: state registers)
-//   Delta = T (beta E)             (A: T rows from LDS,     B: E registers)
-//   O = gamma OQ + P Delta         (A: P rows from LDS,     B: Delta registers)
-//   S^T = gamma_C S^T + K^T Delta~ (A: K^T rows from LDS,   B: Delta registers)
+// of 16 NW state rows).  Wave w owns state rows 16 w .. 16 w + 15 of the block
+// for all 32 tokens of a chunk, so the error E, the pseudo-values Delta and the
+// state itself never leave its registers:
+//   X = K S0^T, OQ = Q S0^T        (A: K / Q fragments, B: state registers)
+//   Delta = T (beta E)             (A: T fragments,     B: E registers)
+//   O = gamma OQ + P Delta         (A: P fragments,     B: Delta registers)
+//   S^T = gamma_C S^T + K^T Delta~ (A: K^T fragments,   B: Delta registers)
 // An accumulator lane holds rows 4 lg + e of a 16-row tile; feeding it back
 // as the B operand of the next product uses the k-slot order
 //   slot (lg, p) -> 32 ks + 16 (p / 4) + 4 lg + p % 4,
-// and the A operand is read from LDS in that same order (two 8-byte reads per
-// plane), so no register ever crosses lanes.  The block's four waves stage K,
-// K^T, Q, T, P and the gates of a chunk in LDS; the next chunk's operands are
-// loaded into registers while the current chunk computes.
+// and the prep kernel wrote the A fragments in that same order, so no register
+// ever crosses lanes.
+//
+// Blocks map to (request, key head) groups so that the blocks sharing a K
+// image run on one XCD (workgroups are dealt to the 8 XCDs round-robin) and
+// the longest requests' groups are dispatched first.
 // ---------------------------------------------------------------------------
-namespace chunk {
-struct ChainSmem {
-    uint16_t Kh[CH][KP], Kl[CH][KP];     // K rows [token][key channel]
-    uint16_t KTh[D][KTP], KTl[D][KTP];   // K transposed [key channel][token]
-    uint16_t Qh[CH][KP], Ql[CH][KP];
-    uint16_t Th[CH][TP], Tl[CH][TP];     // (I + A)^-1 [token][token]
-    uint16_t Ph[CH][TP], Pl[CH][TP];     // decayed causal Q K^T
-    float Gam[CH], Beta[CH], Rev[CH];
-};
-
-// One thread's share of the next chunk.  Thread tid stages K rows 2 tp, 2 tp + 1
-// (tp = tid % 16) at columns 8 cg .. 8 cg + 7 (cg = tid / 16): the K^T planes
-// are then written as packed token pairs, 16 lanes to one row.
-template <typename TA, int RPW> struct ChainPrefetch {
-    chunk::Raw4<TA> kr[2][2], qr[2][2];  // [row of the pair][column half]
-    uint4 tpr[2];                        // T/P planes: 512 pieces of 16 bytes
-    float Gp, Bp;
-    float vr[RPW][2][4];
-
-    __device__ __forceinline__ void load(const TA *__restrict__ k, const TA *__restrict__ q,
-                                         const TA *__restrict__ v, const uint8_t *__restrict__ records,
-                                         int tok0, int L, int cc, int c_first, int Hk, int Hv, int h,
-                                         int kh, const int (&irow)[RPW], bool computes, int tid, int lg) {
-        using namespace chunk;
-        const int tb = tok0 + cc * CH;
-        const int Lc = min(CH, L - cc * CH);
-        const uint8_t *rec = records + ((size_t)(c_first + cc) * Hv + h) * REC_BYTES;
-        const int tp = tid & 15, cg = tid >> 4;
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int t = 2 * tp + rr;
-            const int64_t off = ((int64_t)(tb + t) * Hk + kh) * D + 8 * cg;
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                if (t < Lc) {
-                    kr[rr][hf].load(k + off + 4 * hf);
-                    qr[rr][hf].load(q + off + 4 * hf);
-                } else {
-                    kr[rr][hf].zero();
-                    qr[rr][hf].zero();
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) tpr[m] = reinterpret_cast<const uint4 *>(rec)[tid + 256 * m];
-        Gp = 0.f;
-        Bp = 0.f;
-        if (tid < CH) {
-            Gp = reinterpret_cast<const float *>(rec + REC_G)[tid];
-            Bp = reinterpret_cast<const float *>(rec + REC_B)[tid];
-        }
-        if (computes) {
-#pragma unroll
-            for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-                for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * tau + 4 * lg + e;
-                        vr[rt][tau][e] = t < Lc ? ld(v + ((int64_t)(tb + t) * Hv + h) * D + irow[rt]) : 0.f;
-                    }
-        }
-    }
-
-    __device__ __forceinline__ void stage(chunk::ChainSmem &sm, int tid) const {
-        using namespace chunk;
-        const int tp = tid & 15, cg = tid >> 4;
-        uint16_t kh_[2][8], kl_[2][8];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int t = 2 * tp + rr;
-            const float4 k0 = kr[rr][0].get(), k1 = kr[rr][1].get();
-            const float4 q0 = qr[rr][0].get(), q1 = qr[rr][1].get();
-            const float kx[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const float qx[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            uint16_t qh_[8], ql_[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                split(kx[e], kh_[rr][e], kl_[rr][e]);
-                split(qx[e], qh_[e], ql_[e]);
-            }
-            *reinterpret_cast<uint4 *>(&sm.Kh[t][8 * cg]) =
-                make_uint4(pack2(kh_[rr][0], kh_[rr][1]), pack2(kh_[rr][2], kh_[rr][3]),
-                           pack2(kh_[rr][4], kh_[rr][5]), pack2(kh_[rr][6], kh_[rr][7]));
-            *reinterpret_cast<uint4 *>(&sm.Kl[t][8 * cg]) =
-                make_uint4(pack2(kl_[rr][0], kl_[rr][1]), pack2(kl_[rr][2], kl_[rr][3]),
-                           pack2(kl_[rr][4], kl_[rr][5]), pack2(kl_[rr][6], kl_[rr][7]));
-            *reinterpret_cast<uint4 *>(&sm.Qh[t][8 * cg]) =
-                make_uint4(pack2(qh_[0], qh_[1]), pack2(qh_[2], qh_[3]), pack2(qh_[4], qh_[5]), pack2(qh_[6], qh_[7]));
-            *reinterpret_cast<uint4 *>(&sm.Ql[t][8 * cg]) =
-                make_uint4(pack2(ql_[0], ql_[1]), pack2(ql_[2], ql_[3]), pack2(ql_[4], ql_[5]), pack2(ql_[6], ql_[7]));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = 8 * cg + e;
-            *reinterpret_cast<uint32_t *>(&sm.KTh[j][2 * tp]) = pack2(kh_[0][e], kh_[1][e]);
-            *reinterpret_cast<uint32_t *>(&sm.KTl[j][2 * tp]) = pack2(kl_[0][e], kl_[1][e]);
-        }
-        // T/P planes: piece p = plane (4) x row (32) x 4 groups of 8 columns
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int piece = tid + 256 * m;
-            const int plane = piece >> 7;
-            const int t = (piece >> 2) & 31;
-            const int s8 = (piece & 3) * 8;
-            uint16_t *dst = plane == 0 ? &sm.Th[t][s8] : plane == 1 ? &sm.Tl[t][s8]
-                          : plane == 2 ? &sm.Ph[t][s8] : &sm.Pl[t][s8];
-            *reinterpret_cast<uint4 *>(dst) = tpr[m];
-        }
-        if (tid < CH) {
-            const float Glast = __shfl(Gp, CH - 1, 64);
-            sm.Gam[tid] = expf(Gp);
-            sm.Rev[tid] = expf(Glast - Gp);
-            sm.Beta[tid] = Bp;
-        }
-    }
-};
-}  // namespace chunk
-
-template <int NW, int RPW, typename TA, typename TO>
-__global__ __launch_bounds__(256, 2) void prefill_chain_kernel(
-    const TA *__restrict__ q, const TA *__restrict__ k, const TA *__restrict__ v,
-    float *__restrict__ state, const int32_t *__restrict__ qsl,
-    const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
-    const int32_t *__restrict__ chunk_off, const uint8_t *__restrict__ records, int32_t nreq,
-    int32_t Hk, int32_t Hv, TO *__restrict__ o) {
+template <int NW>
+__device__ __forceinline__ void issue_images(uint8_t *stage, const uint8_t *kim, const uint8_t *tim,
+                                             int w, int lane) {
     using namespace chunk;
-    constexpr int IB = 16 * RPW * NW;  // state rows per block
-    constexpr int NRB = D / IB;        // blocks per (request, head)
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-    ChainSmem &sm = *reinterpret_cast<ChainSmem *>(smem_raw);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const bool computes = w < NW;
+#pragma unroll
+    for (int f = w; f < KIMG_FRAGS + TIMG_FRAGS; f += NW) {
+        const uint8_t *src = f < KIMG_FRAGS ? kim + (size_t)f * FRAG : tim + (size_t)(f - KIMG_FRAGS) * FRAG;
+        copy_frag(src, stage + (size_t)f * FRAG, lane);
+    }
+}
 
-    // blocks are dealt round-robin to the 8 XCDs: give each XCD a contiguous
-    // range of (request, head, row block) so blocks sharing K, Q and the prep
-    // records also share an L2
-    const int G_ = gridDim.x;
-    const int logical = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
-    const int rb = logical % NRB;
-    const int unit = logical / NRB;
-    const int h = unit % Hv;
-    const int r = unit / Hv;
-    if (r >= nreq) return;
-    const int kh = h / (Hv / Hk);
+template <int NW, int STAGES, typename TA, typename TO>
+__global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
+    const TA *__restrict__ v, float *__restrict__ state, const int32_t *__restrict__ qsl,
+    const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
+    const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
+    int32_t Hv, TO *__restrict__ o) {
+    using namespace chunk;
+    constexpr int IB = 16 * NW;  // state rows per block
+    constexpr int NRB = D / IB;  // blocks per (request, head)
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    const int group = Hv / Hk;
+    const int per_group = group * NRB;
+    const int xcd = blockIdx.x & 7;
+    const int qd = blockIdx.x >> 3;
+    const int gi = 8 * (qd / per_group) + xcd;  // (request rank, key head) group
+    const int jj = qd % per_group;
+    if (gi >= nreq * Hk) return;
+    const int r = order[gi / Hk];
+    const int kh = gi % Hk;
+    const int h = kh * group + jj / NRB;
+    const int rb = jj % NRB;
     const int tok0 = qsl[r];
     const int L = qsl[r + 1] - tok0;
     if (L <= 0) return;  // empty request: slot untouched
     const int nch = (L + CH - 1) / CH;
     const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
-    int irow[RPW];  // this lane's state rows (value channels)
-#pragma unroll
-    for (int rt = 0; rt < RPW; ++rt) irow[rt] = IB * rb + 16 * (RPW * w + rt) + lr;
+    const int irow = IB * rb + 16 * w + lr;  // this lane's state row (value channel)
     float *sbase = state + ((int64_t)slots[r] * Hv + h) * D * D;
 
     // state rows of this lane, transposed accumulator layout:
-    // ST[rt][jt][e] = S[irow[rt]][16 jt + 4 lg + e]
-    floatx4_t ST[RPW][8];
+    // ST[jt][e] = S[irow][16 jt + 4 lg + e]
+    floatx4_t ST[8];
 #pragma unroll
-    for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-        for (int jt = 0; jt < 8; ++jt) {
-            ST[rt][jt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-            if (computes && hi_init) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg);
-                ST[rt][jt] = floatx4_t{s4.x, s4.y, s4.z, s4.w};
-            }
+    for (int jt = 0; jt < 8; ++jt) {
+        ST[jt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        if (hi_init) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(sbase + (int64_t)irow * D + 16 * jt + 4 * lg);
+            ST[jt] = floatx4_t{s4.x, s4.y, s4.z, s4.w};
         }
+    }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-    ChainPrefetch<TA, RPW> pf;
-    pf.load(k, q, v, records, tok0, L, 0, c_first, Hk, Hv, h, kh, irow, computes, tid, lg);
-    for (int cc = 0; cc < nch; ++cc) {
+    const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
+    const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
+    const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
+
+    // v of this lane's row for tokens 16 tau + 4 lg + e of chunk cc
+    Raw1<TA> vr[2][4];
+    auto load_v = [&](int cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
-        __syncthreads();  // every wave is done reading the previous chunk's planes
-        pf.stage(sm, tid);
-        float vcur[RPW][2][4];
-#pragma unroll
-        for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vcur[rt][tau][e] = pf.vr[rt][tau][e];
-        __syncthreads();
-        // the next chunk's operands load while this one computes
-        if (cc + 1 < nch)
-            pf.load(k, q, v, records, tok0, L, cc + 1, c_first, Hk, Hv, h, kh, irow, computes, tid, lg);
-        if (!computes) continue;
-
-        // ---------------- X = K S0^T and OQ = Q S0^T  (tokens x this wave's rows)
-        floatx4_t X[RPW][2], OQ[RPW][2];
-#pragma unroll
-        for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau) {
-                X[rt][tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-                OQ[rt][tau] = X[rt][tau];
-            }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8_t sbh[RPW], sbl[RPW];
-#pragma unroll
-            for (int rt = 0; rt < RPW; ++rt) {
-                float sv[8];
-#pragma unroll
-                for (int p = 0; p < 8; ++p) sv[p] = ST[rt][2 * ks + (p >> 2)][p & 3];
-                split_vals(sv, sbh[rt], sbl[rt]);
-            }
-            const int c0 = 32 * ks + 4 * lg;
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau) {
-                const int row = 16 * tau + lr;
-                const bf16x8_t kh_ = frag_slots(sm.Kh[row], c0), kl_ = frag_slots(sm.Kl[row], c0);
-                const bf16x8_t qh_ = frag_slots(sm.Qh[row], c0), ql_ = frag_slots(sm.Ql[row], c0);
-#pragma unroll
-                for (int rt = 0; rt < RPW; ++rt) {
-                    mma3(X[rt][tau], kh_, kl_, sbh[rt], sbl[rt]);
-                    mma3(OQ[rt][tau], qh_, ql_, sbh[rt], sbl[rt]);
-                }
-            }
-        }
-        // E = beta (V - gamma X) (kept in X); OQ scaled by gamma
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tau + 4 * lg + e;
-                const float gm = sm.Gam[t], bt = sm.Beta[t];
-#pragma unroll
-                for (int rt = 0; rt < RPW; ++rt) {
-                    X[rt][tau][e] = bt * (vcur[rt][tau][e] - gm * X[rt][tau][e]);
-                    OQ[rt][tau][e] *= gm;
-                }
+                if (t < Lc) vr[tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow);
+                else vr[tau][e].zero();
             }
+    };
 
-        // ---------------- Delta = T (beta E), then O and the state update
-        const int c0 = 4 * lg;  // the chunk is one k-step
-        bf16x8_t ebh[RPW], ebl[RPW];
+    issue_images<NW>(smem, kim0, tim0, w, lane);
+    load_v(0);
+    for (int cc = 0; cc < nch; ++cc) {
+        const int tb = tok0 + cc * CH;
+        const int Lc = min(CH, L - cc * CH);
+        const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * STAGE : 0);
+        // this wave's copies and loads of chunk cc have landed; after the barrier
+        // every wave's have, and (two stages) every wave is done with chunk cc - 1
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        float vcur[2][4];
 #pragma unroll
-        for (int rt = 0; rt < RPW; ++rt) {
-            float ev[8];
+        for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int p = 0; p < 8; ++p) ev[p] = X[rt][p >> 2][p & 3];
-            split_vals(ev, ebh[rt], ebl[rt]);
+            for (int e = 0; e < 4; ++e) vcur[tau][e] = vr[tau][e].get();
+        if (STAGES == 2 && cc + 1 < nch) {
+            issue_images<NW>(smem + (size_t)((cc + 1) & 1) * STAGE, kim0 + (cc + 1) * kstep,
+                             tim0 + (cc + 1) * tstep, w, lane);
+            load_v(cc + 1);
         }
-        floatx4_t Dl[RPW][2];
+        const uint8_t *kst = stg + 16 * lane;          // this lane's piece of each K fragment
+        const uint8_t *tst = stg + KIMG + 16 * lane;   // and of each T fragment
+
+        // ---------------- X = K S0^T and OQ = Q S0^T  (tokens x this wave's rows)
+        floatx4_t X[2], OQ[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            const bf16x8_t th_ = frag_slots(sm.Th[16 * tau + lr], c0);
-            const bf16x8_t tl_ = frag_slots(sm.Tl[16 * tau + lr], c0);
+            X[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            OQ[tau] = X[tau];
+        }
 #pragma unroll
-            for (int rt = 0; rt < RPW; ++rt) {
-                Dl[rt][tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-                mma3(Dl[rt][tau], th_, tl_, ebh[rt], ebl[rt]);
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8_t sbh, sbl;
+            {
+                float sv[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) sv[p] = ST[2 * ks + (p >> 2)][p & 3];
+                split_vals(sv, sbh, sbl);
+            }
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const bf16x8_t kh_ = frag(kst + (FK + (0 + tau) * 4 + ks) * FRAG);
+                const bf16x8_t kl_ = frag(kst + (FK + (2 + tau) * 4 + ks) * FRAG);
+                const bf16x8_t qh_ = frag(kst + (FQ + (0 + tau) * 4 + ks) * FRAG);
+                const bf16x8_t ql_ = frag(kst + (FQ + (2 + tau) * 4 + ks) * FRAG);
+                mma3(X[tau], kh_, kl_, sbh, sbl);
+                mma3(OQ[tau], qh_, ql_, sbh, sbl);
             }
         }
-        bf16x8_t dbh[RPW], dbl[RPW], tbh[RPW], tbl[RPW];
+        // per-token gamma, e^{G_C - G_t}, beta for this lane's tokens
+        const uint8_t *tvec = stg + KIMG;
+        float4 gam[2], rev[2], bet[2];
 #pragma unroll
-        for (int rt = 0; rt < RPW; ++rt) {
+        for (int tau = 0; tau < 2; ++tau) {
+            const int t0 = 16 * tau + 4 * lg;
+            gam[tau] = *reinterpret_cast<const float4 *>(tvec + T_GAM + 4 * t0);
+            rev[tau] = *reinterpret_cast<const float4 *>(tvec + T_REV + 4 * t0);
+            bet[tau] = *reinterpret_cast<const float4 *>(tvec + T_BETA + 4 * t0);
+        }
+        const float gC = *reinterpret_cast<const float *>(tvec + T_GAM + 4 * (CH - 1));
+        // E = beta (V - gamma X) (kept in X); OQ scaled by gamma
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const float g4[4] = {gam[tau].x, gam[tau].y, gam[tau].z, gam[tau].w};
+            const float b4[4] = {bet[tau].x, bet[tau].y, bet[tau].z, bet[tau].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                X[tau][e] = b4[e] * (vcur[tau][e] - g4[e] * X[tau][e]);
+                OQ[tau][e] *= g4[e];
+            }
+        }
+
+        // ---------------- Delta = T (beta E), then O and the state update
+        bf16x8_t ebh, ebl;
+        {
+            float ev[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) ev[p] = X[p >> 2][p & 3];
+            split_vals(ev, ebh, ebl);
+        }
+        floatx4_t Dl[2];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            Dl[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            mma3(Dl[tau], frag(tst + (FT + tau) * FRAG), frag(tst + (FT + 2 + tau) * FRAG), ebh, ebl);
+        }
+        bf16x8_t dbh, dbl, tbh, tbl;
+        {
+            const float r8[8] = {rev[0].x, rev[0].y, rev[0].z, rev[0].w,
+                                 rev[1].x, rev[1].y, rev[1].z, rev[1].w};
             float dv[8], dtv[8];
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
-                dv[p] = Dl[rt][p >> 2][p & 3];
-                dtv[p] = dv[p] * sm.Rev[16 * (p >> 2) + 4 * lg + (p & 3)];
+                dv[p] = Dl[p >> 2][p & 3];
+                dtv[p] = dv[p] * r8[p];
             }
-            split_vals(dv, dbh[rt], dbl[rt]);
-            split_vals(dtv, tbh[rt], tbl[rt]);
+            split_vals(dv, dbh, dbl);
+            split_vals(dtv, tbh, tbl);
         }
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            const bf16x8_t ph_ = frag_slots(sm.Ph[16 * tau + lr], c0);
-            const bf16x8_t pl_ = frag_slots(sm.Pl[16 * tau + lr], c0);
-#pragma unroll
-            for (int rt = 0; rt < RPW; ++rt) mma3(OQ[rt][tau], ph_, pl_, dbh[rt], dbl[rt]);
-        }
-        const float gC = sm.Gam[CH - 1];
+        for (int tau = 0; tau < 2; ++tau)
+            mma3(OQ[tau], frag(tst + (FP + tau) * FRAG), frag(tst + (FP + 2 + tau) * FRAG), dbh, dbl);
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-            const bf16x8_t kth = frag_slots(sm.KTh[16 * jt + lr], c0);
-            const bf16x8_t ktl = frag_slots(sm.KTl[16 * jt + lr], c0);
-#pragma unroll
-            for (int rt = 0; rt < RPW; ++rt) {
-                ST[rt][jt] *= gC;
-                mma3(ST[rt][jt], kth, ktl, tbh[rt], tbl[rt]);
-            }
+            ST[jt] *= gC;
+            mma3(ST[jt], frag(kst + (FKT + jt) * FRAG), frag(kst + (FKT + 8 + jt) * FRAG), tbh, tbl);
         }
 #pragma unroll
-        for (int rt = 0; rt < RPW; ++rt)
+        for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tau + 4 * lg + e;
-                    if (t < Lc) st(o + ((int64_t)(tb + t) * Hv + h) * D + irow[rt], OQ[rt][tau][e] * inv_sqrt_d);
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tau + 4 * lg + e;
+                if (t < Lc) st(o + ((int64_t)(tb + t) * Hv + h) * D + irow, OQ[tau][e] * inv_sqrt_d);
+            }
+        if (STAGES == 1) {
+            __syncthreads();  // every wave is done reading the stage
+            if (cc + 1 < nch) {
+                issue_images<NW>(smem, kim0 + (cc + 1) * kstep, tim0 + (cc + 1) * tstep, w, lane);
+                load_v(cc + 1);
+            }
+        }
     }
 
-    if (computes) {
 #pragma unroll
-        for (int rt = 0; rt < RPW; ++rt)
-#pragma unroll
-            for (int jt = 0; jt < 8; ++jt)
-                *reinterpret_cast<float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg) =
-                    make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]);
-    }
+    for (int jt = 0; jt < 8; ++jt)
+        *reinterpret_cast<float4 *>(sbase + (int64_t)irow * D + 16 * jt + 4 * lg) =
+            make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -669,9 +678,21 @@ __global__ __launch_bounds__(256, 2) void prefill_chain_kernel(
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t prefill_chunk_workspace_bytes(int32_t Hv, int32_t T, int32_t nreq) {
-    const size_t max_chunks = (size_t)T / chunk::CH + (size_t)nreq;
-    return align256((size_t)(nreq + 1) * 4) + max_chunks * (size_t)Hv * chunk::REC_BYTES;
+// chunk offsets and request order, then the images of every possible chunk
+// (a request of L tokens has ceil(L / 32) <= L / 32 + 1 chunks)
+struct ChunkWorkspace {
+    size_t meta, kimg, timg, total;
+    ChunkWorkspace(int32_t Hk, int32_t Hv, int32_t T, int32_t nreq) {
+        const size_t max_chunks = (size_t)T / chunk::CH + (size_t)nreq;
+        meta = align256((size_t)(2 * nreq + 1) * 4);
+        kimg = max_chunks * (size_t)Hk * chunk::KIMG;
+        timg = max_chunks * (size_t)Hv * chunk::TIMG;
+        total = meta + kimg + timg;
+    }
+};
+
+size_t prefill_chunk_workspace_bytes(int32_t Hk, int32_t Hv, int32_t T, int32_t nreq) {
+    return ChunkWorkspace(Hk, Hv, T, nreq).total;
 }
 
 template <typename K>
@@ -683,29 +704,35 @@ static hipError_t set_smem(K kern, size_t bytes, bool &done) {
     return e;
 }
 
-template <int NW, int RPW, typename TA, typename TO>
+template <int NW, int STAGES, typename TA, typename TO>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
-                               const uint8_t *records) {
+                               const int32_t *order, const uint8_t *kimg, const uint8_t *timg) {
     using namespace chunk;
     static bool set = false;
-    hipError_t e = set_smem(&prefill_chain_kernel<NW, RPW, TA, TO>, sizeof(ChainSmem), set);
+    const size_t smem = STAGES * STAGE;
+    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO>, smem, set);
     if (e != hipSuccess) return e;
-    const int64_t blocks = (int64_t)a.nreq * a.Hv * (D / (16 * NW * RPW));
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, RPW, TA, TO>), dim3((unsigned)blocks), dim3(256),
-                       sizeof(ChainSmem), s, (const TA *)a.q, (const TA *)a.k, (const TA *)a.v,
-                       a.state, a.qsl, a.slots, a.has_init, chunk_off, records, a.nreq, a.Hk, a.Hv,
-                       (TO *)a.o);
+    const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
+    const int64_t groups = (int64_t)a.nreq * a.Hk;
+    const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO>), dim3((unsigned)blocks),
+                       dim3(64 * NW), smem, s, (const TA *)a.v, a.state, a.qsl, a.slots,
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o);
     return hipGetLastError();
 }
 
 template <typename TA, typename TG, typename TO>
 static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     using namespace chunk;
-    int32_t *chunk_off = static_cast<int32_t *>(a.ws);
-    uint8_t *records = static_cast<uint8_t *>(a.ws) + align256((size_t)(a.nreq + 1) * 4);
+    const ChunkWorkspace wl(a.Hk, a.Hv, a.T, a.nreq);
+    uint8_t *base = static_cast<uint8_t *>(a.ws);
+    int32_t *chunk_off = reinterpret_cast<int32_t *>(base);
+    int32_t *order = chunk_off + (a.nreq + 1);
+    uint8_t *kimg = base + wl.meta;
+    uint8_t *timg = kimg + wl.kimg;
     const int64_t max_chunks = (int64_t)a.T / CH + a.nreq;
 
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, s, a.qsl, a.nreq, chunk_off);
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, s, a.qsl, a.nreq, chunk_off, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -714,15 +741,15 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_prep_kernel<TA, TG>), dim3((unsigned)(max_chunks * a.Hk)), dim3(256),
                        sizeof(PrepSmem), s, (const TA *)a.q, (const TA *)a.k, (const TG *)a.a,
-                       (const TG *)a.b, a.gate_ld, a.qsl, chunk_off, a.nreq, a.Hk, a.Hv, records);
+                       (const TG *)a.b, a.gate_ld, a.qsl, chunk_off, a.nreq, a.Hk, a.Hv, kimg, timg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // state rows per chain block: 64 when there are enough (request, head)
-    // units to fill the chip, 32 otherwise
+    // a whole head (8 waves) per block when there are enough (request, head)
+    // units to fill the chip, else 32 state rows per block
     const int64_t units = (int64_t)a.nreq * a.Hv;
-    if (units >= 128) return launch_chain<4, 1, TA, TO>(a, s, chunk_off, records);  // 64 rows
-    return launch_chain<2, 1, TA, TO>(a, s, chunk_off, records);                    // 32 rows
+    if (units >= 256) return launch_chain<8, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
+    return launch_chain<2, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
 }
 template <typename TA, typename TG>
 static hipError_t launch_chunk_o(const PrefillArgs &a, hipStream_t s) {
