@@ -4,8 +4,10 @@
                     [--no-cpu]
 
 Headline workload (N=1): one decode step of 64 requests at full shapes (16 key /
-48 value heads, d = 128, fp32 state [64,48,128,128]): conv1d_update ->
-decode_step -> gated_norm, with every input already resident in HBM.  `value`
+48 value heads, d = 128, fp32 state [64,48,128,128]): conv update -> recurrence
+-> gated norm in one launch (gdn_decode_fused), with every input already
+resident in HBM; the same step as three launches (conv1d_update ->
+decode_step -> gated_norm) is timed beside it.  `value`
 is the state bytes each step reads and writes (2 x 64 x 3 MiB) divided by the
 measured step time.  A prefill leg (single 4096-token sequence; 16-request
 packed varlen batch) reports tokens/s in the same run, a layer leg times the
@@ -55,11 +57,11 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, source):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/<kernel>_traffic.txt: FETCH_SIZE and WRITE_SIZE scaled by
     a plain copy's reading), or None when that summary is missing or was taken
-    on a different version of the kernel's source."""
+    on a different version of the kernel's source file."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -69,10 +71,23 @@ def measured_traffic(kernel):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 vals[key.strip()] = val.strip()
-    src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", vals.get("source", ""))
-    if not os.path.exists(src) or source_digest(src) != vals.get("source_sha256_16"):
+    src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", source)
+    if vals.get("source") != source or source_digest(src) != vals.get("source_sha256_16"):
         return None
     return int(float(vals["hbm_bytes_per_launch"]))
+
+
+def fused_decode_bytes(d, R, act_bytes=2, y_bytes=2):
+    """Algorithmic HBM bytes of one gdn_decode_fused launch: the state read and
+    written once; the token's conv inputs, z and gates read once; its conv
+    history read and written once; y written once (413,413,376 B at 64
+    requests, full shapes, bf16 activations)."""
+    Hv, D = d.num_v_heads, d.head_dim_v
+    C = 2 * d.num_k_heads * d.head_dim_k + Hv * D
+    state = 2 * R * Hv * D * d.head_dim_k * 4
+    io = R * (C * act_bytes + 2 * C * (d.conv_taps - 1) * act_bytes + Hv * D * act_bytes
+              + 2 * Hv * act_bytes + Hv * D * y_bytes)
+    return state + io
 
 
 def decode_bytes(d, R, act_bytes=4, o_bytes=4):
@@ -126,43 +141,65 @@ def main():
     o = torch.empty((R, d.num_v_heads, D), device=dev)
     y = torch.empty((R, d.num_v_heads * D), dtype=torch.bfloat16, device=dev)
 
-    ev = {n: [] for n in ("conv", "decode", "norm")}
-
+    sh = stream.cuda_stream  # raw hipStream_t, passed to every call
     it_count = [0]
 
-    def decode_step(record):
+    def three_launch_step(ev=None):
         conv_pool = conv_pools[it_count[0] % n_rot]
         state = states[it_count[0] % n_rot]
         it_count[0] += 1
-        if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record(stream)
-        gdn.gdn_conv1d_update(d, x, conv_w, conv_pool, qsl, slots, hinit, q, k, v, l2_eps=L2_EPS)
-        if record:
-            e[1].record(stream)
-        gdn.gdn_decode_step(d, q, k, v, a, b, state, slots, o)
-        if record:
-            e[2].record(stream)
-        gdn.gdn_gated_norm(d, o, z, gamma, y, eps=NORM_EPS)
-        if record:
-            e[3].record(stream)
-            ev["conv"].append((e[0], e[1]))
-            ev["decode"].append((e[1], e[2]))
-            ev["norm"].append((e[2], e[3]))
+        if ev:
+            ev[0].record(stream)
+        gdn.gdn_conv1d_update(d, x, conv_w, conv_pool, qsl, slots, hinit, q, k, v, l2_eps=L2_EPS,
+                              stream=sh)
+        if ev:
+            ev[1].record(stream)
+        gdn.gdn_decode_step(d, q, k, v, a, b, state, slots, o, stream=sh)
+        if ev:
+            ev[2].record(stream)
+        gdn.gdn_gated_norm(d, o, z, gamma, y, eps=NORM_EPS, stream=sh)
+        if ev:
+            ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        decode_step(False)
+    def fused_step(ev=None):
+        conv_pool = conv_pools[it_count[0] % n_rot]
+        state = states[it_count[0] % n_rot]
+        it_count[0] += 1
+        gdn.gdn_decode_fused(d, x, z, a, b, conv_w, gamma, conv_pool, state, slots, y,
+                             l2_eps=L2_EPS, norm_eps=NORM_EPS, stream=sh)
+
+    def timed(step):
+        """K back-to-back steps after W warm-up steps: wall-clock ms per step, and
+        the stream's own time per step from one event pair around the region."""
+        for _ in range(args.warmup):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        return wall, e0.elapsed_time(e1) / args.steps
+
+    ms_three, gpu_three = timed(three_launch_step)
+    ms_step, gpu_fused = timed(fused_step)
+    # per-launch breakdown of the three-launch step (events between launches add a
+    # few microseconds each, so this pass is separate from the timed ones)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        three_launch_step(e)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        decode_step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    kern_ms = {n: float(np.mean([s.elapsed_time(e) for s, e in ev[n]])) for n in ev}
+    kern_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+               for i, n in enumerate(("conv", "decode", "norm"))}
+    kern_ms["fused"] = gpu_fused
     state_bytes, dec_bytes = decode_bytes(d, R)
+    step_bytes = fused_decode_bytes(d, R)
     value = state_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dec_bytes / (kern_ms["decode"] * 1e-3) / 1e9
+    achieved = step_bytes / (gpu_fused * 1e-3) / 1e9
+    achieved_dec = dec_bytes / (kern_ms["decode"] * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -180,20 +217,31 @@ def main():
         "config": {
             "workload": "decode_r64: 64 requests x 1 token; 16 key / 48 value heads; "
                         "d_k = d_v = 128; fp32 state [64,48,128,128]; bf16 inputs",
-            "step": "gdn_conv1d_update + gdn_decode_step + gdn_gated_norm",
+            "step": "gdn_decode_fused (conv update + recurrence + gated norm, one launch)",
             "state_bytes_per_step": state_bytes,
             "state_pools_rotated": n_rot,
         },
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
         "roofline": {
-            "kernel": "decode_kernel (gdn_decode_step)",
+            "kernel": "decode_fused_kernel (gdn_decode_fused)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": dec_bytes,
-            "traffic": measured_traffic("decode_kernel"),
+            "bytes_per_launch": step_bytes,
+            "traffic": measured_traffic("decode_fused_kernel", "decode_fused.hip"),
+        },
+        "three_launch": {
+            "step": "gdn_conv1d_update + gdn_decode_step + gdn_gated_norm",
+            "ms_per_step": round(ms_three, 4),
+            "gpu_ms_per_step": round(gpu_three, 4),
+            "value": round(state_bytes / (ms_three * 1e-3) / 1e9, 2),
+            "decode_kernel_roofline": {
+                "achieved": round(achieved_dec, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved_dec / HBM_PEAK_GBS, 4), "bytes_per_launch": dec_bytes,
+                "traffic": measured_traffic("decode_kernel", "decode.hip"),
+            },
         },
     }
     del states, conv_pools

@@ -144,8 +144,230 @@ __global__ __launch_bounds__(256) void conv1d_silu_l2_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Vectorised variant for long packed batches: a lane owns 8 consecutive
+// channels (16-byte accesses), a wave 512 channels, and a wave loads its whole
+// tile of U tokens plus the 3 rows before it and the 2 after it up front, so a
+// tile costs one memory latency instead of one per token.  Token ownership and
+// the history hand-over are the same as above; the history of 8 channels is 24
+// contiguous elements, moved as raw bits so copies stay bit-exact.
+// ---------------------------------------------------------------------------
+// N consecutive elements held as raw 32-bit words (N * sizeof(TX) a multiple of
+// 16 bytes); element access is shifts and masks on registers.
+template <typename TX, int N> struct RawVec {
+    static constexpr int NV = N * (int)sizeof(TX) / 16;
+    uint4 v[NV];
+    __device__ __forceinline__ void load(const TX *p) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = reinterpret_cast<const uint4 *>(p)[i];
+    }
+    __device__ __forceinline__ void store(TX *p) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) reinterpret_cast<uint4 *>(p)[i] = v[i];
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = make_uint4(0, 0, 0, 0);
+    }
+    __device__ __forceinline__ uint32_t word(int wi) const {
+        const uint4 &q = v[wi >> 2];
+        return (wi & 3) == 0 ? q.x : (wi & 3) == 1 ? q.y : (wi & 3) == 2 ? q.z : q.w;
+    }
+    __device__ __forceinline__ void set_word(int wi, uint32_t val) {
+        uint4 &q = v[wi >> 2];
+        if ((wi & 3) == 0) q.x = val;
+        else if ((wi & 3) == 1) q.y = val;
+        else if ((wi & 3) == 2) q.z = val;
+        else q.w = val;
+    }
+    // raw bits of element i (bf16: low 16 bits)
+    __device__ __forceinline__ uint32_t bits(int i) const {
+        if constexpr (sizeof(TX) == 2) return (word(i >> 1) >> (16 * (i & 1))) & 0xffffu;
+        else return word(i);
+    }
+    __device__ __forceinline__ float f(int i) const {
+        if constexpr (sizeof(TX) == 2) return __uint_as_float(bits(i) << 16);
+        else return __uint_as_float(word(i));
+    }
+    // set all elements from raw bits
+    template <int M> __device__ __forceinline__ void set_bits(const uint32_t (&b)[M]) {
+        static_assert(M == N, "element count");
+        if constexpr (sizeof(TX) == 2) {
+#pragma unroll
+            for (int wi = 0; wi < N / 2; ++wi) set_word(wi, b[2 * wi] | (b[2 * wi + 1] << 16));
+        } else {
+#pragma unroll
+            for (int wi = 0; wi < N; ++wi) set_word(wi, b[wi]);
+        }
+    }
+};
+
+constexpr int CV_WAVE_CH = 512;  // 64 lanes x 8 channels
+constexpr int CV_WAVES = 4;
+
+// Output of one token for the lane's 8 channels: SiLU of the 4-tap sum, then
+// the per-head L2 norm for q and k (a head is D / 8 lanes, aligned).
+template <int D, typename TO>
+__device__ __forceinline__ void conv_emit(const float (&wt)[4][8], const float (&xw)[4][8], bool active,
+                                          int c, int t, int nq, int nqk, int nv, float l2_eps,
+                                          TO *__restrict__ q, TO *__restrict__ k, TO *__restrict__ v) {
+    float y[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float a = wt[0][e] * xw[0][e] + wt[1][e] * xw[1][e] + wt[2][e] * xw[2][e] +
+                        wt[3][e] * xw[3][e];
+        y[e] = silu_f(a);
+        ss += y[e] * y[e];
+    }
+    ss = group_sum<D / 8>(ss);
+    if (active) {
+        if (c < nqk) {
+            const float inv = 1.0f / sqrtf(ss + l2_eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= inv;
+            store8(c < nq ? q + (int64_t)t * nq + c : k + (int64_t)t * nq + (c - nq), y);
+        } else {
+            store8(v + (int64_t)t * nv + (c - nqk), y);
+        }
+    }
+}
+
+template <int D, typename TX, typename TW, typename TO, int U>
+__global__ __launch_bounds__(256) void conv1d_vec_kernel(
+    const TX *__restrict__ x, int64_t x_ld, const TW *__restrict__ w, TX *__restrict__ pool,
+    const int32_t *__restrict__ qsl, const int32_t *__restrict__ slots,
+    const uint8_t *__restrict__ has_init, int32_t nreq, int32_t T, int32_t C, int32_t nq,
+    float l2_eps, TO *__restrict__ q, TO *__restrict__ k, TO *__restrict__ v) {
+    static_assert(U + 4 <= 32, "start mask");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = (blockIdx.y * CV_WAVES + wave) * CV_WAVE_CH + 8 * lane;
+    const bool active = c < C;  // C is a multiple of 8 and of D, so a lane never straddles q|k|v
+    const int t_begin = blockIdx.x * U;
+    const int t_nom_end = min(T, t_begin + U);
+    const int nqk = 2 * nq;
+    const int nv = C - nqk;
+
+    // taps: wt[i][e] multiplies x[t - i] in channel c + e (w is [C][4], 32 contiguous elements)
+    float wt[4][8];
+    {
+        RawVec<TW, 32> wr;
+        if (active) wr.load(w + (int64_t)c * 4);
+        else wr.zero();
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wt[i][e] = wr.f(4 * e + i);
+    }
+    // rows t_begin - 3 .. t_begin + U - 1 (xr[m] is row t_begin - 3 + m)
+    RawVec<TX, 8> xr[U + 3];
+#pragma unroll
+    for (int m = 0; m < U + 3; ++m) {
+        const int row = t_begin - 3 + m;
+        if (active && row >= 0 && row < T) xr[m].load(x + (int64_t)row * x_ld + c);
+        else xr[m].zero();
+    }
+
+    // bit b of `starts`: token t_begin - 2 + b is the first token of a non-empty request
+    uint32_t starts = 0;
+    {
+        const int lo = max(t_begin - 2, 0);
+        if (lo < T) {
+            for (int r = locate_request(qsl, nreq, lo); r < nreq && qsl[r] < t_begin + U + 2; ++r)
+                if (qsl[r + 1] > qsl[r] && qsl[r] >= t_begin - 2) starts |= 1u << (qsl[r] - (t_begin - 2));
+        }
+    }
+
+    // tokens whose 4-token window lies inside their request (no start among t-2 .. t)
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int t = t_begin + j;
+        if (t < T && ((starts >> j) & 7u) == 0) {  // uniform over the block
+            float xw[4][8];  // xw[i] = x[t - i]
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xw[i][e] = xr[j + 3 - i].f(e);
+            conv_emit<D>(wt, xw, active, c, t, nq, nqk, nv, l2_eps, q, k, v);
+        }
+    }
+
+    // each request starting in [t_begin, t_nom_end): its first (up to) three
+    // tokens read the request's history, and this lane then writes the new
+    // history (it alone read the old entries)
+    for (int j = 0; j < U; ++j) {
+        if (!((starts >> (j + 2)) & 1u)) continue;
+        const int t0 = t_begin + j;
+        if (t0 >= t_nom_end) break;
+        const int rr = locate_request(qsl, nreq, t0);
+        const int L = qsl[rr + 1] - t0;
+        const bool hi = has_init == nullptr || has_init[rr] != 0;
+        TX *hp = pool + ((int64_t)slots[rr] * C + c) * 3;
+        RawVec<TX, 24> oldh;
+        if (active && hi) oldh.load(hp);
+        else oldh.zero();
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            if (m >= L) break;  // uniform
+            float xw[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (m >= i) {
+                    RawVec<TX, 8> xv;
+                    if (active) xv.load(x + (int64_t)(t0 + m - i) * x_ld + c);
+                    else xv.zero();
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xw[i][e] = xv.f(e);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xw[i][e] = oldh.f(3 * e + 3 + m - i);  // oldest first
+                }
+            }
+            conv_emit<D>(wt, xw, active, c, t0 + m, nq, nqk, nv, l2_eps, q, k, v);
+        }
+        if (active) {
+            // new history: the last three entries of [old history | request rows]
+            uint32_t nb[24];
+#pragma unroll
+            for (int jj = 0; jj < 3; ++jj) {
+                const int m = L + jj;  // index into [h0, h1, h2, x0 .. x_{L-1}]
+                if (m >= 3) {
+                    RawVec<TX, 8> xv;
+                    xv.load(x + (int64_t)(t0 + m - 3) * x_ld + c);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) nb[3 * e + jj] = xv.bits(e);
+                } else {
+                    // m = L + jj <= 2 (L >= 1): entry jj + 1 or jj + 2 of the old history
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        nb[3 * e + jj] = m == jj + 1 ? oldh.bits(3 * e + jj + 1)
+                                                     : oldh.bits(3 * e + (jj + 2 < 3 ? jj + 2 : 2));
+                }
+            }
+            RawVec<TX, 24> newh;
+            newh.set_bits(nb);
+            newh.store(hp);
+        }
+    }
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <int D, typename TX, typename TW, typename TO>
 static hipError_t launch_conv_t(const ConvArgs &a, hipStream_t s) {
+    // long batches with 16-byte aligned rows take the vectorised kernel
+    const bool vec_ok = a.x_ld % (16 / sizeof(TX)) == 0 && aligned16(a.x) && aligned16(a.w) &&
+                        aligned16(a.pool) && aligned16(a.q) && aligned16(a.k) && aligned16(a.v);
+    if (a.T > 1024 && vec_ok) {
+        constexpr int U = sizeof(TX) == 2 ? 16 : 8;
+        dim3 grid((a.T + U - 1) / U, (a.C + CV_WAVES * CV_WAVE_CH - 1) / (CV_WAVES * CV_WAVE_CH));
+        hipLaunchKernelGGL((conv1d_vec_kernel<D, TX, TW, TO, U>), grid, dim3(256), 0, s,
+                           (const TX *)a.x, a.x_ld, (const TW *)a.w, (TX *)a.pool, a.qsl, a.slots,
+                           a.has_init, a.nreq, a.T, a.C, a.nq, a.l2_eps, (TO *)a.q, (TO *)a.k,
+                           (TO *)a.v);
+        return hipGetLastError();
+    }
     // short tiles when the batch is small (decode), longer ones for prefill
     const int tile = a.T <= 1024 ? 1 : (a.T <= 16384 ? 8 : 16);
     dim3 grid((a.T + tile - 1) / tile, (a.C + CONV_CH_PER_BLOCK - 1) / CONV_CH_PER_BLOCK);

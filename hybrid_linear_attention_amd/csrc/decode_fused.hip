@@ -1,0 +1,250 @@
+// One decode step of the GDN mixer core in a single launch: conv1d + SiLU with
+// the 3-entry history, L2 norm of q and k, the gated delta rule on the fp32
+// state, and the gated RMSNorm of the output.
+//
+// The step ("Qwen3.8-27B: from model structure to the vLLM inference
+// dataflow", section 02, one token's journey through a GDN layer; section 01
+// operator table, conv / GDN / gated-output rows) for one token of request r:
+//   c = SiLU(w0 x + w1 h2 + w2 h1 + w3 h0)   h <- [h1, h2, x]   (history oldest first)
+//   q = c_q / |c_q|,  k = c_k / |c_k|,  v = c_v
+//   S' = alpha S + beta (v - alpha S k) k^T,   o = S' q / sqrt(d)
+//   y = o / rms(o) * gamma * SiLU(z)           (per value head over d_v)
+// with alpha = exp(-softplus(a)), beta = sigmoid(b).
+//
+// One block per (request, key head): the key head's q and k channels and the v
+// channels of the value heads that read it are computed once, their history
+// entries are read and rewritten by the same thread (race-free), and the
+// block then streams those value heads' state rows (read once, written once,
+// nontemporal) and normalises whole heads of o from LDS.  The first rows'
+// state loads are issued before the conv so its latency hides under them.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int DF_THREADS = 1024;  // fastest of 256, 512, 1024 threads per group block, measured
+
+template <int D, int PF, typename TX, typename TW, typename TY>
+__global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
+    const TX *__restrict__ x, int64_t x_ld, const TX *__restrict__ z, int64_t z_ld,
+    const TX *__restrict__ ga, const TX *__restrict__ gb, int64_t gate_ld,
+    const TW *__restrict__ w, const TW *__restrict__ gamma, TX *__restrict__ pool,
+    float *__restrict__ state, const int32_t *__restrict__ slots,
+    const uint8_t *__restrict__ has_init, int32_t Hk, int32_t Hv, float l2_eps,
+    float norm_eps, TY *__restrict__ y, float *__restrict__ o_out) {
+    constexpr int LPR = D / 8;              // lanes per state row
+    constexpr int RPP = DF_THREADS / LPR;   // rows per pass
+    extern __shared__ __attribute__((aligned(16))) float dsm[];
+    const int G = Hv / Hk;
+    const int rows = G * D;
+    float *sq = dsm;            // [D]   q (then normalised)
+    float *sk = sq + D;         // [D]   k
+    float *sv = sk + D;         // [G*D] v
+    float *so = sv + rows;      // [G*D] o
+    float *sa = so + rows;      // [G]   alpha
+    float *sb = sa + G;         // [G]   beta
+    float *red = sb + G;        // [32]  reductions
+
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x / Hk;
+    const int kh = blockIdx.x - r * Hk;
+    const int slot = slots[r];
+    const int nq = Hk * D;
+    const int C = 2 * nq + Hv * D;
+    const int l = tid % LPR;
+    const int rg = tid / LPR;
+    const int npass = (rows + RPP - 1) / RPP;
+    // rows R = hh * D + i of the group's heads are contiguous in the slot
+    float *sbase = state + ((int64_t)slot * Hv + (int64_t)kh * G) * D * D + 4 * l;
+
+    // has_initial = 0: a new request, zero history and zero state
+    const bool hi = has_init == nullptr || has_init[r] != 0;
+
+    // state rows of the first PF passes (lane: columns 4 l + 4 LPR m + 0..3)
+    f32x4 buf[PF + 1][2];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int R = p * RPP + rg;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            buf[p][m] = hi && R < rows ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+                                             sbase + (int64_t)R * D + 4 * LPR * m))
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // conv of the group's channels: q (D), k (D), v (G D)
+    for (int e = tid; e < (2 + G) * D; e += DF_THREADS) {
+        int c;
+        float *dst;
+        if (e < D) {
+            c = kh * D + e;
+            dst = sq + e;
+        } else if (e < 2 * D) {
+            c = nq + kh * D + (e - D);
+            dst = sk + (e - D);
+        } else {
+            c = 2 * nq + kh * G * D + (e - 2 * D);
+            dst = sv + (e - 2 * D);
+        }
+        TX *hp = pool + ((int64_t)slot * C + c) * 3;
+        const TX x0 = x[(int64_t)r * x_ld + c];
+        TX h0 = from_f32<TX>(0.f), h1 = h0, h2 = h0;
+        if (hi) {
+            h0 = hp[0];
+            h1 = hp[1];
+            h2 = hp[2];
+        }
+        const float acc = ld(w + (int64_t)c * 4) * to_f32(x0) + ld(w + (int64_t)c * 4 + 1) * to_f32(h2) +
+                          ld(w + (int64_t)c * 4 + 2) * to_f32(h1) + ld(w + (int64_t)c * 4 + 3) * to_f32(h0);
+        *dst = silu_f(acc);
+        hp[0] = h1;  // the window slides: raw copies, bit-exact
+        hp[1] = h2;
+        hp[2] = x0;
+    }
+    if (tid < G) {
+        const int64_t go = (int64_t)r * gate_ld + kh * G + tid;
+        sa[tid] = gate_alpha(ld(ga + go));
+        sb[tid] = gate_beta(ld(gb + go));
+    }
+    __syncthreads();
+
+    // |q|^2, |k|^2 and q.k (one wave each)
+    {
+        const int wv = tid >> 6, lane = tid & 63;
+        if (wv < 3) {
+            float s = 0.f;
+            for (int j = lane; j < D; j += 64)
+                s += wv == 0 ? sq[j] * sq[j] : wv == 1 ? sk[j] * sk[j] : sq[j] * sk[j];
+            s = group_sum<64>(s);
+            if (lane == 0) red[wv] = s;
+        }
+    }
+    __syncthreads();
+    const float inv_q = 1.0f / sqrtf(red[0] + l2_eps);
+    const float inv_k = 1.0f / sqrtf(red[1] + l2_eps);
+    const float kq = red[2] * inv_q * inv_k;
+    float kc[2][4], qc[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kc[m][j] = sk[4 * l + 4 * LPR * m + j] * inv_k;
+            qc[m][j] = sq[4 * l + 4 * LPR * m + j] * inv_q;
+        }
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+    // state rows, PF passes ahead
+    for (int p = 0; p < npass; ++p) {
+        const int Rn = (p + PF) * RPP + rg;
+        if (p + PF < npass) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                buf[PF][m] = hi && Rn < rows ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+                                                   sbase + (int64_t)Rn * D + 4 * LPR * m))
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const int R = p * RPP + rg;
+        const bool valid = R < rows;
+        const int hh = valid ? R / D : 0;
+        const float alpha = sa[hh], beta = sb[hh];
+        const float vi = valid ? sv[R] : 0.f;
+        float pk = 0.f, pq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const f32x4 s = buf[0][m];
+            pk += s.x * kc[m][0] + s.y * kc[m][1] + s.z * kc[m][2] + s.w * kc[m][3];
+            pq += s.x * qc[m][0] + s.y * qc[m][1] + s.z * qc[m][2] + s.w * qc[m][3];
+        }
+        pk = group_sum<LPR>(pk);
+        pq = group_sum<LPR>(pq);
+        const float be = beta * (vi - alpha * pk);
+        if (valid) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                f32x4 s = buf[0][m];
+                s.x = alpha * s.x + be * kc[m][0];
+                s.y = alpha * s.y + be * kc[m][1];
+                s.z = alpha * s.z + be * kc[m][2];
+                s.w = alpha * s.w + be * kc[m][3];
+                __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(sbase + (int64_t)R * D + 4 * LPR * m));
+            }
+            if (l == 0) so[R] = (alpha * pq + be * kq) * inv_sqrt_d;
+        }
+#pragma unroll
+        for (int b = 0; b < PF; ++b) {
+            buf[b][0] = buf[b + 1][0];
+            buf[b][1] = buf[b + 1][1];
+        }
+    }
+    __syncthreads();
+
+    // gated RMSNorm of the group's heads, DF_THREADS elements (whole heads) at a time
+    const int nchunks = (rows + DF_THREADS - 1) / DF_THREADS;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int e = ch * DF_THREADS + tid;
+        const bool valid = e < rows;
+        const float ov = valid ? so[e] : 0.f;
+        float ss;
+        if constexpr (D <= 64) {
+            ss = group_sum<D>(ov * ov);
+        } else {
+            // a head spans D / 64 waves
+            const float part = group_sum<64>(ov * ov);
+            if ((tid & 63) == 0) red[4 + (tid >> 6)] = part;
+            __syncthreads();
+            ss = 0.f;
+            const int w0 = (tid >> 6) & ~(D / 64 - 1);
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) ss += red[4 + w0 + j];
+            __syncthreads();
+        }
+        if (valid) {
+            const int hh = e / D, i = e - hh * D;
+            const int h = kh * G + hh;
+            const float inv = 1.0f / sqrtf(ss * (1.0f / D) + norm_eps);
+            const float zz = ld(z + (int64_t)r * z_ld + (int64_t)h * D + i);
+            st(y + ((int64_t)r * Hv + h) * D + i, ov * inv * ld(gamma + i) * silu_f(zz));
+            if (o_out) o_out[((int64_t)r * Hv + h) * D + i] = ov;
+        }
+    }
+}
+
+size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv) {
+    const int G = Hv / Hk;
+    return (size_t)(2 * D + 2 * G * D + 2 * G + 32) * sizeof(float);
+}
+
+template <int D, typename TX, typename TW, typename TY>
+static hipError_t launch_df_t(const DecodeFusedArgs &a, hipStream_t s) {
+    const size_t smem = decode_fused_smem_bytes(D, a.Hk, a.Hv);
+    hipLaunchKernelGGL((decode_fused_kernel<D, 2, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
+                       dim3(DF_THREADS), smem, s, (const TX *)a.x, a.x_ld, (const TX *)a.z, a.z_ld,
+                       (const TX *)a.a, (const TX *)a.b, a.gate_ld, (const TW *)a.w,
+                       (const TW *)a.gamma, (TX *)a.pool, a.state, a.slots, a.has_init, a.Hk, a.Hv,
+                       a.l2_eps, a.norm_eps, (TY *)a.y, a.o);
+    return hipGetLastError();
+}
+template <int D, typename TX, typename TW>
+static hipError_t launch_df_y(const DecodeFusedArgs &a, hipStream_t s) {
+    return a.y_bf16 ? launch_df_t<D, TX, TW, bf16>(a, s) : launch_df_t<D, TX, TW, float>(a, s);
+}
+template <int D, typename TX>
+static hipError_t launch_df_w(const DecodeFusedArgs &a, hipStream_t s) {
+    return a.w_bf16 ? launch_df_y<D, TX, bf16>(a, s) : launch_df_y<D, TX, float>(a, s);
+}
+template <int D>
+static hipError_t launch_df_x(const DecodeFusedArgs &a, hipStream_t s) {
+    return a.act_bf16 ? launch_df_w<D, bf16>(a, s) : launch_df_w<D, float>(a, s);
+}
+
+hipError_t launch_decode_fused(const DecodeFusedArgs &a, hipStream_t s) {
+    switch (a.D) {
+        case 16: return launch_df_x<16>(a, s);
+        case 32: return launch_df_x<32>(a, s);
+        case 64: return launch_df_x<64>(a, s);
+        case 128: return launch_df_x<128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

@@ -107,6 +107,41 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, c
     return hip_status(gdn::launch_decode(da, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
+                            int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
+                            gdn_dtype act_dt, const void *conv_w, const void *gamma,
+                            gdn_dtype w_dt, void *conv_pool, float *state_pool,
+                            const int32_t *slot_ids, const uint8_t *has_initial,
+                            int32_t num_reqs, int32_t num_slots, float l2_eps, float norm_eps,
+                            void *y, gdn_dtype y_dt, float *o, void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    const int D = dims->head_dim_k;
+    if (gdn::decode_fused_smem_bytes(D, dims->num_k_heads, dims->num_v_heads) > 64 * 1024)
+        return GDN_ERR_DIMS;
+    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    const int64_t C = 2 * (int64_t)dims->num_k_heads * D + (int64_t)dims->num_v_heads * D;
+    if (num_reqs < 0 || num_slots < 0 || num_reqs > num_slots) return GDN_ERR_SHAPE;
+    if (x_ld < C || z_ld < (int64_t)dims->num_v_heads * D || gate_ld < dims->num_v_heads)
+        return GDN_ERR_SHAPE;
+    if (!(l2_eps >= 0.0f) || !(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if (num_reqs == 0) return GDN_OK;
+    if (!x_qkv || !z || !a || !b || !conv_w || !gamma || !conv_pool || !state_pool || !slot_ids ||
+        !y)
+        return GDN_ERR_NULL;
+    const size_t e = dt_size(act_dt);
+    if (!aligned(x_qkv, e) || !aligned(z, e) || !aligned(a, e) || !aligned(b, e) ||
+        !aligned(conv_pool, e) || !aligned(conv_w, dt_size(w_dt)) || !aligned(gamma, dt_size(w_dt)) ||
+        !aligned(state_pool, 16) || !aligned(slot_ids, 4) || !aligned(y, dt_size(y_dt)) ||
+        (o && !aligned(o, 4)))
+        return GDN_ERR_ALIGN;
+    gdn::DecodeFusedArgs da{D, x_qkv, x_ld, z, z_ld, a, b, gate_ld, act_dt == GDN_BF16, conv_w,
+                            gamma, w_dt == GDN_BF16, conv_pool, state_pool, slot_ids, has_initial,
+                            num_reqs, dims->num_k_heads, dims->num_v_heads, l2_eps, norm_eps, y,
+                            y_dt == GDN_BF16, o};
+    return hip_status(gdn::launch_decode_fused(da, static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_tokens, int32_t num_reqs) {
     if (check_dims(dims) != GDN_OK || num_tokens < 0 || num_reqs < 0) return 0;
     return gdn::prefill_workspace_bytes(dims->head_dim_k, dims->num_k_heads, dims->num_v_heads,

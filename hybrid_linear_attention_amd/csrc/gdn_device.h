@@ -55,6 +55,48 @@ __device__ __forceinline__ float4 ld4(const bf16 *p) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+// Eight consecutive elements (p aligned to 16 bytes), kept in their storage
+// format until converted, so that issuing a load never waits for its data.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16 *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void get(float (&f)[8]) const {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void get(float (&f)[8]) const {
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+};
+
+// Store eight consecutive elements (p aligned to 16 bytes); bf16 rounds once (RNE).
+__device__ __forceinline__ void store8(float *p, const float (&f)[8]) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+__device__ __forceinline__ void store8(bf16 *p, const float (&f)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = uint32_t(to_bf16(f[2 * i]).bits) | (uint32_t(to_bf16(f[2 * i + 1]).bits) << 16);
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Butterfly sum over aligned groups of `width` lanes (width a power of two <= 64).
 template <int WIDTH> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

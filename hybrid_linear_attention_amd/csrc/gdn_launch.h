@@ -30,6 +30,20 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
+struct DecodeFusedArgs {
+    int D;
+    const void *x; int64_t x_ld;
+    const void *z; int64_t z_ld;
+    const void *a, *b; int64_t gate_ld; bool act_bf16;
+    const void *w, *gamma; bool w_bf16;
+    void *pool; float *state; const int32_t *slots; const uint8_t *has_init;
+    int32_t R, Hk, Hv;
+    float l2_eps, norm_eps;
+    void *y; bool y_bf16; float *o;
+};
+hipError_t launch_decode_fused(const DecodeFusedArgs &a, hipStream_t s);
+size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv);
+
 struct GatedNormArgs {
     int D;
     const void *o; bool o_bf16;

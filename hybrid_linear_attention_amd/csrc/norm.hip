@@ -39,6 +39,59 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(
     }
 }
 
+// Vectorised gated norm: D / 8 lanes per (token, value head) row, 8 elements
+// per lane as 16-byte accesses, and R rows per thread whose loads are all issued
+// before the first reduction.
+template <int D, int R, typename TO, typename TZ, typename TG, typename TY>
+__global__ __launch_bounds__(256) void gated_norm_vec_kernel(
+    const TO *__restrict__ o, const TZ *__restrict__ z, int64_t z_ld,
+    const TG *__restrict__ gamma, float eps, int32_t T, int32_t Hv, TY *__restrict__ y) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = 256 / LPR;  // rows per pass of the block
+    const int l = threadIdx.x % LPR;
+    const int64_t rows = (int64_t)T * Hv;
+    const int64_t row0 = (int64_t)blockIdx.x * RPB * R + threadIdx.x / LPR;
+    Raw8<TO> ov[R];
+    Raw8<TZ> zv[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t row = row0 + (int64_t)i * RPB;
+        if (row < rows) {
+            const int64_t t = row / Hv;
+            const int h = (int)(row - t * Hv);
+            ov[i].load(o + row * D + 8 * l);
+            zv[i].load(z + t * z_ld + (int64_t)h * D + 8 * l);
+        } else {
+            ov[i].zero();
+            zv[i].zero();
+        }
+    }
+    float g[8];
+    {
+        Raw8<TG> gr;
+        gr.load(gamma + 8 * l);
+        gr.get(g);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        float of[8], zf[8];
+        ov[i].get(of);
+        zv[i].get(zf);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += of[e] * of[e];
+        ss = group_sum<LPR>(ss);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+        const int64_t row = row0 + (int64_t)i * RPB;
+        if (row < rows) {
+            float out[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] = of[e] * inv * g[e] * silu_f(zf[e]);
+            store8(y + row * D + 8 * l, out);
+        }
+    }
+}
+
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {
     static __device__ __forceinline__ void load(const float *p, float *f) {
@@ -111,10 +164,29 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(
     }
 }
 
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <int D, int R, typename TO, typename TZ, typename TG, typename TY>
+static hipError_t launch_gn_vec(const GatedNormArgs &a, hipStream_t s) {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = (int64_t)a.T * a.Hv;
+    hipLaunchKernelGGL((gated_norm_vec_kernel<D, R, TO, TZ, TG, TY>),
+                       dim3((unsigned)((rows + RPB * R - 1) / (RPB * R))), dim3(256), 0, s,
+                       (const TO *)a.o, (const TZ *)a.z, a.z_ld, (const TG *)a.gamma, a.eps, a.T,
+                       a.Hv, (TY *)a.y);
+    return hipGetLastError();
+}
+
 template <int D, typename TO, typename TZ, typename TG, typename TY>
 static hipError_t launch_gn_t(const GatedNormArgs &a, hipStream_t s) {
     constexpr int ROWS = 256 / (D / 2);
     const int64_t rows = (int64_t)a.T * a.Hv;
+    // 16-byte aligned rows take the vectorised kernel (4 rows per thread once
+    // there are enough rows to fill the chip)
+    if (a.z_ld % (16 / sizeof(TZ)) == 0 && aligned16(a.o) && aligned16(a.z) &&
+        aligned16(a.gamma) && aligned16(a.y))
+        return rows >= (int64_t)1 << 18 ? launch_gn_vec<D, 4, TO, TZ, TG, TY>(a, s)
+                                         : launch_gn_vec<D, 1, TO, TZ, TG, TY>(a, s);
     hipLaunchKernelGGL((gated_norm_kernel<D, TO, TZ, TG, TY>), dim3((unsigned)((rows + ROWS - 1) / ROWS)),
                        dim3(256), 0, s, (const TO *)a.o, (const TZ *)a.z, a.z_ld,
                        (const TG *)a.gamma, a.eps, a.T, a.Hv, (TY *)a.y);

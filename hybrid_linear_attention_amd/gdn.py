@@ -47,6 +47,9 @@ _SIGS = {
                            _vp, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _i32, _vp], _i32),
     "gdn_decode_step": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _vp,
                          _vp, _i32, _i32, _vp, _i32, _vp], _i32),
+    "gdn_decode_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
+                          _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _f32, _f32, _vp, _i32, _vp,
+                          _vp], _i32),
     "gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_varlen": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                             _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_size_t,
@@ -158,6 +161,32 @@ def gdn_decode_step(dims, q, k, v, a, b, state_pool, slot_ids, o, stream=None):
         _ptr(slot_ids, "slot_ids"), slot_ids.numel(), state_pool.shape[0], _ptr(o, "o"), _dt(o),
         _stream(stream))
     _check(st, "gdn_decode_step")
+
+
+def gdn_decode_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, slot_ids, y,
+                     has_initial=None, o=None, l2_eps=1e-6, norm_eps=1e-6, stream=None):
+    """One decode step (conv update -> recurrence -> gated norm) in one launch.
+    x [R, >=Cqkv], z [R, >=Hv*dv], a, b [R, >=Hv] share one dtype and give their
+    row strides; y [R, Hv*dv]; o optional fp32 [R, Hv, dv]."""
+    d = dims_c(dims)
+    if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
+        raise ValueError("x, z, a, b and conv_pool share one dtype; a and b share strides")
+    if conv_w.dtype != gamma.dtype:
+        raise ValueError("conv_w and gamma share one dtype")
+    for name, t in (("conv_w", conv_w), ("gamma", gamma), ("conv_pool", conv_pool),
+                    ("state_pool", state_pool), ("y", y)):
+        _contig(t, name)
+    if state_pool.dtype != torch.float32 or (o is not None and o.dtype != torch.float32):
+        raise TypeError("state_pool and o must be float32")
+    zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
+    st = lib().gdn_decode_fused(
+        ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
+        _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
+        _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
+        _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"), slot_ids.numel(),
+        state_pool.shape[0], float(l2_eps), float(norm_eps), _ptr(y, "y"), _dt(y),
+        _ptr(o, "o"), _stream(stream))
+    _check(st, "gdn_decode_fused")
 
 
 def gdn_prefill_workspace_bytes(dims, num_tokens, num_reqs):

@@ -140,6 +140,41 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k,
                            gdn_dtype o_dt, void *stream);
 
 /*
+ * gdn_decode_fused — one whole decode step of the mixer core in one launch:
+ * the conv update of gdn_conv1d_update, the recurrence of gdn_decode_step and
+ * the gated norm of gdn_gated_norm, for one token per request (tutorial page,
+ * section 02, one token's journey through a GDN layer; section 01 operator
+ * table, conv / GDN / gated-output rows).  Results equal the three separate
+ * calls up to fp32 rounding order; the history update is the same bit-exact
+ * copy.
+ *
+ *   x_qkv      [num_reqs, x_ld] in act_dt: the q | k | v conv inputs of the token.
+ *   z          [num_reqs, z_ld] in act_dt: the output gate, head h at columns
+ *              h*d_v .. h*d_v + d_v - 1.
+ *   a, b       [num_reqs, gate_ld] in act_dt: raw gate projections.
+ *   conv_w     [Cqkv, taps] in w_dt; gamma [d_v] in w_dt (gated-norm gain).
+ *   conv_pool  [num_slots, Cqkv, taps-1] in act_dt, updated in place.
+ *   state_pool [num_slots, Hv, d_v, d_k] fp32, slot slot_ids[r] read once and
+ *              written once.
+ *   has_initial [num_reqs] uint8 (device; NULL = all 1): 0 starts the request
+ *              from a zero history and a zero state (its first token).
+ *   y          [num_reqs, Hv * d_v] in y_dt: RMSNorm_dv(o) * gamma * SiLU(z).
+ *   o          optional [num_reqs, Hv, d_v] fp32 copy of o (NULL = not written).
+ * Needs (2 d + 2 (Hv/Hk) d + 2 Hv/Hk + 32) * 4 bytes <= 64 KiB of LDS per
+ * (request, key head) block, else GDN_ERR_DIMS.  Alignment: state_pool
+ * 16-byte aligned, everything else element-aligned.
+ */
+gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld,
+                            const void *z, int64_t z_ld, const void *a,
+                            const void *b, int64_t gate_ld, gdn_dtype act_dt,
+                            const void *conv_w, const void *gamma, gdn_dtype w_dt,
+                            void *conv_pool, float *state_pool,
+                            const int32_t *slot_ids, const uint8_t *has_initial,
+                            int32_t num_reqs, int32_t num_slots, float l2_eps,
+                            float norm_eps, void *y, gdn_dtype y_dt, float *o,
+                            void *stream);
+
+/*
  * gdn_prefill_workspace_bytes — device workspace gdn_prefill_varlen needs for
  * a batch of at most num_tokens tokens in at most num_reqs requests.
  * Returns 0 for unsupported dims.

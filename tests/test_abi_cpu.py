@@ -130,6 +130,36 @@ def test_norm_and_gemm_reject_bad_args():
     assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 64, 0, None, 0, 0, 64, 64, None) == 0
 
 
+def fused_call(d, **kw):
+    args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
+                g=FAKE, wdt=1, pool=FAKE, state=FAKE, slots=FAKE, hi=None, R=4, nslots=8,
+                l2=1e-6, ne=1e-6, y=FAKE, ydt=1, o=None)
+    args.update(kw)
+    return gdn.lib().gdn_decode_fused(
+        None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
+        args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
+        args["pool"], args["state"], args["slots"], args["hi"], args["R"], args["nslots"],
+        args["l2"], args["ne"], args["y"], args["ydt"], args["o"], None)
+
+
+def test_decode_fused_rejects_bad_args():
+    assert fused_call(None) == 1
+    assert fused_call(dims(16, 48, 128, 64, 4)) == 2          # d_k != d_v
+    assert fused_call(dims(1, 64, 128, 128, 4)) == 2          # 64 value heads per key head: LDS
+    assert fused_call(FULL, act=2) == 3
+    assert fused_call(FULL, ydt=7) == 3
+    assert fused_call(FULL, R=9) == 4                         # more requests than slots
+    assert fused_call(FULL, xld=10000) == 4                   # x_ld < Cqkv
+    assert fused_call(FULL, zld=6000) == 4
+    assert fused_call(FULL, gld=40) == 4
+    assert fused_call(FULL, l2=-1.0) == 4
+    assert fused_call(FULL, x=None) == 1
+    assert fused_call(FULL, y=None) == 1
+    assert fused_call(FULL, state=FAKE + 4) == 6              # state not 16-byte aligned
+    assert fused_call(FULL, z=FAKE + 1) == 6
+    assert fused_call(FULL, R=0, x=None) == 0                 # nothing to do
+
+
 def test_workspace_query():
     assert gdn.gdn_prefill_workspace_bytes((16, 48, 128, 128, 3), 100, 2) == 0
     n = gdn.gdn_prefill_workspace_bytes(FULL, 70000, 16)

@@ -115,6 +115,70 @@ def test_conv_strided_input_rows():
     check_pool(case, pool, pr)
 
 
+def long_lengths(seed, n, hi):
+    """Request lengths for batches above 1024 tokens (the vectorised conv path):
+    many 0-3 token requests mixed with longer ones, so request starts fall at
+    every offset of a token tile."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(0, hi, n)]
+    lens[::5] = [int(x) for x in rng.integers(0, 4, len(lens[::5]))]
+    lens += [1100 - sum(lens)] if sum(lens) < 1100 else []
+    return lens
+
+
+@pytest.mark.parametrize("which", ["d128_bf16", "d16_f32", "d64_bf16_out", "d32_tile_edges"])
+def test_conv_long_batch_parity(which):
+    if which == "d128_bf16":
+        case = varlen_case(21, lengths=long_lengths(21, 40, 80), num_slots=48)
+        act = torch.float32
+    elif which == "d16_f32":
+        case = varlen_case(22, D=16, Hk=3, Hv=6, dtype=torch.float32,
+                           lengths=long_lengths(22, 90, 40), num_slots=100)
+        act = torch.float32
+    elif which == "d64_bf16_out":
+        case = varlen_case(23, D=64, Hk=2, Hv=4, lengths=long_lengths(23, 60, 50), num_slots=64)
+        act = torch.bfloat16
+    else:
+        # requests of 15, 16, 17 tokens and 1-3 token requests straddling tile ends
+        lens = [1, 2, 0, 15, 16, 17, 3, 33, 1, 1, 2, 14, 0, 46, 31, 2, 3, 13, 1, 18] * 4
+        case = varlen_case(24, D=32, Hk=2, Hv=4, lengths=lens + [1200], num_slots=90)
+        act = torch.float32
+    assert case.num_tokens > 1024
+    q, k, v, pool = run_conv_gpu(case, act_dtype=act)
+    qr, kr, vr, pr = oracle_conv(case)
+    for name, got, ref in (("q", q, qr), ("k", k, kr), ("v", v, vr)):
+        if act == torch.bfloat16:
+            assert bf16_ulp_ok(got, ref, ulps=1), f"{which} {name}"
+        else:
+            err = rel_l2(f64(got), ref)
+            assert err <= FP32_TOL, f"{which} {name} rel-L2 {err:.3e}"
+    check_pool(case, pool, pr)
+
+
+@pytest.mark.parametrize("extra", [40, 37])
+def test_conv_long_batch_strided(extra):
+    """x as a column slice of a wider row at more than 1024 tokens: a row stride
+    of 1320 bf16 (16-byte rows) takes the vectorised kernel, a stride of 1318
+    (even, but rows not 16-byte aligned) the per-token kernel; both must match."""
+    case = varlen_case(25, lengths=long_lengths(25, 30, 90), num_slots=40)
+    d = case.dims
+    C = d.conv_channels
+    width = C + extra + (extra % 2)  # the ABI needs an even stride
+    wide = torch.randn(case.num_tokens, width, dtype=case.x_qkv.dtype)
+    wide[:, :C] = case.x_qkv
+    T = case.num_tokens
+    q = torch.empty((T, d.num_k_heads, d.head_dim_k), device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, d.num_v_heads, d.head_dim_v), device="cuda")
+    pool = dev(case.conv_pool)
+    gdn.gdn_conv1d_update(d, dev(wide)[:, :C], dev(case.conv_w), pool, dev(case.qsl),
+                          dev(case.slot_ids), dev(case.has_initial), q, k, v, l2_eps=L2_EPS)
+    qr, kr, vr, pr = oracle_conv(case)
+    for got, ref in ((q, qr), (k, kr), (v, vr)):
+        assert rel_l2(f64(got), ref) <= FP32_TOL
+    check_pool(case, pool, pr)
+
+
 # ---------------------------------------------------------------------------
 # decode step
 # ---------------------------------------------------------------------------
@@ -191,6 +255,113 @@ def test_decode_chain_full_size():
     check_pool(case, pool, pr)
 
 
+def run_fused_gpu(case, y_dtype=torch.bfloat16, x=None, z=None, a=None, b=None):
+    d = case.dims
+    R = case.num_reqs
+    pool = dev(case.conv_pool)
+    state = dev(case.state_pool)
+    y = torch.empty((R, d.num_v_heads * d.head_dim_v), dtype=y_dtype, device="cuda")
+    o = torch.empty((R, d.num_v_heads, d.head_dim_v), device="cuda")
+    gdn.gdn_decode_fused(d, dev(case.x_qkv) if x is None else x, dev(case.z) if z is None else z,
+                         dev(case.a) if a is None else a, dev(case.b) if b is None else b,
+                         dev(case.conv_w), dev(case.gamma), pool, state, dev(case.slot_ids), y,
+                         has_initial=dev(case.has_initial), o=o, l2_eps=L2_EPS,
+                         norm_eps=NORM_EPS)
+    return y, o, pool, state
+
+
+def oracle_decode_chain(case):
+    """conv update -> one recurrence step per request (zero state where
+    has_initial is 0) -> gated norm, in fp64 on the exact inputs."""
+    d = case.dims
+    qr, kr, vr, pr = oracle_conv(case)
+    o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
+                                            f64(case.state_pool), case.qsl.numpy(),
+                                            case.slot_ids.numpy(), case.has_initial.numpy())
+    z = f64(case.z).reshape(case.num_tokens, d.num_v_heads, d.head_dim_v)
+    y_ref = oracle.gated_norm(o_ref, z, f64(case.gamma), NORM_EPS)
+    return o_ref, y_ref, st_ref, pr
+
+
+def check_state_slots(case, got, ref, tol):
+    used = sorted(set(int(s) for s in case.slot_ids))
+    e = rel_l2(f64(got)[used], ref[used])
+    unused = sorted(set(range(case.num_slots)) - set(used))
+    if unused:
+        np.testing.assert_array_equal(bits(got)[unused], bits(case.state_pool)[unused])
+    return e
+
+
+def fused_case(which):
+    if which == "decode_r64":
+        return decode_r64(), torch.bfloat16
+    if which == "tiny_f32":
+        c = make_gdn_case(31, TINY_DIMS, [1] * 9, num_slots=14, permute_slots=True,
+                          act_dtype=torch.float32, state_std=0.02, hist_std=1.0, gamma_std=0.1)
+        c.has_initial = torch.tensor([r % 4 != 2 for r in range(9)], dtype=torch.uint8)
+        return c, torch.float32
+    c = make_gdn_case(32, GdnDims(2, 8, 64, 64, 4), [1] * 21, num_slots=30, permute_slots=True,
+                      state_std=0.02, hist_std=1.0, gamma_std=0.1)
+    return c, torch.bfloat16
+
+
+@pytest.mark.parametrize("which", ["decode_r64", "tiny_f32", "d64_g4"])
+def test_decode_fused_parity(which):
+    """One-launch decode step against the fp64 oracle chain: o (fp32 copy) and
+    states to fp32 accuracy, y within one rounding, history bit-exact, unused
+    slots untouched."""
+    case, ydt = fused_case(which)
+    y, o, pool, state = run_fused_gpu(case, y_dtype=ydt)
+    o_ref, y_ref, st_ref, pr = oracle_decode_chain(case)
+    e_o = rel_l2(f64(o), o_ref)
+    e_s = check_state_slots(case, state, st_ref, FP32_TOL)
+    print(f"{which}: o {e_o:.2e} state {e_s:.2e}")
+    assert e_o <= FP32_TOL and e_s <= FP32_TOL
+    y_ref = y_ref.reshape(case.num_tokens, -1)
+    if ydt == torch.bfloat16:
+        assert bf16_ulp_ok(y, y_ref, ulps=1)
+    else:
+        assert rel_l2(f64(y), y_ref) <= FP32_TOL
+    check_pool(case, pool, pr)
+
+
+def test_decode_fused_matches_three_calls_strided():
+    """x, z, a and b as column slices of one wide projection row (the layer's
+    layout): the fused step equals conv1d_update -> decode_step -> gated_norm."""
+    case, _ = fused_case("d64_g4")
+    d = case.dims
+    R = case.num_reqs
+    C = d.conv_channels
+    Hv, D = d.num_v_heads, d.head_dim_v
+    width = C + Hv * D + 2 * Hv + 8
+    wide = torch.zeros((R, width), dtype=torch.bfloat16)
+    wide[:, :C] = case.x_qkv
+    wide[:, C:C + Hv * D] = case.z.reshape(R, -1)
+    wide[:, C + Hv * D:C + Hv * D + Hv] = case.b
+    wide[:, C + Hv * D + Hv:C + Hv * D + 2 * Hv] = case.a
+    W = dev(wide)
+    xs, zs = W[:, :C], W[:, C:C + Hv * D]
+    bs, as_ = W[:, C + Hv * D:C + Hv * D + Hv], W[:, C + Hv * D + Hv:C + Hv * D + 2 * Hv]
+    y1, o1, pool1, state1 = run_fused_gpu(case, x=xs, z=zs, a=as_, b=bs)
+    # the three separate entry points on the same views
+    pool2, state2 = dev(case.conv_pool), dev(case.state_pool)
+    q = torch.empty((R, d.num_k_heads, d.head_dim_k), device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((R, Hv, D), device="cuda")
+    gdn.gdn_conv1d_update(d, xs, dev(case.conv_w), pool2, dev(case.qsl), dev(case.slot_ids),
+                          dev(case.has_initial), q, k, v, l2_eps=L2_EPS)
+    o2 = run_decode_gpu(d, q, k, v, as_, bs, state2, dev(case.slot_ids))
+    y2 = torch.empty((R, Hv * D), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_gated_norm(d, o2, zs, dev(case.gamma), y2, eps=NORM_EPS)
+    np.testing.assert_array_equal(bits(pool1), bits(pool2))
+    used = sorted(set(int(s) for s in case.slot_ids))
+    unused = sorted(set(range(case.num_slots)) - set(used))
+    assert rel_l2(f64(state1)[used], f64(state2)[used]) <= 1e-6
+    np.testing.assert_array_equal(bits(state1)[unused], bits(state2)[unused])
+    assert rel_l2(f64(o1), f64(o2)) <= 1e-6
+    assert bf16_ulp_ok(y1, f64(y2), ulps=1)
+
+
 def test_tiny_core_as_decode_steps():
     """The tiny workload (T=64, fp32) run as 64 single-token steps (conv then decode)
     against the oracle's whole-sequence result."""
@@ -224,18 +395,25 @@ def test_tiny_core_as_decode_steps():
 # ---------------------------------------------------------------------------
 # gated RMSNorm
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("D,Hv,T,odt,ydt", [(128, 48, 37, torch.float32, torch.bfloat16),
-                                            (16, 6, 64, torch.float32, torch.float32),
-                                            (64, 5, 3, torch.bfloat16, torch.float32)])
-def test_gated_norm_parity(D, Hv, T, odt, ydt):
+@pytest.mark.parametrize("D,Hv,T,odt,ydt,zoff", [(128, 48, 37, torch.float32, torch.bfloat16, 8),
+                                                 (16, 6, 64, torch.float32, torch.float32, 8),
+                                                 (64, 5, 3, torch.bfloat16, torch.float32, 8),
+                                                 (128, 48, 37, torch.float32, torch.bfloat16, 2),
+                                                 (32, 6, 50, torch.float32, torch.float32, 6),
+                                                 (128, 48, 6000, torch.float32, torch.bfloat16, 8),
+                                                 (64, 8, 33000, torch.bfloat16, torch.float32, 8)])
+def test_gated_norm_parity(D, Hv, T, odt, ydt, zoff):
+    """z is a column slice of a wider row (z_ld = Hv*D + 16): a slice starting 8
+    columns in keeps 16-byte rows (vectorised kernel; the two large cases use
+    several rows per thread), an offset of 2 or 6 does not (per-pair kernel)."""
     rng = np.random.default_rng(D + T)
     d = GdnDims(1, Hv, D, D, 4)
     o = torch.from_numpy(rng.standard_normal((T, Hv, D)) * rng.uniform(0.01, 3, (T, Hv, 1))).to(odt)
     zw = torch.from_numpy(rng.standard_normal((T, Hv * D + 16))).to(torch.bfloat16)
-    z = zw[:, 8:8 + Hv * D]  # strided view, z_ld = Hv*D + 16
+    z = zw[:, zoff:zoff + Hv * D]
     g = torch.from_numpy(1 + 0.1 * rng.standard_normal(D)).to(torch.bfloat16)
     y = torch.empty((T, Hv * D), dtype=ydt, device="cuda")
-    gdn.gdn_gated_norm(d, dev(o), dev(zw)[:, 8:8 + Hv * D], dev(g), y, eps=NORM_EPS)
+    gdn.gdn_gated_norm(d, dev(o), dev(zw)[:, zoff:zoff + Hv * D], dev(g), y, eps=NORM_EPS)
     y_ref = oracle.gated_norm(f64(o), f64(z).reshape(T, Hv, D), f64(g), NORM_EPS)
     if ydt == torch.bfloat16:
         assert bf16_ulp_ok(y, y_ref, ulps=1)
