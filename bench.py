@@ -358,53 +358,54 @@ def bench_layer(steps, dev, stream, torch, np):
     return out
 
 
+def fused_prefill_bytes(d, T, nreq, n_init, act_bytes=2, y_bytes=2):
+    """Algorithmic HBM bytes of one gdn_prefill_fused call: each token's conv
+    inputs, z and gates read once and its y written once; each request's state
+    written once (read once where it has an initial state) and its conv history
+    read and written once."""
+    Hv, D = d.num_v_heads, d.head_dim_v
+    C = 2 * d.num_k_heads * d.head_dim_k + Hv * D
+    per_tok = act_bytes * (C + Hv * D + 2 * Hv) + y_bytes * Hv * D
+    state = Hv * D * d.head_dim_k * 4
+    hist = 2 * C * (d.conv_taps - 1) * act_bytes
+    return per_tok * T + state * (nreq + n_init) + hist * nreq
+
+
 def bench_prefill(c, steps, dev, stream, torch, gdn, np):
-    """conv1d_update -> prefill_varlen -> gated_norm over one packed batch.
-    State and history are re-seeded from device copies before every step (the
-    copies run outside the timed events)."""
+    """One prefill step (gdn_prefill_fused: conv update -> recurrence -> gated
+    norm) over one packed batch.  State and history are re-seeded from device
+    copies before every step, outside the timed events."""
     d = c.dims
     T = c.num_tokens
-    D = d.head_dim_k
-    x = c.x_qkv.to(dev)
-    conv_w = c.conv_w.to(dev)
-    pool0 = c.conv_pool.to(dev)
-    state0 = c.state_pool.to(dev)
-    pool = pool0.clone()
-    state = state0.clone()
+    x, conv_w = c.x_qkv.to(dev), c.conv_w.to(dev)
+    pool0, state0 = c.conv_pool.to(dev), c.state_pool.to(dev)
+    pool, state = pool0.clone(), state0.clone()
     qsl, slots, hinit = c.qsl.to(dev), c.slot_ids.to(dev), c.has_initial.to(dev)
     a, b, z, gamma = c.a.to(dev), c.b.to(dev), c.z.to(dev), c.gamma.to(dev)
-    q = torch.empty((T, d.num_k_heads, D), device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty((T, d.num_v_heads, D), device=dev)
-    o = torch.empty((T, d.num_v_heads, D), device=dev)
-    y = torch.empty((T, d.num_v_heads * D), dtype=torch.bfloat16, device=dev)
-    nbytes = gdn.gdn_prefill_workspace_bytes(d, T, c.num_reqs)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
-    times, ktimes = [], []
+    y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_fused_workspace_bytes(d, T, c.num_reqs), dtype=torch.uint8,
+                     device=dev)
+    sh = stream.cuda_stream
+    times = []
     for it in range(steps + 1):
         pool.copy_(pool0)
         state.copy_(state0)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        e[0].record(stream)
-        gdn.gdn_conv1d_update(d, x, conv_w, pool, qsl, slots, hinit, q, k, v, l2_eps=L2_EPS)
-        e[1].record(stream)
-        gdn.gdn_prefill_varlen(d, q, k, v, a, b, state, qsl, slots, hinit, o, ws)
-        e[2].record(stream)
-        gdn.gdn_gated_norm(d, o, z, gamma, y, eps=NORM_EPS)
-        e[3].record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gdn.gdn_prefill_fused(d, x, z, a, b, conv_w, gamma, pool, state, qsl, slots, hinit, y, ws,
+                              l2_eps=L2_EPS, norm_eps=NORM_EPS, stream=sh)
+        e1.record(stream)
         torch.cuda.synchronize()
         if it > 0:  # first pass is warm-up
-            times.append(e[0].elapsed_time(e[3]))
-            ktimes.append(e[1].elapsed_time(e[2]))
+            times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
-    kms = float(np.median(ktimes))
     flops = prefill_flops(d, T)
-    nbytes = prefill_bytes(d, T, c.num_reqs, int(c.has_initial.sum()))
-    tflops = flops / (kms * 1e-3) / 1e12
-    gbs = nbytes / (kms * 1e-3) / 1e9
+    nbytes = fused_prefill_bytes(d, T, c.num_reqs, int(c.has_initial.sum()))
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
     # the binding resource is the one whose peak needs longer for this work
     hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12)
-    roof = {"kernel": "prefill plan + prep + chain kernels (gdn_prefill_varlen)"}
+    roof = {"kernel": "prefill step (gdn_prefill_fused: conv, plan, prep, chain, norm)"}
     if hbm_bound:
         roof.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(gbs / HBM_PEAK_GBS, 4))
@@ -420,8 +421,6 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np):
         "requests": c.num_reqs,
         "ms_per_step": round(ms, 4),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "prefill_kernel_ms": round(kms, 4),
-        "prefill_kernel_tokens_per_s": round(T / (kms * 1e-3), 1),
     }
 
 

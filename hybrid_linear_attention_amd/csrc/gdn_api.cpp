@@ -181,6 +181,90 @@ gdn_status gdn_prefill_varlen(const gdn_dims *dims, const void *q, const void *k
     return hip_status(gdn::launch_prefill(pa, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// fused prefill scratch: fp32 q, k, v and o of every token, then the
+// workspace of the prefill kernels
+struct FusedPrefillWs {
+    size_t q, k, v, o, pre, total;
+    FusedPrefillWs(const gdn_dims *d, int32_t T, int32_t nreq) {
+        const size_t D = d->head_dim_k;
+        q = align256((size_t)T * d->num_k_heads * D * 4);
+        k = q;
+        v = align256((size_t)T * d->num_v_heads * D * 4);
+        o = v;
+        pre = align256(gdn::prefill_workspace_bytes(d->head_dim_k, d->num_k_heads, d->num_v_heads, T, nreq));
+        total = q + k + v + o + pre;
+    }
+};
+}  // namespace
+
+size_t gdn_prefill_fused_workspace_bytes(const gdn_dims *dims, int32_t num_tokens, int32_t num_reqs) {
+    if (check_dims(dims) != GDN_OK || num_tokens < 0 || num_reqs < 0) return 0;
+    return FusedPrefillWs(dims, num_tokens, num_reqs).total;
+}
+
+gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
+                             int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
+                             gdn_dtype act_dt, const void *conv_w, const void *gamma,
+                             gdn_dtype w_dt, void *conv_pool, float *state_pool,
+                             const int32_t *query_start_loc, const int32_t *slot_ids,
+                             const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
+                             int32_t num_slots, float l2_eps, float norm_eps, void *y,
+                             gdn_dtype y_dt, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    const int D = dims->head_dim_k;
+    const int32_t nq = dims->num_k_heads * D;
+    const int32_t C = 2 * nq + dims->num_v_heads * D;
+    if (num_reqs < 0 || num_tokens < 0 || num_slots < 0 || num_reqs > num_slots)
+        return GDN_ERR_SHAPE;
+    if (num_tokens > 0 && num_reqs == 0) return GDN_ERR_SHAPE;
+    if (x_ld < C || z_ld < (int64_t)dims->num_v_heads * D || gate_ld < dims->num_v_heads)
+        return GDN_ERR_SHAPE;
+    if (!(l2_eps >= 0.0f) || !(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if (num_tokens == 0 || num_reqs == 0) return GDN_OK;
+    if (!x_qkv || !z || !a || !b || !conv_w || !gamma || !conv_pool || !state_pool ||
+        !query_start_loc || !slot_ids || !y)
+        return GDN_ERR_NULL;
+    const FusedPrefillWs wl(dims, num_tokens, num_reqs);
+    if (!workspace || workspace_bytes < wl.total) return GDN_ERR_WORKSPACE;
+    const size_t e = dt_size(act_dt);
+    if (x_ld % 2 != 0 || z_ld % 2 != 0 || !aligned(x_qkv, 2 * e) || !aligned(z, 2 * e) ||
+        !aligned(a, e) || !aligned(b, e) || !aligned(conv_pool, e) ||
+        !aligned(conv_w, dt_size(w_dt)) || !aligned(gamma, 2 * dt_size(w_dt)) ||
+        !aligned(state_pool, 16) || !aligned(query_start_loc, 4) || !aligned(slot_ids, 4) ||
+        !aligned(y, 2 * dt_size(y_dt)) || !aligned(workspace, 256))
+        return GDN_ERR_ALIGN;
+    uint8_t *w = static_cast<uint8_t *>(workspace);
+    float *q = reinterpret_cast<float *>(w);
+    float *k = reinterpret_cast<float *>(w + wl.q);
+    float *v = reinterpret_cast<float *>(w + wl.q + wl.k);
+    float *o = reinterpret_cast<float *>(w + wl.q + wl.k + wl.v);
+    uint8_t *pre = w + wl.q + wl.k + wl.v + wl.o;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    gdn::ConvArgs ca{D, x_qkv, x_ld, act_dt == GDN_BF16, conv_w, w_dt == GDN_BF16, conv_pool,
+                     query_start_loc, slot_ids, has_initial, num_reqs, num_tokens, C, nq,
+                     l2_eps, q, k, v, false};
+    hipError_t he = gdn::launch_conv1d(ca, s);
+    if (he != hipSuccess) return GDN_ERR_HIP;
+    gdn::PrefillArgs pa{D, q, k, v, false, a, b, gate_ld, act_dt == GDN_BF16, state_pool,
+                        query_start_loc, slot_ids, has_initial, num_reqs, num_tokens,
+                        dims->num_k_heads, dims->num_v_heads, o, false, pre, wl.pre};
+    pa.z = z;
+    pa.z_ld = z_ld;
+    pa.z_bf16 = act_dt == GDN_BF16;
+    pa.gamma = gamma;
+    pa.gamma_bf16 = w_dt == GDN_BF16;
+    pa.norm_eps = norm_eps;
+    pa.y = y;
+    pa.y_bf16 = y_dt == GDN_BF16;
+    return hip_status(gdn::launch_prefill(pa, s));
+}
+
 gdn_status gdn_gated_norm(const gdn_dims *dims, const void *o, gdn_dtype o_dt, const void *z,
                           gdn_dtype z_dt, int64_t z_ld, const void *gamma, gdn_dtype gamma_dt,
                           float eps, int32_t num_tokens, void *y, gdn_dtype y_dt, void *stream) {

@@ -73,6 +73,11 @@ struct PrefillArgs {
     int32_t nreq, T, Hk, Hv;
     void *o; bool o_bf16;
     void *ws; size_t ws_bytes;
+    // optional gated output y = RMSNorm_dv(o) * gamma * SiLU(z) (y == nullptr: o only).
+    // With y set, o is scratch the launcher may use ([T, Hv, D] fp32, o_bf16 false).
+    const void *z = nullptr; int64_t z_ld = 0; bool z_bf16 = false;
+    const void *gamma = nullptr; bool gamma_bf16 = false; float norm_eps = 0.f;
+    void *y = nullptr; bool y_bf16 = false;
 };
 size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

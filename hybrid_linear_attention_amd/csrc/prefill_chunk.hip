@@ -467,14 +467,23 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 // image run on one XCD (workgroups are dealt to the 8 XCDs round-robin) and
 // the longest requests' groups are dispatched first.
 // ---------------------------------------------------------------------------
+// This wave's copies of one chunk's images, slice `part` of NPART: the slices
+// are spread over the previous chunk's MFMA phases so that the wave does not
+// stall on a full memory queue in one burst.
+constexpr int NPART = 4;
 template <int NW>
 __device__ __forceinline__ void issue_images(uint8_t *stage, const uint8_t *kim, const uint8_t *tim,
-                                             int w, int lane) {
+                                             int w, int lane, int part) {
     using namespace chunk;
+    constexpr int NFRAG = KIMG_FRAGS + TIMG_FRAGS;
+    constexpr int PER_WAVE = (NFRAG + NW - 1) / NW;
 #pragma unroll
-    for (int f = w; f < KIMG_FRAGS + TIMG_FRAGS; f += NW) {
-        const uint8_t *src = f < KIMG_FRAGS ? kim + (size_t)f * FRAG : tim + (size_t)(f - KIMG_FRAGS) * FRAG;
-        copy_frag(src, stage + (size_t)f * FRAG, lane);
+    for (int m = part * PER_WAVE / NPART; m < (part + 1) * PER_WAVE / NPART; ++m) {
+        const int f = w + NW * m;
+        if (f < NFRAG) {
+            const uint8_t *src = f < KIMG_FRAGS ? kim + (size_t)f * FRAG : tim + (size_t)(f - KIMG_FRAGS) * FRAG;
+            copy_frag(src, stage + (size_t)f * FRAG, lane);
+        }
     }
 }
 
@@ -544,12 +553,16 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
             }
     };
 
-    issue_images<NW>(smem, kim0, tim0, w, lane);
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) issue_images<NW>(smem, kim0, tim0, w, lane, part);
     load_v(0);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
         const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * STAGE : 0);
+        uint8_t *nstg = smem + (size_t)((cc + 1) & 1) * STAGE;
+        const bool prefetch = STAGES == 2 && cc + 1 < nch;
+        const uint8_t *nkim = kim0 + (cc + 1) * kstep, *ntim = tim0 + (cc + 1) * tstep;
         // this wave's copies and loads of chunk cc have landed; after the barrier
         // every wave's have, and (two stages) every wave is done with chunk cc - 1
         __builtin_amdgcn_s_waitcnt(0);
@@ -559,11 +572,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
             for (int e = 0; e < 4; ++e) vcur[tau][e] = vr[tau][e].get();
-        if (STAGES == 2 && cc + 1 < nch) {
-            issue_images<NW>(smem + (size_t)((cc + 1) & 1) * STAGE, kim0 + (cc + 1) * kstep,
-                             tim0 + (cc + 1) * tstep, w, lane);
-            load_v(cc + 1);
-        }
+        if (prefetch) issue_images<NW>(nstg, nkim, ntim, w, lane, 0);
         const uint8_t *kst = stg + 16 * lane;          // this lane's piece of each K fragment
         const uint8_t *tst = stg + KIMG + 16 * lane;   // and of each T fragment
 
@@ -576,6 +585,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            if (prefetch && ks > 0) issue_images<NW>(nstg, nkim, ntim, w, lane, ks);
             bf16x8_t sbh, sbl;
             {
                 float sv[8];
@@ -593,6 +603,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
                 mma3(OQ[tau], qh_, ql_, sbh, sbl);
             }
         }
+        if (prefetch) load_v(cc + 1);
         // per-token gamma, e^{G_C - G_t}, beta for this lane's tokens
         const uint8_t *tvec = stg + KIMG;
         float4 gam[2], rev[2], bet[2];
@@ -661,7 +672,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         if (STAGES == 1) {
             __syncthreads();  // every wave is done reading the stage
             if (cc + 1 < nch) {
-                issue_images<NW>(smem, kim0 + (cc + 1) * kstep, tim0 + (cc + 1) * tstep, w, lane);
+#pragma unroll
+                for (int part = 0; part < NPART; ++part) issue_images<NW>(smem, nkim, ntim, w, lane, part);
                 load_v(cc + 1);
             }
         }
@@ -671,6 +683,253 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     for (int jt = 0; jt < 8; ++jt)
         *reinterpret_cast<float4 *>(sbase + (int64_t)irow * D + 16 * jt + 4 * lg) =
             make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]);
+}
+
+// ---------------------------------------------------------------------------
+// chain, group variant for large batches: one block per (request, key head,
+// block of 64 state rows) covering all G value heads that read the key head,
+// so the chunk's 48 KiB K image is staged once for G heads; each wave owns 32
+// rows (two 16-row tiles) of one head, so every K / Q / K^T fragment read
+// feeds two row tiles.  Same per-row algebra and operand layout as above.
+// ---------------------------------------------------------------------------
+constexpr int GRP_ROWS = 64;          // state rows per head per block
+constexpr int GRP_RPW = 2;            // 16-row tiles per wave
+constexpr int GRP_MAX_HEADS = 3;      // value heads per key head the variant supports
+
+template <int G, int STAGES, typename TA, typename TO>
+__global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_chain_group_kernel(
+    const TA *__restrict__ v, float *__restrict__ state, const int32_t *__restrict__ qsl,
+    const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
+    const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
+    int32_t Hv, TO *__restrict__ o) {
+    using namespace chunk;
+    constexpr int WPH = GRP_ROWS / (16 * GRP_RPW);  // waves per head
+    constexpr int NW = G * WPH;
+    constexpr int NRB = D / GRP_ROWS;               // row blocks per head
+    constexpr int NFRAG = KIMG_FRAGS + G * TIMG_FRAGS;
+    constexpr size_t GSTAGE = KIMG + G * TIMG;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    // blocks of one (request, key head) group run on one XCD; longest requests first
+    const int xcd = blockIdx.x & 7;
+    const int qd = blockIdx.x >> 3;
+    const int gi = 8 * (qd / NRB) + xcd;
+    const int rb = qd % NRB;
+    if (gi >= nreq * Hk) return;
+    const int r = order[gi / Hk];
+    const int kh = gi % Hk;
+    const int hh = w / WPH;                 // this wave's head within the group
+    const int h = kh * G + hh;
+    const int tok0 = qsl[r];
+    const int L = qsl[r + 1] - tok0;
+    if (L <= 0) return;
+    const int nch = (L + CH - 1) / CH;
+    const int c_first = chunk_off[r];
+    const bool hi_init = has_init == nullptr || has_init[r] != 0;
+    int irow[GRP_RPW];
+#pragma unroll
+    for (int rt = 0; rt < GRP_RPW; ++rt) irow[rt] = GRP_ROWS * rb + 16 * GRP_RPW * (w % WPH) + 16 * rt + lr;
+    float *sbase = state + ((int64_t)slots[r] * Hv + h) * D * D;
+
+    floatx4_t ST[GRP_RPW][8];
+#pragma unroll
+    for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+            ST[rt][jt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            if (hi_init) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg);
+                ST[rt][jt] = floatx4_t{s4.x, s4.y, s4.z, s4.w};
+            }
+        }
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+    const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
+    const uint8_t *tim0 = timg + ((size_t)c_first * Hv + kh * G) * TIMG;  // the group's G heads are adjacent
+    const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
+
+    // this wave's copies of chunk cc's images, in NPART slices so that they can be
+    // spread over the previous chunk's MFMA phases instead of stalling the wave
+    // on a full memory queue in one burst
+    constexpr int PER_WAVE = (NFRAG + NW - 1) / NW;
+    auto issue = [&](uint8_t *stage, int cc, int part) {
+        const uint8_t *kim = kim0 + cc * kstep;
+        const uint8_t *tim = tim0 + cc * tstep;
+#pragma unroll
+        for (int m = part * PER_WAVE / NPART; m < (part + 1) * PER_WAVE / NPART; ++m) {
+            const int f = w + NW * m;
+            if (f < NFRAG) {
+                const uint8_t *src = f < KIMG_FRAGS ? kim + (size_t)f * FRAG : tim + (size_t)(f - KIMG_FRAGS) * FRAG;
+                copy_frag(src, stage + (size_t)f * FRAG, lane);
+            }
+        }
+    };
+    Raw1<TA> vr[GRP_RPW][2][4];
+    auto load_v = [&](int cc) {
+        const int tb = tok0 + cc * CH;
+        const int Lc = min(CH, L - cc * CH);
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tau + 4 * lg + e;
+                    if (t < Lc) vr[rt][tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow[rt]);
+                    else vr[rt][tau][e].zero();
+                }
+    };
+
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) issue(smem, 0, part);
+    load_v(0);
+    for (int cc = 0; cc < nch; ++cc) {
+        const int tb = tok0 + cc * CH;
+        const int Lc = min(CH, L - cc * CH);
+        const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * GSTAGE : 0);
+        uint8_t *nstg = smem + (size_t)((cc + 1) & 1) * GSTAGE;
+        const bool prefetch = STAGES == 2 && cc + 1 < nch;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        float vcur[GRP_RPW][2][4];
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vcur[rt][tau][e] = vr[rt][tau][e].get();
+        if (prefetch) issue(nstg, cc + 1, 0);
+        const uint8_t *kst = stg + 16 * lane;
+        const uint8_t *tst = stg + KIMG + (size_t)hh * TIMG + 16 * lane;
+        const uint8_t *tvec = stg + KIMG + (size_t)hh * TIMG;
+
+        // X = K S0^T, OQ = Q S0^T for both row tiles
+        floatx4_t X[GRP_RPW][2], OQ[GRP_RPW][2];
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                X[rt][tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                OQ[rt][tau] = X[rt][tau];
+            }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (prefetch && ks > 0) issue(nstg, cc + 1, ks);
+            bf16x8_t sbh[GRP_RPW], sbl[GRP_RPW];
+#pragma unroll
+            for (int rt = 0; rt < GRP_RPW; ++rt) {
+                float sv[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) sv[p] = ST[rt][2 * ks + (p >> 2)][p & 3];
+                split_vals(sv, sbh[rt], sbl[rt]);
+            }
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const bf16x8_t kh_ = frag(kst + (FK + (0 + tau) * 4 + ks) * FRAG);
+                const bf16x8_t kl_ = frag(kst + (FK + (2 + tau) * 4 + ks) * FRAG);
+                const bf16x8_t qh_ = frag(kst + (FQ + (0 + tau) * 4 + ks) * FRAG);
+                const bf16x8_t ql_ = frag(kst + (FQ + (2 + tau) * 4 + ks) * FRAG);
+#pragma unroll
+                for (int rt = 0; rt < GRP_RPW; ++rt) {
+                    mma3(X[rt][tau], kh_, kl_, sbh[rt], sbl[rt]);
+                    mma3(OQ[rt][tau], qh_, ql_, sbh[rt], sbl[rt]);
+                }
+            }
+        }
+        if (prefetch) load_v(cc + 1);
+        float4 gam[2], rev[2], bet[2];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const int t0 = 16 * tau + 4 * lg;
+            gam[tau] = *reinterpret_cast<const float4 *>(tvec + T_GAM + 4 * t0);
+            rev[tau] = *reinterpret_cast<const float4 *>(tvec + T_REV + 4 * t0);
+            bet[tau] = *reinterpret_cast<const float4 *>(tvec + T_BETA + 4 * t0);
+        }
+        const float gC = *reinterpret_cast<const float *>(tvec + T_GAM + 4 * (CH - 1));
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            const float g4[4] = {gam[tau].x, gam[tau].y, gam[tau].z, gam[tau].w};
+            const float b4[4] = {bet[tau].x, bet[tau].y, bet[tau].z, bet[tau].w};
+#pragma unroll
+            for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    X[rt][tau][e] = b4[e] * (vcur[rt][tau][e] - g4[e] * X[rt][tau][e]);
+                    OQ[rt][tau][e] *= g4[e];
+                }
+        }
+        // Delta = T (beta E)
+        const bf16x8_t th0 = frag(tst + (FT + 0) * FRAG), th1 = frag(tst + (FT + 1) * FRAG);
+        const bf16x8_t tl0 = frag(tst + (FT + 2) * FRAG), tl1 = frag(tst + (FT + 3) * FRAG);
+        floatx4_t Dl[GRP_RPW][2];
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt) {
+            bf16x8_t ebh, ebl;
+            float ev[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) ev[p] = X[rt][p >> 2][p & 3];
+            split_vals(ev, ebh, ebl);
+            Dl[rt][0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            Dl[rt][1] = Dl[rt][0];
+            mma3(Dl[rt][0], th0, tl0, ebh, ebl);
+            mma3(Dl[rt][1], th1, tl1, ebh, ebl);
+        }
+        // O = OQ + P Delta and S^T = gamma_C S^T + K^T Delta~
+        const float r8[8] = {rev[0].x, rev[0].y, rev[0].z, rev[0].w, rev[1].x, rev[1].y, rev[1].z, rev[1].w};
+        const bf16x8_t ph0 = frag(tst + (FP + 0) * FRAG), ph1 = frag(tst + (FP + 1) * FRAG);
+        const bf16x8_t pl0 = frag(tst + (FP + 2) * FRAG), pl1 = frag(tst + (FP + 3) * FRAG);
+        bf16x8_t tbh[GRP_RPW], tbl[GRP_RPW];
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt) {
+            float dv[8], dtv[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                dv[p] = Dl[rt][p >> 2][p & 3];
+                dtv[p] = dv[p] * r8[p];
+            }
+            bf16x8_t dbh, dbl;
+            split_vals(dv, dbh, dbl);
+            split_vals(dtv, tbh[rt], tbl[rt]);
+            mma3(OQ[rt][0], ph0, pl0, dbh, dbl);
+            mma3(OQ[rt][1], ph1, pl1, dbh, dbl);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+            const bf16x8_t kth = frag(kst + (FKT + jt) * FRAG);
+            const bf16x8_t ktl = frag(kst + (FKT + 8 + jt) * FRAG);
+#pragma unroll
+            for (int rt = 0; rt < GRP_RPW; ++rt) {
+                ST[rt][jt] *= gC;
+                mma3(ST[rt][jt], kth, ktl, tbh[rt], tbl[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tau + 4 * lg + e;
+                    if (t < Lc) st(o + ((int64_t)(tb + t) * Hv + h) * D + irow[rt], OQ[rt][tau][e] * inv_sqrt_d);
+                }
+        if (STAGES == 1) {
+            __syncthreads();
+            if (cc + 1 < nch) {
+#pragma unroll
+                for (int part = 0; part < NPART; ++part) issue(smem, cc + 1, part);
+                load_v(cc + 1);
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt)
+            *reinterpret_cast<float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg) =
+                make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -721,6 +980,23 @@ static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_
     return hipGetLastError();
 }
 
+template <int G, int STAGES, typename TA, typename TO>
+static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
+                                     const int32_t *order, const uint8_t *kimg, const uint8_t *timg) {
+    using namespace chunk;
+    constexpr int NW = G * (GRP_ROWS / (16 * GRP_RPW));
+    static bool set = false;
+    const size_t smem = STAGES * (KIMG + G * TIMG);
+    hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO>, smem, set);
+    if (e != hipSuccess) return e;
+    const int64_t groups = (int64_t)a.nreq * a.Hk;
+    const int64_t blocks = 8 * (int64_t)(D / GRP_ROWS) * ((groups + 7) / 8);
+    hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO>), dim3((unsigned)blocks),
+                       dim3(64 * NW), smem, s, (const TA *)a.v, a.state, a.qsl, a.slots,
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o);
+    return hipGetLastError();
+}
+
 template <typename TA, typename TG, typename TO>
 static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     using namespace chunk;
@@ -745,11 +1021,22 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // a whole head (8 waves) per block when there are enough (request, head)
-    // units to fill the chip, else 32 state rows per block
+    // large batches: key-head group blocks (the K image staged once for the
+    // group's 3 value heads); else per-head blocks, a whole head (8 waves) when
+    // there are enough (request, head) units to fill the chip, else 32 rows
     const int64_t units = (int64_t)a.nreq * a.Hv;
-    if (units >= 256) return launch_chain<8, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
-    return launch_chain<2, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
+    if (units >= 256 && a.Hv == 3 * a.Hk)
+        e = launch_chain_group<3, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
+    else
+        e = units >= 256 ? launch_chain<8, 2, TA, TO>(a, s, chunk_off, order, kimg, timg)
+                         : launch_chain<2, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
+    if (e != hipSuccess || !a.y) return e;
+    // gated output: a separate HBM-streaming pass over o (folding it into the
+    // chain's chunk loop measured slower: its per-token reductions sit on the
+    // chain's critical path)
+    GatedNormArgs g{D, a.o, a.o_bf16, a.z, a.z_ld, a.z_bf16, a.gamma, a.gamma_bf16, a.norm_eps,
+                    a.T, a.Hv, a.y, a.y_bf16};
+    return launch_gated_norm(g, s);
 }
 template <typename TA, typename TG>
 static hipError_t launch_chunk_o(const PrefillArgs &a, hipStream_t s) {

@@ -51,6 +51,10 @@ _SIGS = {
                           _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _f32, _f32, _vp, _i32, _vp,
                           _vp], _i32),
     "gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
+    "gdn_prefill_fused_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
+    "gdn_prefill_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
+                           _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp,
+                           _i32, _vp, ctypes.c_size_t, _vp], _i32),
     "gdn_prefill_varlen": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                             _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_size_t,
                             _vp], _i32),
@@ -215,6 +219,40 @@ def gdn_prefill_varlen(dims, q, k, v, a, b, state_pool, query_start_loc, slot_id
         slot_ids.numel(), q.shape[0], state_pool.shape[0], _ptr(o, "o"), _dt(o), ws_ptr, ws_bytes,
         _stream(stream))
     _check(st, "gdn_prefill_varlen")
+
+
+def gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs):
+    d = dims_c(dims)
+    return int(lib().gdn_prefill_fused_workspace_bytes(ctypes.byref(d), int(num_tokens),
+                                                       int(num_reqs)))
+
+
+def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, query_start_loc,
+                      slot_ids, has_initial, y, workspace, l2_eps=1e-6, norm_eps=1e-6,
+                      stream=None):
+    """A whole prefill step (conv update -> recurrence -> gated norm) over a packed
+    batch; x, z, a, b share one dtype and give their row strides; y [T, Hv*dv];
+    workspace a uint8 device tensor of gdn_prefill_fused_workspace_bytes(...)."""
+    d = dims_c(dims)
+    if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
+        raise ValueError("x, z, a, b and conv_pool share one dtype; a and b share strides")
+    if conv_w.dtype != gamma.dtype:
+        raise ValueError("conv_w and gamma share one dtype")
+    for name, t in (("conv_w", conv_w), ("gamma", gamma), ("conv_pool", conv_pool),
+                    ("state_pool", state_pool), ("y", y)):
+        _contig(t, name)
+    if state_pool.dtype != torch.float32:
+        raise TypeError("state_pool must be float32")
+    zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
+    st = lib().gdn_prefill_fused(
+        ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
+        _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
+        _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
+        _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"),
+        slot_ids.numel(), x.shape[0], state_pool.shape[0], float(l2_eps), float(norm_eps),
+        _ptr(y, "y"), _dt(y), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "gdn_prefill_fused")
 
 
 def gdn_gated_norm(dims, o, z, gamma, y, eps=1e-6, stream=None):

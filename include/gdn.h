@@ -213,6 +213,33 @@ gdn_status gdn_prefill_varlen(const gdn_dims *dims, const void *q,
                               size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill_fused_workspace_bytes / gdn_prefill_fused — a whole prefill
+ * step of the mixer core over a packed batch: the conv update of
+ * gdn_conv1d_update, the recurrence of gdn_prefill_varlen and the gated norm of
+ * gdn_gated_norm (tutorial page, section 01 operator table, conv / GDN /
+ * gated-output rows), with the intermediate q, k, v and o kept in the
+ * workspace.  Arguments follow gdn_decode_fused plus the varlen metadata of
+ * gdn_prefill_varlen; has_initial[r] = 0 starts request r from a zero history
+ * and a zero state.  y [num_tokens, Hv * d_v] in y_dt.  The workspace (at least
+ * gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs) bytes,
+ * 256-byte aligned) is scratch owned by the caller; nothing in it outlives the
+ * call.  Alignment: x_ld and z_ld even, x, z, gamma and y aligned to two
+ * elements, state_pool 16-byte aligned.
+ */
+size_t gdn_prefill_fused_workspace_bytes(const gdn_dims *dims, int32_t num_tokens,
+                                         int32_t num_reqs);
+gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld,
+                             const void *z, int64_t z_ld, const void *a,
+                             const void *b, int64_t gate_ld, gdn_dtype act_dt,
+                             const void *conv_w, const void *gamma, gdn_dtype w_dt,
+                             void *conv_pool, float *state_pool,
+                             const int32_t *query_start_loc, const int32_t *slot_ids,
+                             const uint8_t *has_initial, int32_t num_reqs,
+                             int32_t num_tokens, int32_t num_slots, float l2_eps,
+                             float norm_eps, void *y, gdn_dtype y_dt, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * gdn_gated_norm — Ogate = RMSNorm(o) * SiLU(Z) (operator table, gated-output
  * row: [T,48,128] -> [T,6144]; the GDN output gate is SiLU after RMSNorm,
  * evidence-matrix row on output gates).  Per (token, value head) over d_v:

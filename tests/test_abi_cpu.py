@@ -160,6 +160,36 @@ def test_decode_fused_rejects_bad_args():
     assert fused_call(FULL, R=0, x=None) == 0                 # nothing to do
 
 
+def prefill_fused_call(d, **kw):
+    args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
+                g=FAKE, wdt=1, pool=FAKE, state=FAKE, qsl=FAKE, slots=FAKE, hi=None, R=2, T=100,
+                nslots=8, l2=1e-6, ne=1e-6, y=FAKE, ydt=1, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return gdn.lib().gdn_prefill_fused(
+        None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
+        args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
+        args["pool"], args["state"], args["qsl"], args["slots"], args["hi"], args["R"], args["T"],
+        args["nslots"], args["l2"], args["ne"], args["y"], args["ydt"], args["ws"], args["wsb"],
+        None)
+
+
+def test_prefill_fused_rejects_bad_args():
+    need = gdn.lib().gdn_prefill_fused_workspace_bytes(ctypes.byref(FULL), 100, 2)
+    assert need > 0
+    assert prefill_fused_call(None) == 1
+    assert prefill_fused_call(dims(16, 48, 96, 96, 4)) == 2
+    assert prefill_fused_call(FULL, act=5) == 3
+    assert prefill_fused_call(FULL, R=0) == 4              # tokens but no requests
+    assert prefill_fused_call(FULL, xld=100) == 4
+    assert prefill_fused_call(FULL, ne=-1.0) == 4
+    assert prefill_fused_call(FULL, y=None) == 1
+    assert prefill_fused_call(FULL, wsb=need - 1) == 5     # workspace too small
+    assert prefill_fused_call(FULL, ws=None) == 5
+    assert prefill_fused_call(FULL, ws=FAKE + 16) == 6     # workspace not 256-byte aligned
+    assert prefill_fused_call(FULL, xld=10241) == 6        # odd row stride
+    assert prefill_fused_call(FULL, T=0, R=0, x=None) == 0
+
+
 def test_workspace_query():
     assert gdn.gdn_prefill_workspace_bytes((16, 48, 128, 128, 3), 100, 2) == 0
     n = gdn.gdn_prefill_workspace_bytes(FULL, 70000, 16)

@@ -422,6 +422,60 @@ def test_gated_norm_parity(D, Hv, T, odt, ydt, zoff):
 
 
 # ---------------------------------------------------------------------------
+# fused prefill step (conv update -> recurrence -> gated norm)
+# ---------------------------------------------------------------------------
+def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16):
+    d = case.dims
+    T = case.num_tokens
+    pool = dev(case.conv_pool)
+    state = dev(case.state_pool)
+    y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=y_dtype, device="cuda")
+    nbytes = gdn.gdn_prefill_fused_workspace_bytes(d, T, case.num_reqs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gdn.gdn_prefill_fused(d, dev(case.x_qkv), dev(case.z), dev(case.a), dev(case.b),
+                          dev(case.conv_w), dev(case.gamma), pool, state, dev(case.qsl),
+                          dev(case.slot_ids), dev(case.has_initial), y, ws, l2_eps=L2_EPS,
+                          norm_eps=NORM_EPS)
+    return y, pool, state
+
+
+@pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d32_seq"])
+def test_prefill_fused_parity(which):
+    """One prefill step through gdn_prefill_fused against the fp64 oracle chain:
+    blocks of 32 state rows with a separate gated-norm pass (few heads x
+    requests), whole-head blocks with the norm in the chain (>= 256 of them),
+    and the sequential kernel for d = 32."""
+    if which == "d128_split_rows":
+        case = varlen_case(41, lengths=(1, 2, 5, 37, 0, 130, 3), num_slots=10)
+    elif which == "d128_whole_heads":
+        rng = np.random.default_rng(42)
+        lens = [int(x) for x in rng.integers(0, 70, 48)]
+        case = varlen_case(42, lengths=lens, num_slots=60)
+    else:
+        case = varlen_case(43, D=32, Hk=2, Hv=4, lengths=(3, 40, 1, 77), num_slots=6)
+    y, pool, state = run_prefill_fused_gpu(case)
+    d = case.dims
+    qr, kr, vr, pr = oracle_conv(case)
+    o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
+                                            f64(case.state_pool), case.qsl.numpy(),
+                                            case.slot_ids.numpy(), case.has_initial.numpy())
+    z = f64(case.z).reshape(case.num_tokens, d.num_v_heads, d.head_dim_v)
+    y_ref = oracle.gated_norm(o_ref, z, f64(case.gamma), NORM_EPS).reshape(case.num_tokens, -1)
+    e_y = rel_l2(f64(y), y_ref)
+    e_s = check_state_slots(case, state, st_ref, STATE_TOL)
+    # per (token, head) row: the gated norm divides by the row's own RMS, so a row
+    # whose o nearly cancels (a first token with q.k ~ 0) carries the contraction's
+    # absolute error as a relative one; the bound only catches wrong rows
+    yr = f64(y).reshape(case.num_tokens * d.num_v_heads, -1)
+    rr = y_ref.reshape(yr.shape)
+    row_err = np.linalg.norm(yr - rr, axis=1) / np.maximum(np.linalg.norm(rr, axis=1), 1e-30)
+    print(f"{which}: y {e_y:.2e} (worst row {row_err.max():.2e}) state {e_s:.2e}")
+    assert e_y <= OUT_TOL and e_s <= STATE_TOL
+    assert row_err.max() <= 0.1
+    check_pool(case, pool, pr)
+
+
+# ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
 def run_prefill_gpu(case, q, k, v, state, o_dtype=torch.float32):
@@ -447,12 +501,24 @@ def check_states(case, got_state, ref_state, tol):
     return used
 
 
-@pytest.mark.parametrize("which", ["tiny", "varlen_d128", "varlen_d32"])
+@pytest.mark.parametrize("which", ["tiny", "varlen_d128", "varlen_d32", "group_blocks",
+                                   "whole_head_blocks"])
 def test_prefill_chain_parity(which):
+    """The prefill entry point on each chain shape: 32-row blocks (few heads x
+    requests), key-head group blocks (>= 256 heads x requests, 3 value heads per
+    key head), whole-head blocks (>= 256, 4 value heads per key head), and the
+    sequential kernel for d = 32."""
     if which == "tiny":
         case = tiny_core()
     elif which == "varlen_d128":
         case = varlen_case(21, lengths=(1, 64, 65, 130, 0, 7, 200))
+    elif which == "group_blocks":
+        rng = np.random.default_rng(26)
+        case = varlen_case(26, lengths=[int(x) for x in rng.integers(0, 100, 48)], num_slots=50)
+    elif which == "whole_head_blocks":
+        rng = np.random.default_rng(27)
+        case = varlen_case(27, Hk=2, Hv=8, lengths=[int(x) for x in rng.integers(0, 100, 40)],
+                           num_slots=41)
     else:
         case = varlen_case(22, D=32, Hk=2, Hv=4, lengths=(70, 1, 0, 129), num_slots=6)
     q, k, v, pool = run_conv_gpu(case)
