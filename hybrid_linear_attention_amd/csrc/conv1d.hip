@@ -99,9 +99,11 @@ __global__ __launch_bounds__(256) void conv1d_silu_l2_kernel(
         const float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
         if (active) {
             if (c < nqk) {
-                const float inv = 1.0f / sqrtf(ss + l2_eps);
-                TO *dst = c < nq ? q + (int64_t)t * nq + c : k + (int64_t)t * nq + (c - nq);
-                st2(dst, y0 * inv, y1 * inv);
+                if (q != nullptr) {  // null: v-only mode
+                    const float inv = 1.0f / sqrtf(ss + l2_eps);
+                    TO *dst = c < nq ? q + (int64_t)t * nq + c : k + (int64_t)t * nq + (c - nq);
+                    st2(dst, y0 * inv, y1 * inv);
+                }
             } else {
                 st2(v + (int64_t)t * nv + (c - nqk), y0, y1);
             }
@@ -223,6 +225,7 @@ __device__ __forceinline__ void conv_emit(const float (&wt)[4][8], const float (
     ss = group_sum<D / 8>(ss);
     if (active) {
         if (c < nqk) {
+            if (q == nullptr) return;  // v-only mode: q and k are formed elsewhere
             const float inv = 1.0f / sqrtf(ss + l2_eps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] *= inv;
@@ -248,6 +251,9 @@ __global__ __launch_bounds__(256) void conv1d_vec_kernel(
     const int t_nom_end = min(T, t_begin + U);
     const int nqk = 2 * nq;
     const int nv = C - nqk;
+    // v-only mode (q == nullptr): q / k lanes only rewrite their history; heads
+    // never straddle the q|k|v boundaries, so every reduction group agrees
+    const bool outputs = q != nullptr || c >= nqk;
 
     // taps: wt[i][e] multiplies x[t - i] in channel c + e (w is [C][4], 32 contiguous elements)
     float wt[4][8];
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(256) void conv1d_vec_kernel(
 #pragma unroll
     for (int m = 0; m < U + 3; ++m) {
         const int row = t_begin - 3 + m;
-        if (active && row >= 0 && row < T) xr[m].load(x + (int64_t)row * x_ld + c);
+        if (outputs && active && row >= 0 && row < T) xr[m].load(x + (int64_t)row * x_ld + c);
         else xr[m].zero();
     }
 
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(256) void conv1d_vec_kernel(
 #pragma unroll
     for (int j = 0; j < U; ++j) {
         const int t = t_begin + j;
-        if (t < T && ((starts >> j) & 7u) == 0) {  // uniform over the block
+        if (outputs && t < T && ((starts >> j) & 7u) == 0) {  // uniform over each head
             float xw[4][8];  // xw[i] = x[t - i]
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256) void conv1d_vec_kernel(
         else oldh.zero();
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
-            if (m >= L) break;  // uniform
+            if (m >= L || !outputs) break;  // uniform over each head
             float xw[4][8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -358,7 +364,7 @@ template <int D, typename TX, typename TW, typename TO>
 static hipError_t launch_conv_t(const ConvArgs &a, hipStream_t s) {
     // long batches with 16-byte aligned rows take the vectorised kernel
     const bool vec_ok = a.x_ld % (16 / sizeof(TX)) == 0 && aligned16(a.x) && aligned16(a.w) &&
-                        aligned16(a.pool) && aligned16(a.q) && aligned16(a.k) && aligned16(a.v);
+                        aligned16(a.pool) && aligned16(a.q) && aligned16(a.k) && aligned16(a.v);  // null is aligned
     if (a.T > 1024 && vec_ok) {
         constexpr int U = sizeof(TX) == 2 ? 16 : 8;
         dim3 grid((a.T + U - 1) / U, (a.C + CV_WAVES * CV_WAVE_CH - 1) / (CV_WAVES * CV_WAVE_CH));

@@ -249,11 +249,28 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
     gdn::ConvArgs ca{D, x_qkv, x_ld, act_dt == GDN_BF16, conv_w, w_dt == GDN_BF16, conv_pool,
                      query_start_loc, slot_ids, has_initial, num_reqs, num_tokens, C, nq,
                      l2_eps, q, k, v, false};
-    hipError_t he = gdn::launch_conv1d(ca, s);
-    if (he != hipSuccess) return GDN_ERR_HIP;
     gdn::PrefillArgs pa{D, q, k, v, false, a, b, gate_ld, act_dt == GDN_BF16, state_pool,
                         query_start_loc, slot_ids, has_initial, num_reqs, num_tokens,
                         dims->num_k_heads, dims->num_v_heads, o, false, pre, wl.pre};
+    // d = 128 with 16-byte rows: the prefill's prep kernel forms q and k from x
+    // itself, and the conv pass writes only v and the new history
+    const bool prep_conv = D == 128 && x_ld % (int64_t)(16 / e) == 0 && aligned(x_qkv, 16) &&
+                           aligned(conv_w, 16);
+    gdn::ConvArgs cv = ca;
+    if (prep_conv) {
+        cv.q = nullptr;
+        cv.k = nullptr;
+        pa.x = x_qkv;
+        pa.x_ld = x_ld;
+        pa.x_bf16 = act_dt == GDN_BF16;
+        pa.conv_w = conv_w;
+        pa.w_bf16 = w_dt == GDN_BF16;
+        pa.pool = conv_pool;
+        pa.l2_eps = l2_eps;
+        pa.conv_v = &cv;
+    } else {
+        if (gdn::launch_conv1d(ca, s) != hipSuccess) return GDN_ERR_HIP;
+    }
     pa.z = z;
     pa.z_ld = z_ld;
     pa.z_bf16 = act_dt == GDN_BF16;

@@ -105,6 +105,10 @@ template <int WIDTH> __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ float silu_f(float y) { return y / (1.0f + __expf(-y)); }
+// SiLU with the hardware reciprocal (about 1 ulp of fp32 more error than silu_f)
+__device__ __forceinline__ float silu_fast(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y));
+}
 
 // alpha = exp(-softplus(a)) = 1 / (1 + e^a); beta = sigmoid(b) = 1 / (1 + e^-b).
 // Written in the forms that stay finite for any |a|, |b|.

@@ -212,12 +212,22 @@ struct PrepSmem {
 };
 }  // namespace chunk
 
-template <typename TA, typename TG>
+// Conv inputs of the prep kernel's conv mode: q and k of the chunk are formed
+// from x (4-tap causal conv + SiLU + L2 norm, the request's history for rows
+// before its start) instead of being read.
+struct PrepConvIn {
+    const void *x; int64_t x_ld;
+    const void *w;
+    const void *pool; const int32_t *slots; const uint8_t *has_init;
+    int32_t C; float l2_eps;
+};
+
+template <typename TA, typename TG, typename TX, typename TW, bool CONV>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const TA *__restrict__ q, const TA *__restrict__ k, const TG *__restrict__ ga,
     const TG *__restrict__ gb, int64_t gate_ld, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ chunk_off, int32_t nreq, int32_t Hk, int32_t Hv,
-    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg) {
+    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg, PrepConvIn cv) {
     using namespace chunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
@@ -242,20 +252,84 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         gb0.load(gb + go);
     }
 
-    // stage K and Q of the key head as hi/lo planes (1024 four-element slots each)
+    if constexpr (!CONV) {
+        // stage K and Q of the key head as hi/lo planes (1024 four-element slots each)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int idx = tid + 256 * m;
-        const int t = idx >> 5;
-        const int c4 = (idx & 31) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-        if (t < Lc) {
-            const int64_t off = ((int64_t)(tb + t) * Hk + kh) * D + c4;
-            kv = ld4(k + off);
-            qv = ld4(q + off);
+        for (int m = 0; m < 4; ++m) {
+            const int idx = tid + 256 * m;
+            const int t = idx >> 5;
+            const int c4 = (idx & 31) * 4;
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+            if (t < Lc) {
+                const int64_t off = ((int64_t)(tb + t) * Hk + kh) * D + c4;
+                kv = ld4(k + off);
+                qv = ld4(q + off);
+            }
+            split4_store(kv.x, kv.y, kv.z, kv.w, &sm.Kh[t][c4], &sm.Kl[t][c4]);
+            split4_store(qv.x, qv.y, qv.z, qv.w, &sm.Qh[t][c4], &sm.Ql[t][c4]);
         }
-        split4_store(kv.x, kv.y, kv.z, kv.w, &sm.Kh[t][c4], &sm.Kl[t][c4]);
-        split4_store(qv.x, qv.y, qv.z, qv.w, &sm.Qh[t][c4], &sm.Ql[t][c4]);
+    } else {
+        // thread: token t, 32 channels of q (cg < 4) or k (cg >= 4); the 4 threads
+        // of one token's q (or k) are adjacent lanes for the L2 reduction
+        const int t = tid >> 3, cg = tid & 7;
+        const bool isk = cg >= 4;
+        const int cbase = (isk ? Hk * D : 0) + kh * D + 32 * (cg & 3);
+        const int tok = tb + t;
+        const bool valid = t < Lc;
+        const int p = tok - qsl[r];  // position in the request
+        const bool hi = cv.has_init == nullptr || cv.has_init[r] != 0;
+        const int64_t hbase = (int64_t)cv.slots[r] * cv.C;
+        const TX *x = static_cast<const TX *>(cv.x);
+        const TX *pool = static_cast<const TX *>(cv.pool);
+        const TW *wp = static_cast<const TW *>(cv.w);
+        float yv[32];
+        float ss = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int cch = cbase + 8 * g;
+            float wf[32];  // w[c][i] of channels cch .. cch + 7: element 4 e + i
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Raw8<TW> wr;
+                wr.load(wp + (int64_t)cch * 4 + 8 * j);
+                float f8[8];
+                wr.get(f8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wf[8 * j + e] = f8[e];
+            }
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float xi[8];
+                if (valid && p >= i) {
+                    Raw8<TX> xr;
+                    xr.load(x + (int64_t)(tok - i) * cv.x_ld + cch);
+                    xr.get(xi);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)  // history entry 3 + p - i (oldest first)
+                        xi[e] = (valid && hi) ? to_f32(pool[(hbase + cch + e) * 3 + (3 + p - i)]) : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += wf[4 * e + i] * xi[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = valid ? silu_fast(acc[e]) : 0.f;
+                yv[8 * g + e] = y;
+                ss += y * y;
+            }
+        }
+        ss = group_sum<4>(ss);
+        const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
+        const int col = 32 * (cg & 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint16_t *ph = isk ? &sm.Kh[t][col + 4 * j] : &sm.Qh[t][col + 4 * j];
+            uint16_t *pl = isk ? &sm.Kl[t][col + 4 * j] : &sm.Ql[t][col + 4 * j];
+            split4_store(yv[4 * j] * inv, yv[4 * j + 1] * inv, yv[4 * j + 2] * inv, yv[4 * j + 3] * inv,
+                         ph, pl);
+        }
     }
     __syncthreads();
 
@@ -367,7 +441,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = s0 + e;
-                A[t][s] = s < t ? Bw[t] * expf(fminf(Gw[t] - Gw[s], 0.f)) * sm.KK[t][s] : 0.f;
+                A[t][s] = s < t ? Bw[t] * __expf(fminf(Gw[t] - Gw[s], 0.f)) * sm.KK[t][s] : 0.f;
             }
         }
         // P = lower(e^{G_t-G_s} QK) straight into its fragments:
@@ -379,7 +453,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 const int s = 16 * (p >> 2) + 4 * lg + (p & 3);
-                pv[p] = s <= t ? expf(fminf(Gw[t] - Gw[s], 0.f)) * sm.QK[t][s] : 0.f;
+                pv[p] = s <= t ? __expf(fminf(Gw[t] - Gw[s], 0.f)) * sm.QK[t][s] : 0.f;
             }
             uint4 hi, lo;
             split_pack(pv, hi, lo);
@@ -387,49 +461,78 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
             *reinterpret_cast<uint4 *>(tim + (size_t)(FP + 2 + tau) * FRAG + 16 * lane) = lo;
         }
         __builtin_amdgcn_wave_barrier();
-        // T = (I + A)^-1: the two 16x16 diagonal blocks by substitution
-        // (lane: column lr, rows lg + 4 e), then T10 = -T11 A10 T00
+        // T = (I + A)^-1: the two 16x16 diagonal blocks by substitution, then
+        // T10 = -T11 (A10 T00).  Lane (lr, lg) holds column lr, rows lg + 4 e of a
+        // block; the A rows it needs sit in registers, and columns of earlier
+        // results come from other lanes by shuffles.
+        float xb[2][4];  // T00 and T11 columns
 #pragma unroll
-        for (int bb = 0; bb < 32; bb += 16) {
+        for (int bi = 0; bi < 2; ++bi) {
+            const int bb = 16 * bi;
+            float ar[4][16];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&A[bb + lg + 4 * e][bb + 4 * c4]);
+                    ar[e][4 * c4] = a4.x; ar[e][4 * c4 + 1] = a4.y; ar[e][4 * c4 + 2] = a4.z; ar[e][4 * c4 + 3] = a4.w;
+                }
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = (lg + 4 * e == lr) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const float xs = __shfl(x[s >> 2], (s & 3) * 16 + lr, 64);  // X[s][lr]
+            for (int s2 = 0; s2 < 16; ++s2) {
+                const float xs = __shfl(x[s2 >> 2], (s2 & 3) * 16 + lr, 64);  // X[s2][lr]
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = lg + 4 * e;
-                    if (t > s) x[e] -= A[bb + t][bb + s] * xs;
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (lg + 4 * e > s2) x[e] -= ar[e][s2] * xs;
             }
-            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) A[bb + lg + 4 * e][bb + lr] = x[e];
-            __builtin_amdgcn_wave_barrier();
+            for (int e = 0; e < 4; ++e) xb[bi][e] = x[e];
         }
         {
-            float y[4] = {0.f, 0.f, 0.f, 0.f};  // Y = A10 T00
-#pragma unroll 4
-            for (int uu = 0; uu < 16; ++uu) {
-                const float tu = A[uu][lr];
+            // Y = A10 T00 (rows 16 + lg + 4 e, column lr)
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
+            float a10[4][16];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] += A[16 + lg + 4 * e][uu] * tu;
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&A[16 + lg + 4 * e][4 * c4]);
+                    a10[e][4 * c4] = a4.x; a10[e][4 * c4 + 1] = a4.y; a10[e][4 * c4 + 2] = a4.z; a10[e][4 * c4 + 3] = a4.w;
+                }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float tu = __shfl(xb[0][u >> 2], (u & 3) * 16 + lr, 64);  // T00[u][lr]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] += a10[e][u] * tu;
             }
+            // T11 rows of this lane: lane (u, lg) holds T11[lg + 4 e][u]
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) A[16 + lg + 4 * e][lr] = y[e];
+            for (int e = 0; e < 4; ++e) A[16 + lg + 4 * e][16 + lr] = xb[1][e];
             __builtin_amdgcn_wave_barrier();
+            float t11[4][16];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&A[16 + lg + 4 * e][16 + 4 * c4]);
+                    t11[e][4 * c4] = a4.x; t11[e][4 * c4 + 1] = a4.y; t11[e][4 * c4 + 2] = a4.z; t11[e][4 * c4 + 3] = a4.w;
+                }
             float tv[4] = {0.f, 0.f, 0.f, 0.f};  // T10 = -T11 Y
-#pragma unroll 4
-            for (int uu = 0; uu < 16; ++uu) {
-                const float yu = A[16 + uu][lr];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) tv[e] -= A[16 + lg + 4 * e][16 + uu] * yu;
+            for (int u = 0; u < 16; ++u) {
+                const float yu = __shfl(y[u >> 2], (u & 3) * 16 + lr, 64);  // Y[u][lr]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tv[e] -= t11[e][u] * yu;
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) A[16 + lg + 4 * e][lr] = tv[e];
+            for (int e = 0; e < 4; ++e) {
+                A[lg + 4 * e][lr] = xb[0][e];
+                A[16 + lg + 4 * e][lr] = tv[e];
+            }
             __builtin_amdgcn_wave_barrier();
         }
         // T (lower triangle, zeros above) into its fragments
@@ -997,6 +1100,21 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
     return hipGetLastError();
 }
 
+template <typename TA, typename TG, typename TX, typename TW, bool CONV>
+static hipError_t launch_prep(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
+                              uint8_t *kimg, uint8_t *timg, const PrepConvIn &cv) {
+    using namespace chunk;
+    static bool set = false;
+    hipError_t e = set_smem(&prefill_prep_kernel<TA, TG, TX, TW, CONV>, sizeof(PrepSmem), set);
+    if (e != hipSuccess) return e;
+    const int64_t max_chunks = (int64_t)a.T / CH + a.nreq;
+    hipLaunchKernelGGL((prefill_prep_kernel<TA, TG, TX, TW, CONV>), dim3((unsigned)(max_chunks * a.Hk)),
+                       dim3(256), sizeof(PrepSmem), s, (const TA *)a.q, (const TA *)a.k,
+                       (const TG *)a.a, (const TG *)a.b, a.gate_ld, a.qsl, chunk_off, a.nreq, a.Hk,
+                       a.Hv, kimg, timg, cv);
+    return hipGetLastError();
+}
+
 template <typename TA, typename TG, typename TO>
 static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     using namespace chunk;
@@ -1006,19 +1124,25 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     int32_t *order = chunk_off + (a.nreq + 1);
     uint8_t *kimg = base + wl.meta;
     uint8_t *timg = kimg + wl.kimg;
-    const int64_t max_chunks = (int64_t)a.T / CH + a.nreq;
 
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, s, a.qsl, a.nreq, chunk_off, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    static bool prep_set = false;
-    e = set_smem(&prefill_prep_kernel<TA, TG>, sizeof(PrepSmem), prep_set);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_prep_kernel<TA, TG>), dim3((unsigned)(max_chunks * a.Hk)), dim3(256),
-                       sizeof(PrepSmem), s, (const TA *)a.q, (const TA *)a.k, (const TG *)a.a,
-                       (const TG *)a.b, a.gate_ld, a.qsl, chunk_off, a.nreq, a.Hk, a.Hv, kimg, timg);
-    e = hipGetLastError();
+    const PrepConvIn cv{a.x, a.x_ld, a.conv_w, a.pool, a.slots, a.has_init,
+                        2 * a.Hk * D + a.Hv * D, a.l2_eps};
+    if (a.x) {
+        e = a.x_bf16 ? (a.w_bf16 ? launch_prep<TA, TG, bf16, bf16, true>(a, s, chunk_off, kimg, timg, cv)
+                                 : launch_prep<TA, TG, bf16, float, true>(a, s, chunk_off, kimg, timg, cv))
+                     : (a.w_bf16 ? launch_prep<TA, TG, float, bf16, true>(a, s, chunk_off, kimg, timg, cv)
+                                 : launch_prep<TA, TG, float, float, true>(a, s, chunk_off, kimg, timg, cv));
+        if (e != hipSuccess) return e;
+        // v and the new history of every channel, after the prep kernel has read
+        // the old q / k history
+        if (a.conv_v) e = launch_conv1d(*a.conv_v, s);
+    } else {
+        e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv);
+    }
     if (e != hipSuccess) return e;
 
     // large batches: key-head group blocks (the K image staged once for the

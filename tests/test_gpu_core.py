@@ -424,7 +424,8 @@ def test_gated_norm_parity(D, Hv, T, odt, ydt, zoff):
 # ---------------------------------------------------------------------------
 # fused prefill step (conv update -> recurrence -> gated norm)
 # ---------------------------------------------------------------------------
-def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16):
+def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16, x_pad=0):
+    """x_pad > 0 passes x as a column slice of rows x_pad elements wider."""
     d = case.dims
     T = case.num_tokens
     pool = dev(case.conv_pool)
@@ -432,28 +433,40 @@ def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16):
     y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=y_dtype, device="cuda")
     nbytes = gdn.gdn_prefill_fused_workspace_bytes(d, T, case.num_reqs)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    gdn.gdn_prefill_fused(d, dev(case.x_qkv), dev(case.z), dev(case.a), dev(case.b),
+    x = dev(case.x_qkv)
+    if x_pad:
+        C = d.conv_channels
+        wide = torch.zeros((T, C + x_pad), dtype=case.x_qkv.dtype, device="cuda")
+        wide[:, :C] = x
+        x = wide[:, :C]
+    gdn.gdn_prefill_fused(d, x, dev(case.z), dev(case.a), dev(case.b),
                           dev(case.conv_w), dev(case.gamma), pool, state, dev(case.qsl),
                           dev(case.slot_ids), dev(case.has_initial), y, ws, l2_eps=L2_EPS,
                           norm_eps=NORM_EPS)
     return y, pool, state
 
 
-@pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d32_seq"])
+@pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d32_seq",
+                                   "d128_unaligned_rows"])
 def test_prefill_fused_parity(which):
     """One prefill step through gdn_prefill_fused against the fp64 oracle chain:
-    blocks of 32 state rows with a separate gated-norm pass (few heads x
-    requests), whole-head blocks with the norm in the chain (>= 256 of them),
-    and the sequential kernel for d = 32."""
+    32-row chain blocks (few heads x requests), key-head group blocks (>= 256
+    heads x requests), the sequential kernel for d = 32, and x rows that are not
+    16-byte aligned (the conv pass then forms q and k before the prep kernel
+    instead of the prep kernel forming them from x)."""
+    x_pad = 0
     if which == "d128_split_rows":
         case = varlen_case(41, lengths=(1, 2, 5, 37, 0, 130, 3), num_slots=10)
+    elif which == "d128_unaligned_rows":
+        case = varlen_case(44, lengths=(3, 50, 0, 2, 91), num_slots=7)
+        x_pad = 2
     elif which == "d128_whole_heads":
         rng = np.random.default_rng(42)
         lens = [int(x) for x in rng.integers(0, 70, 48)]
         case = varlen_case(42, lengths=lens, num_slots=60)
     else:
         case = varlen_case(43, D=32, Hk=2, Hv=4, lengths=(3, 40, 1, 77), num_slots=6)
-    y, pool, state = run_prefill_fused_gpu(case)
+    y, pool, state = run_prefill_fused_gpu(case, x_pad=x_pad)
     d = case.dims
     qr, kr, vr, pr = oracle_conv(case)
     o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
