@@ -5,11 +5,14 @@ vLLM inference dataflow", section 01, per-layer operator table, GDN layer):
 
     U = RMSNorm(X)                                     gdn_rmsnorm
     [Q0|K0|V0|Z|b|a] = U W_in                          gdn_gemm_bf16
-    q, k, v = L2/SiLU/conv1d(Q0|K0|V0) + history       gdn_conv1d_update
-    o = gated delta rule (prefill requests)            gdn_prefill_varlen
-    o = gated delta rule (decode requests)             gdn_decode_step
-    y = RMSNorm(o) * SiLU(Z)                           gdn_gated_norm
+    conv + L2 norm -> gated delta rule -> RMSNorm(o) * SiLU(Z):
+        prefill requests                               gdn_prefill_fused
+        decode requests                                gdn_decode_fused
     Y = X + y W_o                                      gdn_gemm_bf16 (residual epilogue)
+
+With fused=False the core runs as its separate entry points instead
+(gdn_conv1d_update, gdn_prefill_varlen, gdn_decode_step, gdn_gated_norm), which
+also leaves o in a buffer.
 
 W_in stacks the in-projection's q | k | v | z columns and then b | a (the
 dispatch page "How the 64 layers of Qwen3.8-27B are dispatched in vLLM", step 7,
@@ -49,7 +52,8 @@ class GdnLayer:
     """Buffers for one mixed batch shape and the launch sequence over them."""
 
     def __init__(self, dims, weights: LayerWeights, num_tokens, num_prefill_reqs,
-                 num_prefill_tokens, num_decode, norm_eps=1e-6, l2_eps=1e-6, device="cuda"):
+                 num_prefill_tokens, num_decode, norm_eps=1e-6, l2_eps=1e-6, device="cuda",
+                 fused=True):
         self.dims = dims
         self.w = weights
         self.T = int(num_tokens)
@@ -59,6 +63,7 @@ class GdnLayer:
         if self.T != self.T_pf + self.n_dec:
             raise ValueError("tokens must be the prefill tokens followed by one per decode request")
         self.norm_eps, self.l2_eps = norm_eps, l2_eps
+        self.fused = fused
         Hk, Hv, dk, dv = dims.num_k_heads, dims.num_v_heads, dims.head_dim_k, dims.head_dim_v
         self.cq = 2 * Hk * dk + Hv * dv
         self.cz = Hv * dv
@@ -69,13 +74,16 @@ class GdnLayer:
         T = self.T
         self.U = torch.empty((T, hidden), dtype=torch.bfloat16, device=device)
         self.P = torch.empty((T, n_in), dtype=torch.bfloat16, device=device)
-        self.q = torch.empty((T, Hk, dk), device=device)
-        self.k = torch.empty((T, Hk, dk), device=device)
-        self.v = torch.empty((T, Hv, dv), device=device)
-        self.o = torch.empty((T, Hv, dv), device=device)
         self.y = torch.empty((T, Hv * dv), dtype=torch.bfloat16, device=device)
         self.Y = torch.empty((T, hidden), dtype=torch.bfloat16, device=device)
-        nbytes = gdn.gdn_prefill_workspace_bytes(dims, self.T_pf, self.n_pf) if self.n_pf else 0
+        if fused:
+            nbytes = gdn.gdn_prefill_fused_workspace_bytes(dims, self.T_pf, self.n_pf) if self.n_pf else 0
+        else:
+            self.q = torch.empty((T, Hk, dk), device=device)
+            self.k = torch.empty((T, Hk, dk), device=device)
+            self.v = torch.empty((T, Hv, dv), device=device)
+            self.o = torch.empty((T, Hv, dv), device=device)
+            nbytes = gdn.gdn_prefill_workspace_bytes(dims, self.T_pf, self.n_pf) if self.n_pf else 0
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
     # views of the projection output
@@ -101,6 +109,23 @@ class GdnLayer:
         out = [
             ("rmsnorm", lambda: gdn.gdn_rmsnorm(X, w.gamma_in, self.U, self.norm_eps, stream)),
             ("in_proj", lambda: gdn.gdn_gemm_bf16(self.U, w.W_in, self.P, stream=stream)),
+        ]
+        if self.fused:
+            x, z = self.x_qkv(), self.z()
+            if n_pf:
+                out.append(("prefill", lambda: gdn.gdn_prefill_fused(
+                    d, x[:T_pf], z[:T_pf], a[:T_pf], b[:T_pf], w.conv_w, w.gamma_out, conv_pool,
+                    state_pool, qsl[:n_pf + 1], slot_ids[:n_pf], has_initial[:n_pf], self.y[:T_pf],
+                    self.ws, self.l2_eps, self.norm_eps, stream)))
+            if self.n_dec:
+                out.append(("decode", lambda: gdn.gdn_decode_fused(
+                    d, x[T_pf:], z[T_pf:], a[T_pf:], b[T_pf:], w.conv_w, w.gamma_out, conv_pool,
+                    state_pool, slot_ids[n_pf:], self.y[T_pf:], has_initial=has_initial[n_pf:],
+                    l2_eps=self.l2_eps, norm_eps=self.norm_eps, stream=stream)))
+            out.append(("out_proj", lambda: gdn.gdn_gemm_bf16(self.y, w.W_out, self.Y, residual=X,
+                                                              stream=stream)))
+            return out
+        out += [
             ("conv1d", lambda: gdn.gdn_conv1d_update(
                 d, self.x_qkv(), w.conv_w, conv_pool, qsl, slot_ids, has_initial, self.q, self.k,
                 self.v, self.l2_eps, stream)),
