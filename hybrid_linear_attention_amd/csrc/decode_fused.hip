@@ -24,7 +24,7 @@ namespace gdn {
 
 constexpr int DF_THREADS = 1024;  // fastest of 256, 512, 1024 threads per group block, measured
 
-template <int D, int PF, typename TX, typename TW, typename TY>
+template <int D, typename TX, typename TW, typename TY>
 __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const TX *__restrict__ x, int64_t x_ld, const TX *__restrict__ z, int64_t z_ld,
     const TX *__restrict__ ga, const TX *__restrict__ gb, int64_t gate_ld,
@@ -60,17 +60,20 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     // has_initial = 0: a new request, zero history and zero state
     const bool hi = has_init == nullptr || has_init[r] != 0;
 
-    // state rows of the first PF passes (lane: columns 4 l + 4 LPR m + 0..3)
-    f32x4 buf[PF + 1][2];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
+    // state rows of the first two passes (lane: columns 4 l + 4 LPR m + 0..3);
+    // pass p lands in buf[p % 2]
+    f32x4 buf[2][2];
+    auto load_pass = [&](f32x4 (&dst)[2], int p) {
         const int R = p * RPP + rg;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            buf[p][m] = hi && R < rows ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
-                                             sbase + (int64_t)R * D + 4 * LPR * m))
-                                       : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+            dst[m] = hi && p < npass && R < rows
+                         ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+                               sbase + (int64_t)R * D + 4 * LPR * m))
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    load_pass(buf[0], 0);
+    load_pass(buf[1], 1);
 
     // conv of the group's channels: q (D), k (D), v (G D)
     for (int e = tid; e < (2 + G) * D; e += DF_THREADS) {
@@ -133,16 +136,8 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-    // state rows, PF passes ahead
-    for (int p = 0; p < npass; ++p) {
-        const int Rn = (p + PF) * RPP + rg;
-        if (p + PF < npass) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                buf[PF][m] = hi && Rn < rows ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
-                                                   sbase + (int64_t)Rn * D + 4 * LPR * m))
-                                             : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    // state rows: pass p, then the load of pass p + 2 into the registers it freed
+    auto run_pass = [&](f32x4 (&cur)[2], int p) {
         const int R = p * RPP + rg;
         const bool valid = R < rows;
         const int hh = valid ? R / D : 0;
@@ -151,7 +146,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         float pk = 0.f, pq = 0.f;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const f32x4 s = buf[0][m];
+            const f32x4 s = cur[m];
             pk += s.x * kc[m][0] + s.y * kc[m][1] + s.z * kc[m][2] + s.w * kc[m][3];
             pq += s.x * qc[m][0] + s.y * qc[m][1] + s.z * qc[m][2] + s.w * qc[m][3];
         }
@@ -161,7 +156,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
         if (valid) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                f32x4 s = buf[0][m];
+                f32x4 s = cur[m];
                 s.x = alpha * s.x + be * kc[m][0];
                 s.y = alpha * s.y + be * kc[m][1];
                 s.z = alpha * s.z + be * kc[m][2];
@@ -170,11 +165,11 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
             }
             if (l == 0) so[R] = (alpha * pq + be * kq) * inv_sqrt_d;
         }
-#pragma unroll
-        for (int b = 0; b < PF; ++b) {
-            buf[b][0] = buf[b + 1][0];
-            buf[b][1] = buf[b + 1][1];
-        }
+        load_pass(cur, p + 2);
+    };
+    for (int p = 0; p < npass; p += 2) {
+        run_pass(buf[0], p);
+        if (p + 1 < npass) run_pass(buf[1], p + 1);
     }
     __syncthreads();
 
@@ -217,7 +212,7 @@ size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv) {
 template <int D, typename TX, typename TW, typename TY>
 static hipError_t launch_df_t(const DecodeFusedArgs &a, hipStream_t s) {
     const size_t smem = decode_fused_smem_bytes(D, a.Hk, a.Hv);
-    hipLaunchKernelGGL((decode_fused_kernel<D, 2, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
+    hipLaunchKernelGGL((decode_fused_kernel<D, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
                        dim3(DF_THREADS), smem, s, (const TX *)a.x, a.x_ld, (const TX *)a.z, a.z_ld,
                        (const TX *)a.a, (const TX *)a.b, a.gate_ld, (const TW *)a.w,
                        (const TW *)a.gamma, (TX *)a.pool, a.state, a.slots, a.has_init, a.Hk, a.Hv,

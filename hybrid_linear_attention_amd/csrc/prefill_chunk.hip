@@ -204,11 +204,23 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
 // its T image
 // ---------------------------------------------------------------------------
 namespace chunk {
+constexpr int XR = CH + 3;      // staged conv rows: the 3 tokens before the chunk, then its own
+constexpr int XSP = 2 * D + 8;  // padded staged row: q channels, then k channels (bf16)
 struct PrepSmem {
-    uint16_t Kh[CH][KP], Kl[CH][KP], Qh[CH][KP], Ql[CH][KP];
-    float KK[CH][AP], QK[CH][AP];
-    float A[4][CH][AP];   // per-wave work matrix: A, then T = (I + A)^-1
-    float G[4][CH], Beta[4][CH];
+    // the hi / lo planes of K and Q are dead once the K image and the K K^T /
+    // Q K^T tiles are written: the per-wave work matrices then take their place
+    union {
+        struct { uint16_t Kh[CH][KP], Kl[CH][KP], Qh[CH][KP], Ql[CH][KP]; };
+        struct {
+            float A[4][CH][AP];   // per-wave work matrix: A, then T = (I + A)^-1
+            float G[4][CH], Beta[4][CH];
+        };
+    };
+    // the conv input rows are dead once the planes are written
+    union {
+        uint16_t xs[XR][XSP];
+        struct { float KK[CH][AP], QK[CH][AP]; };
+    };
 };
 }  // namespace chunk
 
@@ -269,66 +281,113 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
             split4_store(qv.x, qv.y, qv.z, qv.w, &sm.Qh[t][c4], &sm.Ql[t][c4]);
         }
     } else {
-        // thread: token t, 32 channels of q (cg < 4) or k (cg >= 4); the 4 threads
-        // of one token's q (or k) are adjacent lanes for the L2 reduction
-        const int t = tid >> 3, cg = tid & 7;
-        const bool isk = cg >= 4;
-        const int cbase = (isk ? Hk * D : 0) + kh * D + 32 * (cg & 3);
-        const int tok = tb + t;
-        const bool valid = t < Lc;
-        const int p = tok - qsl[r];  // position in the request
-        const bool hi = cv.has_init == nullptr || cv.has_init[r] != 0;
-        const int64_t hbase = (int64_t)cv.slots[r] * cv.C;
+        // The conv input of the chunk's q / k channels is staged in LDS with
+        // coalesced 16-byte loads, NCH channels per pass (bf16: q and k in one
+        // pass; fp32: q, then k): staged row rr holds token tb - 3 + rr.  Rows
+        // before the request start come from its history (zeros without one);
+        // rows past the chunk's last token are zeros.
+        constexpr int NCH = 512 / (int)sizeof(TX);  // channels per pass (512 bytes a row)
+        constexpr int NPASS = 2 * D / NCH;
+        constexpr int EPP = 16 / (int)sizeof(TX);   // channels per 16-byte piece
+        constexpr int NCG = NCH / 8;                // 8-channel groups per pass
+        constexpr int TPT = CH * NCG / 256;         // tokens per thread
+        constexpr int NPIECE = XR * 32;
+        constexpr int NM = (NPIECE + 255) / 256;
+        const int t0 = qsl[r];
         const TX *x = static_cast<const TX *>(cv.x);
-        const TX *pool = static_cast<const TX *>(cv.pool);
-        const TW *wp = static_cast<const TW *>(cv.w);
-        float yv[32];
-        float ss = 0.f;
+        TX(*xs)[XSP * 2 / (int)sizeof(TX)] = reinterpret_cast<TX(*)[XSP * 2 / (int)sizeof(TX)]>(&sm.xs[0][0]);
+        // q / k channel of combined column cq (q: 0 .. D-1, k: D .. 2D-1)
+        auto chan = [&](int cq) { return (cq >= D ? Hk * D : 0) + kh * D + (cq & (D - 1)); };
+        // compute mapping: 8 channels (group cgi) of tokens TPT tg .. TPT tg + TPT - 1;
+        // the 16 groups of one token's q (or k) are 16 aligned adjacent lanes
+        const int tg = tid / NCG, cgi = tid % NCG;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int cch = cbase + 8 * g;
-            float wf[32];  // w[c][i] of channels cch .. cch + 7: element 4 e + i
+        for (int ps = 0; ps < NPASS; ++ps) {
+            if (ps) __syncthreads();  // the previous pass is done with the staged rows
+            uint4 pv[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const int pi = tid + 256 * m;
+                const int rr = pi >> 5, seg = pi & 31;
+                const int tok = tb - 3 + rr;
+                pv[m] = make_uint4(0u, 0u, 0u, 0u);
+                if (pi < NPIECE && tok >= t0 && rr - 3 < Lc)
+                    pv[m] = *reinterpret_cast<const uint4 *>(x + (int64_t)tok * cv.x_ld +
+                                                             chan(ps * NCH + EPP * seg));
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const int pi = tid + 256 * m;
+                const int rr = pi >> 5, seg = pi & 31;
+                if (pi < NPIECE && tb - 3 + rr >= t0)
+                    *reinterpret_cast<uint4 *>(&xs[rr][EPP * seg]) = pv[m];
+            }
+            if (tb == t0) {  // first chunk of its request (uniform over the block)
+                const bool hi = cv.has_init == nullptr || cv.has_init[r] != 0;
+                const int64_t hbase = (int64_t)cv.slots[r] * cv.C;
+                const TX *pool = static_cast<const TX *>(cv.pool);
+#pragma unroll
+                for (int j = 0; j < (3 * NCH + 255) / 256; ++j) {  // history entry rr = row rr
+                    const int idx = tid + 256 * j;
+                    const int rr = idx / NCH, cc = idx % NCH;
+                    if (rr < 3) {
+                        if (hi) xs[rr][cc] = pool[(hbase + chan(ps * NCH + cc)) * 3 + rr];
+                        else xs[rr][cc] = TX{};
+                    }
+                }
+            }
+            __syncthreads();
+            const int cq = ps * NCH + 8 * cgi;
+            const bool isk = cq >= D;
+            const int col = cq & (D - 1);
+            const TW *wp = static_cast<const TW *>(cv.w) + (int64_t)chan(cq) * 4;
+            float wf[32];  // w[channel + e][i] at 4 e + i
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 Raw8<TW> wr;
-                wr.load(wp + (int64_t)cch * 4 + 8 * j);
+                wr.load(wp + 8 * j);
                 float f8[8];
                 wr.get(f8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) wf[8 * j + e] = f8[e];
             }
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float y[TPT][8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float xi[8];
-                if (valid && p >= i) {
-                    Raw8<TX> xr;
-                    xr.load(x + (int64_t)(tok - i) * cv.x_ld + cch);
-                    xr.get(xi);
-                } else {
+            for (int j = 0; j < TPT; ++j)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)  // history entry 3 + p - i (oldest first)
-                        xi[e] = (valid && hi) ? to_f32(pool[(hbase + cch + e) * 3 + (3 + p - i)]) : 0.f;
+                for (int e = 0; e < 8; ++e) y[j][e] = 0.f;
+            // staged row TPT tg + rw is token TPT tg + rw - 3: tap i of token TPT tg + j
+#pragma unroll
+            for (int rw = 0; rw < TPT + 3; ++rw) {
+                Raw8<TX> xr;
+                xr.load(&xs[TPT * tg + rw][8 * cgi]);
+                float xe[8];
+                xr.get(xe);
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    const int i = j + 3 - rw;
+                    if (i >= 0 && i < 4) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) y[j][e] += wf[4 * e + i] * xe[e];
+                    }
                 }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += wf[4 * e + i] * xi[e];
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = valid ? silu_fast(acc[e]) : 0.f;
-                yv[8 * g + e] = y;
-                ss += y * y;
-            }
-        }
-        ss = group_sum<4>(ss);
-        const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
-        const int col = 32 * (cg & 3);
+            for (int j = 0; j < TPT; ++j) {
+                const int t = TPT * tg + j;
+                float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint16_t *ph = isk ? &sm.Kh[t][col + 4 * j] : &sm.Qh[t][col + 4 * j];
-            uint16_t *pl = isk ? &sm.Kl[t][col + 4 * j] : &sm.Ql[t][col + 4 * j];
-            split4_store(yv[4 * j] * inv, yv[4 * j + 1] * inv, yv[4 * j + 2] * inv, yv[4 * j + 3] * inv,
-                         ph, pl);
+                for (int e = 0; e < 8; ++e) {
+                    y[j][e] = t < Lc ? silu_fast(y[j][e]) : 0.f;
+                    ss += y[j][e] * y[j][e];
+                }
+                ss = group_sum<16>(ss);
+                const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
+                uint16_t *ph = isk ? &sm.Kh[t][col] : &sm.Qh[t][col];
+                uint16_t *pl = isk ? &sm.Kl[t][col] : &sm.Ql[t][col];
+                split4_store(y[j][0] * inv, y[j][1] * inv, y[j][2] * inv, y[j][3] * inv, ph, pl);
+                split4_store(y[j][4] * inv, y[j][5] * inv, y[j][6] * inv, y[j][7] * inv, ph + 4, pl + 4);
+            }
         }
     }
     __syncthreads();
