@@ -15,17 +15,35 @@
 // channels of the value heads that read it are computed once, their history
 // entries are read and rewritten by the same thread (race-free), and the
 // block then streams those value heads' state rows (read once, written once,
-// nontemporal) and normalises whole heads of o from LDS.  The first rows'
-// state loads are issued before the conv so its latency hides under them.
+// nontemporal) and normalises whole heads of o from LDS.  The first two
+// passes' state loads are issued before the conv so its latency hides under
+// them; afterwards DF_BUFFERS passes stay in flight.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-constexpr int DF_THREADS = 1024;  // fastest of 256, 512, 1024 threads per group block, measured
+constexpr int DF_THREADS = 1024;
+constexpr int DF_BUFFERS = 3;     // state passes in flight per block
+// buffer resource word 3 (raw 32-bit data, range-checked) and the nontemporal
+// cache policy of the state's buffer loads and stores
+constexpr int BUF_DW3 = 0x00020000;
+constexpr int BUF_NT = 2;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, typename TX, typename TW, typename TY>
-__global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
+// A buffer resource over [base, base + bytes) from wave-uniform values (read
+// from the first lane, so the descriptor lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const float *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0,
+                                             (int)n, BUF_DW3);
+}  // fastest of 256, 512, 1024 threads per group block, measured
+
+template <int D, int NB, typename TX, typename TW, typename TY>
+__global__ __launch_bounds__(DF_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void decode_fused_kernel(
     const TX *__restrict__ x, int64_t x_ld, const TX *__restrict__ z, int64_t z_ld,
     const TX *__restrict__ ga, const TX *__restrict__ gb, int64_t gate_ld,
     const TW *__restrict__ w, const TW *__restrict__ gamma, TX *__restrict__ pool,
@@ -53,27 +71,32 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const int C = 2 * nq + Hv * D;
     const int l = tid % LPR;
     const int rg = tid / LPR;
-    const int npass = (rows + RPP - 1) / RPP;
-    // rows R = hh * D + i of the group's heads are contiguous in the slot
-    float *sbase = state + ((int64_t)slot * Hv + (int64_t)kh * G) * D * D + 4 * l;
+    // passes, rounded up to a multiple of the NB rotating buffers (a pass
+    // past the last row has no rows)
+    const int npass = ((rows + RPP - 1) / RPP + NB - 1) / NB * NB;
 
     // has_initial = 0: a new request, zero history and zero state
     const bool hi = has_init == nullptr || has_init[r] != 0;
 
-    // state rows of the first two passes (lane: columns 4 l + 4 LPR m + 0..3);
-    // pass p lands in buf[p % 2]
-    f32x4 buf[2][2];
+    // The unit's state rows (those of its value heads, contiguous in the slot)
+    // as buffer resources: loads read zeros without an initial state and past
+    // the last row, where stores are dropped, so no branch guards a state
+    // access and every access counts in the memory counters the waits are
+    // derived from.  Lane: row rg of a pass, columns 4 l + 4 LPR m + 0..3.
+    const uint32_t ubytes = (uint32_t)rows * D * 4;
+    float *ubase = state + ((int64_t)slot * Hv + (int64_t)kh * G) * D * D;
+    const __amdgpu_buffer_rsrc_t rld = uniform_rsrc(ubase, hi ? ubytes : 0u);
+    const __amdgpu_buffer_rsrc_t rst = uniform_rsrc(ubase, ubytes);
+    const uint32_t loff = ((uint32_t)rg * D + 4 * l) * 4;
+    f32x4 buf[NB][2];  // pass p lands in buf[p % NB]
     auto load_pass = [&](f32x4 (&dst)[2], int p) {
-        const int R = p * RPP + rg;
+        const uint32_t off = (uint32_t)p * RPP * D * 4 + loff;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            dst[m] = hi && p < npass && R < rows
-                         ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
-                               sbase + (int64_t)R * D + 4 * LPR * m))
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+            dst[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rld, off + 16 * LPR * m, 0, BUF_NT));
     };
-    load_pass(buf[0], 0);
-    load_pass(buf[1], 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) load_pass(buf[b], b);
 
     // conv of the group's channels: q (D), k (D), v (G D)
     for (int e = tid; e < (2 + G) * D; e += DF_THREADS) {
@@ -126,50 +149,53 @@ __global__ __launch_bounds__(DF_THREADS) void decode_fused_kernel(
     const float inv_q = 1.0f / sqrtf(red[0] + l2_eps);
     const float inv_k = 1.0f / sqrtf(red[1] + l2_eps);
     const float kq = red[2] * inv_q * inv_k;
-    float kc[2][4], qc[2][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kc[m][j] = sk[4 * l + 4 * LPR * m + j] * inv_k;
-            qc[m][j] = sq[4 * l + 4 * LPR * m + j] * inv_q;
-        }
+    // q and k normalised in place; each pass reads its lane's columns
+    if (tid < D) sq[tid] *= inv_q;
+    else if (tid < 2 * D) sk[tid - D] *= inv_k;
+    __syncthreads();
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-    // state rows: pass p, then the load of pass p + 2 into the registers it freed
+    // pass p, then the load of pass p + NB into the registers it freed
     auto run_pass = [&](f32x4 (&cur)[2], int p) {
         const int R = p * RPP + rg;
         const bool valid = R < rows;
         const int hh = valid ? R / D : 0;
         const float alpha = sa[hh], beta = sb[hh];
         const float vi = valid ? sv[R] : 0.f;
+        float4 kc[2];
         float pk = 0.f, pq = 0.f;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const f32x4 s = cur[m];
-            pk += s.x * kc[m][0] + s.y * kc[m][1] + s.z * kc[m][2] + s.w * kc[m][3];
-            pq += s.x * qc[m][0] + s.y * qc[m][1] + s.z * qc[m][2] + s.w * qc[m][3];
+            kc[m] = *reinterpret_cast<const float4 *>(sk + 4 * l + 4 * LPR * m);
+            const float4 qm = *reinterpret_cast<const float4 *>(sq + 4 * l + 4 * LPR * m);
+            pk += s.x * kc[m].x + s.y * kc[m].y + s.z * kc[m].z + s.w * kc[m].w;
+            pq += s.x * qm.x + s.y * qm.y + s.z * qm.z + s.w * qm.w;
         }
         pk = group_sum<LPR>(pk);
         pq = group_sum<LPR>(pq);
         const float be = beta * (vi - alpha * pk);
-        if (valid) {
+        const uint32_t off = (uint32_t)p * RPP * D * 4 + loff;
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                f32x4 s = cur[m];
-                s.x = alpha * s.x + be * kc[m][0];
-                s.y = alpha * s.y + be * kc[m][1];
-                s.z = alpha * s.z + be * kc[m][2];
-                s.w = alpha * s.w + be * kc[m][3];
-                __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(sbase + (int64_t)R * D + 4 * LPR * m));
-            }
-            if (l == 0) so[R] = (alpha * pq + be * kq) * inv_sqrt_d;
+        for (int m = 0; m < 2; ++m) {
+            f32x4 s = cur[m];
+            s.x = alpha * s.x + be * kc[m].x;
+            s.y = alpha * s.y + be * kc[m].y;
+            s.z = alpha * s.z + be * kc[m].z;
+            s.w = alpha * s.w + be * kc[m].w;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), rst, off + 16 * LPR * m, 0, BUF_NT);
         }
-        load_pass(cur, p + 2);
+        if (valid && l == 0) so[R] = (alpha * pq + be * kq) * inv_sqrt_d;
+        load_pass(cur, p + NB);
     };
-    for (int p = 0; p < npass; p += 2) {
-        run_pass(buf[0], p);
-        if (p + 1 < npass) run_pass(buf[1], p + 1);
+    // the first NB passes are peeled so that the loop is entered, like its back
+    // edge, right after unconditional state accesses (its waits then leave the
+    // later passes' loads in flight)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) run_pass(buf[b], b);
+    for (int p = NB; p < npass; p += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) run_pass(buf[b], p + b);
     }
     __syncthreads();
 
@@ -212,7 +238,7 @@ size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv) {
 template <int D, typename TX, typename TW, typename TY>
 static hipError_t launch_df_t(const DecodeFusedArgs &a, hipStream_t s) {
     const size_t smem = decode_fused_smem_bytes(D, a.Hk, a.Hv);
-    hipLaunchKernelGGL((decode_fused_kernel<D, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
+    hipLaunchKernelGGL((decode_fused_kernel<D, DF_BUFFERS, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
                        dim3(DF_THREADS), smem, s, (const TX *)a.x, a.x_ld, (const TX *)a.z, a.z_ld,
                        (const TX *)a.a, (const TX *)a.b, a.gate_ld, (const TW *)a.w,
                        (const TW *)a.gamma, (TX *)a.pool, a.state, a.slots, a.has_init, a.Hk, a.Hv,
