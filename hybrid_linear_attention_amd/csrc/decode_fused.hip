@@ -42,8 +42,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const float *base
                                              (int)n, BUF_DW3);
 }  // fastest of 256, 512, 1024 threads per group block, measured
 
-template <int D, int NB, typename TX, typename TW, typename TY>
-__global__ __launch_bounds__(DF_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void decode_fused_kernel(
+template <int D, int NB, int NT, typename TX, typename TW, typename TY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void decode_fused_kernel(
     const TX *__restrict__ x, int64_t x_ld, const TX *__restrict__ z, int64_t z_ld,
     const TX *__restrict__ ga, const TX *__restrict__ gb, int64_t gate_ld,
     const TW *__restrict__ w, const TW *__restrict__ gamma, TX *__restrict__ pool,
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(DF_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const uint8_t *__restrict__ has_init, int32_t Hk, int32_t Hv, float l2_eps,
     float norm_eps, TY *__restrict__ y, float *__restrict__ o_out) {
     constexpr int LPR = D / 8;              // lanes per state row
-    constexpr int RPP = DF_THREADS / LPR;   // rows per pass
+    constexpr int RPP = NT / LPR;   // rows per pass
     extern __shared__ __attribute__((aligned(16))) float dsm[];
     const int G = Hv / Hk;
     const int rows = G * D;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(DF_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     for (int b = 0; b < NB; ++b) load_pass(buf[b], b);
 
     // conv of the group's channels: q (D), k (D), v (G D)
-    for (int e = tid; e < (2 + G) * D; e += DF_THREADS) {
+    for (int e = tid; e < (2 + G) * D; e += NT) {
         int c;
         float *dst;
         if (e < D) {
@@ -150,8 +150,7 @@ __global__ __launch_bounds__(DF_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const float inv_k = 1.0f / sqrtf(red[1] + l2_eps);
     const float kq = red[2] * inv_q * inv_k;
     // q and k normalised in place; each pass reads its lane's columns
-    if (tid < D) sq[tid] *= inv_q;
-    else if (tid < 2 * D) sk[tid - D] *= inv_k;
+    for (int e = tid; e < 2 * D; e += NT) dsm[e] *= e < D ? inv_q : inv_k;  // sq, then sk
     __syncthreads();
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
@@ -199,10 +198,10 @@ __global__ __launch_bounds__(DF_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
     __syncthreads();
 
-    // gated RMSNorm of the group's heads, DF_THREADS elements (whole heads) at a time
-    const int nchunks = (rows + DF_THREADS - 1) / DF_THREADS;
+    // gated RMSNorm of the group's heads, NT elements (whole heads) at a time
+    const int nchunks = (rows + NT - 1) / NT;
     for (int ch = 0; ch < nchunks; ++ch) {
-        const int e = ch * DF_THREADS + tid;
+        const int e = ch * NT + tid;
         const bool valid = e < rows;
         const float ov = valid ? so[e] : 0.f;
         float ss;
@@ -238,7 +237,7 @@ size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv) {
 template <int D, typename TX, typename TW, typename TY>
 static hipError_t launch_df_t(const DecodeFusedArgs &a, hipStream_t s) {
     const size_t smem = decode_fused_smem_bytes(D, a.Hk, a.Hv);
-    hipLaunchKernelGGL((decode_fused_kernel<D, DF_BUFFERS, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
+    hipLaunchKernelGGL((decode_fused_kernel<D, DF_BUFFERS, DF_THREADS, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
                        dim3(DF_THREADS), smem, s, (const TX *)a.x, a.x_ld, (const TX *)a.z, a.z_ld,
                        (const TX *)a.a, (const TX *)a.b, a.gate_ld, (const TW *)a.w,
                        (const TW *)a.gamma, (TX *)a.pool, a.state, a.slots, a.has_init, a.Hk, a.Hv,

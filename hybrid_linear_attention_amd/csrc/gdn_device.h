@@ -97,10 +97,31 @@ __device__ __forceinline__ void store8(bf16 *p, const float (&f)[8]) {
     *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Butterfly sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Lane permutations inside rows of 16 lanes (DPP): xor 1 and xor 2 inside a
+// quad, then the mirror of an 8-lane half and of the 16-lane row.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+    int r;
+    switch (ctrl_sel) {
+        case 0: r = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true); break;   // quad_perm 1,0,3,2
+        case 1: r = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true); break;   // quad_perm 2,3,0,1
+        case 2: r = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+        default: r = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true); break; // row_mirror
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+// Butterfly sum over aligned groups of `width` lanes (width a power of two <=
+// 64); every lane of a group ends with the group's sum.  Up to 16 lanes the
+// partner values move by DPP (no LDS round trip): once the 4 (8) lanes below
+// hold equal partial sums, the mirrored lane holds the same partial sum as the
+// xor-4 (xor-8) partner, so the additions are those of the xor butterfly.
 template <int WIDTH> __device__ __forceinline__ float group_sum(float v) {
+    if constexpr (WIDTH >= 2) v += dpp_f(v, 0);
+    if constexpr (WIDTH >= 4) v += dpp_f(v, 1);
+    if constexpr (WIDTH >= 8) v += dpp_f(v, 2);
+    if constexpr (WIDTH >= 16) v += dpp_f(v, 3);
 #pragma unroll
-    for (int m = 1; m < WIDTH; m <<= 1) v += __shfl_xor(v, m, 64);
+    for (int m = 16; m < WIDTH; m <<= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
 
