@@ -15,9 +15,9 @@
 // channels of the value heads that read it are computed once, their history
 // entries are read and rewritten by the same thread (race-free), and the
 // block then streams those value heads' state rows (read once, written once,
-// nontemporal) and normalises whole heads of o from LDS.  The first two
-// passes' state loads are issued before the conv so its latency hides under
-// them; afterwards DF_BUFFERS passes stay in flight.
+// nontemporal) and normalises whole heads of o from LDS.  The state rows go
+// in groups of DF_BUFFERS passes whose loads are in flight together; the first
+// group's loads are issued before the conv so its latency hides under them.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -71,8 +71,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
     const int C = 2 * nq + Hv * D;
     const int l = tid % LPR;
     const int rg = tid / LPR;
-    // passes, rounded up to a multiple of the NB rotating buffers (a pass
-    // past the last row has no rows)
+    // passes, rounded up to whole groups of NB (a pass past the last row has
+    // no rows)
     const int npass = ((rows + RPP - 1) / RPP + NB - 1) / NB * NB;
 
     // has_initial = 0: a new request, zero history and zero state
@@ -149,27 +149,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
     const float inv_q = 1.0f / sqrtf(red[0] + l2_eps);
     const float inv_k = 1.0f / sqrtf(red[1] + l2_eps);
     const float kq = red[2] * inv_q * inv_k;
-    // q and k normalised in place; each pass reads its lane's columns
+    // q and k normalised in place, then the lane's columns in registers
     for (int e = tid; e < 2 * D; e += NT) dsm[e] *= e < D ? inv_q : inv_k;  // sq, then sk
     __syncthreads();
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    float4 kc[2], qc[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        kc[m] = *reinterpret_cast<const float4 *>(sk + 4 * l + 4 * LPR * m);
+        qc[m] = *reinterpret_cast<const float4 *>(sq + 4 * l + 4 * LPR * m);
+    }
 
-    // pass p, then the load of pass p + NB into the registers it freed
+    // pass p from the registers its load landed in
     auto run_pass = [&](f32x4 (&cur)[2], int p) {
         const int R = p * RPP + rg;
         const bool valid = R < rows;
         const int hh = valid ? R / D : 0;
         const float alpha = sa[hh], beta = sb[hh];
         const float vi = valid ? sv[R] : 0.f;
-        float4 kc[2];
         float pk = 0.f, pq = 0.f;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const f32x4 s = cur[m];
-            kc[m] = *reinterpret_cast<const float4 *>(sk + 4 * l + 4 * LPR * m);
-            const float4 qm = *reinterpret_cast<const float4 *>(sq + 4 * l + 4 * LPR * m);
             pk += s.x * kc[m].x + s.y * kc[m].y + s.z * kc[m].z + s.w * kc[m].w;
-            pq += s.x * qm.x + s.y * qm.y + s.z * qm.z + s.w * qm.w;
+            pq += s.x * qc[m].x + s.y * qc[m].y + s.z * qc[m].z + s.w * qc[m].w;
         }
         pk = group_sum<LPR>(pk);
         pq = group_sum<LPR>(pq);
@@ -185,14 +188,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), rst, off + 16 * LPR * m, 0, BUF_NT);
         }
         if (valid && l == 0) so[R] = (alpha * pq + be * kq) * inv_sqrt_d;
-        load_pass(cur, p + NB);
     };
-    // the first NB passes are peeled so that the loop is entered, like its back
-    // edge, right after unconditional state accesses (its waits then leave the
-    // later passes' loads in flight)
+    // groups of NB passes: all of a group's loads are in flight together, then
+    // its passes are computed and stored (measured faster on this state
+    // stream than rotating each freed buffer to the pass NB ahead)
 #pragma unroll
     for (int b = 0; b < NB; ++b) run_pass(buf[b], b);
     for (int p = NB; p < npass; p += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) load_pass(buf[b], p + b);
 #pragma unroll
         for (int b = 0; b < NB; ++b) run_pass(buf[b], p + b);
     }
