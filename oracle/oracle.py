@@ -258,6 +258,86 @@ def decode_step(q, k, v, a, b, state_pool, slot_ids):
                             np.ones(R, np.uint8))
 
 
+def spec_verify(x_qkv, z, a, b, conv_w, gamma, hist_pool, state_pool, qsl, slot_ids,
+                spec_slots, has_initial, Hk, Hv, dk, dv, l2_eps, norm_eps):
+    """Speculative multi-token verify of the GDN core.
+
+    Each request brings a few tokens at once (the last accepted token followed
+    by draft tokens); they pass through conv -> L2 norm -> gated delta rule ->
+    gated norm exactly as a prefill of those tokens would.  In addition the
+    recurrent state and the conv history reached after EVERY token j are kept,
+    in slot spec_slots[r, j] of the state and history pools, so that rejecting
+    the drafts after token j rolls the request back to that slot.  The pages
+    give this bookkeeping only as extra speculative slots: the tutorial page's
+    data-structure table counts extra speculative slots for the conv history,
+    and the dispatch page (step 5) passes num_spec into the state-shape
+    calculator; the per-position slots are the reading taken.
+
+    Definition used here: the state (history) at position j is that of the same
+    request run over its first j + 1 tokens only — each prefix is a separate
+    call of conv1d_silu / gated_delta_rule from the request's input slot.
+
+    x_qkv [T, Cqkv], z [T, Hv, dv], a, b [T, Hv]; spec_slots [nreq, max_tokens]
+    int; request r has qsl[r+1] - qsl[r] <= max_tokens tokens.  The input slot
+    slot_ids[r] is read and left unchanged unless spec_slots[r, 0] names it.
+    Returns (y [T, Hv*dv], o [T, Hv, dv], new_hist_pool, new_state_pool).
+    """
+    x_qkv = _f64(x_qkv)
+    hist_pool = _f64(hist_pool)
+    state_pool = _f64(state_pool)
+    a = _f64(a)
+    b = _f64(b)
+    T = x_qkv.shape[0]
+    slot_ids = np.asarray(slot_ids, np.int64)
+    nreq = slot_ids.size
+    spec = np.asarray(spec_slots, np.int64).reshape(nreq, -1)
+    max_tokens = spec.shape[1]
+    qsl = np.asarray(qsl, np.int64)
+    lens = np.diff(qsl)
+    _check_meta(qsl, slot_ids, T, state_pool.shape[0])
+    if np.any(lens > max_tokens):
+        raise ValueError("a request has more tokens than spec slots")
+    hi = (np.ones(nreq, np.uint8) if has_initial is None
+          else np.asarray(has_initial, np.uint8))
+    written = [int(spec[r, j]) for r in range(nreq) for j in range(lens[r])]
+    if any(s < 0 or s >= state_pool.shape[0] for s in written):
+        raise ValueError("spec slot out of range")
+    if len(set(written)) != len(written):
+        raise ValueError("spec slots must be distinct")
+    for r in range(nreq):
+        for r2 in range(nreq):
+            for j in range(lens[r2]):
+                if spec[r2, j] == slot_ids[r] and not (r2 == r and j == 0):
+                    raise ValueError("a spec slot may name an input slot only at its own position 0")
+
+    # the outputs do not depend on where the states are kept
+    q, k, v, _ = conv1d_update(x_qkv, conv_w, hist_pool, qsl, slot_ids, hi, Hk, Hv, dk, dv,
+                               l2_eps)
+    o, _ = gated_delta_rule(q, k, v, a, b, state_pool, qsl, slot_ids, hi)
+    y = gated_norm(o, z, gamma, norm_eps)
+
+    new_hist = hist_pool.copy()
+    new_state = state_pool.copy()
+    for j in range(max_tokens):
+        sel = [r for r in range(nreq) if lens[r] > j]
+        if not sel:
+            break
+        # every selected request cut to its first j + 1 tokens, in a compact
+        # pool of its own input slots
+        rows = np.concatenate([np.arange(qsl[r], qsl[r] + j + 1) for r in sel])
+        sub_qsl = np.arange(len(sel) + 1) * (j + 1)
+        sub_slots = np.arange(len(sel))
+        sub_hi = hi[sel]
+        _, hist_j = conv1d_silu(x_qkv[rows], conv_w, hist_pool[slot_ids[sel]], sub_qsl,
+                                sub_slots, sub_hi)
+        _, st_j = gated_delta_rule(q[rows], k[rows], v[rows], a[rows], b[rows],
+                                   state_pool[slot_ids[sel]], sub_qsl, sub_slots, sub_hi)
+        for i, r in enumerate(sel):
+            new_hist[spec[r, j]] = hist_j[i]
+            new_state[spec[r, j]] = st_j[i]
+    return y, o, new_hist, new_state
+
+
 # ---------------------------------------------------------------------------
 # one GDN layer block (operator table rows 1-8)
 # ---------------------------------------------------------------------------
