@@ -1,7 +1,7 @@
 """Benchmark of the GDN mixer core on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-layer]
-                    [--no-cpu]
+                    [--no-spec] [--no-cpu]
 
 Headline workload (N=1): one decode step of 64 requests at full shapes (16 key /
 48 value heads, d = 128, fp32 state [64,48,128,128]): conv update -> recurrence
@@ -10,7 +10,8 @@ resident in HBM; the same step as three launches (conv1d_update ->
 decode_step -> gated_norm) is timed beside it.  `value`
 is the state bytes each step reads and writes (2 x 64 x 3 MiB) divided by the
 measured step time.  A prefill leg (single 4096-token sequence; 16-request
-packed varlen batch) reports tokens/s in the same run, a layer leg times the
+packed varlen batch) reports tokens/s in the same run, a speculative-verify leg
+times 64 requests x 4 tokens with per-position state slots, a layer leg times the
 whole layer block on the mixed 8 x 2048 + 256 batch at hidden 5120, and the
 fp64 CPU oracle is timed on a bounded sample on the host cores.
 
@@ -43,6 +44,8 @@ def parse():
     p.add_argument("--no-varlen", action="store_true")
     p.add_argument("--no-layer", action="store_true")
     p.add_argument("--layer-steps", type=int, default=5)
+    p.add_argument("--no-spec", action="store_true")
+    p.add_argument("--spec-steps", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-ref-mib", type=int, default=0,
@@ -260,6 +263,11 @@ def main():
             torch.cuda.empty_cache()
         result["prefill"] = pre
 
+    # ------------------------------------------------------ speculative verify
+    if not args.no_spec:
+        result["spec_verify"] = bench_spec(args.spec_steps, args.warmup, dev, stream, torch, gdn)
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------- layer block
     if not args.no_layer:
         result["layer"] = bench_layer(args.layer_steps, dev, stream, torch, np)
@@ -421,6 +429,75 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np):
         "requests": c.num_reqs,
         "ms_per_step": round(ms, 4),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
+    }
+
+
+def spec_bytes(d, R, n, act_bytes=2, y_bytes=2):
+    """Algorithmic HBM bytes of one gdn_spec_verify launch over R requests of n
+    tokens: each request's state read once and written once per token; its conv
+    history read once and written once per token; every token's conv inputs, z
+    and gates read once and its y written once (1,037,877,248 B at 64 x 4, full
+    shapes, bf16 activations)."""
+    Hv, D = d.num_v_heads, d.head_dim_v
+    C = 2 * d.num_k_heads * d.head_dim_k + Hv * D
+    state = R * (1 + n) * Hv * D * d.head_dim_k * 4
+    hist = R * (1 + n) * C * (d.conv_taps - 1) * act_bytes
+    tok = R * n * (C * act_bytes + Hv * D * act_bytes + 2 * Hv * act_bytes + Hv * D * y_bytes)
+    return state, state + hist + tok
+
+
+def bench_spec(steps, warmup, dev, stream, torch, gdn):
+    """gdn_spec_verify on 64 requests x 4 tokens (the last accepted token and 3
+    drafts) at full shapes: K back-to-back launches between one event pair, three
+    pools used in turn so that no state is still in the memory-side cache."""
+    from hybrid_linear_attention_amd.workloads import spec_verify_r64
+
+    c = spec_verify_r64()
+    d = c.dims
+    R, T = c.num_reqs, c.num_tokens
+    n = T // R
+    n_rot = 3
+    pools = [c.conv_pool.to(dev) for _ in range(n_rot)]
+    states = [c.state_pool.to(dev) for _ in range(n_rot)]
+    x, z, a, b = c.x_qkv.to(dev), c.z.to(dev), c.a.to(dev), c.b.to(dev)
+    conv_w, gamma = c.conv_w.to(dev), c.gamma.to(dev)
+    qsl, slots, spec = c.qsl.to(dev), c.slot_ids.to(dev), c.meta["spec_slots"].to(dev)
+    y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=torch.bfloat16, device=dev)
+    sh = stream.cuda_stream
+    it = [0]
+
+    def step():
+        i = it[0] % n_rot
+        it[0] += 1
+        gdn.gdn_spec_verify(d, x, z, a, b, conv_w, gamma, pools[i], states[i], qsl, slots, spec,
+                            y, l2_eps=L2_EPS, norm_eps=NORM_EPS, stream=sh)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    gpu = e0.elapsed_time(e1) / steps
+    state_b, nbytes = spec_bytes(d, R, n)
+    achieved = nbytes / (gpu * 1e-3) / 1e9
+    del pools, states
+    return {
+        "workload": f"spec_verify_r64: {R} requests x {n} tokens (1 accepted + {n - 1} drafts), "
+                    "16/48 heads, d = 128, state and history kept after every token",
+        "ms_per_step": round(wall, 4),
+        "gpu_ms_per_step": round(gpu, 4),
+        "tokens_per_s": round(T / (wall * 1e-3), 1),
+        "state_gbs": round(state_b / (wall * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "spec_verify_kernel (gdn_spec_verify)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                     "traffic": measured_traffic("spec_verify_kernel", "spec_verify.hip")},
     }
 
 

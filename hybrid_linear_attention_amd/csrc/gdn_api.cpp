@@ -142,6 +142,48 @@ gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_l
     return hip_status(gdn::launch_decode_fused(da, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
+                           int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
+                           gdn_dtype act_dt, const void *conv_w, const void *gamma,
+                           gdn_dtype w_dt, void *conv_pool, float *state_pool,
+                           const int32_t *query_start_loc, const int32_t *slot_ids,
+                           const int32_t *spec_slot_ids, int32_t max_tokens,
+                           const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
+                           int32_t num_slots, float l2_eps, float norm_eps, void *y,
+                           gdn_dtype y_dt, float *o, void *stream) {
+    gdn_status st = check_dims(dims);
+    if (st != GDN_OK) return st;
+    const int D = dims->head_dim_k;
+    if (max_tokens < 1 || max_tokens > GDN_SPEC_MAX_TOKENS) return GDN_ERR_SHAPE;
+    if (gdn::spec_verify_smem_bytes(D, dims->num_k_heads, dims->num_v_heads, max_tokens) > 64 * 1024)
+        return GDN_ERR_DIMS;
+    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    const int64_t C = 2 * (int64_t)dims->num_k_heads * D + (int64_t)dims->num_v_heads * D;
+    if (num_reqs < 0 || num_tokens < 0 || num_slots < 0 || num_reqs > num_slots)
+        return GDN_ERR_SHAPE;
+    if (num_tokens > 0 && num_reqs == 0) return GDN_ERR_SHAPE;
+    if ((int64_t)num_tokens > (int64_t)num_reqs * max_tokens) return GDN_ERR_SHAPE;
+    if (x_ld < C || z_ld < (int64_t)dims->num_v_heads * D || gate_ld < dims->num_v_heads)
+        return GDN_ERR_SHAPE;
+    if (!(l2_eps >= 0.0f) || !(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if (num_tokens == 0 || num_reqs == 0) return GDN_OK;
+    if (!x_qkv || !z || !a || !b || !conv_w || !gamma || !conv_pool || !state_pool ||
+        !query_start_loc || !slot_ids || !spec_slot_ids || !y)
+        return GDN_ERR_NULL;
+    const size_t e = dt_size(act_dt);
+    if (!aligned(x_qkv, e) || !aligned(z, e) || !aligned(a, e) || !aligned(b, e) ||
+        !aligned(conv_pool, e) || !aligned(conv_w, dt_size(w_dt)) || !aligned(gamma, dt_size(w_dt)) ||
+        !aligned(state_pool, 16) || !aligned(query_start_loc, 4) || !aligned(slot_ids, 4) ||
+        !aligned(spec_slot_ids, 4) || !aligned(y, dt_size(y_dt)) || (o && !aligned(o, 4)))
+        return GDN_ERR_ALIGN;
+    gdn::SpecVerifyArgs sa{D, x_qkv, x_ld, z, z_ld, a, b, gate_ld, act_dt == GDN_BF16, conv_w,
+                           gamma, w_dt == GDN_BF16, conv_pool, state_pool, query_start_loc,
+                           slot_ids, spec_slot_ids, max_tokens, has_initial, num_reqs,
+                           dims->num_k_heads, dims->num_v_heads, l2_eps, norm_eps, y,
+                           y_dt == GDN_BF16, o};
+    return hip_status(gdn::launch_spec_verify(sa, static_cast<hipStream_t>(stream)));
+}
+
 size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_tokens, int32_t num_reqs) {
     if (check_dims(dims) != GDN_OK || num_tokens < 0 || num_reqs < 0) return 0;
     return gdn::prefill_workspace_bytes(dims->head_dim_k, dims->num_k_heads, dims->num_v_heads,
@@ -354,6 +396,33 @@ gdn_status gdn_validate_metadata(const int32_t *qsl, const int32_t *slots, int32
         for (int32_t r = 0; r < num_reqs; ++r)
             for (int32_t u = r + 1; u < num_reqs; ++u)
                 if (slots[r] == slots[u]) return GDN_ERR_METADATA;
+    }
+    return GDN_OK;
+}
+
+gdn_status gdn_validate_spec_metadata(const int32_t *qsl, const int32_t *slots,
+                                      const int32_t *spec, int32_t max_tokens,
+                                      int32_t num_reqs, int32_t num_tokens, int32_t num_slots) {
+    if (max_tokens < 1 || max_tokens > GDN_SPEC_MAX_TOKENS) return GDN_ERR_SHAPE;
+    gdn_status st = gdn_validate_metadata(qsl, slots, num_reqs, num_tokens, num_slots);
+    if (st != GDN_OK) return st;
+    if (num_reqs > 0 && !spec) return GDN_ERR_NULL;
+    // every slot a call writes (spec[r][j] for j < length of r) and every input
+    // slot: distinct, except that spec[r][0] may name slot_ids[r] itself
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        const int32_t len = qsl[r + 1] - qsl[r];
+        if (len > max_tokens) return GDN_ERR_METADATA;
+        for (int32_t j = 0; j < len; ++j) {
+            const int32_t s = spec[(int64_t)r * max_tokens + j];
+            if (s < 0 || s >= num_slots) return GDN_ERR_METADATA;
+            for (int32_t r2 = 0; r2 < num_reqs; ++r2) {
+                if (slots[r2] == s && !(r2 == r && j == 0)) return GDN_ERR_METADATA;
+                const int32_t len2 = qsl[r2 + 1] - qsl[r2];
+                for (int32_t j2 = 0; j2 < len2; ++j2)
+                    if ((r2 != r || j2 != j) && spec[(int64_t)r2 * max_tokens + j2] == s)
+                        return GDN_ERR_METADATA;
+            }
+        }
     }
     return GDN_OK;
 }

@@ -44,6 +44,21 @@ struct DecodeFusedArgs {
 hipError_t launch_decode_fused(const DecodeFusedArgs &a, hipStream_t s);
 size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv);
 
+struct SpecVerifyArgs {
+    int D;
+    const void *x; int64_t x_ld;
+    const void *z; int64_t z_ld;
+    const void *a, *b; int64_t gate_ld; bool act_bf16;
+    const void *w, *gamma; bool w_bf16;
+    void *pool; float *state;
+    const int32_t *qsl, *slots, *spec; int32_t max_tokens; const uint8_t *has_init;
+    int32_t R, Hk, Hv;
+    float l2_eps, norm_eps;
+    void *y; bool y_bf16; float *o;
+};
+hipError_t launch_spec_verify(const SpecVerifyArgs &a, hipStream_t s);
+size_t spec_verify_smem_bytes(int D, int32_t Hk, int32_t Hv, int32_t max_tokens);
+
 struct GatedNormArgs {
     int D;
     const void *o; bool o_bf16;

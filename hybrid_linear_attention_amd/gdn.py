@@ -50,6 +50,9 @@ _SIGS = {
     "gdn_decode_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
                           _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _f32, _f32, _vp, _i32, _vp,
                           _vp], _i32),
+    "gdn_spec_verify": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
+                         _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                         _f32, _vp, _i32, _vp, _vp], _i32),
     "gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_fused_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
@@ -63,7 +66,10 @@ _SIGS = {
     "gdn_rmsnorm": ([_vp, _i32, _vp, _i32, _f32, _i32, _i32, _vp, _i32, _vp], _i32),
     "gdn_gemm_bf16": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _i32, _vp], _i32),
     "gdn_validate_metadata": ([_vp, _vp, _i32, _i32, _i32], _i32),
+    "gdn_validate_spec_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32], _i32),
 }
+
+SPEC_MAX_TOKENS = 8
 
 _lib = None
 
@@ -193,6 +199,36 @@ def gdn_decode_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, slo
     _check(st, "gdn_decode_fused")
 
 
+def gdn_spec_verify(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, query_start_loc,
+                    slot_ids, spec_slot_ids, y, has_initial=None, o=None, l2_eps=1e-6,
+                    norm_eps=1e-6, stream=None):
+    """Speculative multi-token verify in one launch.  x [T, >=Cqkv], z [T, >=Hv*dv],
+    a, b [T, >=Hv] share one dtype and give their row strides; spec_slot_ids
+    int32 [R, max_tokens]; y [T, Hv*dv]; o optional fp32 [T, Hv, dv]."""
+    d = dims_c(dims)
+    if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
+        raise ValueError("x, z, a, b and conv_pool share one dtype; a and b share strides")
+    if conv_w.dtype != gamma.dtype:
+        raise ValueError("conv_w and gamma share one dtype")
+    for name, t in (("conv_w", conv_w), ("gamma", gamma), ("conv_pool", conv_pool),
+                    ("state_pool", state_pool), ("y", y), ("spec_slot_ids", spec_slot_ids)):
+        _contig(t, name)
+    if state_pool.dtype != torch.float32 or (o is not None and o.dtype != torch.float32):
+        raise TypeError("state_pool and o must be float32")
+    if spec_slot_ids.dim() != 2 or spec_slot_ids.shape[0] != slot_ids.numel():
+        raise ValueError("spec_slot_ids must be [num_reqs, max_tokens]")
+    zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
+    st = lib().gdn_spec_verify(
+        ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
+        _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
+        _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
+        _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"),
+        _ptr(spec_slot_ids, "spec_slot_ids"), spec_slot_ids.shape[1],
+        _ptr(has_initial, "has_initial"), slot_ids.numel(), x.shape[0], state_pool.shape[0],
+        float(l2_eps), float(norm_eps), _ptr(y, "y"), _dt(y), _ptr(o, "o"), _stream(stream))
+    _check(st, "gdn_spec_verify")
+
+
 def gdn_prefill_workspace_bytes(dims, num_tokens, num_reqs):
     d = dims_c(dims)
     return int(lib().gdn_prefill_workspace_bytes(ctypes.byref(d), int(num_tokens), int(num_reqs)))
@@ -302,3 +338,13 @@ def gdn_validate_metadata(query_start_loc, slot_ids, num_tokens, num_slots):
     sl = slot_ids.cpu().to(torch.int32).contiguous()
     return int(lib().gdn_validate_metadata(qsl.data_ptr(), sl.data_ptr() if sl.numel() else None,
                                            sl.numel(), int(num_tokens), int(num_slots)))
+
+
+def gdn_validate_spec_metadata(query_start_loc, slot_ids, spec_slot_ids, num_tokens, num_slots):
+    """Host-side check of host (CPU) int32 copies of the spec-verify metadata."""
+    qsl = query_start_loc.cpu().to(torch.int32).contiguous()
+    sl = slot_ids.cpu().to(torch.int32).contiguous()
+    sp = spec_slot_ids.cpu().to(torch.int32).contiguous()
+    return int(lib().gdn_validate_spec_metadata(
+        qsl.data_ptr(), sl.data_ptr() if sl.numel() else None, sp.data_ptr() if sp.numel() else None,
+        sp.shape[1] if sp.dim() == 2 else 0, sl.numel(), int(num_tokens), int(num_slots)))

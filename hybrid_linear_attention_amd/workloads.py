@@ -206,6 +206,19 @@ def prefill_varlen16(seed: int = 1237) -> GdnCase:
                          hist_std=1.0)
 
 
+def spec_verify_r64(seed: int = 1239, tokens: int = 4) -> GdnCase:
+    """Speculative verify at full shapes: 64 requests of `tokens` tokens each (the
+    last accepted token and tokens - 1 drafts), state ~ N(0, 0.02) and history
+    ~ N(0, 1) in slots 0..63 (request r in slot r); slots 64 + tokens r + j
+    receive the state and history after token j of request r
+    (meta["spec_slots"], int32 [64, tokens])."""
+    R = 64
+    case = make_gdn_case(seed, FULL_DIMS, [tokens] * R, num_slots=R * (tokens + 1),
+                         state_std=0.02, hist_std=1.0)
+    case.meta["spec_slots"] = (R + torch.arange(R * tokens, dtype=torch.int32)).reshape(R, tokens)
+    return case
+
+
 @dataclass
 class LayerCase:
     core: GdnCase                 # GDN-core tensors (x_qkv/z/a/b unused: made by the projection)
@@ -270,4 +283,5 @@ WORKLOADS = {
     "prefill_4096": prefill_4096,
     "prefill_varlen16": prefill_varlen16,
     "layer_mixed": layer_mixed,
+    "spec_verify_r64": spec_verify_r64,
 }

@@ -175,6 +175,55 @@ gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_l
                             void *stream);
 
 /*
+ * gdn_spec_verify — speculative multi-token verify: a few tokens per request
+ * (the last accepted token followed by draft tokens) through the conv update,
+ * the recurrence and the gated norm in one launch, keeping the state and the
+ * conv history reached after EVERY token in a slot of its own, so that
+ * rejecting drafts rolls a request back by choosing the slot of its last
+ * accepted token.  The pages count extra speculative slots for the conv
+ * history (tutorial page, section 01 data-structure table, conv-history row)
+ * and pass the number of speculative tokens into the state-shape calculator
+ * (dispatch page, step 5); per-position slots are this library's reading.
+ * The outputs equal gdn_prefill_fused over the same tokens; the state and
+ * history in spec_slot_ids[r][j] equal those a prefill of the request's
+ * first j + 1 tokens would leave.
+ *
+ *   x_qkv, z, a, b, conv_w, gamma, l2_eps, norm_eps, y, y_dt, o: as
+ *              gdn_decode_fused, with one row per token of the packed batch.
+ *   query_start_loc [num_reqs + 1] int32 (device): request r owns tokens
+ *              qsl[r] .. qsl[r+1]-1, at most max_tokens of them (a longer
+ *              request is cut to its first max_tokens tokens).
+ *   slot_ids   [num_reqs] int32 (device): the slot the request starts from
+ *              (state and history), read and not written, unless
+ *              spec_slot_ids[r][0] names it.
+ *   spec_slot_ids [num_reqs, max_tokens] int32 (device): after token j of
+ *              request r, its state goes to state_pool[spec_slot_ids[r][j]] and
+ *              its last taps-1 conv inputs to conv_pool[spec_slot_ids[r][j]].
+ *              Entries past a request's length are not read.  Every written
+ *              slot must be distinct from every other written slot and from
+ *              every other request's input slot (gdn_validate_spec_metadata).
+ *   max_tokens 1 .. GDN_SPEC_MAX_TOKENS.
+ *   has_initial [num_reqs] uint8 (device; NULL = all 1): 0 starts the request
+ *              from a zero history and a zero state.
+ * Needs max_tokens (2 d + 2 (Hv/Hk) d + 2 Hv/Hk + 1) * 4 + 256 bytes <= 64 KiB
+ * of LDS per (request, key head) block, else GDN_ERR_DIMS.  Alignment as
+ * gdn_decode_fused.  HBM traffic per request: the state read once, written
+ * once per token.
+ */
+#define GDN_SPEC_MAX_TOKENS 8
+gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld,
+                           const void *z, int64_t z_ld, const void *a,
+                           const void *b, int64_t gate_ld, gdn_dtype act_dt,
+                           const void *conv_w, const void *gamma, gdn_dtype w_dt,
+                           void *conv_pool, float *state_pool,
+                           const int32_t *query_start_loc, const int32_t *slot_ids,
+                           const int32_t *spec_slot_ids, int32_t max_tokens,
+                           const uint8_t *has_initial, int32_t num_reqs,
+                           int32_t num_tokens, int32_t num_slots, float l2_eps,
+                           float norm_eps, void *y, gdn_dtype y_dt, float *o,
+                           void *stream);
+
+/*
  * gdn_prefill_workspace_bytes — device workspace gdn_prefill_varlen needs for
  * a batch of at most num_tokens tokens in at most num_reqs requests.
  * Returns 0 for unsupported dims.
@@ -292,6 +341,20 @@ gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb,
 gdn_status gdn_validate_metadata(const int32_t *query_start_loc_host,
                                  const int32_t *slot_ids_host, int32_t num_reqs,
                                  int32_t num_tokens, int32_t num_slots);
+
+/*
+ * gdn_validate_spec_metadata — HOST-side check of host copies of the metadata
+ * of gdn_spec_verify: everything gdn_validate_metadata checks, every request at
+ * most max_tokens long, and the slots a call writes (spec_slot_ids[r][j] for j
+ * below the request's length) in range, distinct, and distinct from the other
+ * requests' input slots (spec_slot_ids[r][0] == slot_ids[r] is allowed).
+ * Enqueues nothing; GDN_ERR_METADATA on violation.
+ */
+gdn_status gdn_validate_spec_metadata(const int32_t *query_start_loc_host,
+                                      const int32_t *slot_ids_host,
+                                      const int32_t *spec_slot_ids_host,
+                                      int32_t max_tokens, int32_t num_reqs,
+                                      int32_t num_tokens, int32_t num_slots);
 
 #ifdef __cplusplus
 }

@@ -217,3 +217,51 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         gdn.gdn_rmsnorm(torch.zeros(4, 8), torch.ones(8), x.new_zeros(4, 8))
+
+
+def spec_call(d, **kw):
+    args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
+                g=FAKE, wdt=1, pool=FAKE, state=FAKE, qsl=FAKE, slots=FAKE, spec=FAKE, maxn=4,
+                hi=None, R=4, T=16, nslots=32, l2=1e-6, ne=1e-6, y=FAKE, ydt=1, o=None)
+    args.update(kw)
+    return gdn.lib().gdn_spec_verify(
+        None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
+        args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
+        args["pool"], args["state"], args["qsl"], args["slots"], args["spec"], args["maxn"],
+        args["hi"], args["R"], args["T"], args["nslots"], args["l2"], args["ne"], args["y"],
+        args["ydt"], args["o"], None)
+
+
+def test_spec_verify_rejects_bad_args():
+    assert spec_call(None) == 1
+    assert spec_call(dims(16, 48, 128, 128, 3)) == 2
+    assert spec_call(FULL, maxn=0) == 4
+    assert spec_call(FULL, maxn=9) == 4
+    assert spec_call(FULL, T=17) == 4             # more tokens than R x max_tokens
+    assert spec_call(FULL, R=33) == 4             # more requests than slots
+    assert spec_call(FULL, xld=10239) == 4
+    assert spec_call(FULL, gld=47) == 4
+    assert spec_call(FULL, l2=-1.0) == 4
+    assert spec_call(FULL, act=5) == 3
+    assert spec_call(FULL, spec=None) == 1
+    assert spec_call(FULL, y=None) == 1
+    assert spec_call(FULL, state=FAKE + 4) == 6
+    assert spec_call(FULL, spec=FAKE + 2) == 6
+    assert spec_call(FULL, maxn=8, x=None) == 1   # 8 tokens of LDS still fit at full shapes
+
+
+def test_validate_spec_metadata_host():
+    def v(qsl, slots, spec, T, nslots):
+        return gdn.gdn_validate_spec_metadata(torch.tensor(qsl), torch.tensor(slots),
+                                              torch.tensor(spec), T, nslots)
+    qsl, slots = [0, 3, 4, 6], [0, 1, 2]
+    spec = [[10, 11, 12], [0 + 13, -1, -1], [14, 15, -1]]  # entries past a request's length unread
+    assert v(qsl, slots, spec, 6, 16) == 0
+    spec_in_place = [[0, 11, 12], [1, -1, -1], [2, 15, -1]]
+    assert v(qsl, slots, spec_in_place, 6, 16) == 0
+    assert v(qsl, slots, [[10, 11, 12], [11, -1, -1], [14, 15, -1]], 6, 16) == 8  # repeated
+    assert v(qsl, slots, [[10, 1, 12], [13, -1, -1], [14, 15, -1]], 6, 16) == 8   # other input slot
+    assert v(qsl, slots, [[10, 11, 1], [13, -1, -1], [14, 15, -1]], 6, 16) == 8
+    assert v(qsl, slots, [[10, 11, 16], [13, -1, -1], [14, 15, -1]], 6, 16) == 8  # out of range
+    assert v([0, 4, 4, 6], slots, [[10, 11, 12], [13, -1, -1], [14, 15, -1]], 6, 16) == 8  # too long
+    assert v(qsl, [0, 1, 1], spec, 6, 16) == 8                                    # input slots repeat
