@@ -145,11 +145,44 @@ template <> struct Raw1<bf16> {
 };
 
 // One 16-byte direct-to-LDS copy per lane: lane l's bytes land at dst + 16 l.
+// Issued as inline assembly (LDS base in M0) rather than through the builtin:
+// the compiler cannot tell the two ring stages apart, so after a builtin copy
+// into the next stage it waits for every outstanding load before any LDS read
+// of the current stage, which stalls each chunk mid-way on the next chunk's
+// copies.  Here the copies are invisible to its wait analysis and the chain
+// waits for them itself, once per chunk, before the barrier that publishes
+// the stage (vector-memory counts complete in order, so the compiler's own
+// waits for other loads stay correct, only more conservative).
 __device__ __forceinline__ void copy_frag(const uint8_t *src_frag, uint8_t *dst_frag, int lane) {
-    __builtin_amdgcn_global_load_lds(
-        static_cast<const void *>(src_frag + 16 * lane),
-        (__attribute__((address_space(3))) void *)(dst_frag), 16, 0, 0);
+    const auto lds = (__attribute__((address_space(3))) uint8_t *)(dst_frag);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src_frag + 16 * lane), "{m0}"(m0) : "memory");
 }
+
+// A buffer resource over [base, base + bytes) from wave-uniform values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0,
+                                             (int)n, 0x00020000);
+}
+
+// o of one token and state row through a range-checked buffer store: tokens
+// past the chunk's last fall outside the resource and are dropped, so every
+// chunk issues the same number of stores and the chunk-top wait can leave
+// them in flight.
+template <typename TO> __device__ __forceinline__ void store_o(__amdgpu_buffer_rsrc_t r, uint32_t off, float v);
+template <> __device__ __forceinline__ void store_o<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)(off * 4), 0, 0);
+}
+template <> __device__ __forceinline__ void store_o<bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)to_bf16(v).bits, r, (int)(off * 2), 0, 0);
+}
+
+// s_waitcnt immediate: vector-memory count <= vm, LDS/scalar and export counts 0
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14); }
 
 }  // namespace chunk
 
@@ -718,6 +751,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
 #pragma unroll
     for (int part = 0; part < NPART; ++part) issue_images<NW>(smem, kim0, tim0, w, lane, part);
     load_v(0);
+    // everything above (state rows, chunk 0's copies and v) lands before the
+    // loop, so that no wait for the state rows' loads is left inside it
+    __builtin_amdgcn_s_waitcnt(0);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
@@ -725,9 +761,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         uint8_t *nstg = smem + (size_t)((cc + 1) & 1) * STAGE;
         const bool prefetch = STAGES == 2 && cc + 1 < nch;
         const uint8_t *nkim = kim0 + (cc + 1) * kstep, *ntim = tim0 + (cc + 1) * tstep;
-        // this wave's copies and loads of chunk cc have landed; after the barrier
-        // every wave's have, and (two stages) every wave is done with chunk cc - 1
-        __builtin_amdgcn_s_waitcnt(0);
+        // this wave's copies and loads of chunk cc have landed (issued before the
+        // previous chunk's 8 o stores, which may stay in flight); after the
+        // barrier every wave's have, and (two stages) every wave is done with
+        // chunk cc - 1
+        if (STAGES == 2 && cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+        else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float vcur[2][4];
 #pragma unroll
@@ -824,13 +863,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
             ST[jt] *= gC;
             mma3(ST[jt], frag(kst + (FKT + jt) * FRAG), frag(kst + (FKT + 8 + jt) * FRAG), tbh, tbl);
         }
+        {
+            const __amdgpu_buffer_rsrc_t orr = wave_rsrc(o + ((int64_t)tb * Hv + h) * D,
+                                                         (uint32_t)((Lc - 1) * Hv + 1) * D * sizeof(TO));
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
+            for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tau + 4 * lg + e;
-                if (t < Lc) st(o + ((int64_t)(tb + t) * Hv + h) * D + irow, OQ[tau][e] * inv_sqrt_d);
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tau + 4 * lg + e;
+                    store_o<TO>(orr, (uint32_t)(t * Hv * D + irow), OQ[tau][e] * inv_sqrt_d);
+                }
+        }
         if (STAGES == 1) {
             __syncthreads();  // every wave is done reading the stage
             if (cc + 1 < nch) {
@@ -948,13 +991,18 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
 #pragma unroll
     for (int part = 0; part < NPART; ++part) issue(smem, 0, part);
     load_v(0);
+    // everything above (state rows, chunk 0's copies and v) lands before the
+    // loop, so that no wait for the state rows' loads is left inside it
+    __builtin_amdgcn_s_waitcnt(0);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
         const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * GSTAGE : 0);
         uint8_t *nstg = smem + (size_t)((cc + 1) & 1) * GSTAGE;
         const bool prefetch = STAGES == 2 && cc + 1 < nch;
-        __builtin_amdgcn_s_waitcnt(0);
+        // as in the per-head chain: the previous chunk's o stores stay in flight
+        if (STAGES == 2 && cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * GRP_RPW));
+        else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float vcur[GRP_RPW][2][4];
 #pragma unroll
@@ -1068,15 +1116,19 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
                 mma3(ST[rt][jt], kth, ktl, tbh[rt], tbl[rt]);
             }
         }
+        {
+            const __amdgpu_buffer_rsrc_t orr = wave_rsrc(o + ((int64_t)tb * Hv + h) * D,
+                                                         (uint32_t)((Lc - 1) * Hv + 1) * D * sizeof(TO));
 #pragma unroll
-        for (int rt = 0; rt < GRP_RPW; ++rt)
+            for (int rt = 0; rt < GRP_RPW; ++rt)
 #pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
+                for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tau + 4 * lg + e;
-                    if (t < Lc) st(o + ((int64_t)(tb + t) * Hv + h) * D + irow[rt], OQ[rt][tau][e] * inv_sqrt_d);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * tau + 4 * lg + e;
+                        store_o<TO>(orr, (uint32_t)(t * Hv * D + irow[rt]), OQ[rt][tau][e] * inv_sqrt_d);
+                    }
+        }
         if (STAGES == 1) {
             __syncthreads();
             if (cc + 1 < nch) {
