@@ -234,8 +234,10 @@ struct FusedPrefillWs {
         const size_t D = d->head_dim_k;
         q = align256((size_t)T * d->num_k_heads * D * 4);
         k = q;
-        v = align256((size_t)T * d->num_v_heads * D * 4);
-        o = v;
+        // v [T, Hv, D] fp32, or (d = 128 conv mode) the prefill's V images: one
+        // 32-token block per chunk and value head, at most T / 32 + nreq chunks
+        v = align256(((size_t)T / 32 + (size_t)nreq) * 32 * d->num_v_heads * D * 4);
+        o = align256((size_t)T * d->num_v_heads * D * 4);
         pre = align256(gdn::prefill_workspace_bytes(d->head_dim_k, d->num_k_heads, d->num_v_heads, T, nreq));
         total = q + k + v + o + pre;
     }
@@ -295,13 +297,10 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
                         query_start_loc, slot_ids, has_initial, num_reqs, num_tokens,
                         dims->num_k_heads, dims->num_v_heads, o, false, pre, wl.pre};
     // d = 128 with 16-byte rows: the prefill's prep kernel forms q and k from x
-    // itself, and the conv pass writes only v and the new history
+    // itself and its chain forms v, so no conv pass runs
     const bool prep_conv = D == 128 && x_ld % (int64_t)(16 / e) == 0 && aligned(x_qkv, 16) &&
                            aligned(conv_w, 16);
-    gdn::ConvArgs cv = ca;
     if (prep_conv) {
-        cv.q = nullptr;
-        cv.k = nullptr;
         pa.x = x_qkv;
         pa.x_ld = x_ld;
         pa.x_bf16 = act_dt == GDN_BF16;
@@ -309,7 +308,6 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
         pa.w_bf16 = w_dt == GDN_BF16;
         pa.pool = conv_pool;
         pa.l2_eps = l2_eps;
-        pa.conv_v = &cv;
     } else {
         if (gdn::launch_conv1d(ca, s) != hipSuccess) return GDN_ERR_HIP;
     }

@@ -93,12 +93,12 @@ struct PrefillArgs {
     const void *z = nullptr; int64_t z_ld = 0; bool z_bf16 = false;
     const void *gamma = nullptr; bool gamma_bf16 = false; float norm_eps = 0.f;
     void *y = nullptr; bool y_bf16 = false;
-    // optional conv inputs (d = 128): the prep kernel forms q and k from x itself
-    // (q and k unused), then `conv_v` (v and the new history) runs before the chain
+    // optional conv inputs (d = 128): the prep kernel forms q and k from x, the
+    // chain forms v from x and writes the new history of every channel (q, k and
+    // v unused; o must be fp32)
     const void *x = nullptr; int64_t x_ld = 0; bool x_bf16 = false;
     const void *conv_w = nullptr; bool w_bf16 = false;
-    const void *pool = nullptr; float l2_eps = 0.f;
-    const struct ConvArgs *conv_v = nullptr;
+    void *pool = nullptr; float l2_eps = 0.f;
 };
 size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

@@ -47,6 +47,8 @@
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
+#include <type_traits>
+
 namespace gdn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const TA *__restrict__ q, const TA *__restrict__ k, const TG *__restrict__ ga,
     const TG *__restrict__ gb, int64_t gate_ld, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ chunk_off, int32_t nreq, int32_t Hk, int32_t Hv,
-    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg, PrepConvIn cv) {
+    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg, PrepConvIn cv, float *__restrict__ vimg) {
     using namespace chunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
@@ -314,13 +316,18 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
             split4_store(qv.x, qv.y, qv.z, qv.w, &sm.Qh[t][c4], &sm.Ql[t][c4]);
         }
     } else {
-        // The conv input of the chunk's q / k channels is staged in LDS with
-        // coalesced 16-byte loads, NCH channels per pass (bf16: q and k in one
-        // pass; fp32: q, then k): staged row rr holds token tb - 3 + rr.  Rows
-        // before the request start come from its history (zeros without one);
-        // rows past the chunk's last token are zeros.
+        // The conv inputs of the chunk are staged in LDS with coalesced 16-byte
+        // loads, NCH channels per pass: first the key head's q and k channels
+        // (bf16: one pass; fp32: q, then k), then (V images requested) the v
+        // channels of its value heads.  Staged row rr holds token tb - 3 + rr;
+        // rows before the request start come from its history (zeros without
+        // one); rows past the chunk's last token are zeros.  The next pass's
+        // rows are loaded while the current pass computes: every lane issues
+        // the same loads (out-of-range pieces read a valid address and are
+        // zeroed when staged), so the compiler's waits for the pass's taps
+        // leave them in flight.
         constexpr int NCH = 512 / (int)sizeof(TX);  // channels per pass (512 bytes a row)
-        constexpr int NPASS = 2 * D / NCH;
+        constexpr int NPASS = 2 * D / NCH;          // q / k passes
         constexpr int EPP = 16 / (int)sizeof(TX);   // channels per 16-byte piece
         constexpr int NCG = NCH / 8;                // 8-channel groups per pass
         constexpr int TPT = CH * NCG / 256;         // tokens per thread
@@ -329,31 +336,41 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         const int t0 = qsl[r];
         const TX *x = static_cast<const TX *>(cv.x);
         TX(*xs)[XSP * 2 / (int)sizeof(TX)] = reinterpret_cast<TX(*)[XSP * 2 / (int)sizeof(TX)]>(&sm.xs[0][0]);
-        // q / k channel of combined column cq (q: 0 .. D-1, k: D .. 2D-1)
-        auto chan = [&](int cq) { return (cq >= D ? Hk * D : 0) + kh * D + (cq & (D - 1)); };
-        // compute mapping: 8 channels (group cgi) of tokens TPT tg .. TPT tg + TPT - 1;
-        // the 16 groups of one token's q (or k) are 16 aligned adjacent lanes
-        const int tg = tid / NCG, cgi = tid % NCG;
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-            if (ps) __syncthreads();  // the previous pass is done with the staged rows
-            uint4 pv[NM];
+        const int nvc = group * D;                  // v channels of the key head
+        const int vbase = 2 * Hk * D + kh * nvc;
+        const int nvpass = vimg != nullptr ? (nvc + NCH - 1) / NCH : 0;
+        const int npass_all = NPASS + nvpass;
+        // channel of column cq of pass ps (q: 0 .. D-1, k: D .. 2D-1 over the q / k
+        // passes; then the v channels), or -1 past the last v channel
+        auto pass_chan = [&](int ps, int cq) -> int {
+            if (ps < NPASS) {
+                const int c2 = ps * NCH + cq;
+                return (c2 >= D ? Hk * D : 0) + kh * D + (c2 & (D - 1));
+            }
+            const int vc = (ps - NPASS) * NCH + cq;
+            return vc < nvc ? vbase + vc : -1;
+        };
+        auto load_pass = [&](uint4 (&pv)[NM], int ps) {
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const int pi = tid + 256 * m;
                 const int rr = pi >> 5, seg = pi & 31;
                 const int tok = tb - 3 + rr;
-                pv[m] = make_uint4(0u, 0u, 0u, 0u);
-                if (pi < NPIECE && tok >= t0 && rr - 3 < Lc)
-                    pv[m] = *reinterpret_cast<const uint4 *>(x + (int64_t)tok * cv.x_ld +
-                                                             chan(ps * NCH + EPP * seg));
+                const int ch = pass_chan(ps, EPP * seg);
+                const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc && ch >= 0;
+                pv[m] = *reinterpret_cast<const uint4 *>(x + (ok ? (int64_t)tok * cv.x_ld + ch : (int64_t)0));
             }
+        };
+        auto stage_pass = [&](const uint4 (&pv)[NM], int ps) {
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const int pi = tid + 256 * m;
                 const int rr = pi >> 5, seg = pi & 31;
-                if (pi < NPIECE && tb - 3 + rr >= t0)
-                    *reinterpret_cast<uint4 *>(&xs[rr][EPP * seg]) = pv[m];
+                const int tok = tb - 3 + rr;
+                const int ch = pass_chan(ps, EPP * seg);
+                const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc && ch >= 0;
+                if (pi < NPIECE && tok >= t0)
+                    *reinterpret_cast<uint4 *>(&xs[rr][EPP * seg]) = ok ? pv[m] : make_uint4(0u, 0u, 0u, 0u);
             }
             if (tb == t0) {  // first chunk of its request (uniform over the block)
                 const bool hi = cv.has_init == nullptr || cv.has_init[r] != 0;
@@ -363,27 +380,41 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 for (int j = 0; j < (3 * NCH + 255) / 256; ++j) {  // history entry rr = row rr
                     const int idx = tid + 256 * j;
                     const int rr = idx / NCH, cc = idx % NCH;
-                    if (rr < 3) {
-                        if (hi) xs[rr][cc] = pool[(hbase + chan(ps * NCH + cc)) * 3 + rr];
-                        else xs[rr][cc] = TX{};
-                    }
+                    const int ch = pass_chan(ps, cc);
+                    if (rr < 3 && ch >= 0) xs[rr][cc] = hi ? pool[(hbase + ch) * 3 + rr] : TX{};
                 }
             }
+        };
+        // compute mapping: 8 channels (group cgi) of tokens TPT tg .. TPT tg + TPT - 1;
+        // the 16 groups of one token's q (or k) are 16 aligned adjacent lanes
+        const int tg = tid / NCG, cgi = tid % NCG;
+        uint4 pv[NM];
+        load_pass(pv, 0);
+        for (int ps = 0; ps < npass_all; ++ps) {
+            if (ps) __syncthreads();  // the previous pass is done with the staged rows
+            stage_pass(pv, ps);
             __syncthreads();
-            const int cq = ps * NCH + 8 * cgi;
-            const bool isk = cq >= D;
-            const int col = cq & (D - 1);
-            const TW *wp = static_cast<const TW *>(cv.w) + (int64_t)chan(cq) * 4;
-            float wf[32];  // w[channel + e][i] at 4 e + i
+            const int ch0 = pass_chan(ps, 8 * cgi);
+            float wf[32];  // w[channel + e][i] at 4 e + i (unconditional loads, see above)
+            {
+                const TW *wp = static_cast<const TW *>(cv.w) + (int64_t)max(ch0, 0) * 4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Raw8<TW> wr;
-                wr.load(wp + 8 * j);
-                float f8[8];
-                wr.get(f8);
+                for (int j = 0; j < 4; ++j) {
+                    Raw8<TW> wr;
+                    wr.load(wp + 8 * j);
+                    float f8[8];
+                    wr.get(f8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) wf[8 * j + e] = f8[e];
+                    for (int e = 0; e < 8; ++e) wf[8 * j + e] = f8[e];
+                }
             }
+            // unconditional (the last pass reloads its own rows, L2-resident) and
+            // kept after the taps' loads, so that the wait for the taps never
+            // covers these loads
+            __builtin_amdgcn_sched_barrier(0);
+            load_pass(pv, min(ps + 1, npass_all - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            if (ch0 < 0) continue;  // past the last v channel (no barrier below)
             float y[TPT][8];
 #pragma unroll
             for (int j = 0; j < TPT; ++j)
@@ -405,21 +436,49 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                     }
                 }
             }
+            if (ps < NPASS) {
+                // q or k: SiLU, L2 norm over the head, hi / lo planes
+                const int cq = ps * NCH + 8 * cgi;
+                const bool isk = cq >= D;
+                const int col = cq & (D - 1);
 #pragma unroll
-            for (int j = 0; j < TPT; ++j) {
-                const int t = TPT * tg + j;
-                float ss = 0.f;
+                for (int j = 0; j < TPT; ++j) {
+                    const int t = TPT * tg + j;
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        y[j][e] = t < Lc ? silu_fast(y[j][e]) : 0.f;
+                        ss += y[j][e] * y[j][e];
+                    }
+                    ss = group_sum<16>(ss);
+                    const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
+                    uint16_t *ph = isk ? &sm.Kh[t][col] : &sm.Qh[t][col];
+                    uint16_t *pl = isk ? &sm.Kl[t][col] : &sm.Ql[t][col];
+                    split4_store(y[j][0] * inv, y[j][1] * inv, y[j][2] * inv, y[j][3] * inv, ph, pl);
+                    split4_store(y[j][4] * inv, y[j][5] * inv, y[j][6] * inv, y[j][7] * inv, ph + 4, pl + 4);
+                }
+            } else {
+                // v: SiLU, straight into the V image the chain reads: per (chunk,
+                // value head) 32 tokens x 128 rows fp32, ordered so that chain lane
+                // (lr, lg) of row tile rt finds tokens 16 tau + 4 lg + 0..3 of row
+                // 16 rt + lr as one 16-byte piece: float (((rt 2 + tau) 4 + lg) 16 + lr) 4 + e
+                const int vc = (ps - NPASS) * NCH + 8 * cgi;
+                const int hh = vc / D, row0 = vc % D;
+                float *vh = vimg + ((size_t)c * Hv + kh * group + hh) * (CH * D);
+                const int t0g = TPT * tg;  // first token; TPT (2 or 4) divides 4
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    y[j][e] = t < Lc ? silu_fast(y[j][e]) : 0.f;
-                    ss += y[j][e] * y[j][e];
+                    const int row = row0 + e;
+                    float vals[TPT];
+#pragma unroll
+                    for (int j = 0; j < TPT; ++j) vals[j] = t0g + j < Lc ? silu_f(y[j][e]) : 0.f;
+                    float *dst = vh + ((((row >> 4) * 2 + (t0g >> 4)) * 4 + ((t0g >> 2) & 3)) * 16 + (row & 15)) * 4 +
+                                 (t0g & 3);
+                    if constexpr (TPT == 4)
+                        *reinterpret_cast<float4 *>(dst) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                    else
+                        *reinterpret_cast<float2 *>(dst) = make_float2(vals[0], vals[1]);
                 }
-                ss = group_sum<16>(ss);
-                const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
-                uint16_t *ph = isk ? &sm.Kh[t][col] : &sm.Qh[t][col];
-                uint16_t *pl = isk ? &sm.Kl[t][col] : &sm.Ql[t][col];
-                split4_store(y[j][0] * inv, y[j][1] * inv, y[j][2] * inv, y[j][3] * inv, ph, pl);
-                split4_store(y[j][4] * inv, y[j][5] * inv, y[j][6] * inv, y[j][7] * inv, ph + 4, pl + 4);
             }
         }
     }
@@ -662,6 +721,83 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 // image run on one XCD (workgroups are dealt to the 8 XCDs round-robin) and
 // the longest requests' groups are dispatched first.
 // ---------------------------------------------------------------------------
+// Conv inputs the chain needs in its fused mode, where the prep kernel has
+// formed v into V images: the chain writes the request's new conv history
+// once the old one has been read (q / k and v by the prep kernel).
+struct ChainConvIn {
+    const void *x; int64_t x_ld;
+    void *pool;
+    int32_t C;   // conv channels q | k | v
+    int32_t nq;  // Hk * D
+};
+
+// v for the tokens a lane holds in the accumulator layout, 16 tau + 4 lg + e
+// of a chunk: either four scalar loads per tau from v [T, Hv, D] (VIMG false),
+// or one 16-byte load per tau from the chunk's V image (VIMG true; the prep
+// kernel wrote zeros past the chunk's last token).  Loads stay raw until the
+// next chunk uses them.
+template <int RT, bool VIMG, typename TA>
+struct ChainVLoads {
+    chunk::Raw1<TA> r[RT][2][4];
+    float4 r4[RT][2];
+
+    __device__ __forceinline__ void load(const TA *v, const int (&irow)[RT], int h, int Hv, int tb,
+                                         int chunk_idx, int Lc, int lane) {
+        using namespace chunk;
+        const int lg = lane >> 4;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                if constexpr (!VIMG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * tau + 4 * lg + e;
+                        if (t < Lc) r[rt][tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow[rt]);
+                        else r[rt][tau][e].zero();
+                    }
+                } else {
+                    const float *img = reinterpret_cast<const float *>(v) + ((size_t)chunk_idx * Hv + h) * (CH * D);
+                    r4[rt][tau] = *reinterpret_cast<const float4 *>(img + (((irow[rt] >> 4) * 2 + tau) * 64 + lane) * 4);
+                }
+            }
+    }
+
+    __device__ __forceinline__ void get(float (&vc)[RT][2][4]) const {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                if constexpr (!VIMG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vc[rt][tau][e] = r[rt][tau][e].get();
+                } else {
+                    vc[rt][tau][0] = r4[rt][tau].x;
+                    vc[rt][tau][1] = r4[rt][tau].y;
+                    vc[rt][tau][2] = r4[rt][tau].z;
+                    vc[rt][tau][3] = r4[rt][tau].w;
+                }
+            }
+    }
+};
+
+// New conv history of channel c: the last 3 entries of the window [history,
+// the request's L rows] (raw copies; zeros stand in for a missing history).
+// One thread per channel reads all three before writing any.
+template <typename TX>
+__device__ __forceinline__ void chain_write_history(const ChainConvIn &cv, int c, int slot, bool hi, int tok0, int L) {
+    const TX *x = static_cast<const TX *>(cv.x);
+    TX *hp = static_cast<TX *>(cv.pool) + ((int64_t)slot * cv.C + c) * 3;
+    TX nv[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int wi = L + k;  // window index: 0..2 history, 3.. the request's rows
+        nv[k] = wi >= 3 ? x[(int64_t)(tok0 + wi - 3) * cv.x_ld + c] : (hi ? hp[wi] : TX{});
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) hp[k] = nv[k];
+}
+
 // This wave's copies of one chunk's images, slice `part` of NPART: the slices
 // are spread over the previous chunk's MFMA phases so that the wave does not
 // stall on a full memory queue in one burst.
@@ -682,13 +818,13 @@ __device__ __forceinline__ void issue_images(uint8_t *stage, const uint8_t *kim,
     }
 }
 
-template <int NW, int STAGES, typename TA, typename TO>
+template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
 __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const TA *__restrict__ v, float *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
-    int32_t Hv, TO *__restrict__ o) {
+    int32_t Hv, TO *__restrict__ o, ChainConvIn cv) {
     using namespace chunk;
     constexpr int IB = 16 * NW;  // state rows per block
     constexpr int NRB = D / IB;  // blocks per (request, head)
@@ -714,7 +850,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
     const int irow = IB * rb + 16 * w + lr;  // this lane's state row (value channel)
-    float *sbase = state + ((int64_t)slots[r] * Hv + h) * D * D;
+    const int irows[1] = {irow};
+    const int slot = slots[r];
+    float *sbase = state + ((int64_t)slot * Hv + h) * D * D;
 
     // state rows of this lane, transposed accumulator layout:
     // ST[jt][e] = S[irow][16 jt + 4 lg + e]
@@ -734,19 +872,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
 
     // v of this lane's row for tokens 16 tau + 4 lg + e of chunk cc
-    Raw1<TA> vr[2][4];
-    auto load_v = [&](int cc) {
-        const int tb = tok0 + cc * CH;
-        const int Lc = min(CH, L - cc * CH);
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tau + 4 * lg + e;
-                if (t < Lc) vr[tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow);
-                else vr[tau][e].zero();
-            }
-    };
+    ChainVLoads<1, VIMG, TA> vr;
+    auto load_v = [&](int cc) { vr.load(v, irows, h, Hv, tok0 + cc * CH, c_first + cc, min(CH, L - cc * CH), lane); };
 
 #pragma unroll
     for (int part = 0; part < NPART; ++part) issue_images<NW>(smem, kim0, tim0, w, lane, part);
@@ -768,11 +895,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         if (STAGES == 2 && cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        float vcur[2][4];
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vcur[tau][e] = vr[tau][e].get();
+        float vcur1[1][2][4];
+        vr.get(vcur1);
+        float(&vcur)[2][4] = vcur1[0];
         if (prefetch) issue_images<NW>(nstg, nkim, ntim, w, lane, 0);
         const uint8_t *kst = stg + 16 * lane;          // this lane's piece of each K fragment
         const uint8_t *tst = stg + KIMG + 16 * lane;   // and of each T fragment
@@ -888,6 +1013,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     for (int jt = 0; jt < 8; ++jt)
         *reinterpret_cast<float4 *>(sbase + (int64_t)irow * D + 16 * jt + 4 * lg) =
             make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]);
+    if constexpr (VIMG) {
+        // new history (the prep kernel has read the old one): this lane's v
+        // channel, and the key head's q / k channels from one block of the key
+        // head's first value head
+        if (lg == 0) chain_write_history<TX>(cv, 2 * cv.nq + h * D + irow, slot, hi_init, tok0, L);
+        if (h % group == 0 && rb == 0)
+            for (int j = threadIdx.x; j < 2 * D; j += 64 * NW)
+                chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -901,13 +1035,13 @@ constexpr int GRP_ROWS = 64;          // state rows per head per block
 constexpr int GRP_RPW = 2;            // 16-row tiles per wave
 constexpr int GRP_MAX_HEADS = 3;      // value heads per key head the variant supports
 
-template <int G, int STAGES, typename TA, typename TO>
+template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
 __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_chain_group_kernel(
     const TA *__restrict__ v, float *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
-    int32_t Hv, TO *__restrict__ o) {
+    int32_t Hv, TO *__restrict__ o, ChainConvIn cv) {
     using namespace chunk;
     constexpr int WPH = GRP_ROWS / (16 * GRP_RPW);  // waves per head
     constexpr int NW = G * WPH;
@@ -937,7 +1071,8 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     int irow[GRP_RPW];
 #pragma unroll
     for (int rt = 0; rt < GRP_RPW; ++rt) irow[rt] = GRP_ROWS * rb + 16 * GRP_RPW * (w % WPH) + 16 * rt + lr;
-    float *sbase = state + ((int64_t)slots[r] * Hv + h) * D * D;
+    const int slot = slots[r];
+    float *sbase = state + ((int64_t)slot * Hv + h) * D * D;
 
     floatx4_t ST[GRP_RPW][8];
 #pragma unroll
@@ -972,21 +1107,8 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
             }
         }
     };
-    Raw1<TA> vr[GRP_RPW][2][4];
-    auto load_v = [&](int cc) {
-        const int tb = tok0 + cc * CH;
-        const int Lc = min(CH, L - cc * CH);
-#pragma unroll
-        for (int rt = 0; rt < GRP_RPW; ++rt)
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tau + 4 * lg + e;
-                    if (t < Lc) vr[rt][tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow[rt]);
-                    else vr[rt][tau][e].zero();
-                }
-    };
+    ChainVLoads<GRP_RPW, VIMG, TA> vr;
+    auto load_v = [&](int cc) { vr.load(v, irow, h, Hv, tok0 + cc * CH, c_first + cc, min(CH, L - cc * CH), lane); };
 
 #pragma unroll
     for (int part = 0; part < NPART; ++part) issue(smem, 0, part);
@@ -1005,12 +1127,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float vcur[GRP_RPW][2][4];
-#pragma unroll
-        for (int rt = 0; rt < GRP_RPW; ++rt)
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vcur[rt][tau][e] = vr[rt][tau][e].get();
+        vr.get(vcur);
         if (prefetch) issue(nstg, cc + 1, 0);
         const uint8_t *kst = stg + 16 * lane;
         const uint8_t *tst = stg + KIMG + (size_t)hh * TIMG + 16 * lane;
@@ -1144,6 +1261,17 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
         for (int jt = 0; jt < 8; ++jt)
             *reinterpret_cast<float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg) =
                 make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]);
+    if constexpr (VIMG) {
+        // new history (the prep kernel has read the old one): this lane's v
+        // channels, and the key head's q / k channels from the first row block
+        if (lg == 0)
+#pragma unroll
+            for (int rt = 0; rt < GRP_RPW; ++rt)
+                chain_write_history<TX>(cv, 2 * cv.nq + h * D + irow[rt], slot, hi_init, tok0, L);
+        if (rb == 0)
+            for (int j = threadIdx.x; j < 2 * D; j += 64 * NW)
+                chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1177,43 +1305,62 @@ static hipError_t set_smem(K kern, size_t bytes, bool &done) {
     return e;
 }
 
-template <int NW, int STAGES, typename TA, typename TO>
+// TA: the type of v (or float for V images); VIMG: v from the V images the
+// prep kernel wrote, and the chain writes the new conv history (of type TX).
+template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
-                               const int32_t *order, const uint8_t *kimg, const uint8_t *timg) {
+                               const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
+                               const ChainConvIn &cv) {
     using namespace chunk;
     static bool set = false;
     const size_t smem = STAGES * STAGE;
-    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO>, smem, set);
+    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX>), dim3((unsigned)blocks),
                        dim3(64 * NW), smem, s, (const TA *)a.v, a.state, a.qsl, a.slots,
-                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o);
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv);
     return hipGetLastError();
 }
 
-template <int G, int STAGES, typename TA, typename TO>
+template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
 static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
-                                     const int32_t *order, const uint8_t *kimg, const uint8_t *timg) {
+                                     const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
+                                     const ChainConvIn &cv) {
     using namespace chunk;
     constexpr int NW = G * (GRP_ROWS / (16 * GRP_RPW));
     static bool set = false;
     const size_t smem = STAGES * (KIMG + G * TIMG);
-    hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO>, smem, set);
+    hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * (int64_t)(D / GRP_ROWS) * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX>), dim3((unsigned)blocks),
                        dim3(64 * NW), smem, s, (const TA *)a.v, a.state, a.qsl, a.slots,
-                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o);
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv);
     return hipGetLastError();
+}
+
+// Block shape: large batches take key-head group blocks (the K image staged
+// once for the group's 3 value heads); else per-head blocks, a whole head
+// (8 waves) when there are enough (request, head) units to fill the chip,
+// else 32 rows.
+template <typename TA, typename TO, bool VIMG, typename TX>
+static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
+                                   const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
+                                   const ChainConvIn &cv) {
+    const int64_t units = (int64_t)a.nreq * a.Hv;
+    if (units >= 256 && a.Hv == 3 * a.Hk)
+        return launch_chain_group<3, 2, TA, TO, VIMG, TX>(a, s, chunk_off, order, kimg, timg, cv);
+    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX>(a, s, chunk_off, order, kimg, timg, cv)
+                        : launch_chain<2, 2, TA, TO, VIMG, TX>(a, s, chunk_off, order, kimg, timg, cv);
 }
 
 template <typename TA, typename TG, typename TX, typename TW, bool CONV>
 static hipError_t launch_prep(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
-                              uint8_t *kimg, uint8_t *timg, const PrepConvIn &cv) {
+                              uint8_t *kimg, uint8_t *timg, const PrepConvIn &cv, float *vimg) {
     using namespace chunk;
     static bool set = false;
     hipError_t e = set_smem(&prefill_prep_kernel<TA, TG, TX, TW, CONV>, sizeof(PrepSmem), set);
@@ -1222,7 +1369,7 @@ static hipError_t launch_prep(const PrefillArgs &a, hipStream_t s, const int32_t
     hipLaunchKernelGGL((prefill_prep_kernel<TA, TG, TX, TW, CONV>), dim3((unsigned)(max_chunks * a.Hk)),
                        dim3(256), sizeof(PrepSmem), s, (const TA *)a.q, (const TA *)a.k,
                        (const TG *)a.a, (const TG *)a.b, a.gate_ld, a.qsl, chunk_off, a.nreq, a.Hk,
-                       a.Hv, kimg, timg, cv);
+                       a.Hv, kimg, timg, cv, vimg);
     return hipGetLastError();
 }
 
@@ -1243,28 +1390,28 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     const PrepConvIn cv{a.x, a.x_ld, a.conv_w, a.pool, a.slots, a.has_init,
                         2 * a.Hk * D + a.Hv * D, a.l2_eps};
     if (a.x) {
-        e = a.x_bf16 ? (a.w_bf16 ? launch_prep<TA, TG, bf16, bf16, true>(a, s, chunk_off, kimg, timg, cv)
-                                 : launch_prep<TA, TG, bf16, float, true>(a, s, chunk_off, kimg, timg, cv))
-                     : (a.w_bf16 ? launch_prep<TA, TG, float, bf16, true>(a, s, chunk_off, kimg, timg, cv)
-                                 : launch_prep<TA, TG, float, float, true>(a, s, chunk_off, kimg, timg, cv));
+        // conv mode: the prep kernel forms q and k (into the K images) and v
+        // (into V images at a.v, one per chunk and value head) from x; the chain
+        // reads the V images and writes the new history of every channel; o is
+        // fp32 scratch in this mode
+        float *vimg = static_cast<float *>(const_cast<void *>(a.v));
+        e = a.x_bf16 ? (a.w_bf16 ? launch_prep<TA, TG, bf16, bf16, true>(a, s, chunk_off, kimg, timg, cv, vimg)
+                                 : launch_prep<TA, TG, bf16, float, true>(a, s, chunk_off, kimg, timg, cv, vimg))
+                     : (a.w_bf16 ? launch_prep<TA, TG, float, bf16, true>(a, s, chunk_off, kimg, timg, cv, vimg)
+                                 : launch_prep<TA, TG, float, float, true>(a, s, chunk_off, kimg, timg, cv, vimg));
         if (e != hipSuccess) return e;
-        // v and the new history of every channel, after the prep kernel has read
-        // the old q / k history
-        if (a.conv_v) e = launch_conv1d(*a.conv_v, s);
+        const ChainConvIn ci{a.x, a.x_ld, a.pool, 2 * a.Hk * D + a.Hv * D, a.Hk * D};
+        if constexpr (std::is_same<TO, float>::value) {
+            e = a.x_bf16 ? launch_chain_any<float, float, true, bf16>(a, s, chunk_off, order, kimg, timg, ci)
+                         : launch_chain_any<float, float, true, float>(a, s, chunk_off, order, kimg, timg, ci);
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
-        e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv);
+        e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv, nullptr);
+        if (e != hipSuccess) return e;
+        e = launch_chain_any<TA, TO, false, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{});
     }
-    if (e != hipSuccess) return e;
-
-    // large batches: key-head group blocks (the K image staged once for the
-    // group's 3 value heads); else per-head blocks, a whole head (8 waves) when
-    // there are enough (request, head) units to fill the chip, else 32 rows
-    const int64_t units = (int64_t)a.nreq * a.Hv;
-    if (units >= 256 && a.Hv == 3 * a.Hk)
-        e = launch_chain_group<3, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
-    else
-        e = units >= 256 ? launch_chain<8, 2, TA, TO>(a, s, chunk_off, order, kimg, timg)
-                         : launch_chain<2, 2, TA, TO>(a, s, chunk_off, order, kimg, timg);
     if (e != hipSuccess || !a.y) return e;
     // gated output: a separate HBM-streaming pass over o (folding it into the
     // chain's chunk loop measured slower: its per-token reductions sit on the
