@@ -10,7 +10,7 @@ two share no code.
 
 Parity status per function (see the oracle tests for the pins):
   conv1d_silu, l2norm, gates, gated_delta_rule, decode_step, gated_norm,
-  rmsnorm, linear, residual_add, gdn_layer, spec_verify — pinned (closed forms, brute force,
+  rmsnorm, linear, residual_add, gdn_layer, spec_verify, round_bf16 — pinned (closed forms, brute force,
   library reductions, worked examples printed on the pages).
   Absolute output values for the full-size workloads are not printed anywhere
   on the pages; beyond the pins they are parity-unpinned by construction.
@@ -28,6 +28,7 @@ from .oracle import (  # noqa: F401
     num_threads,
     residual_add,
     rmsnorm,
+    round_bf16,
     silu,
     spec_verify,
     split_qkv,

@@ -136,6 +136,32 @@ def residual_add(x, delta):
     return _f64(x) + _f64(delta)
 
 
+def round_bf16(x):
+    """Round to the nearest bfloat16 value, ties to even (the state-dtype
+    variant stores S in bf16: the engine's `auto` state dtype may resolve away
+    from float32, tutorial page, section 01 data-structure table, state row).
+
+    bf16 has float32's exponent range and 8 significant bits: a value is rounded
+    to a multiple of 2^(e-7) for 2^e <= |x| < 2^(e+1), e >= -126, and to a
+    multiple of 2^-133 below 2^-126 (subnormals); magnitudes that round past
+    the largest finite bf16 become infinite.  NaN stays NaN.  Returns float64
+    holding the bf16 values exactly."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    ax = np.abs(x[fin])
+    e = np.floor(np.log2(ax))
+    # log2 can be off by one next to powers of two: fix e so 2^e <= |x| < 2^(e+1)
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > ax, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= ax, e + 1, e)
+    q = np.ldexp(1.0, (np.maximum(e, -126) - 7).astype(np.int64))  # the quantum
+    r = np.rint(x[fin] / q) * q  # np.rint: round half to even
+    top = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r = np.where(np.abs(r) > top, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
+
+
 # ---------------------------------------------------------------------------
 # causal depthwise conv1d + SiLU with per-request history
 # ---------------------------------------------------------------------------

@@ -186,3 +186,25 @@ def test_layer_composition_and_residual_identity():
     Y0, *_ = oracle.gdn_layer(X, gi, Wqkvz, Wba, cw, go, np.zeros_like(Wo), hist, st, qsl, [1, 0],
                               [0, 1], Hk, Hv, dk, dv, 1e-6, 1e-6)
     np.testing.assert_array_equal(Y0, X)
+
+
+def test_round_bf16_matches_library_rounding():
+    """The bf16 state rounding: round to nearest, ties to even, checked against
+    torch's float32 -> bfloat16 conversion (a library rounding routine) on random
+    values, values exactly halfway between two bf16 numbers, and specials."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-30, 30, 100000),
+                        [0.0, -0.0, np.inf, -np.inf, 1e-40, -3.4e38]])
+    # halfway cases: a bf16 value plus half of its ulp (ties go to the even neighbour)
+    base = rng.standard_normal(2000).astype(np.float32)
+    bits = base.view(np.uint32) & np.uint32(0xFFFF0000)
+    halfway = (bits | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    for v in (x, halfway):
+        v32 = v.astype(np.float32)  # float32 inputs: one rounding on both sides
+        ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(oracle.round_bf16(v32.astype(np.float64)), ref)
+    assert np.isnan(oracle.round_bf16(np.array([np.nan]))[0])
+    # round-tripping a bf16 value is the identity
+    y = oracle.round_bf16(x[:1000])
+    np.testing.assert_array_equal(oracle.round_bf16(y), y)
