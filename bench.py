@@ -80,14 +80,15 @@ def measured_traffic(kernel, source):
     return int(float(vals["hbm_bytes_per_launch"]))
 
 
-def fused_decode_bytes(d, R, act_bytes=2, y_bytes=2):
+def fused_decode_bytes(d, R, act_bytes=2, y_bytes=2, state_bytes=4):
     """Algorithmic HBM bytes of one gdn_decode_fused launch: the state read and
     written once; the token's conv inputs, z and gates read once; its conv
     history read and written once; y written once (413,413,376 B at 64
-    requests, full shapes, bf16 activations)."""
+    requests, full shapes, bf16 activations, fp32 state; 212,086,784 B with a
+    bf16 state)."""
     Hv, D = d.num_v_heads, d.head_dim_v
     C = 2 * d.num_k_heads * d.head_dim_k + Hv * D
-    state = 2 * R * Hv * D * d.head_dim_k * 4
+    state = 2 * R * Hv * D * d.head_dim_k * state_bytes
     io = R * (C * act_bytes + 2 * C * (d.conv_taps - 1) * act_bytes + Hv * D * act_bytes
               + 2 * Hv * act_bytes + Hv * D * y_bytes)
     return state + io
@@ -247,7 +248,31 @@ def main():
             },
         },
     }
-    del states, conv_pools
+    # the same step with the state stored in bf16 (the state-dtype variant)
+    states16 = [st.to(torch.bfloat16) for st in states]
+    it_count[0] = 0
+
+    def fused_step_bf16():
+        i = it_count[0] % n_rot
+        it_count[0] += 1
+        gdn.gdn_decode_fused(d, x, z, a, b, conv_w, gamma, conv_pools[i], states16[i], slots, y,
+                             l2_eps=L2_EPS, norm_eps=NORM_EPS, stream=sh)
+
+    ms16, gpu16 = timed(fused_step_bf16)
+    b16 = fused_decode_bytes(d, R, state_bytes=2)
+    a16 = b16 / (gpu16 * 1e-3) / 1e9
+    result["decode_bf16_state"] = {
+        "step": "gdn_decode_fused with a bf16 state [64,48,128,128] (widened on load, "
+                "rounded once on store)",
+        "ms_per_step": round(ms16, 4),
+        "gpu_ms_per_step": round(gpu16, 4),
+        "state_gbs": round(state_bytes / 2 / (ms16 * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "decode_fused_kernel (bf16 state)", "bound": "hbm",
+                     "achieved": round(a16, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(a16 / HBM_PEAK_GBS, 4), "bytes_per_launch": b16,
+                     "traffic": None},
+    }
+    del states, conv_pools, states16
     torch.cuda.empty_cache()
 
     # ----------------------------------------------------------------- prefill

@@ -1,6 +1,7 @@
 // One decode step of the GDN mixer core in a single launch: conv1d + SiLU with
-// the 3-entry history, L2 norm of q and k, the gated delta rule on the fp32
-// state, and the gated RMSNorm of the output.
+// the 3-entry history, L2 norm of q and k, the gated delta rule on the state
+// (fp32, or bf16 widened on load and rounded once on store; arithmetic in
+// fp32 either way), and the gated RMSNorm of the output.
 //
 // The step ("Qwen3.8-27B: from model structure to the vLLM inference
 // dataflow", section 02, one token's journey through a GDN layer; section 01
@@ -29,11 +30,10 @@ constexpr int DF_BUFFERS = 3;     // state passes in flight per block
 // cache policy of the state's buffer loads and stores
 constexpr int BUF_DW3 = 0x00020000;
 constexpr int BUF_NT = 2;
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // A buffer resource over [base, base + bytes) from wave-uniform values (read
 // from the first lane, so the descriptor lives in scalar registers).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const float *base, uint32_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
@@ -42,16 +42,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const float *base
                                              (int)n, BUF_DW3);
 }  // fastest of 256, 512, 1024 threads per group block, measured
 
-template <int D, int NB, int NT, typename TX, typename TW, typename TY>
+template <int D, int NB, int NT, typename TX, typename TW, typename TY, typename TS>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void decode_fused_kernel(
     const TX *__restrict__ x, int64_t x_ld, const TX *__restrict__ z, int64_t z_ld,
     const TX *__restrict__ ga, const TX *__restrict__ gb, int64_t gate_ld,
     const TW *__restrict__ w, const TW *__restrict__ gamma, TX *__restrict__ pool,
-    float *__restrict__ state, const int32_t *__restrict__ slots,
+    TS *__restrict__ state, const int32_t *__restrict__ slots,
     const uint8_t *__restrict__ has_init, int32_t Hk, int32_t Hv, float l2_eps,
     float norm_eps, TY *__restrict__ y, float *__restrict__ o_out) {
     constexpr int LPR = D / 8;              // lanes per state row
     constexpr int RPP = NT / LPR;   // rows per pass
+    constexpr int SB = (int)sizeof(TS);     // bytes per state element
+    using SR = StateRow<TS, LPR>;
     extern __shared__ __attribute__((aligned(16))) float dsm[];
     const int G = Hv / Hk;
     const int rows = G * D;
@@ -82,18 +84,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
     // as buffer resources: loads read zeros without an initial state and past
     // the last row, where stores are dropped, so no branch guards a state
     // access and every access counts in the memory counters the waits are
-    // derived from.  Lane: row rg of a pass, columns 4 l + 4 LPR m + 0..3.
-    const uint32_t ubytes = (uint32_t)rows * D * 4;
-    float *ubase = state + ((int64_t)slot * Hv + (int64_t)kh * G) * D * D;
+    // derived from.  Lane: row rg of a pass, its columns as StateRow lays them out.
+    const uint32_t ubytes = (uint32_t)rows * D * SB;
+    TS *ubase = state + ((int64_t)slot * Hv + (int64_t)kh * G) * D * D;
     const __amdgpu_buffer_rsrc_t rld = uniform_rsrc(ubase, hi ? ubytes : 0u);
     const __amdgpu_buffer_rsrc_t rst = uniform_rsrc(ubase, ubytes);
-    const uint32_t loff = ((uint32_t)rg * D + 4 * l) * 4;
+    const uint32_t roff = (uint32_t)rg * D * SB;
     f32x4 buf[NB][2];  // pass p lands in buf[p % NB]
     auto load_pass = [&](f32x4 (&dst)[2], int p) {
-        const uint32_t off = (uint32_t)p * RPP * D * 4 + loff;
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-            dst[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rld, off + 16 * LPR * m, 0, BUF_NT));
+        SR::template load<BUF_NT>(dst, rld, (uint32_t)p * RPP * D * SB + roff, l);
     };
 #pragma unroll
     for (int b = 0; b < NB; ++b) load_pass(buf[b], b);
@@ -156,8 +155,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
     float4 kc[2], qc[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        kc[m] = *reinterpret_cast<const float4 *>(sk + 4 * l + 4 * LPR * m);
-        qc[m] = *reinterpret_cast<const float4 *>(sq + 4 * l + 4 * LPR * m);
+        kc[m] = *reinterpret_cast<const float4 *>(sk + SR::col(l, m));
+        qc[m] = *reinterpret_cast<const float4 *>(sq + SR::col(l, m));
     }
 
     // pass p from the registers its load landed in
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
         pk = group_sum<LPR>(pk);
         pq = group_sum<LPR>(pq);
         const float be = beta * (vi - alpha * pk);
-        const uint32_t off = (uint32_t)p * RPP * D * 4 + loff;
+        f32x4 sn[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             f32x4 s = cur[m];
@@ -185,8 +184,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void de
             s.y = alpha * s.y + be * kc[m].y;
             s.z = alpha * s.z + be * kc[m].z;
             s.w = alpha * s.w + be * kc[m].w;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), rst, off + 16 * LPR * m, 0, BUF_NT);
+            sn[m] = s;
         }
+        SR::template store<BUF_NT>(sn[0], sn[1], rst, (uint32_t)p * RPP * D * SB + roff, l);
         if (valid && l == 0) so[R] = (alpha * pq + be * kq) * inv_sqrt_d;
     };
     // groups of NB passes: all of a group's loads are in flight together, then
@@ -238,19 +238,23 @@ size_t decode_fused_smem_bytes(int D, int32_t Hk, int32_t Hv) {
     return (size_t)(2 * D + 2 * G * D + 2 * G + 32) * sizeof(float);
 }
 
-template <int D, typename TX, typename TW, typename TY>
+template <int D, typename TX, typename TW, typename TY, typename TS>
 static hipError_t launch_df_t(const DecodeFusedArgs &a, hipStream_t s) {
     const size_t smem = decode_fused_smem_bytes(D, a.Hk, a.Hv);
-    hipLaunchKernelGGL((decode_fused_kernel<D, DF_BUFFERS, DF_THREADS, TX, TW, TY>), dim3((unsigned)((int64_t)a.R * a.Hk)),
+    hipLaunchKernelGGL((decode_fused_kernel<D, DF_BUFFERS, DF_THREADS, TX, TW, TY, TS>), dim3((unsigned)((int64_t)a.R * a.Hk)),
                        dim3(DF_THREADS), smem, s, (const TX *)a.x, a.x_ld, (const TX *)a.z, a.z_ld,
                        (const TX *)a.a, (const TX *)a.b, a.gate_ld, (const TW *)a.w,
-                       (const TW *)a.gamma, (TX *)a.pool, a.state, a.slots, a.has_init, a.Hk, a.Hv,
+                       (const TW *)a.gamma, (TX *)a.pool, (TS *)a.state, a.slots, a.has_init, a.Hk, a.Hv,
                        a.l2_eps, a.norm_eps, (TY *)a.y, a.o);
     return hipGetLastError();
 }
+template <int D, typename TX, typename TW, typename TY>
+static hipError_t launch_df_s(const DecodeFusedArgs &a, hipStream_t s) {
+    return a.state_bf16 ? launch_df_t<D, TX, TW, TY, bf16>(a, s) : launch_df_t<D, TX, TW, TY, float>(a, s);
+}
 template <int D, typename TX, typename TW>
 static hipError_t launch_df_y(const DecodeFusedArgs &a, hipStream_t s) {
-    return a.y_bf16 ? launch_df_t<D, TX, TW, bf16>(a, s) : launch_df_t<D, TX, TW, float>(a, s);
+    return a.y_bf16 ? launch_df_s<D, TX, TW, bf16>(a, s) : launch_df_s<D, TX, TW, float>(a, s);
 }
 template <int D, typename TX>
 static hipError_t launch_df_w(const DecodeFusedArgs &a, hipStream_t s) {

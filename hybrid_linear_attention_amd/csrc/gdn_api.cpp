@@ -110,16 +110,18 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, c
 gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
                             int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
                             gdn_dtype act_dt, const void *conv_w, const void *gamma,
-                            gdn_dtype w_dt, void *conv_pool, float *state_pool,
-                            const int32_t *slot_ids, const uint8_t *has_initial,
-                            int32_t num_reqs, int32_t num_slots, float l2_eps, float norm_eps,
-                            void *y, gdn_dtype y_dt, float *o, void *stream) {
+                            gdn_dtype w_dt, void *conv_pool, void *state_pool,
+                            gdn_dtype state_dt, const int32_t *slot_ids,
+                            const uint8_t *has_initial, int32_t num_reqs, int32_t num_slots,
+                            float l2_eps, float norm_eps, void *y, gdn_dtype y_dt, float *o,
+                            void *stream) {
     gdn_status st = check_dims(dims);
     if (st != GDN_OK) return st;
     const int D = dims->head_dim_k;
     if (gdn::decode_fused_smem_bytes(D, dims->num_k_heads, dims->num_v_heads) > 64 * 1024)
         return GDN_ERR_DIMS;
-    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt) || !valid_dtype(state_dt))
+        return GDN_ERR_DTYPE;
     const int64_t C = 2 * (int64_t)dims->num_k_heads * D + (int64_t)dims->num_v_heads * D;
     if (num_reqs < 0 || num_slots < 0 || num_reqs > num_slots) return GDN_ERR_SHAPE;
     if (x_ld < C || z_ld < (int64_t)dims->num_v_heads * D || gate_ld < dims->num_v_heads)
@@ -136,18 +138,18 @@ gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_l
         (o && !aligned(o, 4)))
         return GDN_ERR_ALIGN;
     gdn::DecodeFusedArgs da{D, x_qkv, x_ld, z, z_ld, a, b, gate_ld, act_dt == GDN_BF16, conv_w,
-                            gamma, w_dt == GDN_BF16, conv_pool, state_pool, slot_ids, has_initial,
-                            num_reqs, dims->num_k_heads, dims->num_v_heads, l2_eps, norm_eps, y,
-                            y_dt == GDN_BF16, o};
+                            gamma, w_dt == GDN_BF16, conv_pool, state_pool, state_dt == GDN_BF16,
+                            slot_ids, has_initial, num_reqs, dims->num_k_heads, dims->num_v_heads,
+                            l2_eps, norm_eps, y, y_dt == GDN_BF16, o};
     return hip_status(gdn::launch_decode_fused(da, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
                            int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
                            gdn_dtype act_dt, const void *conv_w, const void *gamma,
-                           gdn_dtype w_dt, void *conv_pool, float *state_pool,
-                           const int32_t *query_start_loc, const int32_t *slot_ids,
-                           const int32_t *spec_slot_ids, int32_t max_tokens,
+                           gdn_dtype w_dt, void *conv_pool, void *state_pool,
+                           gdn_dtype state_dt, const int32_t *query_start_loc,
+                           const int32_t *slot_ids, const int32_t *spec_slot_ids, int32_t max_tokens,
                            const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
                            int32_t num_slots, float l2_eps, float norm_eps, void *y,
                            gdn_dtype y_dt, float *o, void *stream) {
@@ -157,7 +159,8 @@ gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld
     if (max_tokens < 1 || max_tokens > GDN_SPEC_MAX_TOKENS) return GDN_ERR_SHAPE;
     if (gdn::spec_verify_smem_bytes(D, dims->num_k_heads, dims->num_v_heads, max_tokens) > 64 * 1024)
         return GDN_ERR_DIMS;
-    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt) || !valid_dtype(state_dt))
+        return GDN_ERR_DTYPE;
     const int64_t C = 2 * (int64_t)dims->num_k_heads * D + (int64_t)dims->num_v_heads * D;
     if (num_reqs < 0 || num_tokens < 0 || num_slots < 0 || num_reqs > num_slots)
         return GDN_ERR_SHAPE;
@@ -177,7 +180,8 @@ gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld
         !aligned(spec_slot_ids, 4) || !aligned(y, dt_size(y_dt)) || (o && !aligned(o, 4)))
         return GDN_ERR_ALIGN;
     gdn::SpecVerifyArgs sa{D, x_qkv, x_ld, z, z_ld, a, b, gate_ld, act_dt == GDN_BF16, conv_w,
-                           gamma, w_dt == GDN_BF16, conv_pool, state_pool, query_start_loc,
+                           gamma, w_dt == GDN_BF16, conv_pool, state_pool, state_dt == GDN_BF16,
+                           query_start_loc,
                            slot_ids, spec_slot_ids, max_tokens, has_initial, num_reqs,
                            dims->num_k_heads, dims->num_v_heads, l2_eps, norm_eps, y,
                            y_dt == GDN_BF16, o};
@@ -252,15 +256,16 @@ size_t gdn_prefill_fused_workspace_bytes(const gdn_dims *dims, int32_t num_token
 gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
                              int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
                              gdn_dtype act_dt, const void *conv_w, const void *gamma,
-                             gdn_dtype w_dt, void *conv_pool, float *state_pool,
-                             const int32_t *query_start_loc, const int32_t *slot_ids,
+                             gdn_dtype w_dt, void *conv_pool, void *state_pool,
+                             gdn_dtype state_dt, const int32_t *query_start_loc, const int32_t *slot_ids,
                              const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
                              int32_t num_slots, float l2_eps, float norm_eps, void *y,
                              gdn_dtype y_dt, void *workspace, size_t workspace_bytes,
                              void *stream) {
     gdn_status st = check_dims(dims);
     if (st != GDN_OK) return st;
-    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt)) return GDN_ERR_DTYPE;
+    if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt) || !valid_dtype(state_dt))
+        return GDN_ERR_DTYPE;
     const int D = dims->head_dim_k;
     const int32_t nq = dims->num_k_heads * D;
     const int32_t C = 2 * nq + dims->num_v_heads * D;
@@ -300,6 +305,9 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
     // itself and its chain forms v, so no conv pass runs
     const bool prep_conv = D == 128 && x_ld % (int64_t)(16 / e) == 0 && aligned(x_qkv, 16) &&
                            aligned(conv_w, 16);
+    // a bf16 state at d = 128 needs the prep-conv path (16-byte conv rows)
+    if (state_dt == GDN_BF16 && D == 128 && !prep_conv) return GDN_ERR_ALIGN;
+    pa.state_bf16 = state_dt == GDN_BF16;
     if (prep_conv) {
         pa.x = x_qkv;
         pa.x_ld = x_ld;

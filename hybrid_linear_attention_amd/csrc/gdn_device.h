@@ -55,6 +55,15 @@ __device__ __forceinline__ float4 ld4(const bf16 *p) {
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+// Store four consecutive elements (p aligned to four elements); bf16 rounds
+// once (RNE).
+__device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+__device__ __forceinline__ void st4(bf16 *p, float4 v) {
+    const uint32_t a = uint32_t(to_bf16(v.x).bits) | (uint32_t(to_bf16(v.y).bits) << 16);
+    const uint32_t b = uint32_t(to_bf16(v.z).bits) | (uint32_t(to_bf16(v.w).bits) << 16);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+}
+
 // Eight consecutive elements (p aligned to 16 bytes), kept in their storage
 // format until converted, so that issuing a load never waits for its data.
 template <typename T> struct Raw8;
@@ -96,6 +105,51 @@ __device__ __forceinline__ void store8(bf16 *p, const float (&f)[8]) {
         w[i] = uint32_t(to_bf16(f[2 * i]).bits) | (uint32_t(to_bf16(f[2 * i + 1]).bits) << 16);
     *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
+
+// State rows streamed through range-checked buffer loads and stores: a row of D
+// elements is held by D / 8 lanes, 8 elements (two float4) per lane.  fp32 rows:
+// lane l holds columns 4 l .. 4 l + 3 and 4 l + D / 2 .. + 3 (two 16-byte
+// accesses, each covering half the row across the lanes); bf16 rows: columns
+// 8 l .. 8 l + 7 (one 16-byte access), widened exactly on load and rounded to
+// nearest-even on store.  `off` is the byte offset of the row in the resource;
+// AUX the cache policy of the accesses.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <typename TS, int LPR> struct StateRow;
+template <int LPR> struct StateRow<float, LPR> {
+    __device__ static __forceinline__ int col(int l, int m) { return 4 * l + 4 * LPR * m; }
+    template <int AUX>
+    __device__ static __forceinline__ void load(f32x4 (&dst)[2], __amdgpu_buffer_rsrc_t r, uint32_t off, int l) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            dst[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * l + 16 * LPR * m, 0, AUX));
+    }
+    template <int AUX>
+    __device__ static __forceinline__ void store(const f32x4 &a, const f32x4 &b, __amdgpu_buffer_rsrc_t r,
+                                                 uint32_t off, int l) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), r, off + 16 * l, 0, AUX);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, b), r, off + 16 * l + 16 * LPR, 0, AUX);
+    }
+};
+template <int LPR> struct StateRow<bf16, LPR> {
+    __device__ static __forceinline__ int col(int l, int m) { return 8 * l + 4 * m; }
+    template <int AUX>
+    __device__ static __forceinline__ void load(f32x4 (&dst)[2], __amdgpu_buffer_rsrc_t r, uint32_t off, int l) {
+        const u32x4_t u = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * l, 0, AUX));
+        dst[0] = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        dst[1] = f32x4{__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
+                       __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u)};
+    }
+    __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+        return uint32_t(to_bf16(lo).bits) | (uint32_t(to_bf16(hi).bits) << 16);
+    }
+    template <int AUX>
+    __device__ static __forceinline__ void store(const f32x4 &a, const f32x4 &b, __amdgpu_buffer_rsrc_t r,
+                                                 uint32_t off, int l) {
+        const u32x4_t u = u32x4_t{pack(a.x, a.y), pack(a.z, a.w), pack(b.x, b.y), pack(b.z, b.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(u, r, off + 16 * l, 0, AUX);
+    }
+};
 
 // Lane permutations inside rows of 16 lanes (DPP): xor 1 and xor 2 inside a
 // quad, then the mirror of an 8-lane half and of the 16-lane row.

@@ -36,7 +36,7 @@ struct DecodeFusedArgs {
     const void *z; int64_t z_ld;
     const void *a, *b; int64_t gate_ld; bool act_bf16;
     const void *w, *gamma; bool w_bf16;
-    void *pool; float *state; const int32_t *slots; const uint8_t *has_init;
+    void *pool; void *state; bool state_bf16; const int32_t *slots; const uint8_t *has_init;
     int32_t R, Hk, Hv;
     float l2_eps, norm_eps;
     void *y; bool y_bf16; float *o;
@@ -50,7 +50,7 @@ struct SpecVerifyArgs {
     const void *z; int64_t z_ld;
     const void *a, *b; int64_t gate_ld; bool act_bf16;
     const void *w, *gamma; bool w_bf16;
-    void *pool; float *state;
+    void *pool; void *state; bool state_bf16;
     const int32_t *qsl, *slots, *spec; int32_t max_tokens; const uint8_t *has_init;
     int32_t R, Hk, Hv;
     float l2_eps, norm_eps;
@@ -83,7 +83,7 @@ struct PrefillArgs {
     int D;
     const void *q, *k, *v; bool act_bf16;
     const void *a, *b; int64_t gate_ld; bool gate_bf16;
-    float *state;
+    void *state;  // [slots, Hv, D, D], fp32 (or bf16 with state_bf16, below)
     const int32_t *qsl, *slots; const uint8_t *has_init;
     int32_t nreq, T, Hk, Hv;
     void *o; bool o_bf16;
@@ -99,6 +99,7 @@ struct PrefillArgs {
     const void *x = nullptr; int64_t x_ld = 0; bool x_bf16 = false;
     const void *conv_w = nullptr; bool w_bf16 = false;
     void *pool = nullptr; float l2_eps = 0.f;
+    bool state_bf16 = false;  // bf16 state: widened on load, rounded once (RNE) on store
 };
 size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);

@@ -818,9 +818,9 @@ __device__ __forceinline__ void issue_images(uint8_t *stage, const uint8_t *kim,
     }
 }
 
-template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
+template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
-    const TA *__restrict__ v, float *__restrict__ state, const int32_t *__restrict__ qsl,
+    const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
@@ -852,7 +852,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const int irow = IB * rb + 16 * w + lr;  // this lane's state row (value channel)
     const int irows[1] = {irow};
     const int slot = slots[r];
-    float *sbase = state + ((int64_t)slot * Hv + h) * D * D;
+    TS *sbase = state + ((int64_t)slot * Hv + h) * D * D;
 
     // state rows of this lane, transposed accumulator layout:
     // ST[jt][e] = S[irow][16 jt + 4 lg + e]
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     for (int jt = 0; jt < 8; ++jt) {
         ST[jt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         if (hi_init) {
-            const float4 s4 = *reinterpret_cast<const float4 *>(sbase + (int64_t)irow * D + 16 * jt + 4 * lg);
+            const float4 s4 = ld4(sbase + (int64_t)irow * D + 16 * jt + 4 * lg);
             ST[jt] = floatx4_t{s4.x, s4.y, s4.z, s4.w};
         }
     }
@@ -1011,8 +1011,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
 
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt)
-        *reinterpret_cast<float4 *>(sbase + (int64_t)irow * D + 16 * jt + 4 * lg) =
-            make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]);
+        st4(sbase + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
     if constexpr (VIMG) {
         // new history (the prep kernel has read the old one): this lane's v
         // channel, and the key head's q / k channels from one block of the key
@@ -1035,9 +1034,9 @@ constexpr int GRP_ROWS = 64;          // state rows per head per block
 constexpr int GRP_RPW = 2;            // 16-row tiles per wave
 constexpr int GRP_MAX_HEADS = 3;      // value heads per key head the variant supports
 
-template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
+template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_chain_group_kernel(
-    const TA *__restrict__ v, float *__restrict__ state, const int32_t *__restrict__ qsl,
+    const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
@@ -1072,7 +1071,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
 #pragma unroll
     for (int rt = 0; rt < GRP_RPW; ++rt) irow[rt] = GRP_ROWS * rb + 16 * GRP_RPW * (w % WPH) + 16 * rt + lr;
     const int slot = slots[r];
-    float *sbase = state + ((int64_t)slot * Hv + h) * D * D;
+    TS *sbase = state + ((int64_t)slot * Hv + h) * D * D;
 
     floatx4_t ST[GRP_RPW][8];
 #pragma unroll
@@ -1081,7 +1080,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
         for (int jt = 0; jt < 8; ++jt) {
             ST[rt][jt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             if (hi_init) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg);
+                const float4 s4 = ld4(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg);
                 ST[rt][jt] = floatx4_t{s4.x, s4.y, s4.z, s4.w};
             }
         }
@@ -1259,8 +1258,8 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     for (int rt = 0; rt < GRP_RPW; ++rt)
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt)
-            *reinterpret_cast<float4 *>(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg) =
-                make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]);
+            st4(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
+                make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
     if constexpr (VIMG) {
         // new history (the prep kernel has read the old one): this lane's v
         // channels, and the key head's q / k channels from the first row block
@@ -1307,25 +1306,25 @@ static hipError_t set_smem(K kern, size_t bytes, bool &done) {
 
 // TA: the type of v (or float for V images); VIMG: v from the V images the
 // prep kernel wrote, and the chain writes the new conv history (of type TX).
-template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
+template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                const ChainConvIn &cv) {
     using namespace chunk;
     static bool set = false;
     const size_t smem = STAGES * STAGE;
-    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX>, smem, set);
+    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX>), dim3((unsigned)blocks),
-                       dim3(64 * NW), smem, s, (const TA *)a.v, a.state, a.qsl, a.slots,
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS>), dim3((unsigned)blocks),
+                       dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv);
     return hipGetLastError();
 }
 
-template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX>
+template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                      const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                      const ChainConvIn &cv) {
@@ -1333,12 +1332,12 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
     constexpr int NW = G * (GRP_ROWS / (16 * GRP_RPW));
     static bool set = false;
     const size_t smem = STAGES * (KIMG + G * TIMG);
-    hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX>, smem, set);
+    hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * (int64_t)(D / GRP_ROWS) * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX>), dim3((unsigned)blocks),
-                       dim3(64 * NW), smem, s, (const TA *)a.v, a.state, a.qsl, a.slots,
+    hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>), dim3((unsigned)blocks),
+                       dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv);
     return hipGetLastError();
 }
@@ -1347,15 +1346,15 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
 // once for the group's 3 value heads); else per-head blocks, a whole head
 // (8 waves) when there are enough (request, head) units to fill the chip,
 // else 32 rows.
-template <typename TA, typename TO, bool VIMG, typename TX>
+template <typename TA, typename TO, bool VIMG, typename TX, typename TS>
 static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                    const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                    const ChainConvIn &cv) {
     const int64_t units = (int64_t)a.nreq * a.Hv;
     if (units >= 256 && a.Hv == 3 * a.Hk)
-        return launch_chain_group<3, 2, TA, TO, VIMG, TX>(a, s, chunk_off, order, kimg, timg, cv);
-    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX>(a, s, chunk_off, order, kimg, timg, cv)
-                        : launch_chain<2, 2, TA, TO, VIMG, TX>(a, s, chunk_off, order, kimg, timg, cv);
+        return launch_chain_group<3, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv);
+    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv)
+                        : launch_chain<2, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv);
 }
 
 template <typename TA, typename TG, typename TX, typename TW, bool CONV>
@@ -1402,15 +1401,20 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         const ChainConvIn ci{a.x, a.x_ld, a.pool, 2 * a.Hk * D + a.Hv * D, a.Hk * D};
         if constexpr (std::is_same<TO, float>::value) {
-            e = a.x_bf16 ? launch_chain_any<float, float, true, bf16>(a, s, chunk_off, order, kimg, timg, ci)
-                         : launch_chain_any<float, float, true, float>(a, s, chunk_off, order, kimg, timg, ci);
+            if (a.state_bf16)
+                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, bf16>(a, s, chunk_off, order, kimg, timg, ci)
+                             : launch_chain_any<float, float, true, float, bf16>(a, s, chunk_off, order, kimg, timg, ci);
+            else
+                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, float>(a, s, chunk_off, order, kimg, timg, ci)
+                             : launch_chain_any<float, float, true, float, float>(a, s, chunk_off, order, kimg, timg, ci);
         } else {
             return hipErrorInvalidValue;
         }
     } else {
         e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv, nullptr);
         if (e != hipSuccess) return e;
-        e = launch_chain_any<TA, TO, false, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{});
+        if (a.state_bf16) return hipErrorInvalidValue;  // the unfused prefill keeps an fp32 state
+        e = launch_chain_any<TA, TO, false, float, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{});
     }
     if (e != hipSuccess || !a.y) return e;
     // gated output: a separate HBM-streaming pass over o (folding it into the

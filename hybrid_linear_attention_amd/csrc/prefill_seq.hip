@@ -15,11 +15,11 @@
 
 namespace gdn {
 
-template <int D, typename TA, typename TG, typename TO>
+template <int D, typename TA, typename TG, typename TO, typename TS>
 __global__ __launch_bounds__(256) void prefill_seq_kernel(
     const TA *__restrict__ q, const TA *__restrict__ k, const TA *__restrict__ v,
     const TG *__restrict__ ga, const TG *__restrict__ gb, int64_t gate_ld,
-    float *__restrict__ state, const int32_t *__restrict__ qsl,
+    TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init, int32_t nreq,
     int32_t Hk, int32_t Hv, TO *__restrict__ o) {
     constexpr int LPR = D / 16;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
     const int t0 = qsl[r], t1 = qsl[r + 1];
     if (t1 <= t0) return;  // empty request: slot untouched
     const bool hi = has_init == nullptr || has_init[r] != 0;
-    float *sp = state + ((int64_t)slots[r] * Hv + h) * D * D;
+    TS *sp = state + ((int64_t)slots[r] * Hv + h) * D * D;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
     float4 s[RPT][4];
@@ -98,23 +98,27 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
         const int i = rg + p * RG;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            *reinterpret_cast<float4 *>(sp + (int64_t)i * D + 4 * l + 4 * LPR * m) = s[p][m];
+            st4(sp + (int64_t)i * D + 4 * l + 4 * LPR * m, s[p][m]);
     }
 }
 
-template <int D, typename TA, typename TG, typename TO>
+template <int D, typename TA, typename TG, typename TO, typename TS>
 static hipError_t launch_seq_t(const PrefillArgs &a, hipStream_t s) {
     constexpr int UPB = 16384 / (D * D);
     const int64_t units = (int64_t)a.nreq * a.Hv;
-    hipLaunchKernelGGL((prefill_seq_kernel<D, TA, TG, TO>), dim3((unsigned)((units + UPB - 1) / UPB)),
+    hipLaunchKernelGGL((prefill_seq_kernel<D, TA, TG, TO, TS>), dim3((unsigned)((units + UPB - 1) / UPB)),
                        dim3(256), 0, s, (const TA *)a.q, (const TA *)a.k, (const TA *)a.v,
-                       (const TG *)a.a, (const TG *)a.b, a.gate_ld, a.state, a.qsl, a.slots,
+                       (const TG *)a.a, (const TG *)a.b, a.gate_ld, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, a.nreq, a.Hk, a.Hv, (TO *)a.o);
     return hipGetLastError();
 }
+template <int D, typename TA, typename TG, typename TO>
+static hipError_t launch_seq_s(const PrefillArgs &a, hipStream_t s) {
+    return a.state_bf16 ? launch_seq_t<D, TA, TG, TO, bf16>(a, s) : launch_seq_t<D, TA, TG, TO, float>(a, s);
+}
 template <int D, typename TA, typename TG>
 static hipError_t launch_seq_o(const PrefillArgs &a, hipStream_t s) {
-    return a.o_bf16 ? launch_seq_t<D, TA, TG, bf16>(a, s) : launch_seq_t<D, TA, TG, float>(a, s);
+    return a.o_bf16 ? launch_seq_s<D, TA, TG, bf16>(a, s) : launch_seq_s<D, TA, TG, float>(a, s);
 }
 template <int D, typename TA>
 static hipError_t launch_seq_g(const PrefillArgs &a, hipStream_t s) {

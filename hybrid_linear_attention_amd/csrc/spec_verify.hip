@@ -31,9 +31,8 @@ constexpr int SV_THREADS = 1024;
 constexpr int SV_BUFFERS = 2;   // state passes whose loads are in flight together
 constexpr int SV_DW3 = 0x00020000;
 constexpr int SV_NT = 2;        // nontemporal cache policy of the state stream
-typedef unsigned sv_u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sv_rsrc(const float *base, uint32_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sv_rsrc(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
@@ -47,17 +46,19 @@ size_t spec_verify_smem_bytes(int D, int32_t Hk, int32_t Hv, int32_t max_tokens)
     return ((size_t)max_tokens * (2 * D + 2 * G * D + 2 * G + 1) + 64) * sizeof(float);
 }
 
-template <int D, int NB, int NT, typename TX, typename TW, typename TY>
+template <int D, int NB, int NT, typename TX, typename TW, typename TY, typename TS>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void spec_verify_kernel(
     const TX *__restrict__ x, int64_t x_ld, const TX *__restrict__ z, int64_t z_ld,
     const TX *__restrict__ ga, const TX *__restrict__ gb, int64_t gate_ld,
     const TW *__restrict__ w, const TW *__restrict__ gamma, TX *__restrict__ pool,
-    float *__restrict__ state, const int32_t *__restrict__ qsl, const int32_t *__restrict__ slots,
+    TS *__restrict__ state, const int32_t *__restrict__ qsl, const int32_t *__restrict__ slots,
     const int32_t *__restrict__ spec, int32_t max_tokens, const uint8_t *__restrict__ has_init,
     int32_t Hk, int32_t Hv, float l2_eps, float norm_eps, TY *__restrict__ y,
     float *__restrict__ o_out) {
     constexpr int LPR = D / 8;      // lanes per state row
     constexpr int RPP = NT / LPR;   // rows per pass
+    constexpr int SB = (int)sizeof(TS);
+    using SR = StateRow<TS, LPR>;
     extern __shared__ __attribute__((aligned(16))) float ssm[];
     const int G = Hv / Hk;
     const int rows = G * D;
@@ -90,16 +91,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void sp
 
     // the unit's state rows as buffer resources: loads read zeros without an
     // initial state and past the last row, stores past the last row are dropped
-    const uint32_t ubytes = (uint32_t)rows * D * 4;
+    const uint32_t ubytes = (uint32_t)rows * D * SB;
     const int64_t unit_off = (int64_t)kh * G * D * D;
     const __amdgpu_buffer_rsrc_t rld = sv_rsrc(state + (int64_t)slot * Hv * D * D + unit_off, hi ? ubytes : 0u);
-    const uint32_t loff = ((uint32_t)rg * D + 4 * l) * 4;
+    const uint32_t roff = (uint32_t)rg * D * SB;
     f32x4 buf[NB][2];
     auto load_pass = [&](f32x4 (&dst)[2], int p) {
-        const uint32_t off = (uint32_t)p * RPP * D * 4 + loff;
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-            dst[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rld, off + 16 * LPR * m, 0, SV_NT));
+        SR::template load<SV_NT>(dst, rld, (uint32_t)p * RPP * D * SB + roff, l);
     };
 #pragma unroll
     for (int b = 0; b < NB; ++b) load_pass(buf[b], b);
@@ -186,13 +184,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void sp
         const int R = p * RPP + rg;
         const bool valid = R < rows;
         const int hh = valid ? R / D : 0;
-        const uint32_t off = (uint32_t)p * RPP * D * 4 + loff;
+        const uint32_t off = (uint32_t)p * RPP * D * SB + roff;
         f32x4 s0 = cur[0], s1 = cur[1];
         for (int j = 0; j < n; ++j) {
-            const f32x4 k0 = *reinterpret_cast<const f32x4 *>(sk + j * D + 4 * l);
-            const f32x4 k1 = *reinterpret_cast<const f32x4 *>(sk + j * D + 4 * l + 4 * LPR);
-            const f32x4 q0 = *reinterpret_cast<const f32x4 *>(sq + j * D + 4 * l);
-            const f32x4 q1 = *reinterpret_cast<const f32x4 *>(sq + j * D + 4 * l + 4 * LPR);
+            const f32x4 k0 = *reinterpret_cast<const f32x4 *>(sk + j * D + SR::col(l, 0));
+            const f32x4 k1 = *reinterpret_cast<const f32x4 *>(sk + j * D + SR::col(l, 1));
+            const f32x4 q0 = *reinterpret_cast<const f32x4 *>(sq + j * D + SR::col(l, 0));
+            const f32x4 q1 = *reinterpret_cast<const f32x4 *>(sq + j * D + SR::col(l, 1));
             float pk = s0.x * k0.x + s0.y * k0.y + s0.z * k0.z + s0.w * k0.w +
                        s1.x * k1.x + s1.y * k1.y + s1.z * k1.z + s1.w * k1.w;
             float pq = s0.x * q0.x + s0.y * q0.y + s0.z * q0.z + s0.w * q0.w +
@@ -206,8 +204,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void sp
             s1 = alpha * s1 + be * k1;
             const __amdgpu_buffer_rsrc_t rst =
                 sv_rsrc(state + (int64_t)sslots[j] * Hv * D * D + unit_off, ubytes);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, s0), rst, off, 0, SV_NT);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(sv_u32x4, s1), rst, off + 16 * LPR, 0, SV_NT);
+            SR::template store<SV_NT>(s0, s1, rst, off, l);
             if (valid && l == 0) so[j * rows + R] = (alpha * pq + be * skq[j]) * inv_sqrt_d;
         }
     };
@@ -254,20 +251,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void sp
     }
 }
 
-template <int D, typename TX, typename TW, typename TY>
+template <int D, typename TX, typename TW, typename TY, typename TS>
 static hipError_t launch_sv_t(const SpecVerifyArgs &a, hipStream_t s) {
     const size_t smem = spec_verify_smem_bytes(D, a.Hk, a.Hv, a.max_tokens);
-    hipLaunchKernelGGL((spec_verify_kernel<D, SV_BUFFERS, SV_THREADS, TX, TW, TY>),
+    hipLaunchKernelGGL((spec_verify_kernel<D, SV_BUFFERS, SV_THREADS, TX, TW, TY, TS>),
                        dim3((unsigned)((int64_t)a.R * a.Hk)), dim3(SV_THREADS), smem, s,
                        (const TX *)a.x, a.x_ld, (const TX *)a.z, a.z_ld, (const TX *)a.a,
                        (const TX *)a.b, a.gate_ld, (const TW *)a.w, (const TW *)a.gamma,
-                       (TX *)a.pool, a.state, a.qsl, a.slots, a.spec, a.max_tokens, a.has_init,
+                       (TX *)a.pool, (TS *)a.state, a.qsl, a.slots, a.spec, a.max_tokens, a.has_init,
                        a.Hk, a.Hv, a.l2_eps, a.norm_eps, (TY *)a.y, a.o);
     return hipGetLastError();
 }
+template <int D, typename TX, typename TW, typename TY>
+static hipError_t launch_sv_s(const SpecVerifyArgs &a, hipStream_t s) {
+    return a.state_bf16 ? launch_sv_t<D, TX, TW, TY, bf16>(a, s) : launch_sv_t<D, TX, TW, TY, float>(a, s);
+}
 template <int D, typename TX, typename TW>
 static hipError_t launch_sv_y(const SpecVerifyArgs &a, hipStream_t s) {
-    return a.y_bf16 ? launch_sv_t<D, TX, TW, bf16>(a, s) : launch_sv_t<D, TX, TW, float>(a, s);
+    return a.y_bf16 ? launch_sv_s<D, TX, TW, bf16>(a, s) : launch_sv_s<D, TX, TW, float>(a, s);
 }
 template <int D, typename TX>
 static hipError_t launch_sv_w(const SpecVerifyArgs &a, hipStream_t s) {

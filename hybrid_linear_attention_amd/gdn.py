@@ -48,16 +48,16 @@ _SIGS = {
     "gdn_decode_step": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _vp,
                          _vp, _i32, _i32, _vp, _i32, _vp], _i32),
     "gdn_decode_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
-                          _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _f32, _f32, _vp, _i32, _vp,
-                          _vp], _i32),
+                          _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _f32, _vp, _i32,
+                          _vp, _vp], _i32),
     "gdn_spec_verify": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
-                         _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
-                         _f32, _vp, _i32, _vp, _vp], _i32),
+                         _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                         _f32, _f32, _vp, _i32, _vp, _vp], _i32),
     "gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_fused_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
-                           _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp,
-                           _i32, _vp, ctypes.c_size_t, _vp], _i32),
+                           _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
+                           _vp, _i32, _vp, ctypes.c_size_t, _vp], _i32),
     "gdn_prefill_varlen": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                             _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_size_t,
                             _vp], _i32),
@@ -177,7 +177,8 @@ def gdn_decode_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, slo
                      has_initial=None, o=None, l2_eps=1e-6, norm_eps=1e-6, stream=None):
     """One decode step (conv update -> recurrence -> gated norm) in one launch.
     x [R, >=Cqkv], z [R, >=Hv*dv], a, b [R, >=Hv] share one dtype and give their
-    row strides; y [R, Hv*dv]; o optional fp32 [R, Hv, dv]."""
+    row strides; state_pool fp32 or bf16 (its dtype is passed as state_dt);
+    y [R, Hv*dv]; o optional fp32 [R, Hv, dv]."""
     d = dims_c(dims)
     if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
         raise ValueError("x, z, a, b and conv_pool share one dtype; a and b share strides")
@@ -186,14 +187,14 @@ def gdn_decode_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, slo
     for name, t in (("conv_w", conv_w), ("gamma", gamma), ("conv_pool", conv_pool),
                     ("state_pool", state_pool), ("y", y)):
         _contig(t, name)
-    if state_pool.dtype != torch.float32 or (o is not None and o.dtype != torch.float32):
-        raise TypeError("state_pool and o must be float32")
+    if o is not None and o.dtype != torch.float32:
+        raise TypeError("o must be float32")
     zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
     st = lib().gdn_decode_fused(
         ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
         _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
         _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
-        _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"), slot_ids.numel(),
+        _dt(state_pool), _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"), slot_ids.numel(),
         state_pool.shape[0], float(l2_eps), float(norm_eps), _ptr(y, "y"), _dt(y),
         _ptr(o, "o"), _stream(stream))
     _check(st, "gdn_decode_fused")
@@ -213,8 +214,8 @@ def gdn_spec_verify(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, quer
     for name, t in (("conv_w", conv_w), ("gamma", gamma), ("conv_pool", conv_pool),
                     ("state_pool", state_pool), ("y", y), ("spec_slot_ids", spec_slot_ids)):
         _contig(t, name)
-    if state_pool.dtype != torch.float32 or (o is not None and o.dtype != torch.float32):
-        raise TypeError("state_pool and o must be float32")
+    if o is not None and o.dtype != torch.float32:
+        raise TypeError("o must be float32")
     if spec_slot_ids.dim() != 2 or spec_slot_ids.shape[0] != slot_ids.numel():
         raise ValueError("spec_slot_ids must be [num_reqs, max_tokens]")
     zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
@@ -222,7 +223,7 @@ def gdn_spec_verify(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, quer
         ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
         _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
         _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
-        _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"),
+        _dt(state_pool), _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"),
         _ptr(spec_slot_ids, "spec_slot_ids"), spec_slot_ids.shape[1],
         _ptr(has_initial, "has_initial"), slot_ids.numel(), x.shape[0], state_pool.shape[0],
         float(l2_eps), float(norm_eps), _ptr(y, "y"), _dt(y), _ptr(o, "o"), _stream(stream))
@@ -267,7 +268,8 @@ def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, qu
                       slot_ids, has_initial, y, workspace, l2_eps=1e-6, norm_eps=1e-6,
                       stream=None):
     """A whole prefill step (conv update -> recurrence -> gated norm) over a packed
-    batch; x, z, a, b share one dtype and give their row strides; y [T, Hv*dv];
+    batch; x, z, a, b share one dtype and give their row strides; state_pool fp32
+    or bf16; y [T, Hv*dv];
     workspace a uint8 device tensor of gdn_prefill_fused_workspace_bytes(...)."""
     d = dims_c(dims)
     if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
@@ -277,14 +279,12 @@ def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, qu
     for name, t in (("conv_w", conv_w), ("gamma", gamma), ("conv_pool", conv_pool),
                     ("state_pool", state_pool), ("y", y)):
         _contig(t, name)
-    if state_pool.dtype != torch.float32:
-        raise TypeError("state_pool must be float32")
     zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
     st = lib().gdn_prefill_fused(
         ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
         _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
         _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
-        _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"),
+        _dt(state_pool), _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"),
         slot_ids.numel(), x.shape[0], state_pool.shape[0], float(l2_eps), float(norm_eps),
         _ptr(y, "y"), _dt(y), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))

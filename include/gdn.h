@@ -26,7 +26,9 @@
  *  - Value head h reads key head h / (Hv / Hk): contiguous groups, the layout
  *    the page's 4-way tensor-parallel table implies (key heads 0-3 travel with
  *    value heads 0-11).
- *  - Recurrent state is fp32 [num_slots, Hv, d_v, d_k], d_k contiguous.
+ *  - Recurrent state is [num_slots, Hv, d_v, d_k], d_k contiguous, fp32; the
+ *    fused entry points (gdn_decode_fused, gdn_prefill_fused, gdn_spec_verify)
+ *    also take a bf16 state through their state_dt argument.
  *    Conv history is [num_slots, Cqkv, taps-1], oldest -> newest, where
  *    Cqkv = 2*Hk*d_k + Hv*d_v and channels are ordered q | k | v.
  *  - Slots named in one call must be distinct (a duplicate is a data race).
@@ -154,8 +156,11 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k,
  *   a, b       [num_reqs, gate_ld] in act_dt: raw gate projections.
  *   conv_w     [Cqkv, taps] in w_dt; gamma [d_v] in w_dt (gated-norm gain).
  *   conv_pool  [num_slots, Cqkv, taps-1] in act_dt, updated in place.
- *   state_pool [num_slots, Hv, d_v, d_k] fp32, slot slot_ids[r] read once and
- *              written once.
+ *   state_pool [num_slots, Hv, d_v, d_k] in state_dt, slot slot_ids[r] read once
+ *              and written once.  GDN_BF16 is the state-dtype variant (the
+ *              engine's `auto` state dtype may resolve away from float32; same
+ *              data-structure table, state row): each element is widened exactly,
+ *              updated in fp32 and rounded once to nearest-even on store.
  *   has_initial [num_reqs] uint8 (device; NULL = all 1): 0 starts the request
  *              from a zero history and a zero state (its first token).
  *   y          [num_reqs, Hv * d_v] in y_dt: RMSNorm_dv(o) * gamma * SiLU(z).
@@ -168,7 +173,7 @@ gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_l
                             const void *z, int64_t z_ld, const void *a,
                             const void *b, int64_t gate_ld, gdn_dtype act_dt,
                             const void *conv_w, const void *gamma, gdn_dtype w_dt,
-                            void *conv_pool, float *state_pool,
+                            void *conv_pool, void *state_pool, gdn_dtype state_dt,
                             const int32_t *slot_ids, const uint8_t *has_initial,
                             int32_t num_reqs, int32_t num_slots, float l2_eps,
                             float norm_eps, void *y, gdn_dtype y_dt, float *o,
@@ -188,8 +193,9 @@ gdn_status gdn_decode_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_l
  * history in spec_slot_ids[r][j] equal those a prefill of the request's
  * first j + 1 tokens would leave.
  *
- *   x_qkv, z, a, b, conv_w, gamma, l2_eps, norm_eps, y, y_dt, o: as
- *              gdn_decode_fused, with one row per token of the packed batch.
+ *   x_qkv, z, a, b, conv_w, gamma, state_pool, state_dt, l2_eps, norm_eps, y,
+ *              y_dt, o: as gdn_decode_fused, with one row per token of the packed
+ *              batch (a bf16 state is rounded once per written position).
  *   query_start_loc [num_reqs + 1] int32 (device): request r owns tokens
  *              qsl[r] .. qsl[r+1]-1, at most max_tokens of them (a longer
  *              request is cut to its first max_tokens tokens).
@@ -215,7 +221,7 @@ gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld
                            const void *z, int64_t z_ld, const void *a,
                            const void *b, int64_t gate_ld, gdn_dtype act_dt,
                            const void *conv_w, const void *gamma, gdn_dtype w_dt,
-                           void *conv_pool, float *state_pool,
+                           void *conv_pool, void *state_pool, gdn_dtype state_dt,
                            const int32_t *query_start_loc, const int32_t *slot_ids,
                            const int32_t *spec_slot_ids, int32_t max_tokens,
                            const uint8_t *has_initial, int32_t num_reqs,
@@ -269,7 +275,10 @@ gdn_status gdn_prefill_varlen(const gdn_dims *dims, const void *q,
  * gated-output rows), with the intermediate q, k, v and o kept in the
  * workspace.  Arguments follow gdn_decode_fused plus the varlen metadata of
  * gdn_prefill_varlen; has_initial[r] = 0 starts request r from a zero history
- * and a zero state.  y [num_tokens, Hv * d_v] in y_dt.  The workspace (at least
+ * and a zero state.  state_pool in state_dt as gdn_decode_fused (a bf16 state
+ * is widened once on entry and rounded once on exit; at d = 128 it needs x
+ * 16-byte aligned with 16-byte rows, else GDN_ERR_ALIGN).  y [num_tokens, Hv *
+ * d_v] in y_dt.  The workspace (at least
  * gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs) bytes,
  * 256-byte aligned) is scratch owned by the caller; nothing in it outlives the
  * call.  Alignment: x_ld and z_ld even, x, z, gamma and y aligned to two
@@ -281,7 +290,7 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
                              const void *z, int64_t z_ld, const void *a,
                              const void *b, int64_t gate_ld, gdn_dtype act_dt,
                              const void *conv_w, const void *gamma, gdn_dtype w_dt,
-                             void *conv_pool, float *state_pool,
+                             void *conv_pool, void *state_pool, gdn_dtype state_dt,
                              const int32_t *query_start_loc, const int32_t *slot_ids,
                              const uint8_t *has_initial, int32_t num_reqs,
                              int32_t num_tokens, int32_t num_slots, float l2_eps,

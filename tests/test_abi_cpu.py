@@ -132,14 +132,14 @@ def test_norm_and_gemm_reject_bad_args():
 
 def fused_call(d, **kw):
     args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
-                g=FAKE, wdt=1, pool=FAKE, state=FAKE, slots=FAKE, hi=None, R=4, nslots=8,
+                g=FAKE, wdt=1, pool=FAKE, state=FAKE, sdt=0, slots=FAKE, hi=None, R=4, nslots=8,
                 l2=1e-6, ne=1e-6, y=FAKE, ydt=1, o=None)
     args.update(kw)
     return gdn.lib().gdn_decode_fused(
         None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
         args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
-        args["pool"], args["state"], args["slots"], args["hi"], args["R"], args["nslots"],
-        args["l2"], args["ne"], args["y"], args["ydt"], args["o"], None)
+        args["pool"], args["state"], args["sdt"], args["slots"], args["hi"], args["R"],
+        args["nslots"], args["l2"], args["ne"], args["y"], args["ydt"], args["o"], None)
 
 
 def test_decode_fused_rejects_bad_args():
@@ -148,6 +148,8 @@ def test_decode_fused_rejects_bad_args():
     assert fused_call(dims(1, 64, 128, 128, 4)) == 2          # 64 value heads per key head: LDS
     assert fused_call(FULL, act=2) == 3
     assert fused_call(FULL, ydt=7) == 3
+    assert fused_call(FULL, sdt=2) == 3                       # state dtype
+    assert fused_call(FULL, sdt=1, R=0, x=None) == 0          # bf16 state accepted
     assert fused_call(FULL, R=9) == 4                         # more requests than slots
     assert fused_call(FULL, xld=10000) == 4                   # x_ld < Cqkv
     assert fused_call(FULL, zld=6000) == 4
@@ -162,15 +164,15 @@ def test_decode_fused_rejects_bad_args():
 
 def prefill_fused_call(d, **kw):
     args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
-                g=FAKE, wdt=1, pool=FAKE, state=FAKE, qsl=FAKE, slots=FAKE, hi=None, R=2, T=100,
+                g=FAKE, wdt=1, pool=FAKE, state=FAKE, sdt=0, qsl=FAKE, slots=FAKE, hi=None, R=2, T=100,
                 nslots=8, l2=1e-6, ne=1e-6, y=FAKE, ydt=1, ws=FAKE, wsb=1 << 40)
     args.update(kw)
     return gdn.lib().gdn_prefill_fused(
         None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
         args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
-        args["pool"], args["state"], args["qsl"], args["slots"], args["hi"], args["R"], args["T"],
-        args["nslots"], args["l2"], args["ne"], args["y"], args["ydt"], args["ws"], args["wsb"],
-        None)
+        args["pool"], args["state"], args["sdt"], args["qsl"], args["slots"], args["hi"], args["R"],
+        args["T"], args["nslots"], args["l2"], args["ne"], args["y"], args["ydt"], args["ws"],
+        args["wsb"], None)
 
 
 def test_prefill_fused_rejects_bad_args():
@@ -188,6 +190,8 @@ def test_prefill_fused_rejects_bad_args():
     assert prefill_fused_call(FULL, ws=FAKE + 16) == 6     # workspace not 256-byte aligned
     assert prefill_fused_call(FULL, xld=10241) == 6        # odd row stride
     assert prefill_fused_call(FULL, T=0, R=0, x=None) == 0
+    assert prefill_fused_call(FULL, sdt=4) == 3
+    assert prefill_fused_call(FULL, sdt=1, x=FAKE + 2) == 6   # bf16 state needs 16-byte conv rows
 
 
 def test_workspace_query():
@@ -221,15 +225,15 @@ def test_binding_refuses_cpu_tensors():
 
 def spec_call(d, **kw):
     args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
-                g=FAKE, wdt=1, pool=FAKE, state=FAKE, qsl=FAKE, slots=FAKE, spec=FAKE, maxn=4,
+                g=FAKE, wdt=1, pool=FAKE, state=FAKE, sdt=0, qsl=FAKE, slots=FAKE, spec=FAKE, maxn=4,
                 hi=None, R=4, T=16, nslots=32, l2=1e-6, ne=1e-6, y=FAKE, ydt=1, o=None)
     args.update(kw)
     return gdn.lib().gdn_spec_verify(
         None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
         args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
-        args["pool"], args["state"], args["qsl"], args["slots"], args["spec"], args["maxn"],
-        args["hi"], args["R"], args["T"], args["nslots"], args["l2"], args["ne"], args["y"],
-        args["ydt"], args["o"], None)
+        args["pool"], args["state"], args["sdt"], args["qsl"], args["slots"], args["spec"],
+        args["maxn"], args["hi"], args["R"], args["T"], args["nslots"], args["l2"], args["ne"],
+        args["y"], args["ydt"], args["o"], None)
 
 
 def test_spec_verify_rejects_bad_args():
@@ -243,6 +247,7 @@ def test_spec_verify_rejects_bad_args():
     assert spec_call(FULL, gld=47) == 4
     assert spec_call(FULL, l2=-1.0) == 4
     assert spec_call(FULL, act=5) == 3
+    assert spec_call(FULL, sdt=3) == 3
     assert spec_call(FULL, spec=None) == 1
     assert spec_call(FULL, y=None) == 1
     assert spec_call(FULL, state=FAKE + 4) == 6
