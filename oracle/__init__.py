@@ -10,7 +10,8 @@ two share no code.
 
 Parity status per function (see the oracle tests for the pins):
   conv1d_silu, l2norm, gates, gated_delta_rule, decode_step, gated_norm,
-  rmsnorm, linear, residual_add, gdn_layer, spec_verify, round_bf16 — pinned (closed forms, brute force,
+  rmsnorm, linear, residual_add, gdn_layer, spec_verify, round_bf16,
+  prefill_snapshots — pinned (closed forms, brute force,
   library reductions, worked examples printed on the pages).
   Absolute output values for the full-size workloads are not printed anywhere
   on the pages; beyond the pins they are parity-unpinned by construction.
@@ -26,6 +27,7 @@ from .oracle import (  # noqa: F401
     l2norm,
     linear,
     num_threads,
+    prefill_snapshots,
     residual_add,
     rmsnorm,
     round_bf16,

@@ -364,6 +364,72 @@ def spec_verify(x_qkv, z, a, b, conv_w, gamma, hist_pool, state_pool, qsl, slot_
     return y, o, new_hist, new_state
 
 
+def prefill_snapshots(x_qkv, z, a, b, conv_w, gamma, hist_pool, state_pool, qsl, slot_ids,
+                      has_initial, snap_slots, interval, Hk, Hv, dk, dv, l2_eps, norm_eps):
+    """A prefill that also keeps prefix-cache snapshots ("align" mode).
+
+    The dispatch page shows the hybrid model refusing prefix caching in mode
+    'all' and asking for '--mamba-cache-mode=align' instead; the pages say no
+    more.  Reading taken: in align mode the prefill keeps, besides the final
+    state, the recurrent state and conv history reached after every
+    `interval` tokens of the call, so that a later request sharing that
+    prefix can start from them.  Snapshot j of request r (for
+    (j + 1) * interval <= its length, and j < snap_slots.shape[1]) is the state
+    and history after its first (j + 1) * interval tokens, written to slot
+    snap_slots[r, j] of both pools.
+
+    Definition used here: each snapshot is a separate prefill of the prefix
+    from the request's input slot (conv1d_silu / gated_delta_rule on the
+    first (j + 1) * interval tokens); the outputs and the final state and
+    history are those of the whole request.
+    Returns (y [T, Hv*dv], o [T, Hv, dv], new_hist_pool, new_state_pool).
+    """
+    x_qkv = _f64(x_qkv)
+    hist_pool = _f64(hist_pool)
+    state_pool = _f64(state_pool)
+    a = _f64(a)
+    b = _f64(b)
+    T = x_qkv.shape[0]
+    slot_ids = np.asarray(slot_ids, np.int64)
+    nreq = slot_ids.size
+    snaps = np.asarray(snap_slots, np.int64).reshape(nreq, -1)
+    max_snaps = snaps.shape[1]
+    qsl = np.asarray(qsl, np.int64)
+    lens = np.diff(qsl)
+    _check_meta(qsl, slot_ids, T, state_pool.shape[0])
+    if interval <= 0:
+        raise ValueError("snapshot interval must be positive")
+    hi = (np.ones(nreq, np.uint8) if has_initial is None
+          else np.asarray(has_initial, np.uint8))
+    nsnap = [int(min(lens[r] // interval, max_snaps)) for r in range(nreq)]
+    written = [int(snaps[r, j]) for r in range(nreq) for j in range(nsnap[r])]
+    if any(s_ < 0 or s_ >= state_pool.shape[0] for s_ in written):
+        raise ValueError("snapshot slot out of range")
+    if len(set(written)) != len(written) or set(written) & set(int(s_) for s_ in slot_ids):
+        raise ValueError("snapshot slots must be distinct from each other and from the requests' slots")
+
+    q, k, v, new_hist = conv1d_update(x_qkv, conv_w, hist_pool, qsl, slot_ids, hi, Hk, Hv, dk,
+                                      dv, l2_eps)
+    o, new_state = gated_delta_rule(q, k, v, a, b, state_pool, qsl, slot_ids, hi)
+    y = gated_norm(o, z, gamma, norm_eps)
+    for j in range(max_snaps):
+        sel = [r for r in range(nreq) if nsnap[r] > j]
+        if not sel:
+            break
+        n = (j + 1) * interval
+        rows = np.concatenate([np.arange(qsl[r], qsl[r] + n) for r in sel])
+        sub_qsl = np.arange(len(sel) + 1) * n
+        sub_slots = np.arange(len(sel))
+        _, hist_j = conv1d_silu(x_qkv[rows], conv_w, hist_pool[slot_ids[sel]], sub_qsl, sub_slots,
+                                hi[sel])
+        _, st_j = gated_delta_rule(q[rows], k[rows], v[rows], a[rows], b[rows],
+                                   state_pool[slot_ids[sel]], sub_qsl, sub_slots, hi[sel])
+        for i, r in enumerate(sel):
+            new_hist[snaps[r, j]] = hist_j[i]
+            new_state[snaps[r, j]] = st_j[i]
+    return y, o, new_hist, new_state
+
+
 # ---------------------------------------------------------------------------
 # one GDN layer block (operator table rows 1-8)
 # ---------------------------------------------------------------------------
