@@ -409,4 +409,39 @@ hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s) {
     }
 }
 
+// Prefix-cache snapshots of the conv history: after the first (j + 1) I tokens
+// of request r the history is that prefix's last three conv inputs (I >= 3, so
+// rows of x only), copied raw into slot snap_slots[r][j].  One block per
+// (request, snapshot), threads over the channels.
+template <typename TX>
+__global__ __launch_bounds__(256) void snapshot_history_kernel(
+    const TX *__restrict__ x, int64_t x_ld, TX *__restrict__ pool, const int32_t *__restrict__ qsl,
+    const int32_t *__restrict__ snap_slots, int32_t interval, int32_t max_snaps, int32_t C) {
+    const int r = blockIdx.x / max_snaps;
+    const int j = blockIdx.x - r * max_snaps;
+    const int t0 = qsl[r];
+    const int L = qsl[r + 1] - t0;
+    const int n = (j + 1) * interval;
+    if (n > L) return;  // no such snapshot
+    TX *hp = pool + (int64_t)snap_slots[(int64_t)r * max_snaps + j] * C * 3;
+    const TX *xr = x + (int64_t)(t0 + n - 3) * x_ld;
+    for (int c = threadIdx.x; c < C; c += 256) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) hp[(int64_t)c * 3 + k] = xr[(int64_t)k * x_ld + c];
+    }
+}
+
+hipError_t launch_snapshot_history(const void *x, int64_t x_ld, bool x_bf16, void *pool,
+                                   const int32_t *qsl, const int32_t *snap_slots, int32_t interval,
+                                   int32_t max_snaps, int32_t nreq, int32_t C, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)nreq * max_snaps));
+    if (x_bf16)
+        hipLaunchKernelGGL(snapshot_history_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)x, x_ld,
+                           (bf16 *)pool, qsl, snap_slots, interval, max_snaps, C);
+    else
+        hipLaunchKernelGGL(snapshot_history_kernel<float>, grid, dim3(256), 0, s, (const float *)x, x_ld,
+                           (float *)pool, qsl, snap_slots, interval, max_snaps, C);
+    return hipGetLastError();
+}
+
 }  // namespace gdn

@@ -259,7 +259,8 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
                              gdn_dtype w_dt, void *conv_pool, void *state_pool,
                              gdn_dtype state_dt, const int32_t *query_start_loc, const int32_t *slot_ids,
                              const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
-                             int32_t num_slots, float l2_eps, float norm_eps, void *y,
+                             int32_t num_slots, const int32_t *snap_slot_ids, int32_t max_snaps,
+                             int32_t snap_interval, float l2_eps, float norm_eps, void *y,
                              gdn_dtype y_dt, void *workspace, size_t workspace_bytes,
                              void *stream) {
     gdn_status st = check_dims(dims);
@@ -275,7 +276,11 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
     if (x_ld < C || z_ld < (int64_t)dims->num_v_heads * D || gate_ld < dims->num_v_heads)
         return GDN_ERR_SHAPE;
     if (!(l2_eps >= 0.0f) || !(norm_eps >= 0.0f)) return GDN_ERR_SHAPE;
+    if (max_snaps < 0 || (max_snaps > 0 && (snap_interval <= 0 || snap_interval % GDN_SNAPSHOT_QUANTUM != 0)))
+        return GDN_ERR_SHAPE;
     if (num_tokens == 0 || num_reqs == 0) return GDN_OK;
+    if (max_snaps > 0 && !snap_slot_ids) return GDN_ERR_NULL;
+    if (max_snaps > 0 && !aligned(snap_slot_ids, 4)) return GDN_ERR_ALIGN;
     if (!x_qkv || !z || !a || !b || !conv_w || !gamma || !conv_pool || !state_pool ||
         !query_start_loc || !slot_ids || !y)
         return GDN_ERR_NULL;
@@ -327,7 +332,15 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
     pa.norm_eps = norm_eps;
     pa.y = y;
     pa.y_bf16 = y_dt == GDN_BF16;
-    return hip_status(gdn::launch_prefill(pa, s));
+    pa.snap_slots = max_snaps > 0 ? snap_slot_ids : nullptr;
+    pa.snap_interval = snap_interval;
+    pa.max_snaps = max_snaps;
+    if (gdn::launch_prefill(pa, s) != hipSuccess) return GDN_ERR_HIP;
+    if (max_snaps > 0)
+        return hip_status(gdn::launch_snapshot_history(x_qkv, x_ld, act_dt == GDN_BF16, conv_pool,
+                                                       query_start_loc, snap_slot_ids, snap_interval,
+                                                       max_snaps, num_reqs, C, s));
+    return GDN_OK;
 }
 
 gdn_status gdn_gated_norm(const gdn_dims *dims, const void *o, gdn_dtype o_dt, const void *z,
@@ -426,6 +439,33 @@ gdn_status gdn_validate_spec_metadata(const int32_t *qsl, const int32_t *slots,
                 const int32_t len2 = qsl[r2 + 1] - qsl[r2];
                 for (int32_t j2 = 0; j2 < len2; ++j2)
                     if ((r2 != r || j2 != j) && spec[(int64_t)r2 * max_tokens + j2] == s)
+                        return GDN_ERR_METADATA;
+            }
+        }
+    }
+    return GDN_OK;
+}
+
+gdn_status gdn_validate_snapshot_metadata(const int32_t *qsl, const int32_t *slots,
+                                          const int32_t *snaps, int32_t max_snaps,
+                                          int32_t snap_interval, int32_t num_reqs,
+                                          int32_t num_tokens, int32_t num_slots) {
+    if (max_snaps < 0 || (max_snaps > 0 && (snap_interval <= 0 || snap_interval % GDN_SNAPSHOT_QUANTUM != 0)))
+        return GDN_ERR_SHAPE;
+    gdn_status st = gdn_validate_metadata(qsl, slots, num_reqs, num_tokens, num_slots);
+    if (st != GDN_OK || max_snaps == 0) return st;
+    if (num_reqs > 0 && !snaps) return GDN_ERR_NULL;
+    // the slots a call writes: snaps[r][j] for (j + 1) * interval <= length of r
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        const int32_t n = (qsl[r + 1] - qsl[r]) / snap_interval;
+        for (int32_t j = 0; j < n && j < max_snaps; ++j) {
+            const int32_t s = snaps[(int64_t)r * max_snaps + j];
+            if (s < 0 || s >= num_slots) return GDN_ERR_METADATA;
+            for (int32_t r2 = 0; r2 < num_reqs; ++r2) {
+                if (slots[r2] == s) return GDN_ERR_METADATA;
+                const int32_t n2 = (qsl[r2 + 1] - qsl[r2]) / snap_interval;
+                for (int32_t j2 = 0; j2 < n2 && j2 < max_snaps; ++j2)
+                    if ((r2 != r || j2 != j) && snaps[(int64_t)r2 * max_snaps + j2] == s)
                         return GDN_ERR_METADATA;
             }
         }

@@ -100,7 +100,13 @@ struct PrefillArgs {
     const void *conv_w = nullptr; bool w_bf16 = false;
     void *pool = nullptr; float l2_eps = 0.f;
     bool state_bf16 = false;  // bf16 state: widened on load, rounded once (RNE) on store
+    // optional prefix-cache snapshots: the state after every snap_interval tokens
+    // (a multiple of 32) of request r goes to slot snap_slots[r * max_snaps + j]
+    const int32_t *snap_slots = nullptr; int32_t snap_interval = 0, max_snaps = 0;
 };
+hipError_t launch_snapshot_history(const void *x, int64_t x_ld, bool x_bf16, void *pool,
+                                   const int32_t *qsl, const int32_t *snap_slots, int32_t interval,
+                                   int32_t max_snaps, int32_t nreq, int32_t C, hipStream_t s);
 size_t prefill_workspace_bytes(int D, int32_t Hk, int32_t Hv, int32_t T, int32_t nreq);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 

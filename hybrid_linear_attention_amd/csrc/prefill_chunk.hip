@@ -731,6 +731,14 @@ struct ChainConvIn {
     int32_t nq;  // Hk * D
 };
 
+// Prefix-cache snapshots taken by the chain: after every `every` full chunks
+// of a request, the state goes to the request's next snapshot slot.
+struct ChainSnap {
+    const int32_t *slots;  // [nreq, max] snapshot slot table, nullptr: none
+    int32_t every;         // chunks between snapshots
+    int32_t max;           // snapshots per request at most
+};
+
 // v for the tokens a lane holds in the accumulator layout, 16 tau + 4 lg + e
 // of a chunk: either four scalar loads per tau from v [T, Hv, D] (VIMG false),
 // or one 16-byte load per tau from the chunk's V image (VIMG true; the prep
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
-    int32_t Hv, TO *__restrict__ o, ChainConvIn cv) {
+    int32_t Hv, TO *__restrict__ o, ChainConvIn cv, ChainSnap snap) {
     using namespace chunk;
     constexpr int IB = 16 * NW;  // state rows per block
     constexpr int NRB = D / IB;  // blocks per (request, head)
@@ -999,6 +1007,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
                     store_o<TO>(orr, (uint32_t)(t * Hv * D + irow), OQ[tau][e] * inv_sqrt_d);
                 }
         }
+        // prefix-cache snapshot after this chunk (full chunks only)
+        if (snap.slots != nullptr && (cc + 1) % snap.every == 0 && (cc + 1) * CH <= L &&
+            (cc + 1) / snap.every <= snap.max) {
+            TS *sp = state + ((int64_t)snap.slots[(int64_t)r * snap.max + (cc + 1) / snap.every - 1] * Hv + h) * D * D;
+#pragma unroll
+            for (int jt = 0; jt < 8; ++jt)
+                st4(sp + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
+        }
         if (STAGES == 1) {
             __syncthreads();  // every wave is done reading the stage
             if (cc + 1 < nch) {
@@ -1040,7 +1056,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
-    int32_t Hv, TO *__restrict__ o, ChainConvIn cv) {
+    int32_t Hv, TO *__restrict__ o, ChainConvIn cv, ChainSnap snap) {
     using namespace chunk;
     constexpr int WPH = GRP_ROWS / (16 * GRP_RPW);  // waves per head
     constexpr int NW = G * WPH;
@@ -1245,6 +1261,17 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
                         store_o<TO>(orr, (uint32_t)(t * Hv * D + irow[rt]), OQ[rt][tau][e] * inv_sqrt_d);
                     }
         }
+        // prefix-cache snapshot after this chunk (full chunks only)
+        if (snap.slots != nullptr && (cc + 1) % snap.every == 0 && (cc + 1) * CH <= L &&
+            (cc + 1) / snap.every <= snap.max) {
+            TS *sp = state + ((int64_t)snap.slots[(int64_t)r * snap.max + (cc + 1) / snap.every - 1] * Hv + h) * D * D;
+#pragma unroll
+            for (int rt = 0; rt < GRP_RPW; ++rt)
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt)
+                    st4(sp + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
+                        make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
+        }
         if (STAGES == 1) {
             __syncthreads();
             if (cc + 1 < nch) {
@@ -1309,7 +1336,7 @@ static hipError_t set_smem(K kern, size_t bytes, bool &done) {
 template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
-                               const ChainConvIn &cv) {
+                               const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
     static bool set = false;
     const size_t smem = STAGES * STAGE;
@@ -1320,14 +1347,14 @@ static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
     hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS>), dim3((unsigned)blocks),
                        dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
-                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv);
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
     return hipGetLastError();
 }
 
 template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                      const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
-                                     const ChainConvIn &cv) {
+                                     const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
     constexpr int NW = G * (GRP_ROWS / (16 * GRP_RPW));
     static bool set = false;
@@ -1338,7 +1365,7 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
     const int64_t blocks = 8 * (int64_t)(D / GRP_ROWS) * ((groups + 7) / 8);
     hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>), dim3((unsigned)blocks),
                        dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
-                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv);
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
     return hipGetLastError();
 }
 
@@ -1349,12 +1376,12 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
 template <typename TA, typename TO, bool VIMG, typename TX, typename TS>
 static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                    const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
-                                   const ChainConvIn &cv) {
+                                   const ChainConvIn &cv, const ChainSnap &sn) {
     const int64_t units = (int64_t)a.nreq * a.Hv;
     if (units >= 256 && a.Hv == 3 * a.Hk)
-        return launch_chain_group<3, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv);
-    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv)
-                        : launch_chain<2, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv);
+        return launch_chain_group<3, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
+    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn)
+                        : launch_chain<2, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
 }
 
 template <typename TA, typename TG, typename TX, typename TW, bool CONV>
@@ -1388,6 +1415,8 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
 
     const PrepConvIn cv{a.x, a.x_ld, a.conv_w, a.pool, a.slots, a.has_init,
                         2 * a.Hk * D + a.Hv * D, a.l2_eps};
+    const ChainSnap sn{a.max_snaps > 0 ? a.snap_slots : nullptr, a.max_snaps > 0 ? a.snap_interval / CH : 1,
+                       a.max_snaps};
     if (a.x) {
         // conv mode: the prep kernel forms q and k (into the K images) and v
         // (into V images at a.v, one per chunk and value head) from x; the chain
@@ -1402,11 +1431,11 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
         const ChainConvIn ci{a.x, a.x_ld, a.pool, 2 * a.Hk * D + a.Hv * D, a.Hk * D};
         if constexpr (std::is_same<TO, float>::value) {
             if (a.state_bf16)
-                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, bf16>(a, s, chunk_off, order, kimg, timg, ci)
-                             : launch_chain_any<float, float, true, float, bf16>(a, s, chunk_off, order, kimg, timg, ci);
+                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn)
+                             : launch_chain_any<float, float, true, float, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn);
             else
-                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, float>(a, s, chunk_off, order, kimg, timg, ci)
-                             : launch_chain_any<float, float, true, float, float>(a, s, chunk_off, order, kimg, timg, ci);
+                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, float>(a, s, chunk_off, order, kimg, timg, ci, sn)
+                             : launch_chain_any<float, float, true, float, float>(a, s, chunk_off, order, kimg, timg, ci, sn);
         } else {
             return hipErrorInvalidValue;
         }
@@ -1414,7 +1443,7 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
         e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv, nullptr);
         if (e != hipSuccess) return e;
         if (a.state_bf16) return hipErrorInvalidValue;  // the unfused prefill keeps an fp32 state
-        e = launch_chain_any<TA, TO, false, float, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{});
+        e = launch_chain_any<TA, TO, false, float, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{}, sn);
     }
     if (e != hipSuccess || !a.y) return e;
     // gated output: a separate HBM-streaming pass over o (folding it into the

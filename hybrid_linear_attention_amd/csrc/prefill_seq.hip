@@ -21,7 +21,8 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
     const TG *__restrict__ ga, const TG *__restrict__ gb, int64_t gate_ld,
     TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init, int32_t nreq,
-    int32_t Hk, int32_t Hv, TO *__restrict__ o) {
+    int32_t Hk, int32_t Hv, TO *__restrict__ o, const int32_t *__restrict__ snap_slots,
+    int32_t snap_interval, int32_t max_snaps) {
     constexpr int LPR = D / 16;
     constexpr int RPT = 4;
     constexpr int RG = D / RPT;                   // row groups per unit
@@ -92,6 +93,16 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
             }
             if (l == 0) st(o + ((int64_t)t * Hv + h) * D + i, (alpha * pq + be * kq) * inv_sqrt_d);
         }
+        // prefix-cache snapshot after every snap_interval tokens of the request
+        const int done = t - t0 + 1;
+        if (snap_slots != nullptr && done % snap_interval == 0 && done / snap_interval <= max_snaps) {
+            TS *snp = state + ((int64_t)snap_slots[(int64_t)r * max_snaps + done / snap_interval - 1] * Hv + h) * D * D;
+#pragma unroll
+            for (int p = 0; p < RPT; ++p)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    st4(snp + (int64_t)(rg + p * RG) * D + 4 * l + 4 * LPR * m, s[p][m]);
+        }
     }
 #pragma unroll
     for (int p = 0; p < RPT; ++p) {
@@ -109,7 +120,9 @@ static hipError_t launch_seq_t(const PrefillArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((prefill_seq_kernel<D, TA, TG, TO, TS>), dim3((unsigned)((units + UPB - 1) / UPB)),
                        dim3(256), 0, s, (const TA *)a.q, (const TA *)a.k, (const TA *)a.v,
                        (const TG *)a.a, (const TG *)a.b, a.gate_ld, (TS *)a.state, a.qsl, a.slots,
-                       a.has_init, a.nreq, a.Hk, a.Hv, (TO *)a.o);
+                       a.has_init, a.nreq, a.Hk, a.Hv, (TO *)a.o,
+                       a.max_snaps > 0 ? a.snap_slots : nullptr, a.max_snaps > 0 ? a.snap_interval : 1,
+                       a.max_snaps);
     return hipGetLastError();
 }
 template <int D, typename TA, typename TG, typename TO>

@@ -56,8 +56,8 @@ _SIGS = {
     "gdn_prefill_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_fused_workspace_bytes": ([ctypes.POINTER(GdnDimsC), _i32, _i32], ctypes.c_size_t),
     "gdn_prefill_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
-                           _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32,
-                           _vp, _i32, _vp, ctypes.c_size_t, _vp], _i32),
+                           _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32,
+                           _i32, _f32, _f32, _vp, _i32, _vp, ctypes.c_size_t, _vp], _i32),
     "gdn_prefill_varlen": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                             _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_size_t,
                             _vp], _i32),
@@ -67,6 +67,7 @@ _SIGS = {
     "gdn_gemm_bf16": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _i32, _vp], _i32),
     "gdn_validate_metadata": ([_vp, _vp, _i32, _i32, _i32], _i32),
     "gdn_validate_spec_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32], _i32),
+    "gdn_validate_snapshot_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _i32),
 }
 
 SPEC_MAX_TOKENS = 8
@@ -266,11 +267,13 @@ def gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs):
 
 def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, query_start_loc,
                       slot_ids, has_initial, y, workspace, l2_eps=1e-6, norm_eps=1e-6,
-                      stream=None):
+                      snap_slot_ids=None, snap_interval=0, stream=None):
     """A whole prefill step (conv update -> recurrence -> gated norm) over a packed
     batch; x, z, a, b share one dtype and give their row strides; state_pool fp32
     or bf16; y [T, Hv*dv];
-    workspace a uint8 device tensor of gdn_prefill_fused_workspace_bytes(...)."""
+    workspace a uint8 device tensor of gdn_prefill_fused_workspace_bytes(...);
+    snap_slot_ids int32 [R, max_snaps] with snap_interval (tokens, a multiple of
+    32) keeps prefix-cache snapshots."""
     d = dims_c(dims)
     if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
         raise ValueError("x, z, a, b and conv_pool share one dtype; a and b share strides")
@@ -280,12 +283,19 @@ def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, qu
                     ("state_pool", state_pool), ("y", y)):
         _contig(t, name)
     zz = z.reshape(z.shape[0], -1) if z.is_contiguous() else z
+    max_snaps = 0
+    if snap_slot_ids is not None:
+        _contig(snap_slot_ids, "snap_slot_ids")
+        if snap_slot_ids.dim() != 2 or snap_slot_ids.shape[0] != slot_ids.numel():
+            raise ValueError("snap_slot_ids must be [num_reqs, max_snaps]")
+        max_snaps = snap_slot_ids.shape[1]
     st = lib().gdn_prefill_fused(
         ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
         _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
         _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
         _dt(state_pool), _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"),
-        slot_ids.numel(), x.shape[0], state_pool.shape[0], float(l2_eps), float(norm_eps),
+        slot_ids.numel(), x.shape[0], state_pool.shape[0], _ptr(snap_slot_ids, "snap_slot_ids"),
+        max_snaps, int(snap_interval), float(l2_eps), float(norm_eps),
         _ptr(y, "y"), _dt(y), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_prefill_fused")
@@ -348,3 +358,15 @@ def gdn_validate_spec_metadata(query_start_loc, slot_ids, spec_slot_ids, num_tok
     return int(lib().gdn_validate_spec_metadata(
         qsl.data_ptr(), sl.data_ptr() if sl.numel() else None, sp.data_ptr() if sp.numel() else None,
         sp.shape[1] if sp.dim() == 2 else 0, sl.numel(), int(num_tokens), int(num_slots)))
+
+
+def gdn_validate_snapshot_metadata(query_start_loc, slot_ids, snap_slot_ids, snap_interval,
+                                   num_tokens, num_slots):
+    """Host-side check of host (CPU) int32 copies of the snapshot metadata."""
+    qsl = query_start_loc.cpu().to(torch.int32).contiguous()
+    sl = slot_ids.cpu().to(torch.int32).contiguous()
+    sp = snap_slot_ids.cpu().to(torch.int32).contiguous()
+    return int(lib().gdn_validate_snapshot_metadata(
+        qsl.data_ptr(), sl.data_ptr() if sl.numel() else None, sp.data_ptr() if sp.numel() else None,
+        sp.shape[1] if sp.dim() == 2 else 0, int(snap_interval), sl.numel(), int(num_tokens),
+        int(num_slots)))

@@ -278,12 +278,24 @@ gdn_status gdn_prefill_varlen(const gdn_dims *dims, const void *q,
  * and a zero state.  state_pool in state_dt as gdn_decode_fused (a bf16 state
  * is widened once on entry and rounded once on exit; at d = 128 it needs x
  * 16-byte aligned with 16-byte rows, else GDN_ERR_ALIGN).  y [num_tokens, Hv *
- * d_v] in y_dt.  The workspace (at least
+ * d_v] in y_dt.
+ *   Prefix-cache snapshots ("align" mode; the dispatch page shows the hybrid
+ *   model asking for --mamba-cache-mode=align): with max_snaps > 0, after the
+ *   first (j + 1) * snap_interval tokens of request r (for every such prefix
+ *   within the request, j < max_snaps) its state and conv history are also
+ *   written to slot snap_slot_ids[r * max_snaps + j] (int32 device table
+ *   [num_reqs, max_snaps]), exactly as a prefill of that prefix alone would
+ *   leave them; the request's own slot still receives the final state.
+ *   snap_interval is a positive multiple of GDN_SNAPSHOT_QUANTUM (the prefill's
+ *   chunk), else GDN_ERR_SHAPE; snapshot slots must be distinct and distinct
+ *   from every request's slot (gdn_validate_snapshot_metadata).  max_snaps = 0
+ *   (snap_slot_ids may be NULL) takes none.  The workspace (at least
  * gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs) bytes,
  * 256-byte aligned) is scratch owned by the caller; nothing in it outlives the
  * call.  Alignment: x_ld and z_ld even, x, z, gamma and y aligned to two
  * elements, state_pool 16-byte aligned.
  */
+#define GDN_SNAPSHOT_QUANTUM 32
 size_t gdn_prefill_fused_workspace_bytes(const gdn_dims *dims, int32_t num_tokens,
                                          int32_t num_reqs);
 gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld,
@@ -293,8 +305,10 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
                              void *conv_pool, void *state_pool, gdn_dtype state_dt,
                              const int32_t *query_start_loc, const int32_t *slot_ids,
                              const uint8_t *has_initial, int32_t num_reqs,
-                             int32_t num_tokens, int32_t num_slots, float l2_eps,
-                             float norm_eps, void *y, gdn_dtype y_dt, void *workspace,
+                             int32_t num_tokens, int32_t num_slots,
+                             const int32_t *snap_slot_ids, int32_t max_snaps,
+                             int32_t snap_interval, float l2_eps, float norm_eps,
+                             void *y, gdn_dtype y_dt, void *workspace,
                              size_t workspace_bytes, void *stream);
 
 /*
@@ -359,6 +373,21 @@ gdn_status gdn_validate_metadata(const int32_t *query_start_loc_host,
  * requests' input slots (spec_slot_ids[r][0] == slot_ids[r] is allowed).
  * Enqueues nothing; GDN_ERR_METADATA on violation.
  */
+/*
+ * gdn_validate_snapshot_metadata — HOST-side check of host copies of
+ * gdn_prefill_fused's snapshot metadata: everything gdn_validate_metadata
+ * checks, snap_interval a positive multiple of GDN_SNAPSHOT_QUANTUM, and the
+ * slots a call writes (snap[r][j] for (j + 1) * snap_interval within request
+ * r, j < max_snaps) in range, distinct, and distinct from every request's
+ * slot.  Enqueues nothing; GDN_ERR_METADATA on violation.
+ */
+gdn_status gdn_validate_snapshot_metadata(const int32_t *query_start_loc_host,
+                                          const int32_t *slot_ids_host,
+                                          const int32_t *snap_slot_ids_host,
+                                          int32_t max_snaps, int32_t snap_interval,
+                                          int32_t num_reqs, int32_t num_tokens,
+                                          int32_t num_slots);
+
 gdn_status gdn_validate_spec_metadata(const int32_t *query_start_loc_host,
                                       const int32_t *slot_ids_host,
                                       const int32_t *spec_slot_ids_host,

@@ -165,14 +165,15 @@ def test_decode_fused_rejects_bad_args():
 def prefill_fused_call(d, **kw):
     args = dict(x=FAKE, xld=10240, z=FAKE, zld=6144, a=FAKE, b=FAKE, gld=48, act=1, w=FAKE,
                 g=FAKE, wdt=1, pool=FAKE, state=FAKE, sdt=0, qsl=FAKE, slots=FAKE, hi=None, R=2, T=100,
-                nslots=8, l2=1e-6, ne=1e-6, y=FAKE, ydt=1, ws=FAKE, wsb=1 << 40)
+                nslots=8, snaps=None, nsnap=0, sint=0, l2=1e-6, ne=1e-6, y=FAKE, ydt=1, ws=FAKE,
+                wsb=1 << 40)
     args.update(kw)
     return gdn.lib().gdn_prefill_fused(
         None if d is None else ctypes.byref(d), args["x"], args["xld"], args["z"], args["zld"],
         args["a"], args["b"], args["gld"], args["act"], args["w"], args["g"], args["wdt"],
         args["pool"], args["state"], args["sdt"], args["qsl"], args["slots"], args["hi"], args["R"],
-        args["T"], args["nslots"], args["l2"], args["ne"], args["y"], args["ydt"], args["ws"],
-        args["wsb"], None)
+        args["T"], args["nslots"], args["snaps"], args["nsnap"], args["sint"], args["l2"], args["ne"],
+        args["y"], args["ydt"], args["ws"], args["wsb"], None)
 
 
 def test_prefill_fused_rejects_bad_args():
@@ -191,6 +192,11 @@ def test_prefill_fused_rejects_bad_args():
     assert prefill_fused_call(FULL, xld=10241) == 6        # odd row stride
     assert prefill_fused_call(FULL, T=0, R=0, x=None) == 0
     assert prefill_fused_call(FULL, sdt=4) == 3
+    assert prefill_fused_call(FULL, nsnap=2, sint=48, snaps=FAKE) == 4   # not a multiple of 32
+    assert prefill_fused_call(FULL, nsnap=2, sint=0, snaps=FAKE) == 4
+    assert prefill_fused_call(FULL, nsnap=-1) == 4
+    assert prefill_fused_call(FULL, nsnap=2, sint=64, snaps=None) == 1
+    assert prefill_fused_call(FULL, nsnap=2, sint=64, snaps=FAKE + 2) == 6
     assert prefill_fused_call(FULL, sdt=1, x=FAKE + 2) == 6   # bf16 state needs 16-byte conv rows
 
 
@@ -270,3 +276,17 @@ def test_validate_spec_metadata_host():
     assert v(qsl, slots, [[10, 11, 16], [13, -1, -1], [14, 15, -1]], 6, 16) == 8  # out of range
     assert v([0, 4, 4, 6], slots, [[10, 11, 12], [13, -1, -1], [14, 15, -1]], 6, 16) == 8  # too long
     assert v(qsl, [0, 1, 1], spec, 6, 16) == 8                                    # input slots repeat
+
+
+def test_validate_snapshot_metadata_host():
+    def v(qsl, slots, snaps, interval, T, nslots):
+        return gdn.gdn_validate_snapshot_metadata(torch.tensor(qsl), torch.tensor(slots),
+                                                  torch.tensor(snaps), interval, T, nslots)
+    qsl, slots = [0, 70, 100, 200], [0, 1, 2]
+    snaps = [[5, 6, -1], [-1, -1, -1], [7, 8, 9]]   # 70 -> 2 snapshots, 30 -> 0, 100 -> 3
+    assert v(qsl, slots, snaps, 32, 200, 16) == 0
+    assert v(qsl, slots, [[5, 5, -1], [-1, -1, -1], [7, 8, 9]], 32, 200, 16) == 8   # repeated
+    assert v(qsl, slots, [[5, 6, -1], [-1, -1, -1], [7, 8, 2]], 32, 200, 16) == 8   # a request's slot
+    assert v(qsl, slots, [[5, 16, -1], [-1, -1, -1], [7, 8, 9]], 32, 200, 16) == 8  # out of range
+    assert v(qsl, slots, snaps, 48, 200, 16) == 4                                   # interval
+    assert v(qsl, slots, [[5, 6, 6], [-1, -1, -1], [7, 8, 9]], 32, 200, 16) == 0    # unread entry
