@@ -284,6 +284,10 @@ def main():
         for name, make in legs:
             c = make()
             pre[name] = bench_prefill(c, args.prefill_steps, dev, stream, torch, gdn, np)
+            if name == "prefill_varlen16":
+                # the same step keeping a prefix-cache snapshot every 512 tokens
+                pre[name]["with_snapshots"] = bench_prefill(c, args.prefill_steps, dev, stream,
+                                                            torch, gdn, np, snap_interval=512)
             del c
             torch.cuda.empty_cache()
         result["prefill"] = pre
@@ -404,14 +408,30 @@ def fused_prefill_bytes(d, T, nreq, n_init, act_bytes=2, y_bytes=2):
     return per_tok * T + state * (nreq + n_init) + hist * nreq
 
 
-def bench_prefill(c, steps, dev, stream, torch, gdn, np):
+def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0):
     """One prefill step (gdn_prefill_fused: conv update -> recurrence -> gated
     norm) over one packed batch.  State and history are re-seeded from device
-    copies before every step, outside the timed events."""
+    copies before every step, outside the timed events.  With snap_interval,
+    the step also keeps a prefix-cache snapshot every snap_interval tokens, in
+    slots appended to the pools."""
     d = c.dims
     T = c.num_tokens
     x, conv_w = c.x_qkv.to(dev), c.conv_w.to(dev)
-    pool0, state0 = c.conv_pool.to(dev), c.state_pool.to(dev)
+    snaps, nsnap = None, 0
+    if snap_interval:
+        lens = np.diff(c.qsl.numpy())
+        max_snaps = int(lens.max() // snap_interval)
+        nsnap = int(sum(min(L // snap_interval, max_snaps) for L in lens))
+        base = c.num_slots
+        snaps = (base + torch.arange(c.num_reqs * max_snaps, dtype=torch.int32)).reshape(
+            c.num_reqs, max_snaps).to(dev)
+        extra = c.num_reqs * max_snaps
+        pool0 = torch.cat([c.conv_pool, torch.zeros((extra,) + tuple(c.conv_pool.shape[1:]),
+                                                    dtype=c.conv_pool.dtype)]).to(dev)
+        state0 = torch.cat([c.state_pool, torch.zeros((extra,) + tuple(c.state_pool.shape[1:]),
+                                                      dtype=c.state_pool.dtype)]).to(dev)
+    else:
+        pool0, state0 = c.conv_pool.to(dev), c.state_pool.to(dev)
     pool, state = pool0.clone(), state0.clone()
     qsl, slots, hinit = c.qsl.to(dev), c.slot_ids.to(dev), c.has_initial.to(dev)
     a, b, z, gamma = c.a.to(dev), c.b.to(dev), c.z.to(dev), c.gamma.to(dev)
@@ -426,12 +446,16 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         gdn.gdn_prefill_fused(d, x, z, a, b, conv_w, gamma, pool, state, qsl, slots, hinit, y, ws,
-                              l2_eps=L2_EPS, norm_eps=NORM_EPS, stream=sh)
+                              l2_eps=L2_EPS, norm_eps=NORM_EPS, snap_slot_ids=snaps,
+                              snap_interval=snap_interval, stream=sh)
         e1.record(stream)
         torch.cuda.synchronize()
         if it > 0:  # first pass is warm-up
             times.append(e0.elapsed_time(e1))
     ms = float(np.median(times))
+    if snap_interval:
+        return {"snap_interval": snap_interval, "snapshots": nsnap, "ms_per_step": round(ms, 4),
+                "tokens_per_s": round(T / (ms * 1e-3), 1)}
     flops = prefill_flops(d, T)
     nbytes = fused_prefill_bytes(d, T, c.num_reqs, int(c.has_initial.sum()))
     tflops = flops / (ms * 1e-3) / 1e12
