@@ -146,19 +146,26 @@ template <> struct Raw1<bf16> {
     __device__ __forceinline__ float get() const { return __uint_as_float(uint32_t(v) << 16); }
 };
 
-// One 16-byte direct-to-LDS copy per lane: lane l's bytes land at dst + 16 l.
-// Issued as inline assembly (LDS base in M0) rather than through the builtin:
-// the compiler cannot tell the two ring stages apart, so after a builtin copy
-// into the next stage it waits for every outstanding load before any LDS read
-// of the current stage, which stalls each chunk mid-way on the next chunk's
-// copies.  Here the copies are invisible to its wait analysis and the chain
-// waits for them itself, once per chunk, before the barrier that publishes
-// the stage (vector-memory counts complete in order, so the compiler's own
-// waits for other loads stay correct, only more conservative).
-__device__ __forceinline__ void copy_frag(const uint8_t *src_frag, uint8_t *dst_frag, int lane) {
-    const auto lds = (__attribute__((address_space(3))) uint8_t *)(dst_frag);
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src_frag + 16 * lane), "{m0}"(m0) : "memory");
+// One 16-byte direct-to-LDS copy per lane: lane l's bytes land at LDS address
+// lds_frag + 16 l.  Issued as inline assembly (LDS base in M0, the fragment's
+// global address in scalar registers, the lane's byte offset 16 l in a vector
+// register) rather than through the compiler builtin: the compiler cannot tell
+// the two ring stages apart, so after a builtin copy into the next stage it
+// waits for every outstanding load before any LDS read of the current stage,
+// which stalls each chunk mid-way on the next chunk's copies; and the builtin
+// forms each address in vector registers and moves it to M0 through a
+// readfirstlane, eight instructions per copy.  Here the copies are invisible to
+// the compiler's wait analysis and the chain waits for them itself, once per
+// chunk, before the barrier that publishes the stage (vector-memory counts
+// complete in order, so the compiler's own waits for other loads stay correct,
+// only more conservative).  src_frag and lds_frag must be wave-uniform.
+__device__ __forceinline__ void copy_frag(const uint8_t *src_frag, uint32_t lds_frag, uint32_t lane_off) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(src_frag), "{m0}"(lds_frag) : "memory");
+}
+
+// The wave-uniform LDS address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)(p));
 }
 
 // A buffer resource over [base, base + bytes) from wave-uniform values.
@@ -811,7 +818,7 @@ __device__ __forceinline__ void chain_write_history(const ChainConvIn &cv, int c
 // stall on a full memory queue in one burst.
 constexpr int NPART = 4;
 template <int NW>
-__device__ __forceinline__ void issue_images(uint8_t *stage, const uint8_t *kim, const uint8_t *tim,
+__device__ __forceinline__ void issue_images(uint32_t stage, const uint8_t *kim, const uint8_t *tim,
                                              int w, int lane, int part) {
     using namespace chunk;
     constexpr int NFRAG = KIMG_FRAGS + TIMG_FRAGS;
@@ -821,13 +828,17 @@ __device__ __forceinline__ void issue_images(uint8_t *stage, const uint8_t *kim,
         const int f = w + NW * m;
         if (f < NFRAG) {
             const uint8_t *src = f < KIMG_FRAGS ? kim + (size_t)f * FRAG : tim + (size_t)(f - KIMG_FRAGS) * FRAG;
-            copy_frag(src, stage + (size_t)f * FRAG, lane);
+            copy_frag(src, stage + (uint32_t)f * FRAG, 16u * lane);
         }
     }
 }
 
-template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
-__global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
+// NCW extra waves only copy the images (STAGES == 2): a wave issues
+// direct-to-LDS copies at a limited rate, so a block of few compute waves
+// spends more time issuing a chunk's copies than computing it unless other
+// waves share that work.
+template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS, int NCW>
+__global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
@@ -837,7 +848,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     constexpr int IB = 16 * NW;  // state rows per block
     constexpr int NRB = D / IB;  // blocks per (request, head)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds0 = lds_addr(smem);
     const int lr = lane & 15, lg = lane >> 4;
 
     const int group = Hv / Hk;
@@ -857,6 +869,30 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const int nch = (L + CH - 1) / CH;
     const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
+    const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
+    const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
+    const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
+    if constexpr (NCW > 0) {
+        static_assert(STAGES == 2, "copy waves fill the two-stage ring");
+        if (w >= NW) {
+            // copy wave: chunk cc + 1's images go into the free stage while the
+            // compute waves work on chunk cc; one barrier per chunk, as theirs
+            const int cw = w - NW;
+#pragma unroll
+            for (int part = 0; part < NPART; ++part) issue_images<NCW>(lds0, kim0, tim0, cw, lane, part);
+            for (int cc = 0; cc < nch; ++cc) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (cc + 1 < nch) {
+                    const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * (uint32_t)STAGE;
+#pragma unroll
+                    for (int part = 0; part < NPART; ++part)
+                        issue_images<NCW>(nstg, kim0 + (cc + 1) * kstep, tim0 + (cc + 1) * tstep, cw, lane, part);
+                }
+            }
+            return;
+        }
+    }
     const int irow = IB * rb + 16 * w + lr;  // this lane's state row (value channel)
     const int irows[1] = {irow};
     const int slot = slots[r];
@@ -875,16 +911,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-    const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
-    const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
-    const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
-
     // v of this lane's row for tokens 16 tau + 4 lg + e of chunk cc
     ChainVLoads<1, VIMG, TA> vr;
     auto load_v = [&](int cc) { vr.load(v, irows, h, Hv, tok0 + cc * CH, c_first + cc, min(CH, L - cc * CH), lane); };
 
+    if constexpr (NCW == 0) {
 #pragma unroll
-    for (int part = 0; part < NPART; ++part) issue_images<NW>(smem, kim0, tim0, w, lane, part);
+        for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, kim0, tim0, w, lane, part);
+    }
     load_v(0);
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
@@ -893,8 +927,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
         const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * STAGE : 0);
-        uint8_t *nstg = smem + (size_t)((cc + 1) & 1) * STAGE;
-        const bool prefetch = STAGES == 2 && cc + 1 < nch;
+        const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * (uint32_t)STAGE;
+        const bool more = STAGES == 2 && cc + 1 < nch;   // chunk cc + 1's v loads
+        const bool prefetch = NCW == 0 && more;          // and its copies, by this wave
         const uint8_t *nkim = kim0 + (cc + 1) * kstep, *ntim = tim0 + (cc + 1) * tstep;
         // this wave's copies and loads of chunk cc have landed (issued before the
         // previous chunk's 8 o stores, which may stay in flight); after the
@@ -937,7 +972,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
                 mma3(OQ[tau], qh_, ql_, sbh, sbl);
             }
         }
-        if (prefetch) load_v(cc + 1);
+        if (more) load_v(cc + 1);
         // per-token gamma, e^{G_C - G_t}, beta for this lane's tokens
         const uint8_t *tvec = stg + KIMG;
         float4 gam[2], rev[2], bet[2];
@@ -1019,7 +1054,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
             __syncthreads();  // every wave is done reading the stage
             if (cc + 1 < nch) {
 #pragma unroll
-                for (int part = 0; part < NPART; ++part) issue_images<NW>(smem, nkim, ntim, w, lane, part);
+                for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, nkim, ntim, w, lane, part);
                 load_v(cc + 1);
             }
         }
@@ -1041,30 +1076,36 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
 
 // ---------------------------------------------------------------------------
 // chain, group variant for large batches: one block per (request, key head,
-// block of 64 state rows) covering all G value heads that read the key head,
-// so the chunk's 48 KiB K image is staged once for G heads; each wave owns 32
-// rows (two 16-row tiles) of one head, so every K / Q / K^T fragment read
-// feeds two row tiles.  Same per-row algebra and operand layout as above.
+// block of 64 state rows) covering the 3 value heads that read the key head,
+// so the chunk's 48 KiB K image is staged once for them.  The 12 row tiles of
+// 16 rows go to 8 waves: four waves hold two tiles of one head (every K / Q /
+// K^T fragment read feeds both) and four hold one, so that with waves dealt
+// to the 4 SIMDs in turn each SIMD carries one of each, 3 tiles (6 waves of
+// two tiles left two SIMDs with twice the work of the others, and the block
+// waited for them at every chunk).  Same per-row algebra and operand layout
+// as above.
 // ---------------------------------------------------------------------------
 constexpr int GRP_ROWS = 64;          // state rows per head per block
-constexpr int GRP_RPW = 2;            // 16-row tiles per wave
+constexpr int GRP_RPW = 2;            // 16-row tiles per wave, at most
+constexpr int GRP_NW = 8;             // waves per block
 constexpr int GRP_MAX_HEADS = 3;      // value heads per key head the variant supports
 
 template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
-__global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_chain_group_kernel(
+__global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
     int32_t Hv, TO *__restrict__ o, ChainConvIn cv, ChainSnap snap) {
     using namespace chunk;
-    constexpr int WPH = GRP_ROWS / (16 * GRP_RPW);  // waves per head
-    constexpr int NW = G * WPH;
+    static_assert(G == 3 && GRP_ROWS == 64 && GRP_RPW == 2, "tile map below is for 3 heads x 4 tiles");
+    constexpr int NW = GRP_NW;
     constexpr int NRB = D / GRP_ROWS;               // row blocks per head
     constexpr int NFRAG = KIMG_FRAGS + G * TIMG_FRAGS;
     constexpr size_t GSTAGE = KIMG + G * TIMG;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds0 = lds_addr(smem);
     const int lr = lane & 15, lg = lane >> 4;
 
     // blocks of one (request, key head) group run on one XCD; longest requests first
@@ -1075,7 +1116,12 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     if (gi >= nreq * Hk) return;
     const int r = order[gi / Hk];
     const int kh = gi % Hk;
-    const int hh = w / WPH;                 // this wave's head within the group
+    // this wave's head within the group, first tile and tile count: waves 0-2
+    // tiles 0-1 of heads 0-2, wave 3 tiles 2-3 of head 0, waves 4-7 tile 2 or 3
+    // of heads 1, 2
+    const int hh = w < 4 ? (w < 3 ? w : 0) : 1 + ((w - 4) >> 1);
+    const int tile0 = w < 4 ? (w < 3 ? 0 : 2) : 2 + ((w - 4) & 1);
+    const int nt = w < 4 ? 2 : 1;
     const int h = kh * G + hh;
     const int tok0 = qsl[r];
     const int L = qsl[r + 1] - tok0;
@@ -1083,9 +1129,11 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     const int nch = (L + CH - 1) / CH;
     const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
+    // a one-tile wave's second tile repeats its first: loads stay in bounds and
+    // every store of it is dropped or skipped
     int irow[GRP_RPW];
 #pragma unroll
-    for (int rt = 0; rt < GRP_RPW; ++rt) irow[rt] = GRP_ROWS * rb + 16 * GRP_RPW * (w % WPH) + 16 * rt + lr;
+    for (int rt = 0; rt < GRP_RPW; ++rt) irow[rt] = GRP_ROWS * rb + 16 * (tile0 + (rt < nt ? rt : 0)) + lr;
     const int slot = slots[r];
     TS *sbase = state + ((int64_t)slot * Hv + h) * D * D;
 
@@ -1110,7 +1158,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     // spread over the previous chunk's MFMA phases instead of stalling the wave
     // on a full memory queue in one burst
     constexpr int PER_WAVE = (NFRAG + NW - 1) / NW;
-    auto issue = [&](uint8_t *stage, int cc, int part) {
+    auto issue = [&](uint32_t stage, int cc, int part) {
         const uint8_t *kim = kim0 + cc * kstep;
         const uint8_t *tim = tim0 + cc * tstep;
 #pragma unroll
@@ -1118,7 +1166,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
             const int f = w + NW * m;
             if (f < NFRAG) {
                 const uint8_t *src = f < KIMG_FRAGS ? kim + (size_t)f * FRAG : tim + (size_t)(f - KIMG_FRAGS) * FRAG;
-                copy_frag(src, stage + (size_t)f * FRAG, lane);
+                copy_frag(src, stage + (uint32_t)f * FRAG, 16u * lane);
             }
         }
     };
@@ -1126,7 +1174,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
     auto load_v = [&](int cc) { vr.load(v, irow, h, Hv, tok0 + cc * CH, c_first + cc, min(CH, L - cc * CH), lane); };
 
 #pragma unroll
-    for (int part = 0; part < NPART; ++part) issue(smem, 0, part);
+    for (int part = 0; part < NPART; ++part) issue(lds0, 0, part);
     load_v(0);
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
@@ -1135,7 +1183,7 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
         const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * GSTAGE : 0);
-        uint8_t *nstg = smem + (size_t)((cc + 1) & 1) * GSTAGE;
+        const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * (uint32_t)GSTAGE;
         const bool prefetch = STAGES == 2 && cc + 1 < nch;
         // as in the per-head chain: the previous chunk's o stores stay in flight
         if (STAGES == 2 && cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * GRP_RPW));
@@ -1176,8 +1224,10 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
                 const bf16x8_t ql_ = frag(kst + (FQ + (2 + tau) * 4 + ks) * FRAG);
 #pragma unroll
                 for (int rt = 0; rt < GRP_RPW; ++rt) {
-                    mma3(X[rt][tau], kh_, kl_, sbh[rt], sbl[rt]);
-                    mma3(OQ[rt][tau], qh_, ql_, sbh[rt], sbl[rt]);
+                    if (rt < nt) {
+                        mma3(X[rt][tau], kh_, kl_, sbh[rt], sbl[rt]);
+                        mma3(OQ[rt][tau], qh_, ql_, sbh[rt], sbl[rt]);
+                    }
                 }
             }
         }
@@ -1216,8 +1266,10 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
             split_vals(ev, ebh, ebl);
             Dl[rt][0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             Dl[rt][1] = Dl[rt][0];
-            mma3(Dl[rt][0], th0, tl0, ebh, ebl);
-            mma3(Dl[rt][1], th1, tl1, ebh, ebl);
+            if (rt < nt) {
+                mma3(Dl[rt][0], th0, tl0, ebh, ebl);
+                mma3(Dl[rt][1], th1, tl1, ebh, ebl);
+            }
         }
         // O = OQ + P Delta and S^T = gamma_C S^T + K^T Delta~
         const float r8[8] = {rev[0].x, rev[0].y, rev[0].z, rev[0].w, rev[1].x, rev[1].y, rev[1].z, rev[1].w};
@@ -1235,8 +1287,10 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
             bf16x8_t dbh, dbl;
             split_vals(dv, dbh, dbl);
             split_vals(dtv, tbh[rt], tbl[rt]);
-            mma3(OQ[rt][0], ph0, pl0, dbh, dbl);
-            mma3(OQ[rt][1], ph1, pl1, dbh, dbl);
+            if (rt < nt) {
+                mma3(OQ[rt][0], ph0, pl0, dbh, dbl);
+                mma3(OQ[rt][1], ph1, pl1, dbh, dbl);
+            }
         }
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
@@ -1244,8 +1298,10 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
             const bf16x8_t ktl = frag(kst + (FKT + 8 + jt) * FRAG);
 #pragma unroll
             for (int rt = 0; rt < GRP_RPW; ++rt) {
-                ST[rt][jt] *= gC;
-                mma3(ST[rt][jt], kth, ktl, tbh[rt], tbl[rt]);
+                if (rt < nt) {
+                    ST[rt][jt] *= gC;
+                    mma3(ST[rt][jt], kth, ktl, tbh[rt], tbl[rt]);
+                }
             }
         }
         {
@@ -1258,7 +1314,11 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * tau + 4 * lg + e;
-                        store_o<TO>(orr, (uint32_t)(t * Hv * D + irow[rt]), OQ[rt][tau][e] * inv_sqrt_d);
+                        // every wave issues the same number of stores (the chunk-top
+                        // wait counts them); a one-tile wave's second tile falls
+                        // outside the resource and is dropped
+                        const uint32_t off = rt < nt ? (uint32_t)(t * Hv * D + irow[rt]) : 0x3FFFFFFFu;
+                        store_o<TO>(orr, off, OQ[rt][tau][e] * inv_sqrt_d);
                     }
         }
         // prefix-cache snapshot after this chunk (full chunks only)
@@ -1267,33 +1327,35 @@ __global__ __launch_bounds__(64 * G * (GRP_ROWS / (16 * GRP_RPW))) void prefill_
             TS *sp = state + ((int64_t)snap.slots[(int64_t)r * snap.max + (cc + 1) / snap.every - 1] * Hv + h) * D * D;
 #pragma unroll
             for (int rt = 0; rt < GRP_RPW; ++rt)
+                if (rt < nt)
 #pragma unroll
-                for (int jt = 0; jt < 8; ++jt)
-                    st4(sp + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
-                        make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
+                    for (int jt = 0; jt < 8; ++jt)
+                        st4(sp + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
+                            make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
         }
         if (STAGES == 1) {
             __syncthreads();
             if (cc + 1 < nch) {
 #pragma unroll
-                for (int part = 0; part < NPART; ++part) issue(smem, cc + 1, part);
+                for (int part = 0; part < NPART; ++part) issue(lds0, cc + 1, part);
                 load_v(cc + 1);
             }
         }
     }
 #pragma unroll
     for (int rt = 0; rt < GRP_RPW; ++rt)
+        if (rt < nt)
 #pragma unroll
-        for (int jt = 0; jt < 8; ++jt)
-            st4(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
-                make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
+            for (int jt = 0; jt < 8; ++jt)
+                st4(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
+                    make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
     if constexpr (VIMG) {
         // new history (the prep kernel has read the old one): this lane's v
         // channels, and the key head's q / k channels from the first row block
         if (lg == 0)
 #pragma unroll
             for (int rt = 0; rt < GRP_RPW; ++rt)
-                chain_write_history<TX>(cv, 2 * cv.nq + h * D + irow[rt], slot, hi_init, tok0, L);
+                if (rt < nt) chain_write_history<TX>(cv, 2 * cv.nq + h * D + irow[rt], slot, hi_init, tok0, L);
         if (rb == 0)
             for (int j = threadIdx.x; j < 2 * D; j += 64 * NW)
                 chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
@@ -1333,20 +1395,20 @@ static hipError_t set_smem(K kern, size_t bytes, bool &done) {
 
 // TA: the type of v (or float for V images); VIMG: v from the V images the
 // prep kernel wrote, and the chain writes the new conv history (of type TX).
-template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
+template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS, int NCW>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
     static bool set = false;
     const size_t smem = STAGES * STAGE;
-    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
+    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS, NCW>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS>), dim3((unsigned)blocks),
-                       dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS, NCW>), dim3((unsigned)blocks),
+                       dim3(64 * (NW + NCW)), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
     return hipGetLastError();
 }
@@ -1356,7 +1418,7 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
                                      const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                      const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
-    constexpr int NW = G * (GRP_ROWS / (16 * GRP_RPW));
+    constexpr int NW = GRP_NW;
     static bool set = false;
     const size_t smem = STAGES * (KIMG + G * TIMG);
     hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
@@ -1380,8 +1442,8 @@ static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const in
     const int64_t units = (int64_t)a.nreq * a.Hv;
     if (units >= 256 && a.Hv == 3 * a.Hk)
         return launch_chain_group<3, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
-    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn)
-                        : launch_chain<2, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
+    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX, TS, 0>(a, s, chunk_off, order, kimg, timg, cv, sn)
+                        : launch_chain<2, 2, TA, TO, VIMG, TX, TS, 6>(a, s, chunk_off, order, kimg, timg, cv, sn);
 }
 
 template <typename TA, typename TG, typename TX, typename TW, bool CONV>
