@@ -1,0 +1,361 @@
+// Decode step of the full-attention (GQA) layers over a paged KV cache, gfx950.
+//
+// The operation ("Qwen3.8-27B: from model structure to the vLLM inference
+// dataflow", section 03 GQA / attention lab, section 04 PRECISION & CACHE,
+// section 05 PagedAttention card): 24 query heads share 4 key/value heads of
+// 256 dims (query head h reads head h / 6); RoPE turns 64 of the 256 dims; the
+// attention output is gated by a sigmoid ahead of the output projection; keys
+// and values live in fixed-size pages reached through a per-request block
+// table.
+//
+// Three launches:
+//  1. rope_append: per request, rotates q and k of the new token at position
+//     L - 1 in fp64 (one sincos per dim, shared by all heads), keeps q in fp32
+//     for the attention pass and stores the rotated k (rounded once to bf16)
+//     and v into the token's page.
+//  2. attn_split: one block per (request, key/value head, run of 256
+//     positions); 4 waves of 64 positions.  A wave takes 16 positions at a
+//     time: q . K^T for the group's query heads on v_mfma_f32_16x16x32_bf16
+//     (the rows are the <= 8 query heads, q split into three bf16 terms so the
+//     scores keep fp32 accuracy; K is bf16 already), an online softmax in
+//     base 2 across the 16 lanes that hold a head row (DPP), then P V on the
+//     VALU with every lane owning 4 of the 256 value dims, the 16 positions'
+//     V rows streamed as 512-byte coalesced rows.  The block merges its
+//     4 waves and writes one partial (max, sum, unnormalised o) per query head.
+//  3. combine: per (request, query head), merges the partials of the
+//     request's runs, applies the sigmoid gate and writes y (and o).
+// The cache traffic (every position's K and V read once per key/value head)
+// is the bound; the scores run on the matrix cores so that the VALU only
+// carries P V.
+#include "gdn_device.h"
+#include "gqa_launch.h"
+
+namespace gdn {
+namespace gqa {
+
+constexpr int D = 256;          // head dim
+constexpr int SPLIT = 256;      // positions per attention block
+constexpr int NWAVE = 4;
+constexpr int WKEYS = SPLIT / NWAVE;
+constexpr int GMAX = 8;         // query heads per key/value head, at most
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// fp64 -> bf16 nearest-even with a single rounding: truncate to fp32, record
+// inexactness in the last mantissa bit (round to odd; fp32 keeps 16 bits more
+// than bf16, so the second rounding cannot land on a false tie), then round
+// the fp32 pattern to nearest-even bf16.
+__device__ __forceinline__ uint16_t bf16_from_f64(double x) {
+    const float f = __double2float_rz(x);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != x) u |= 1u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+template <typename TA>
+__global__ __launch_bounds__(D) void gqa_rope_append_kernel(
+    const TA *__restrict__ q, int64_t q_ld, const TA *__restrict__ k, const TA *__restrict__ v,
+    int64_t kv_ld, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
+    const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens,
+    int32_t Hq, int32_t Hkv, int32_t rd, int32_t P, int32_t num_pages, int32_t lmax, double theta,
+    float *__restrict__ qrot) {
+    const int r = blockIdx.x;
+    const int d = threadIdx.x;
+    const int L = lens[r];
+    if (L < 1 || L > lmax) return;  // skipped request
+    const int pos = L - 1;
+    const int half = rd / 2;
+    // x'_d = x_d cos + sgn x_partner sin over the rotated dims
+    double c = 1.0, s = 0.0, sgn = 0.0;
+    int partner = d;
+    if (d < rd) {
+        const int i = d < half ? d : d - half;
+        sincos((double)pos * pow(theta, -2.0 * i / rd), &s, &c);
+        partner = d < half ? d + half : d - half;
+        sgn = d < half ? -1.0 : 1.0;
+    }
+    for (int h = 0; h < Hq; ++h) {
+        const TA *row = q + (int64_t)r * q_ld + h * D;
+        const double x = to_f32(row[d]), xp = to_f32(row[partner]);
+        qrot[((int64_t)r * Hq + h) * D + d] = (float)(d < rd ? x * c + sgn * xp * s : x);
+    }
+    int pg = bt[(int64_t)r * max_pages + pos / P];
+    if (pg < 0 || pg >= num_pages) return;  // contract broken: no append
+    const int off = pos % P;
+    for (int j = 0; j < Hkv; ++j) {
+        const TA *krow = k + (int64_t)r * kv_ld + j * D;
+        const double x = to_f32(krow[d]), xp = to_f32(krow[partner]);
+        const int64_t dst = (((int64_t)pg * Hkv + j) * P + off) * D + d;
+        kc[dst] = bf16_from_f64(d < rd ? x * c + sgn * xp * s : x);
+        vc[dst] = to_bf16(to_f32(v[(int64_t)r * kv_ld + j * D + d])).bits;
+    }
+}
+
+// max over the 16 lanes of a row (same butterfly as group_sum)
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f(v, 0));
+    v = fmaxf(v, dpp_f(v, 1));
+    v = fmaxf(v, dpp_f(v, 2));
+    v = fmaxf(v, dpp_f(v, 3));
+    return v;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+template <int G>
+__global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
+    const float *__restrict__ qrot, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens, int32_t Hq,
+    int32_t Hkv, int32_t P, int32_t num_pages, int32_t lmax, int32_t nsplit, float qscale,
+    float *__restrict__ po, float2 *__restrict__ pml) {
+    static_assert(G >= 1 && G <= GMAX, "query heads per key/value head");
+    __shared__ __attribute__((aligned(16))) uint16_t qf[3][G][D];        // q terms, bf16 bits
+    __shared__ __attribute__((aligned(16))) float pbuf[NWAVE][17][GMAX];  // p per position; row 16: rescale
+    __shared__ float2 wml[NWAVE][GMAX];
+    __shared__ __attribute__((aligned(16))) float obuf[NWAVE][G][D];
+
+    const int s = blockIdx.x % nsplit;
+    const int rg = blockIdx.x / nsplit;
+    const int g = rg % Hkv;
+    const int r = rg / Hkv;
+    const int L = lens[r];
+    if (L < 1 || L > lmax) return;
+    const int k0 = s * SPLIT;
+    if (k0 >= L) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, kg = lane >> 4;
+
+    // rotated q of the group, scaled by log2(e) / sqrt(D), as hi + mid + lo bf16
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        const float x = qrot[((int64_t)r * Hq + g * G + m) * D + tid] * qscale;
+        const uint16_t h0 = bf16_rne_bits(x);
+        const float r1 = x - __uint_as_float(uint32_t(h0) << 16);
+        const uint16_t h1 = bf16_rne_bits(r1);
+        const float r2 = r1 - __uint_as_float(uint32_t(h1) << 16);
+        qf[0][m][tid] = h0;
+        qf[1][m][tid] = h1;
+        qf[2][m][tid] = bf16_rne_bits(r2);
+    }
+    __syncthreads();
+
+    const int wk0 = k0 + w * WKEYS;
+    const int nk = min(WKEYS, L - wk0);  // positions of this wave (<= 0: none)
+    float M[4], lsum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        M[i] = -INFINITY;
+        lsum[i] = 0.f;
+    }
+    float O[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[h][e] = 0.f;
+
+    const int64_t bt0 = (int64_t)r * max_pages;
+    for (int t = 0; t < (nk + 15) / 16; ++t) {
+        const int j0 = wk0 + 16 * t;
+        const int nt = min(16, L - j0);
+        // this lane's position (clamped into the request) and its cache row
+        const int j = j0 + min(n, nt - 1);
+        int pg = bt[bt0 + j / P];
+        pg = min(max(pg, 0), num_pages - 1);
+        const uint32_t row = ((uint32_t)pg * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(j % P);
+        const uint16_t *krow = kc + (size_t)row * D + 8 * kg;
+        bf16x8_t kf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t *>(krow + 32 * ks);
+        uint2 vraw[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < nt) {
+                const uint32_t ri = __builtin_amdgcn_readlane(row, i);
+                vraw[i] = *reinterpret_cast<const uint2 *>(vc + (size_t)ri * D + 4 * lane);
+            }
+        }
+        // scores (log2 units): S[i] = row 4 kg + i, position j0 + n
+        floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        const int m = n;  // A-operand row of this lane
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+            for (int p = 2; p >= 0; --p) {
+                bf16x8_t a = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                if (m < G) a = *reinterpret_cast<const bf16x8_t *>(&qf[p][m < G ? m : 0][32 * ks + 8 * kg]);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], S, 0, 0, 0);
+            }
+        }
+        float pr[4], al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sc = n < nt ? S[i] : -INFINITY;
+            const float mnew = fmaxf(M[i], row16_max(sc));
+            al[i] = __builtin_amdgcn_exp2f(M[i] - mnew);
+            pr[i] = __builtin_amdgcn_exp2f(sc - mnew);
+            lsum[i] = lsum[i] * al[i] + pr[i];
+            M[i] = mnew;
+        }
+        if (kg < 2) {
+            *reinterpret_cast<float4 *>(&pbuf[w][n][4 * kg]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+            if (n == 0) *reinterpret_cast<float4 *>(&pbuf[w][16][4 * kg]) = make_float4(al[0], al[1], al[2], al[3]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // P V: this lane's value dims 4 lane .. 4 lane + 3
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float a = pbuf[w][16][h];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[h][e] *= a;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < nt) {
+                const float vf[4] = {__uint_as_float(vraw[i].x << 16), __uint_as_float(vraw[i].x & 0xffff0000u),
+                                     __uint_as_float(vraw[i].y << 16), __uint_as_float(vraw[i].y & 0xffff0000u)};
+                float pv[GMAX];
+                *reinterpret_cast<float4 *>(&pv[0]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][0]);
+                if constexpr (G > 4) *reinterpret_cast<float4 *>(&pv[4]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][4]);
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) O[h][e] = fmaf(pv[h], vf[e], O[h][e]);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // the wave's (max, sum) per head row, then the block merge
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] = group_sum<16>(lsum[i]);
+    if (n == 0 && kg < 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wml[w][4 * kg + i] = make_float2(M[i], lsum[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float mb = wml[0][h].x;
+#pragma unroll
+        for (int u = 1; u < NWAVE; ++u) mb = fmaxf(mb, wml[u][h].x);
+        const float sc = __builtin_amdgcn_exp2f(wml[w][h].x - mb);
+        *reinterpret_cast<float4 *>(&obuf[w][h][4 * lane]) =
+            make_float4(O[h][0] * sc, O[h][1] * sc, O[h][2] * sc, O[h][3] * sc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < NWAVE; ++u) acc += obuf[u][h][tid];
+        const int64_t ph = ((int64_t)r * Hq + g * G + h) * nsplit + s;
+        po[ph * D + tid] = acc;
+        if (tid == 0) {
+            float mb = wml[0][h].x;
+#pragma unroll
+            for (int u = 1; u < NWAVE; ++u) mb = fmaxf(mb, wml[u][h].x);
+            float l = 0.f;
+#pragma unroll
+            for (int u = 0; u < NWAVE; ++u) l += wml[u][h].y * __builtin_amdgcn_exp2f(wml[u][h].x - mb);
+            pml[ph] = make_float2(mb, l);
+        }
+    }
+}
+
+template <typename TA, typename TY>
+__global__ __launch_bounds__(D) void gqa_combine_kernel(
+    const float *__restrict__ po, const float2 *__restrict__ pml, const TA *__restrict__ gate,
+    int64_t gate_ld, const int32_t *__restrict__ lens, int32_t Hq, int32_t lmax, int32_t nsplit,
+    TY *__restrict__ y, float *__restrict__ o) {
+    const int rh = blockIdx.x;
+    const int r = rh / Hq, h = rh % Hq;
+    const int d = threadIdx.x;
+    const int L = lens[r];
+    float out = 0.f;
+    if (L >= 1 && L <= lmax) {
+        const int ns = (L + SPLIT - 1) / SPLIT;
+        const float2 *ml = pml + (int64_t)rh * nsplit;
+        float mx = -INFINITY;
+        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[s].x);
+        float num = 0.f, den = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const float2 e = ml[s];
+            const float wgt = __builtin_amdgcn_exp2f(e.x - mx);
+            den = fmaf(wgt, e.y, den);
+            num = fmaf(wgt, po[((int64_t)rh * nsplit + s) * D + d], num);
+        }
+        out = num / den;
+    }
+    if (o != nullptr) o[(int64_t)rh * D + d] = out;
+    const float gt = to_f32(gate[(int64_t)r * gate_ld + h * D + d]);
+    y[(int64_t)rh * D + d] = from_f32<TY>(out / (1.0f + expf(-gt)));
+}
+
+template <int G>
+static hipError_t launch_attn(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float *qrot,
+                              float2 *pml, float *po) {
+    const float qscale = 1.4426950408889634f / sqrtf((float)D);
+    const int64_t blocks = (int64_t)a.R * a.Hkv * nsplit;
+    hipLaunchKernelGGL(gqa_attn_split_kernel<G>, dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st, qrot,
+                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.bt, a.max_pages, a.lens,
+                       a.Hq, a.Hkv, a.P, a.num_pages, lmax, nsplit, qscale, po, pml);
+    return hipGetLastError();
+}
+
+template <typename TA, typename TY>
+static hipError_t launch_all(const GqaArgs &a, hipStream_t st) {
+    const int64_t lmax64 = std::min<int64_t>(a.max_ctx, (int64_t)a.max_pages * a.P);
+    const int32_t lmax = (int32_t)lmax64;
+    const int32_t nsplit = (a.max_ctx + SPLIT - 1) / SPLIT;
+    float *qrot = (float *)a.ws;
+    float2 *pml = (float2 *)((uint8_t *)a.ws + gqa_ws_qrot_bytes(a.R, a.Hq));
+    float *po = (float *)((uint8_t *)pml + gqa_ws_ml_bytes(a.R, a.Hq, nsplit));
+    hipLaunchKernelGGL(gqa_rope_append_kernel<TA>, dim3(a.R), dim3(D), 0, st, (const TA *)a.q, a.q_ld,
+                       (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint16_t *)a.k_cache, (uint16_t *)a.v_cache,
+                       a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages, lmax, a.theta, qrot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (a.Hq / a.Hkv) {
+        case 1: e = launch_attn<1>(a, st, lmax, nsplit, qrot, pml, po); break;
+        case 2: e = launch_attn<2>(a, st, lmax, nsplit, qrot, pml, po); break;
+        case 3: e = launch_attn<3>(a, st, lmax, nsplit, qrot, pml, po); break;
+        case 4: e = launch_attn<4>(a, st, lmax, nsplit, qrot, pml, po); break;
+        case 5: e = launch_attn<5>(a, st, lmax, nsplit, qrot, pml, po); break;
+        case 6: e = launch_attn<6>(a, st, lmax, nsplit, qrot, pml, po); break;
+        case 7: e = launch_attn<7>(a, st, lmax, nsplit, qrot, pml, po); break;
+        default: e = launch_attn<8>(a, st, lmax, nsplit, qrot, pml, po); break;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gqa_combine_kernel<TA, TY>), dim3((unsigned)(a.R * a.Hq)), dim3(D), 0, st, po, pml,
+                       (const TA *)a.gate, a.gate_ld, a.lens, a.Hq, lmax, nsplit, (TY *)a.y, a.o);
+    return hipGetLastError();
+}
+
+}  // namespace gqa
+
+size_t gqa_ws_qrot_bytes(int64_t R, int64_t Hq) { return (size_t)(R * Hq * gqa::D * 4); }
+size_t gqa_ws_ml_bytes(int64_t R, int64_t Hq, int64_t nsplit) {
+    return (size_t)((R * Hq * nsplit * 8 + 255) / 256 * 256);
+}
+size_t gqa_ws_bytes(int64_t R, int64_t Hq, int64_t max_ctx) {
+    const int64_t nsplit = (max_ctx + gqa::SPLIT - 1) / gqa::SPLIT;
+    return gqa_ws_qrot_bytes(R, Hq) + gqa_ws_ml_bytes(R, Hq, nsplit) + (size_t)(R * Hq * nsplit * gqa::D * 4);
+}
+
+hipError_t launch_gqa_decode(const GqaArgs &a, hipStream_t s) {
+    if (a.act_bf16) return a.y_bf16 ? gqa::launch_all<bf16, bf16>(a, s) : gqa::launch_all<bf16, float>(a, s);
+    return a.y_bf16 ? gqa::launch_all<float, bf16>(a, s) : gqa::launch_all<float, float>(a, s);
+}
+
+}  // namespace gdn

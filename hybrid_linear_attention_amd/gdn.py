@@ -36,6 +36,11 @@ class GdnDimsC(ctypes.Structure):
                 ("conv_taps", ctypes.c_int32)]
 
 
+class GqaDimsC(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rotary_dim", ctypes.c_int32)]
+
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -68,6 +73,11 @@ _SIGS = {
     "gdn_validate_metadata": ([_vp, _vp, _i32, _i32, _i32], _i32),
     "gdn_validate_spec_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32], _i32),
     "gdn_validate_snapshot_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _i32),
+    "gqa_decode_workspace_bytes": ([ctypes.POINTER(GqaDimsC), _i32, _i32], ctypes.c_size_t),
+    "gqa_decode_paged": ([ctypes.POINTER(GqaDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
+                          _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp,
+                          _i32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "gqa_validate_decode_metadata": ([_vp, _i32, _vp, _i32, _i32, _i32, _i32], _i32),
 }
 
 SPEC_MAX_TOKENS = 8

@@ -277,6 +277,78 @@ def layer_mixed(seed: int = 1238, hidden: int = 5120, num_prefill: int = 8,
                      num_decode=num_decode)
 
 
+@dataclass
+class GqaDims:
+    """Full-attention layer geometry (tutorial page, section 03 GQA lab):
+    24 query heads, 4 key/value heads, 256 dims, 64 of them rotated."""
+    num_q_heads: int = 24
+    num_kv_heads: int = 4
+    head_dim: int = 256
+    rotary_dim: int = 64
+
+
+GQA_DIMS = GqaDims()
+
+
+@dataclass
+class GqaCase:
+    dims: GqaDims
+    q: torch.Tensor              # [R, Hq, D]   new token's query (before rotation)
+    gate: torch.Tensor           # [R, Hq, D]   output-gate projection
+    k: torch.Tensor              # [R, Hkv, D]  new token's key (before rotation)
+    v: torch.Tensor              # [R, Hkv, D]
+    k_cache: torch.Tensor        # [num_pages, Hkv, page_size, D] bf16
+    v_cache: torch.Tensor        # [num_pages, Hkv, page_size, D] bf16
+    block_tables: torch.Tensor   # [R, max_pages] int32 (-1 past each request's pages)
+    context_lens: torch.Tensor   # [R] int32, new token included
+    page_size: int
+    max_context_len: int
+    rope_theta: float = 10000.0
+
+    @property
+    def num_reqs(self) -> int:
+        return int(self.context_lens.numel())
+
+
+def make_gqa_case(seed: int, lens: List[int], page_size: int, dims: GqaDims = GQA_DIMS,
+                  spare_pages: int = 3, act_dtype=torch.bfloat16, max_context_len: Optional[int] = None,
+                  std: float = 1.0, rope_theta: float = 10000.0) -> GqaCase:
+    """Draw order: q, gate, k, v, k_cache, v_cache (normal, `std` for q, k and
+    the K cache, 1 otherwise), then one permutation of the physical pages that
+    deals each request its pages in table order; spare pages stay unused."""
+    rng = np.random.default_rng(seed)
+    R, Hq, Hkv, D = len(lens), dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+    q = _normal(rng, (R, Hq, D), std, act_dtype)
+    gate = _normal(rng, (R, Hq, D), 1.0, act_dtype)
+    k = _normal(rng, (R, Hkv, D), std, act_dtype)
+    v = _normal(rng, (R, Hkv, D), 1.0, act_dtype)
+    need = [(L + page_size - 1) // page_size for L in lens]
+    num_pages = sum(need) + spare_pages
+    k_cache = _normal(rng, (num_pages, Hkv, page_size, D), std, torch.bfloat16)
+    v_cache = _normal(rng, (num_pages, Hkv, page_size, D), 1.0, torch.bfloat16)
+    perm = rng.permutation(num_pages)
+    max_pages = max(need) + 1
+    bt = np.full((R, max_pages), -1, np.int32)
+    at = 0
+    for r, n in enumerate(need):
+        bt[r, :n] = perm[at:at + n]
+        at += n
+    return GqaCase(dims=dims, q=q, gate=gate, k=k, v=v, k_cache=k_cache, v_cache=v_cache,
+                   block_tables=torch.from_numpy(bt), context_lens=torch.tensor(lens, dtype=torch.int32),
+                   page_size=page_size,
+                   max_context_len=max(lens) if max_context_len is None else max_context_len,
+                   rope_theta=rope_theta)
+
+
+def gqa_decode_r64(seed: int = 1240, page_size: int = 16) -> GqaCase:
+    """64 decoding requests with context lengths uniform in [1024, 3072]
+    (about 131k cached positions in all: the page's logical-KV example of
+    4 GiB at 2 KiB per position per attention layer over 16 layers), pages of
+    16 positions."""
+    lens = np.random.default_rng(seed).integers(1024, 3073, 64).tolist()
+    return make_gqa_case(seed + 1, lens, page_size)
+
+
 WORKLOADS = {
     "tiny_core": tiny_core,
     "decode_r64": decode_r64,
@@ -284,4 +356,5 @@ WORKLOADS = {
     "prefill_varlen16": prefill_varlen16,
     "layer_mixed": layer_mixed,
     "spec_verify_r64": spec_verify_r64,
+    "gqa_decode_r64": gqa_decode_r64,
 }

@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point
-declared in include/gdn.h, and rejects bad arguments on the host before any HIP
+declared in include/gdn.h and include/gqa.h, and rejects bad arguments on the host before any HIP
 call (every call here fails validation, so nothing is ever enqueued)."""
 import ctypes
 import os
@@ -21,15 +21,18 @@ FAKE = 0x10000  # 64 KiB-aligned non-null address; never dereferenced (validatio
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in ("gdn.h", "gqa.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b((?:gdn|gqa)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     lib = gdn.lib()
     names = declared_functions()
-    assert "gdn_decode_step" in names and "gdn_prefill_varlen" in names
+    assert "gdn_decode_step" in names and "gdn_prefill_varlen" in names and "gqa_decode_paged" in names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) <= set(gdn._SIGS), "binding is missing a declared entry point"
@@ -290,3 +293,62 @@ def test_validate_snapshot_metadata_host():
     assert v(qsl, slots, [[5, 16, -1], [-1, -1, -1], [7, 8, 9]], 32, 200, 16) == 8  # out of range
     assert v(qsl, slots, snaps, 48, 200, 16) == 4                                   # interval
     assert v(qsl, slots, [[5, 6, 6], [-1, -1, -1], [7, 8, 9]], 32, 200, 16) == 0    # unread entry
+
+
+GQA = gdn.GqaDimsC(24, 4, 256, 64)
+
+
+def gqa_call(d=GQA, **kw):
+    args = dict(q=FAKE, qld=24 * 256, gate=FAKE, gld=24 * 256, k=FAKE, v=FAKE, kvld=4 * 256, act=1,
+                kc=FAKE, vc=FAKE, cdt=1, bt=FAKE, maxp=40, lens=FAKE, R=8, npages=400, P=64,
+                maxctx=2048, theta=1e4, y=FAKE, ydt=1, o=None, ws=FAKE, wsb=1 << 30)
+    args.update(kw)
+    return gdn.lib().gqa_decode_paged(
+        None if d is None else ctypes.byref(d), args["q"], args["qld"], args["gate"], args["gld"],
+        args["k"], args["v"], args["kvld"], args["act"], args["kc"], args["vc"], args["cdt"],
+        args["bt"], args["maxp"], args["lens"], args["R"], args["npages"], args["P"],
+        args["maxctx"], args["theta"], args["y"], args["ydt"], args["o"], args["ws"], args["wsb"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=None), 1),
+    (dict(d=gdn.GqaDimsC(24, 5, 256, 64)), 2),     # Hq % Hkv
+    (dict(d=gdn.GqaDimsC(24, 2, 256, 64)), 2),     # 12 query heads per kv head
+    (dict(d=gdn.GqaDimsC(24, 4, 128, 64)), 2),     # head dim
+    (dict(d=gdn.GqaDimsC(24, 4, 256, 63)), 2),     # odd rotary dim
+    (dict(d=gdn.GqaDimsC(24, 4, 256, 258)), 2),    # rotary dim > head dim
+    (dict(act=2), 3), (dict(cdt=0), 3), (dict(ydt=5), 3),
+    (dict(R=-1), 4), (dict(P=0), 4), (dict(maxctx=0), 4), (dict(maxp=0), 4),
+    (dict(qld=24 * 256 - 1), 4), (dict(kvld=100), 4), (dict(theta=0.0), 4),
+    (dict(npages=1 << 20, P=1024), 4),             # cache rows beyond 2^31
+    (dict(k=None), 1), (dict(bt=None), 1), (dict(ws=None), 1),
+    (dict(kc=FAKE + 8), 6), (dict(ws=FAKE + 4), 6),
+    (dict(wsb=16), 5),
+])
+def test_gqa_decode_rejects_bad_args(kw, status):
+    d = kw.pop("d", GQA)
+    assert gqa_call(d, **kw) == status
+
+
+def test_gqa_empty_batch_and_workspace_query():
+    assert gqa_call(R=0, q=None, k=None, ws=None) == 0     # nothing to do: no pointer needed
+    lib = gdn.lib()
+    ws = lib.gqa_decode_workspace_bytes(ctypes.byref(GQA), 64, 3584)
+    nsplit = (3584 + 255) // 256
+    assert ws == 64 * 24 * 256 * 4 + (64 * 24 * nsplit * 8 + 255) // 256 * 256 + 64 * 24 * nsplit * 256 * 4
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(gdn.GqaDimsC(24, 4, 128, 64)), 64, 10) == 0
+    assert lib.gqa_decode_workspace_bytes(ctypes.byref(GQA), 64, 0) == 0
+
+
+def test_gqa_validate_metadata_host():
+    from hybrid_linear_attention_amd import gqa
+    bt = np.array([[3, 0, -1], [1, 2, -1]], np.int32)
+    assert gqa.gqa_validate_decode_metadata(bt, [5, 8], 5, 4, 12) == 0
+    assert gqa.gqa_validate_decode_metadata(bt, [0, 8], 5, 4, 12) == 8           # empty context
+    assert gqa.gqa_validate_decode_metadata(bt, [5, 9], 5, 4, 12) == 8           # past the table
+    assert gqa.gqa_validate_decode_metadata(bt, [5, 8], 5, 4, 7) == 8            # past max_context_len
+    assert gqa.gqa_validate_decode_metadata(bt, [5, 8], 3, 4, 12) == 8           # page id 3 >= 3
+    shared = np.array([[3, 0, -1], [3, 2, -1]], np.int32)
+    assert gqa.gqa_validate_decode_metadata(shared, [5, 8], 5, 4, 12) == 0       # shared read-only prefix page
+    assert gqa.gqa_validate_decode_metadata(shared, [3, 8], 5, 4, 12) == 8       # request 0 appends into it

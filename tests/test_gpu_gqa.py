@@ -1,0 +1,104 @@
+"""GPU parity of gqa_decode_paged (GQA decode over a paged KV cache) against the
+fp64 oracle (oracle.gqa_decode_paged), through the C ABI.
+
+Bars: o (fp32, before the gate) within FP32_TOL rel-L2 (the scores keep fp32
+accuracy: q enters the matrix cores as three bf16 terms against the exact bf16
+K); y within one bf16 ulp where stored as bf16, FP32_TOL where fp32; the K/V
+cache bit for bit (the rotated k is rounded once to bf16 on both sides from
+fp64, v is copied), every position other than the new tokens' untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import FP32_TOL, bf16_ulp_ok, bits, dev, f64, rel_l2
+from hybrid_linear_attention_amd import gqa
+from hybrid_linear_attention_amd.workloads import GqaDims, gqa_decode_r64, make_gqa_case
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(case, y_dtype=torch.bfloat16):
+    d = case.dims
+    R = case.num_reqs
+    kc, vc = dev(case.k_cache), dev(case.v_cache)
+    y = torch.empty((R, d.num_q_heads * d.head_dim), dtype=y_dtype, device="cuda")
+    o = torch.empty((R, d.num_q_heads, d.head_dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(d, R, case.max_context_len), dtype=torch.uint8,
+                     device="cuda")
+    gqa.gqa_decode_paged(d, dev(case.q), dev(case.gate), dev(case.k), dev(case.v), kc, vc,
+                         dev(case.block_tables), dev(case.context_lens), case.page_size,
+                         case.max_context_len, y, ws, rope_theta=case.rope_theta, o=o)
+    torch.cuda.synchronize()
+    return y, o, kc, vc
+
+
+def run_oracle(case, reqs=None):
+    d = case.dims
+    sel = slice(None) if reqs is None else reqs
+    return oracle.gqa_decode_paged(
+        f64(case.q)[sel], f64(case.k)[sel], f64(case.v)[sel], f64(case.gate)[sel], f64(case.k_cache),
+        f64(case.v_cache), case.block_tables.numpy()[sel], case.context_lens.numpy()[sel],
+        case.page_size, d.rotary_dim, case.rope_theta)
+
+
+def check(case, y, o, kc, vc, y_dtype=torch.bfloat16):
+    d = case.dims
+    R = case.num_reqs
+    y_ref, o_ref, kc_ref, vc_ref = run_oracle(case)
+    e_o = rel_l2(f64(o), o_ref)
+    print(f"o rel-L2 {e_o:.2e}")
+    assert e_o <= FP32_TOL
+    if y_dtype == torch.bfloat16:
+        assert bf16_ulp_ok(y, y_ref.reshape(R, -1), ulps=1)
+    else:
+        assert rel_l2(f64(y), y_ref.reshape(R, -1)) <= FP32_TOL
+    np.testing.assert_array_equal(bits(kc), bits(torch.from_numpy(kc_ref).to(torch.bfloat16)))
+    np.testing.assert_array_equal(bits(vc), bits(torch.from_numpy(vc_ref).to(torch.bfloat16)))
+
+
+@pytest.mark.parametrize("which", ["pages16", "pages1", "pages100", "g8_f32", "g1_norope"])
+def test_gqa_decode_parity(which):
+    y_dtype = torch.bfloat16
+    if which == "pages16":     # lengths around the 16-position tiles and 256-position runs
+        case = make_gqa_case(81, [1, 2, 15, 16, 17, 255, 256, 257, 700, 64], 16)
+    elif which == "pages1":    # every position on a page of its own
+        case = make_gqa_case(82, [1, 3, 40, 300], 1)
+    elif which == "pages100":  # a page size that is no power of two, a tile straddling pages
+        case = make_gqa_case(83, [530, 1, 1200, 99, 101], 100)
+    elif which == "g8_f32":    # 8 query heads per kv head, fp32 activations and y, all dims rotated
+        case = make_gqa_case(84, [33, 513, 7], 16, dims=GqaDims(16, 2, 256, 256),
+                             act_dtype=torch.float32)
+        y_dtype = torch.float32
+    else:                      # one query head per kv head, no rotation
+        case = make_gqa_case(85, [20, 290], 32, dims=GqaDims(8, 8, 256, 0))
+    assert gqa.gqa_validate_decode_metadata(case.block_tables, case.context_lens,
+                                            case.k_cache.shape[0], case.page_size,
+                                            case.max_context_len) == 0
+    y, o, kc, vc = run_gpu(case, y_dtype)
+    check(case, y, o, kc, vc, y_dtype)
+
+
+def test_gqa_skipped_request_and_slack_context_bound():
+    """A request whose length is 0 is skipped (zero rows, cache untouched) and
+    max_context_len may exceed every length (extra runs of positions exit)."""
+    case = make_gqa_case(86, [40, 5, 300], 16, max_context_len=1000)
+    lens = case.context_lens.clone()
+    case.context_lens[1] = 0
+    y, o, kc, vc = run_gpu(case)
+    keep = [0, 2]
+    y_ref, o_ref, kc_ref, vc_ref = run_oracle(case, reqs=keep)
+    assert rel_l2(f64(o)[keep], o_ref) <= FP32_TOL
+    assert bf16_ulp_ok(y[keep], y_ref.reshape(2, -1), ulps=1)
+    assert not torch.any(y[1]).item() and not torch.any(o[1]).item()
+    np.testing.assert_array_equal(bits(kc), bits(torch.from_numpy(kc_ref).to(torch.bfloat16)))
+    np.testing.assert_array_equal(bits(vc), bits(torch.from_numpy(vc_ref).to(torch.bfloat16)))
+    assert int(lens[1]) == 5
+
+
+def test_gqa_decode_full_size():
+    """The benchmarked workload (64 requests, 1024-3072 positions, pages of 16),
+    launched as the benchmark launches it, against the oracle on every request."""
+    case = gqa_decode_r64()
+    y, o, kc, vc = run_gpu(case)
+    check(case, y, o, kc, vc)
