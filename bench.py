@@ -1,7 +1,7 @@
 """Benchmark of the GDN mixer core on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-layer]
-                    [--no-spec] [--no-cpu]
+                    [--no-spec] [--no-gqa] [--no-cpu]
 
 Headline workload (N=1): one decode step of 64 requests at full shapes (16 key /
 48 value heads, d = 128, fp32 state [64,48,128,128]): conv update -> recurrence
@@ -11,7 +11,9 @@ decode_step -> gated_norm) is timed beside it.  `value`
 is the state bytes each step reads and writes (2 x 64 x 3 MiB) divided by the
 measured step time.  A prefill leg (single 4096-token sequence; 16-request
 packed varlen batch) reports tokens/s in the same run, a speculative-verify leg
-times 64 requests x 4 tokens with per-position state slots, a layer leg times the
+times 64 requests x 4 tokens with per-position state slots, a GQA leg times the
+full-attention layers' decode core (64 requests over a paged bf16 KV cache of
+about 131k positions), a layer leg times the
 whole layer block on the mixed 8 x 2048 + 256 batch at hidden 5120, and the
 fp64 CPU oracle is timed on a bounded sample on the host cores.
 
@@ -46,6 +48,8 @@ def parse():
     p.add_argument("--layer-steps", type=int, default=5)
     p.add_argument("--no-spec", action="store_true")
     p.add_argument("--spec-steps", type=int, default=20)
+    p.add_argument("--no-gqa", action="store_true")
+    p.add_argument("--gqa-steps", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-ref-mib", type=int, default=0,
@@ -295,6 +299,12 @@ def main():
     # ------------------------------------------------------ speculative verify
     if not args.no_spec:
         result["spec_verify"] = bench_spec(args.spec_steps, args.warmup, dev, stream, torch, gdn)
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------- GQA layer decode core
+    if not args.no_gqa:
+        from hybrid_linear_attention_amd import gqa
+        result["gqa_decode"] = bench_gqa(args.gqa_steps, args.warmup, dev, stream, torch, gqa)
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- layer block
@@ -547,6 +557,75 @@ def bench_spec(steps, warmup, dev, stream, torch, gdn):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
                      "traffic": measured_traffic("spec_verify_kernel", "spec_verify.hip")},
+    }
+
+
+def gqa_bytes(c, act_bytes=2, y_bytes=2):
+    """Algorithmic HBM bytes of one gqa_decode_paged call: every cached position
+    of every request read once per key/value head as K and V (the new token's
+    included), the new token's q, gate, k and v read once, its rotated k and v
+    written into the cache once, y written once."""
+    d = c.dims
+    R, Hq, Hkv, D = c.num_reqs, d.num_q_heads, d.num_kv_heads, d.head_dim
+    kv = int(c.context_lens.sum()) * Hkv * D * 2 * 2
+    tok = R * (2 * Hq * D + 2 * Hkv * D) * act_bytes + R * 2 * Hkv * D * 2 + R * Hq * D * y_bytes
+    return kv, kv + tok
+
+
+def bench_gqa(steps, warmup, dev, stream, torch, gqa):
+    """gqa_decode_paged on 64 requests with 1024-3072 cached positions (pages of
+    16): K back-to-back calls between one event pair, two cache copies used in
+    turn so that no K/V is still in the memory-side cache from the call before."""
+    from hybrid_linear_attention_amd.workloads import gqa_decode_r64
+
+    c = gqa_decode_r64()
+    d = c.dims
+    R = c.num_reqs
+    n_rot = 2
+    kcs = [c.k_cache.to(dev) for _ in range(n_rot)]
+    vcs = [c.v_cache.to(dev) for _ in range(n_rot)]
+    q, gate, k, v = c.q.to(dev), c.gate.to(dev), c.k.to(dev), c.v.to(dev)
+    bt, lens = c.block_tables.to(dev), c.context_lens.to(dev)
+    y = torch.empty((R, d.num_q_heads * d.head_dim), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(d, R, c.max_context_len), dtype=torch.uint8,
+                     device=dev)
+    sh = stream.cuda_stream
+    it = [0]
+
+    def step():
+        i = it[0] % n_rot
+        it[0] += 1
+        gqa.gqa_decode_paged(d, q, gate, k, v, kcs[i], vcs[i], bt, lens, c.page_size,
+                             c.max_context_len, y, ws, rope_theta=c.rope_theta, stream=sh)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    gpu = e0.elapsed_time(e1) / steps
+    kv_b, nbytes = gqa_bytes(c)
+    achieved = nbytes / (gpu * 1e-3) / 1e9
+    ctx = int(c.context_lens.sum())
+    del kcs, vcs
+    return {
+        "workload": f"gqa_decode_r64: {R} requests, {ctx} cached positions "
+                    f"({int(c.context_lens.min())}-{int(c.context_lens.max())} each), pages of "
+                    f"{c.page_size}, 24 query / 4 kv heads x 256, RoPE on 64 dims, bf16 K/V",
+        "ms_per_step": round(wall, 4),
+        "gpu_ms_per_step": round(gpu, 4),
+        "tokens_per_s": round(R / (wall * 1e-3), 1),
+        "kv_gbs": round(kv_b / (gpu * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "gqa_decode_paged (rope_append, attn_split, combine)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                     "traffic": measured_traffic("gqa_attn_split_kernel", "gqa_decode.hip")},
     }
 
 

@@ -9,10 +9,9 @@
 // table.
 //
 // Three launches:
-//  1. rope_append: per request, rotates q and k of the new token at position
-//     L - 1 in fp64 (one sincos per dim, shared by all heads), keeps q in fp32
-//     for the attention pass and stores the rotated k (rounded once to bf16)
-//     and v into the token's page.
+//  1. rope_append: per (request, head), rotates q or k of the new token at
+//     position L - 1 in fp64, keeps q in fp32 for the attention pass and
+//     stores the rotated k (rounded once to bf16) and v into the token's page.
 //  2. attn_split: one block per (request, key/value head, run of 256
 //     positions); 4 waves of 64 positions.  A wave takes 16 positions at a
 //     time: q . K^T for the group's query heads on v_mfma_f32_16x16x32_bf16
@@ -37,7 +36,9 @@ constexpr int D = 256;          // head dim
 constexpr int SPLIT = 256;      // positions per attention block
 constexpr int NWAVE = 4;
 constexpr int WKEYS = SPLIT / NWAVE;
+constexpr int NTILE = WKEYS / 16;  // 16-position tiles per wave
 constexpr int GMAX = 8;         // query heads per key/value head, at most
+constexpr int QROW = D + 8;     // padded LDS row of a q term
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
@@ -61,36 +62,36 @@ __global__ __launch_bounds__(D) void gqa_rope_append_kernel(
     const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens,
     int32_t Hq, int32_t Hkv, int32_t rd, int32_t P, int32_t num_pages, int32_t lmax, double theta,
     float *__restrict__ qrot) {
+    // block (request r, head hh): hh < Hq a query head, else key/value head hh - Hq
     const int r = blockIdx.x;
+    const int hh = blockIdx.y;
     const int d = threadIdx.x;
     const int L = lens[r];
     if (L < 1 || L > lmax) return;  // skipped request
     const int pos = L - 1;
     const int half = rd / 2;
+    const bool is_q = hh < Hq;
+    const TA *row = is_q ? q + (int64_t)r * q_ld + hh * D : k + (int64_t)r * kv_ld + (hh - Hq) * D;
     // x'_d = x_d cos + sgn x_partner sin over the rotated dims
-    double c = 1.0, s = 0.0, sgn = 0.0;
-    int partner = d;
+    double val = to_f32(row[d]);
     if (d < rd) {
         const int i = d < half ? d : d - half;
+        const int partner = d < half ? d + half : d - half;
+        double c, s;
         sincos((double)pos * pow(theta, -2.0 * i / rd), &s, &c);
-        partner = d < half ? d + half : d - half;
-        sgn = d < half ? -1.0 : 1.0;
+        const double xp = to_f32(row[partner]);
+        val = d < half ? val * c - xp * s : val * c + xp * s;
     }
-    for (int h = 0; h < Hq; ++h) {
-        const TA *row = q + (int64_t)r * q_ld + h * D;
-        const double x = to_f32(row[d]), xp = to_f32(row[partner]);
-        qrot[((int64_t)r * Hq + h) * D + d] = (float)(d < rd ? x * c + sgn * xp * s : x);
+    if (is_q) {
+        qrot[((int64_t)r * Hq + hh) * D + d] = (float)val;
+        return;
     }
-    int pg = bt[(int64_t)r * max_pages + pos / P];
+    const int pg = bt[(int64_t)r * max_pages + pos / P];
     if (pg < 0 || pg >= num_pages) return;  // contract broken: no append
-    const int off = pos % P;
-    for (int j = 0; j < Hkv; ++j) {
-        const TA *krow = k + (int64_t)r * kv_ld + j * D;
-        const double x = to_f32(krow[d]), xp = to_f32(krow[partner]);
-        const int64_t dst = (((int64_t)pg * Hkv + j) * P + off) * D + d;
-        kc[dst] = bf16_from_f64(d < rd ? x * c + sgn * xp * s : x);
-        vc[dst] = to_bf16(to_f32(v[(int64_t)r * kv_ld + j * D + d])).bits;
-    }
+    const int j = hh - Hq;
+    const int64_t dst = (((int64_t)pg * Hkv + j) * P + pos % P) * D + d;
+    kc[dst] = bf16_from_f64(val);
+    vc[dst] = to_bf16(to_f32(v[(int64_t)r * kv_ld + j * D + d])).bits;
 }
 
 // max over the 16 lanes of a row (same butterfly as group_sum)
@@ -115,7 +116,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
     int32_t Hkv, int32_t P, int32_t num_pages, int32_t lmax, int32_t nsplit, float qscale,
     float *__restrict__ po, float2 *__restrict__ pml) {
     static_assert(G >= 1 && G <= GMAX, "query heads per key/value head");
-    __shared__ __attribute__((aligned(16))) uint16_t qf[3][G][D];        // q terms, bf16 bits
+    // q terms (bf16 bits) for all 16 MFMA rows (rows >= G zero); rows padded by
+    // 16 bytes so that the 16 rows of a fragment read fall in distinct banks
+    __shared__ __attribute__((aligned(16))) uint16_t qf[3][16][QROW];
     __shared__ __attribute__((aligned(16))) float pbuf[NWAVE][17][GMAX];  // p per position; row 16: rescale
     __shared__ float2 wml[NWAVE][GMAX];
     __shared__ __attribute__((aligned(16))) float obuf[NWAVE][G][D];
@@ -134,8 +137,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
 
     // rotated q of the group, scaled by log2(e) / sqrt(D), as hi + mid + lo bf16
 #pragma unroll
-    for (int m = 0; m < G; ++m) {
-        const float x = qrot[((int64_t)r * Hq + g * G + m) * D + tid] * qscale;
+    for (int m = 0; m < 16; ++m) {
+        const float x = m < G ? qrot[((int64_t)r * Hq + g * G + m) * D + tid] * qscale : 0.f;
         const uint16_t h0 = bf16_rne_bits(x);
         const float r1 = x - __uint_as_float(uint32_t(h0) << 16);
         const uint16_t h1 = bf16_rne_bits(r1);
@@ -147,7 +150,6 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
     __syncthreads();
 
     const int wk0 = k0 + w * WKEYS;
-    const int nk = min(WKEYS, L - wk0);  // positions of this wave (<= 0: none)
     float M[4], lsum[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -160,37 +162,52 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) O[h][e] = 0.f;
 
+    // cache rows of this lane's position in each of the wave's tiles (clamped
+    // into the request), fetched once so that no tile waits on a table read
     const int64_t bt0 = (int64_t)r * max_pages;
-    for (int t = 0; t < (nk + 15) / 16; ++t) {
-        const int j0 = wk0 + 16 * t;
-        const int nt = min(16, L - j0);
-        // this lane's position (clamped into the request) and its cache row
-        const int j = j0 + min(n, nt - 1);
+    uint32_t rows[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+        const int j = min(wk0 + 16 * t + n, L - 1);
         int pg = bt[bt0 + j / P];
         pg = min(max(pg, 0), num_pages - 1);
-        const uint32_t row = ((uint32_t)pg * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(j % P);
-        const uint16_t *krow = kc + (size_t)row * D + 8 * kg;
-        bf16x8_t kf[8];
+        rows[t] = ((uint32_t)pg * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(j % P);
+    }
+    // the table reads land here, before any cache load is issued, so that no
+    // later wait for them has to count the cache loads in flight behind them
+    __builtin_amdgcn_s_waitcnt(0);
+    // K fragments and V rows of a tile.  Every wave runs all its tiles and
+    // issues every load: positions past the request read the request's last
+    // row again (a cache hit, not HBM traffic) and get p = 0.  No load sits
+    // behind a branch, so the compiler's wait counts are exact and the next
+    // tile's loads stay in flight while this tile computes.
+    bf16x8_t kf[2][8];
+    uint2 vraw[2][16];
+    auto issue = [&](int t, int b) {
+        const uint16_t *krow = kc + (size_t)rows[t] * D + 8 * kg;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t *>(krow + 32 * ks);
-        uint2 vraw[16];
+        for (int ks = 0; ks < 8; ++ks) kf[b][ks] = *reinterpret_cast<const bf16x8_t *>(krow + 32 * ks);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (i < nt) {
-                const uint32_t ri = __builtin_amdgcn_readlane(row, i);
-                vraw[i] = *reinterpret_cast<const uint2 *>(vc + (size_t)ri * D + 4 * lane);
-            }
+            const uint32_t ri = __builtin_amdgcn_readlane(rows[t], i);
+            vraw[b][i] = *reinterpret_cast<const uint2 *>(vc + (size_t)ri * D + 4 * lane);
         }
-        // scores (log2 units): S[i] = row 4 kg + i, position j0 + n
+    };
+    issue(0, 0);
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) {
+        const int b = t & 1;
+        if (t + 1 < NTILE) issue(t + 1, b ^ 1);
+        const int nt = L - (wk0 + 16 * t);  // positions of the tile inside the request (may be <= 0)
+        // scores (log2 units): S[i] = row 4 kg + i, position wk0 + 16 t + n
         floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
         const int m = n;  // A-operand row of this lane
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int p = 2; p >= 0; --p) {
-                bf16x8_t a = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-                if (m < G) a = *reinterpret_cast<const bf16x8_t *>(&qf[p][m < G ? m : 0][32 * ks + 8 * kg]);
-                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], S, 0, 0, 0);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&qf[p][m][32 * ks + 8 * kg]);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[b][ks], S, 0, 0, 0);
             }
         }
         float pr[4], al[4];
@@ -198,8 +215,9 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
         for (int i = 0; i < 4; ++i) {
             const float sc = n < nt ? S[i] : -INFINITY;
             const float mnew = fmaxf(M[i], row16_max(sc));
-            al[i] = __builtin_amdgcn_exp2f(M[i] - mnew);
-            pr[i] = __builtin_amdgcn_exp2f(sc - mnew);
+            const float mref = mnew == -INFINITY ? 0.f : mnew;  // nothing seen yet: p = 0, no NaN
+            al[i] = __builtin_amdgcn_exp2f(M[i] - mref);
+            pr[i] = __builtin_amdgcn_exp2f(sc - mref);
             lsum[i] = lsum[i] * al[i] + pr[i];
             M[i] = mnew;
         }
@@ -219,17 +237,16 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (i < nt) {
-                const float vf[4] = {__uint_as_float(vraw[i].x << 16), __uint_as_float(vraw[i].x & 0xffff0000u),
-                                     __uint_as_float(vraw[i].y << 16), __uint_as_float(vraw[i].y & 0xffff0000u)};
-                float pv[GMAX];
-                *reinterpret_cast<float4 *>(&pv[0]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][0]);
-                if constexpr (G > 4) *reinterpret_cast<float4 *>(&pv[4]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][4]);
+            const uint2 vr = vraw[b][i];
+            const float vf[4] = {__uint_as_float(vr.x << 16), __uint_as_float(vr.x & 0xffff0000u),
+                                 __uint_as_float(vr.y << 16), __uint_as_float(vr.y & 0xffff0000u)};
+            float pv[GMAX];
+            *reinterpret_cast<float4 *>(&pv[0]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][0]);
+            if constexpr (G > 4) *reinterpret_cast<float4 *>(&pv[4]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][4]);
 #pragma unroll
-                for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) O[h][e] = fmaf(pv[h], vf[e], O[h][e]);
-            }
+                for (int e = 0; e < 4; ++e) O[h][e] = fmaf(pv[h], vf[e], O[h][e]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -321,7 +338,7 @@ static hipError_t launch_all(const GqaArgs &a, hipStream_t st) {
     float *qrot = (float *)a.ws;
     float2 *pml = (float2 *)((uint8_t *)a.ws + gqa_ws_qrot_bytes(a.R, a.Hq));
     float *po = (float *)((uint8_t *)pml + gqa_ws_ml_bytes(a.R, a.Hq, nsplit));
-    hipLaunchKernelGGL(gqa_rope_append_kernel<TA>, dim3(a.R), dim3(D), 0, st, (const TA *)a.q, a.q_ld,
+    hipLaunchKernelGGL(gqa_rope_append_kernel<TA>, dim3(a.R, a.Hq + a.Hkv), dim3(D), 0, st, (const TA *)a.q, a.q_ld,
                        (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint16_t *)a.k_cache, (uint16_t *)a.v_cache,
                        a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages, lmax, a.theta, qrot);
     hipError_t e = hipGetLastError();
