@@ -13,19 +13,23 @@
 //     position L - 1 in fp64, keeps q in fp32 for the attention pass and
 //     stores the rotated k (rounded once to bf16) and v into the token's page.
 //  2. attn_split: one block per (request, key/value head, run of 256
-//     positions); 4 waves of 64 positions.  A wave takes 16 positions at a
-//     time: q . K^T for the group's query heads on v_mfma_f32_16x16x32_bf16
-//     (the rows are the <= 8 query heads, q split into three bf16 terms so the
-//     scores keep fp32 accuracy; K is bf16 already), an online softmax in
-//     base 2 across the 16 lanes that hold a head row (DPP), then P V on the
-//     VALU with every lane owning 4 of the 256 value dims, the 16 positions'
-//     V rows streamed as 512-byte coalesced rows.  The block merges its
-//     4 waves and writes one partial (max, sum, unnormalised o) per query head.
+//     positions); 4 waves of 64 positions, 16 at a time.  Scores q . K^T on
+//     v_mfma_f32_16x16x32_bf16 (rows: the <= 8 query heads of the group, q
+//     split into three bf16 terms so that the scores keep fp32 accuracy
+//     against the exact bf16 K); an online softmax in base 2 across the 16
+//     lanes that hold a head row (DPP), its reference max moved only when a
+//     score passes it by 2^8; then P V on v_mfma_f32_16x16x16_bf16 (p as
+//     bf16 hi + lo) with both operands taken from row-major LDS tiles by the
+//     transposed LDS read.  The block merges its 4 waves and writes one
+//     partial (max, sum, unnormalised o) per query head.
 //  3. combine: per (request, query head), merges the partials of the
-//     request's runs, applies the sigmoid gate and writes y (and o).
+//     request's runs, applies the sigmoid gate and writes y (and o).  (A
+//     separate launch: merging in the last block of each group would need a
+//     device-scope release per block, which writes back the L2 of every
+//     XCD.)
 // The cache traffic (every position's K and V read once per key/value head)
-// is the bound; the scores run on the matrix cores so that the VALU only
-// carries P V.
+// is the bound; the arithmetic all sits on the matrix cores, and the
+// loads of the next 16 positions are in flight while a tile computes.
 #include "gdn_device.h"
 #include "gqa_launch.h"
 
@@ -109,19 +113,46 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
     return uint16_t(u >> 16);
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Transposed LDS read (gfx950): within each 16-lane group, lane i receives
+// element i % 4 of the 4-element words read by lanes 4j + i / 4, j = 0..3.  With
+// lane 4j + q of group kg reading row 4 kg + j, columns 4q .. 4q + 3 of a
+// row-major tile of 16-bit values, lane i ends up with rows 4 kg .. 4 kg + 3 of
+// column i: the k-major operand layout of v_mfma_f32_16x16x16_bf16.
+__device__ __forceinline__ s16x4_t lds_read_tr(const uint8_t *base, uint32_t off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t *)((__attribute__((address_space(3))) uint8_t *)(base) + off));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-wave LDS region: the tile's V rows (16 positions x 256 dims bf16, rows
+// padded to VROW bytes so that the transposed reads of 16 rows spread over
+// the banks) and its p as bf16 hi / lo terms ([16 positions][16 heads]).
+constexpr int VROW = 2 * D + 16;
+constexpr int PT_OFF = 16 * VROW;
+constexpr int WREG = PT_OFF + 2 * 16 * 16 * 2;
+constexpr float RESCALE_LOG2 = 8.f;  // keep p below 2^8 before moving the reference max
+
 template <int G>
-__global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2))) void gqa_attn_split_kernel(
     const float *__restrict__ qrot, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
     const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens, int32_t Hq,
     int32_t Hkv, int32_t P, int32_t num_pages, int32_t lmax, int32_t nsplit, float qscale,
     float *__restrict__ po, float2 *__restrict__ pml) {
     static_assert(G >= 1 && G <= GMAX, "query heads per key/value head");
+    static_assert(G * D * 4 <= WREG, "the merge reuses a wave's region");
     // q terms (bf16 bits) for all 16 MFMA rows (rows >= G zero); rows padded by
     // 16 bytes so that the 16 rows of a fragment read fall in distinct banks
     __shared__ __attribute__((aligned(16))) uint16_t qf[3][16][QROW];
-    __shared__ __attribute__((aligned(16))) float pbuf[NWAVE][17][GMAX];  // p per position; row 16: rescale
+    __shared__ __attribute__((aligned(16))) uint8_t wreg[NWAVE][WREG];
     __shared__ float2 wml[NWAVE][GMAX];
-    __shared__ __attribute__((aligned(16))) float obuf[NWAVE][G][D];
 
     const int s = blockIdx.x % nsplit;
     const int rg = blockIdx.x / nsplit;
@@ -134,6 +165,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, kg = lane >> 4;
+    uint8_t *const vt = wreg[w];
+    uint8_t *const pt = wreg[w] + PT_OFF;
 
     // rotated q of the group, scaled by log2(e) / sqrt(D), as hi + mid + lo bf16
 #pragma unroll
@@ -147,20 +180,22 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
         qf[1][m][tid] = h1;
         qf[2][m][tid] = bf16_rne_bits(r2);
     }
+    // p rows of heads 8 .. 15 are never written: zero them once
+    for (int e = lane; e < 2 * 16 * 16 / 2; e += 64) reinterpret_cast<uint32_t *>(pt)[e] = 0u;
     __syncthreads();
 
     const int wk0 = k0 + w * WKEYS;
-    float M[4], lsum[4];
+    // Mu: reference max (log2 units) of rows 4 kg + i; lsum: this lane's sum of p
+    float Mu[4], lsum[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        M[i] = -INFINITY;
+        Mu[i] = -INFINITY;
         lsum[i] = 0.f;
     }
-    float O[G][4];
+    // O[db]: rows 4 kg + i (query heads), value dim 16 db + n
+    floatx4_t O[16];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[h][e] = 0.f;
+    for (int db = 0; db < 16; ++db) O[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     // cache rows of this lane's position in each of the wave's tiles (clamped
     // into the request), fetched once so that no tile waits on a table read
@@ -176,106 +211,147 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
     // the table reads land here, before any cache load is issued, so that no
     // later wait for them has to count the cache loads in flight behind them
     __builtin_amdgcn_s_waitcnt(0);
-    // K fragments and V rows of a tile.  Every wave runs all its tiles and
-    // issues every load: positions past the request read the request's last
-    // row again (a cache hit, not HBM traffic) and get p = 0.  No load sits
-    // behind a branch, so the compiler's wait counts are exact and the next
-    // tile's loads stay in flight while this tile computes.
-    bf16x8_t kf[2][8];
-    uint2 vraw[2][16];
-    auto issue = [&](int t, int b) {
+
+    // Every wave runs all its tiles and issues every load: positions past the
+    // request read the request's last row again (a cache hit, not HBM
+    // traffic) and get p = 0.  No load sits behind a branch, so the compiler's
+    // wait counts are exact.  K fragments (B operand of the scores: lane n
+    // holds 8 dims of position n) are reloaded once the scores' MFMAs have
+    // taken them; V rows (lane l holds dims 4 l .. 4 l + 3 of each of the 16
+    // positions) go to LDS at the top of a tile, which frees their registers
+    // for the next tile's rows.  Either load thus has most of a tile to land.
+    bf16x8_t kf[8];
+    uint2 vraw[16];
+    auto load_k = [&](int t) {
         const uint16_t *krow = kc + (size_t)rows[t] * D + 8 * kg;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kf[b][ks] = *reinterpret_cast<const bf16x8_t *>(krow + 32 * ks);
+        for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t *>(krow + 32 * ks);
+    };
+    auto load_v = [&](int t) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t ri = __builtin_amdgcn_readlane(rows[t], i);
-            vraw[b][i] = *reinterpret_cast<const uint2 *>(vc + (size_t)ri * D + 4 * lane);
+            vraw[i] = *reinterpret_cast<const uint2 *>(vc + (size_t)ri * D + 4 * lane);
         }
     };
-    issue(0, 0);
+    load_k(0);
+    load_v(0);
+    // the scheduler keeps the phases below in program order: loads issued
+    // early stay early, and no wait for a later load lands in front of one
+    // for an earlier load (wait counts complete in order)
+    __builtin_amdgcn_sched_barrier(0);
+    // transposed-read offsets: lane 4j + q of group kg reads row 4 kg + j,
+    // columns 4q .. 4q + 3
+    const uint32_t tr_row = (uint32_t)(4 * kg + (n >> 2)), tr_col = (uint32_t)(8 * (n & 3));
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
-        const int b = t & 1;
-        if (t + 1 < NTILE) issue(t + 1, b ^ 1);
         const int nt = L - (wk0 + 16 * t);  // positions of the tile inside the request (may be <= 0)
         // scores (log2 units): S[i] = row 4 kg + i, position wk0 + 16 t + n
         floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        const int m = n;  // A-operand row of this lane
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int p = 2; p >= 0; --p) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&qf[p][m][32 * ks + 8 * kg]);
-                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[b][ks], S, 0, 0, 0);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&qf[p][n][32 * ks + 8 * kg]);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], S, 0, 0, 0);
             }
         }
-        float pr[4], al[4];
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < NTILE) load_k(t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // online softmax with a lazily moved reference max: p = 2^(s - Mu) stays
+        // below 2^8; the reference (and with it O and the sums) moves only when a
+        // score exceeds it by more than that
+        float sc[4], tmax[4];
+        bool need = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float sc = n < nt ? S[i] : -INFINITY;
-            const float mnew = fmaxf(M[i], row16_max(sc));
-            const float mref = mnew == -INFINITY ? 0.f : mnew;  // nothing seen yet: p = 0, no NaN
-            al[i] = __builtin_amdgcn_exp2f(M[i] - mref);
-            pr[i] = __builtin_amdgcn_exp2f(sc - mref);
-            lsum[i] = lsum[i] * al[i] + pr[i];
-            M[i] = mnew;
+            sc[i] = n < nt ? S[i] : -INFINITY;
+            tmax[i] = row16_max(sc[i]);
+            need |= tmax[i] > Mu[i] + RESCALE_LOG2;
         }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mnew = tmax[i] > Mu[i] + RESCALE_LOG2 ? tmax[i] : Mu[i];
+                const float al = Mu[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mu[i] - mnew);
+                lsum[i] *= al;
+#pragma unroll
+                for (int db = 0; db < 16; ++db) O[db][i] *= al;
+                Mu[i] = mnew;
+            }
+        }
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float mref = Mu[i] == -INFINITY ? 0.f : Mu[i];
+            pr[i] = __builtin_amdgcn_exp2f(sc[i] - mref);
+            lsum[i] += pr[i];
+        }
+        // p as bf16 hi + lo at [position n][heads 4 kg .. 4 kg + 3] (heads < 8)
         if (kg < 2) {
-            *reinterpret_cast<float4 *>(&pbuf[w][n][4 * kg]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-            if (n == 0) *reinterpret_cast<float4 *>(&pbuf[w][16][4 * kg]) = make_float4(al[0], al[1], al[2], al[3]);
+            uint32_t hi[2], lo[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint16_t h0 = bf16_rne_bits(pr[2 * e]), h1 = bf16_rne_bits(pr[2 * e + 1]);
+                const uint16_t l0 = bf16_rne_bits(pr[2 * e] - __uint_as_float(uint32_t(h0) << 16));
+                const uint16_t l1 = bf16_rne_bits(pr[2 * e + 1] - __uint_as_float(uint32_t(h1) << 16));
+                hi[e] = uint32_t(h0) | (uint32_t(h1) << 16);
+                lo[e] = uint32_t(l0) | (uint32_t(l1) << 16);
+            }
+            *reinterpret_cast<uint2 *>(pt + n * 32 + 8 * kg) = make_uint2(hi[0], hi[1]);
+            *reinterpret_cast<uint2 *>(pt + 512 + n * 32 + 8 * kg) = make_uint2(lo[0], lo[1]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // P V: this lane's value dims 4 lane .. 4 lane + 3
+        // V rows of this tile to LDS, then the next tile's rows into the registers
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float a = pbuf[w][16][h];
+        for (int i = 0; i < 16; ++i) *reinterpret_cast<uint2 *>(vt + i * VROW + 8 * lane) = vraw[i];
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < NTILE) load_v(t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_lds_sync();
+        // O += P V on the matrix cores: A = p (heads x 16 positions, hi and lo),
+        // B = V (16 positions x 16 dims per block), both by transposed reads
+        const s16x4_t ph = lds_read_tr(pt, tr_row * 32 + tr_col);
+        const s16x4_t pl = lds_read_tr(pt, 512 + tr_row * 32 + tr_col);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) O[h][e] *= a;
+        for (int db = 0; db < 16; ++db) {
+            const s16x4_t vb = lds_read_tr(vt, tr_row * VROW + 32 * db + tr_col);
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, O[db], 0, 0, 0);
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, O[db], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint2 vr = vraw[b][i];
-            const float vf[4] = {__uint_as_float(vr.x << 16), __uint_as_float(vr.x & 0xffff0000u),
-                                 __uint_as_float(vr.y << 16), __uint_as_float(vr.y & 0xffff0000u)};
-            float pv[GMAX];
-            *reinterpret_cast<float4 *>(&pv[0]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][0]);
-            if constexpr (G > 4) *reinterpret_cast<float4 *>(&pv[4]) = *reinterpret_cast<const float4 *>(&pbuf[w][i][4]);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) O[h][e] = fmaf(pv[h], vf[e], O[h][e]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
     }
 
-    // the wave's (max, sum) per head row, then the block merge
+    // the wave's (reference max, sum) per head row, then the block merge
 #pragma unroll
     for (int i = 0; i < 4; ++i) lsum[i] = group_sum<16>(lsum[i]);
     if (n == 0 && kg < 2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wml[w][4 * kg + i] = make_float2(M[i], lsum[i]);
+        for (int i = 0; i < 4; ++i) wml[w][4 * kg + i] = make_float2(Mu[i], lsum[i]);
     }
     __syncthreads();
+    // this wave's O rows, scaled to the block's max, into its own region
+    float *const ob = reinterpret_cast<float *>(wreg[w]);
+    if (kg < 2) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float mb = wml[0][h].x;
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * kg + i;
+            if (h < G) {
+                float mb = wml[0][h].x;
 #pragma unroll
-        for (int u = 1; u < NWAVE; ++u) mb = fmaxf(mb, wml[u][h].x);
-        const float sc = __builtin_amdgcn_exp2f(wml[w][h].x - mb);
-        *reinterpret_cast<float4 *>(&obuf[w][h][4 * lane]) =
-            make_float4(O[h][0] * sc, O[h][1] * sc, O[h][2] * sc, O[h][3] * sc);
+                for (int u = 1; u < NWAVE; ++u) mb = fmaxf(mb, wml[u][h].x);
+                const float scw = wml[w][h].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wml[w][h].x - mb);
+#pragma unroll
+                for (int db = 0; db < 16; ++db) ob[h * D + 16 * db + n] = O[db][i] * scw;
+            }
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float acc = 0.f;
 #pragma unroll
-        for (int u = 0; u < NWAVE; ++u) acc += obuf[u][h][tid];
+        for (int u = 0; u < NWAVE; ++u) acc += reinterpret_cast<const float *>(wreg[u])[h * D + tid];
         const int64_t ph = ((int64_t)r * Hq + g * G + h) * nsplit + s;
         po[ph * D + tid] = acc;
         if (tid == 0) {
@@ -284,7 +360,8 @@ __global__ __launch_bounds__(64 * NWAVE) void gqa_attn_split_kernel(
             for (int u = 1; u < NWAVE; ++u) mb = fmaxf(mb, wml[u][h].x);
             float l = 0.f;
 #pragma unroll
-            for (int u = 0; u < NWAVE; ++u) l += wml[u][h].y * __builtin_amdgcn_exp2f(wml[u][h].x - mb);
+            for (int u = 0; u < NWAVE; ++u)
+                if (wml[u][h].x != -INFINITY) l += wml[u][h].y * __builtin_amdgcn_exp2f(wml[u][h].x - mb);
             pml[ph] = make_float2(mb, l);
         }
     }
