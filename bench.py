@@ -622,10 +622,14 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa):
         "gpu_ms_per_step": round(gpu, 4),
         "tokens_per_s": round(R / (wall * 1e-3), 1),
         "kv_gbs": round(kv_b / (gpu * 1e-3) / 1e9, 1),
+        # call level (three launches between the events); the counters are the
+        # attention kernel's alone, which moves all but ~3 MB of the call's bytes
         "roofline": {"kernel": "gqa_decode_paged (rope_append, attn_split, combine)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
-                     "traffic": measured_traffic("gqa_attn_split_kernel", "gqa_decode.hip")},
+                     "traffic": None,
+                     "attn_split_kernel_hbm_bytes": measured_traffic("gqa_attn_split_kernel", "gqa_decode.hip"),
+                     "attn_split_kernel_kv_bytes": kv_b},
     }
 
 
