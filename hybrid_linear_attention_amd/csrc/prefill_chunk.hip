@@ -1088,7 +1088,6 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
 constexpr int GRP_ROWS = 64;          // state rows per head per block
 constexpr int GRP_RPW = 2;            // 16-row tiles per wave, at most
 constexpr int GRP_NW = 8;             // waves per block
-constexpr int GRP_MAX_HEADS = 3;      // value heads per key head the variant supports
 
 template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
 __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
