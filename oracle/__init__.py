@@ -11,13 +11,21 @@ two share no code.
 Parity status per function (see the oracle tests for the pins):
   conv1d_silu, l2norm, gates, gated_delta_rule, decode_step, gated_norm,
   rmsnorm, linear, residual_add, gdn_layer, spec_verify, round_bf16,
-  prefill_snapshots, and (gqa.py) rope_partial, gqa_decode_paged — pinned
+  prefill_snapshots, and (gqa.py) rope_partial, gqa_decode_paged, e4m3_decode,
+  e4m3_round, e4m3_encode — pinned
   (closed forms, brute force, library reductions, worked examples printed on
   the pages).
   Absolute output values for the full-size workloads are not printed anywhere
   on the pages; beyond the pins they are parity-unpinned by construction.
 """
-from .gqa import gqa_decode_paged, rope_partial  # noqa: F401
+from .gqa import (  # noqa: F401
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_round,
+    fp8_cache_round,
+    gqa_decode_paged,
+    rope_partial,
+)
 from .oracle import (  # noqa: F401
     conv1d_silu,
     conv1d_update,

@@ -24,11 +24,52 @@ Readings taken where the pages are silent (listed in the design notes):
   * the gate is elementwise over the attention output [Hq, 256];
   * the new token's position is L - 1;
   * cache layout [num_pages, Hkv, page_size, 256]; the stored value of the
-    rotated k is its round-to-nearest-even in the cache dtype.
+    rotated k is its round-to-nearest-even in the cache dtype;
+  * an fp8 cache (the server profile's e4m3, section 04) holds OCP e4m3 codes of
+    x / scale with one scale per cache (k_scale, v_scale), rounded to nearest-even
+    and saturated at +-448; a code c stands for scale * e4m3(c).
 """
 import numpy as np
 
 from .oracle import round_bf16
+
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """Values of OCP e4m3 codes (uint8): sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); 0x7f and 0xff are NaN;
+    there is no infinity."""
+    c = np.asarray(codes).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((c & 0x7f) == 0x7f, np.nan, s * mag)
+
+
+def e4m3_round(x):
+    """x (fp64) rounded to the nearest e4m3 value, ties to even, saturated at
+    +-448: the value the cache stores for x (at scale 1)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    # the spacing of e4m3 values around a: 2^(e - 3) in binade [2^e, 2^(e+1)),
+    # 2^-9 for the subnormals below 2^-6
+    e = np.frexp(np.where(a > 0, a, 1.0))[1].astype(np.float64) - 1.0
+    q = np.exp2(np.maximum(e, -6.0) - 3.0)
+    r = np.rint(a / q) * q            # rint: round half to even; a / q is exact
+    r = np.minimum(r, E4M3_MAX)
+    return np.where(a == 0, 0.0 * x, np.copysign(r, x))
+
+
+def e4m3_encode(x):
+    """Codes of the e4m3 values nearest to x (ties to even, saturating); -0 keeps
+    its sign (0x80)."""
+    r = e4m3_round(x)
+    pos = e4m3_decode(np.arange(0x7f))          # codes 0x00 .. 0x7e, increasing
+    c = np.searchsorted(pos, np.abs(r)).astype(np.uint8)
+    return np.where(np.signbit(r), c | np.uint8(0x80), c).astype(np.uint8)
 
 
 def rope_partial(x, positions, rotary_dim, theta):
@@ -70,14 +111,21 @@ def _check_paged(block_tables, context_lens, page_size, num_pages):
                 raise ValueError(f"page {wp} written by request {r} is read by request {r2}")
 
 
+def fp8_cache_round(scale):
+    """The value an e4m3 cache with this scale stores for x."""
+    return lambda x: scale * e4m3_round(np.asarray(x, dtype=np.float64) / scale)
+
+
 def gqa_decode_paged(q, k, v, gate, k_cache, v_cache, block_tables, context_lens, page_size,
-                     rotary_dim, theta, cache_round=round_bf16):
+                     rotary_dim, theta, cache_round=round_bf16, v_round=None):
     """One GQA decode step over a paged KV cache.
 
     q, gate [R, Hq, D]; k, v [R, Hkv, D]; k_cache, v_cache [num_pages, Hkv,
-    page_size, D] (values as held in the cache); block_tables [R, max_pages]
-    int; context_lens [R] (new token included).  cache_round maps a value to
-    the cache dtype (round_bf16 for a bf16 cache, None for fp32).
+    page_size, D] (the values the cache holds, decoded); block_tables
+    [R, max_pages] int; context_lens [R] (new token included).  cache_round
+    maps a new k to the value the K cache stores (round_bf16 for a bf16 cache,
+    fp8_cache_round(k_scale) for an e4m3 one, None for exact); v_round the
+    same for V (default: cache_round).
     Returns y [R, Hq, D], o [R, Hq, D] and the updated caches (copies)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -94,6 +142,7 @@ def gqa_decode_paged(q, k, v, gate, k_cache, v_cache, block_tables, context_lens
     G = Hq // Hkv
     _check_paged(bt, lens, page_size, kc.shape[0])
     rnd = (lambda t: t) if cache_round is None else cache_round
+    vrnd = rnd if v_round is None else v_round
     pos = lens.astype(np.int64) - 1
     qr = rope_partial(q, pos, rotary_dim, theta)
     kr = rope_partial(k, pos, rotary_dim, theta)
@@ -103,7 +152,7 @@ def gqa_decode_paged(q, k, v, gate, k_cache, v_cache, block_tables, context_lens
         p = int(pos[r])
         page, off = int(bt[r, p // page_size]), p % page_size
         kc[page, :, off, :] = rnd(kr[r])
-        vc[page, :, off, :] = rnd(v[r])
+        vc[page, :, off, :] = vrnd(v[r])
 
     # 3. attention over the request's positions, read through the block table
     o = np.zeros((R, Hq, D))

@@ -204,3 +204,56 @@ def test_contract_errors():
     bad[0, 0] = c["kc"].shape[0]
     with pytest.raises(ValueError):
         _check_paged(bad, c["lens"], 4, c["kc"].shape[0])
+
+
+# ---------------------------------------------------------------- fp8 e4m3 cache
+
+def test_e4m3_decode_matches_torch_float8():
+    import torch
+    got = oracle.e4m3_decode(np.arange(256))
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9        # largest normal, smallest subnormal
+
+
+def test_e4m3_round_matches_torch_and_ties_to_even():
+    import torch
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(200000) * np.exp2(rng.uniform(-14, 9, 200000))).astype(np.float32).astype(np.float64)
+    x = x[np.abs(x) < 440]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_round(x), ref)
+    # halfway cases go to the even mantissa; saturation at +-448
+    cases = {1 + 1 / 16: 1.0, 1 + 3 / 16: 1.25, 2.0 ** -10: 0.0, 1.5 * 2.0 ** -9: 2.0 ** -8,
+             -(1 + 1 / 16): -1.0, 464.0: 448.0, 500.0: 448.0, -1e9: -448.0, 0.0: 0.0}
+    for a, b in cases.items():
+        assert oracle.e4m3_round(a) == b, (a, oracle.e4m3_round(a), b)
+    # every finite code round-trips
+    vals = oracle.e4m3_decode(np.arange(256))
+    fin = ~np.isnan(vals)
+    codes = oracle.e4m3_encode(vals[fin])
+    np.testing.assert_array_equal(codes, np.arange(256)[fin].astype(np.uint8))
+
+
+def test_fp8_cache_append_and_attention():
+    c = paged_case(12, [1, 9, 33], page_size=8)
+    ks, vs = 0.5, 2.0
+    kc = ks * oracle.e4m3_round(c["kc"] / ks)
+    vc = vs * oracle.e4m3_round(c["vc"] / vs)
+    y, o, kc2, vc2 = oracle.gqa_decode_paged(c["q"], c["k"], c["v"], c["gate"], kc, vc, c["bt"], c["lens"],
+                                             c["P"], RD, THETA, cache_round=oracle.fp8_cache_round(ks),
+                                             v_round=oracle.fp8_cache_round(vs))
+    for r, L in enumerate(c["lens"]):
+        p, off = c["bt"][r, (L - 1) // 8], (L - 1) % 8
+        kr = oracle.rope_partial(c["k"][r:r + 1], [L - 1], RD, THETA)[0]
+        np.testing.assert_array_equal(kc2[p, :, off], ks * oracle.e4m3_round(kr / ks))
+        np.testing.assert_array_equal(vc2[p, :, off], vs * oracle.e4m3_round(c["v"][r] / vs))
+        rows = [(c["bt"][r, j // 8], j % 8) for j in range(L)]
+        qr = oracle.rope_partial(c["q"][r:r + 1], [L - 1], RD, THETA)[0]
+        for h in (0, 7, 23):
+            K = np.array([kc2[pp, h // 6, oo] for pp, oo in rows])
+            V = np.array([vc2[pp, h // 6, oo] for pp, oo in rows])
+            np.testing.assert_allclose(o[r, h], softmax(K @ qr[h] / 16.0) @ V, rtol=1e-12, atol=1e-12)
+    # every stored value is a scaled e4m3 value
+    assert np.all(oracle.e4m3_round(kc2 / ks) == kc2 / ks)
