@@ -12,8 +12,8 @@ is the state bytes each step reads and writes (2 x 64 x 3 MiB) divided by the
 measured step time.  A prefill leg (single 4096-token sequence; 16-request
 packed varlen batch) reports tokens/s in the same run, a speculative-verify leg
 times 64 requests x 4 tokens with per-position state slots, a GQA leg times the
-full-attention layers' decode core (64 requests over a paged bf16 KV cache of
-about 131k positions), a layer leg times the
+full-attention layers' decode core (64 requests over a paged KV cache of about
+131k positions, bf16 and fp8 e4m3), a layer leg times the
 whole layer block on the mixed 8 x 2048 + 256 batch at hidden 5120, and the
 fp64 CPU oracle is timed on a bounded sample on the host cores.
 
@@ -306,6 +306,8 @@ def main():
         from hybrid_linear_attention_amd import gqa
         result["gqa_decode"] = bench_gqa(args.gqa_steps, args.warmup, dev, stream, torch, gqa)
         torch.cuda.empty_cache()
+        result["gqa_decode_fp8"] = bench_gqa(args.gqa_steps, args.warmup, dev, stream, torch, gqa, fp8=True)
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- layer block
     if not args.no_layer:
@@ -567,18 +569,20 @@ def gqa_bytes(c, act_bytes=2, y_bytes=2):
     written into the cache once, y written once."""
     d = c.dims
     R, Hq, Hkv, D = c.num_reqs, d.num_q_heads, d.num_kv_heads, d.head_dim
-    kv = int(c.context_lens.sum()) * Hkv * D * 2 * 2
-    tok = R * (2 * Hq * D + 2 * Hkv * D) * act_bytes + R * 2 * Hkv * D * 2 + R * Hq * D * y_bytes
+    eb = c.k_cache.element_size()   # 2 (bf16) or 1 (e4m3 codes)
+    kv = int(c.context_lens.sum()) * Hkv * D * eb * 2
+    tok = R * (2 * Hq * D + 2 * Hkv * D) * act_bytes + R * 2 * Hkv * D * eb + R * Hq * D * y_bytes
     return kv, kv + tok
 
 
-def bench_gqa(steps, warmup, dev, stream, torch, gqa):
+def bench_gqa(steps, warmup, dev, stream, torch, gqa, fp8=False):
     """gqa_decode_paged on 64 requests with 1024-3072 cached positions (pages of
-    16): K back-to-back calls between one event pair, two cache copies used in
-    turn so that no K/V is still in the memory-side cache from the call before."""
-    from hybrid_linear_attention_amd.workloads import gqa_decode_r64
+    16), bf16 or e4m3 K/V: K back-to-back calls between one event pair, two
+    cache copies used in turn so that no K/V is still in the memory-side cache
+    from the call before."""
+    from hybrid_linear_attention_amd.workloads import gqa_decode_r64, gqa_decode_r64_fp8
 
-    c = gqa_decode_r64()
+    c = gqa_decode_r64_fp8() if fp8 else gqa_decode_r64()
     d = c.dims
     R = c.num_reqs
     n_rot = 2
@@ -596,7 +600,8 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa):
         i = it[0] % n_rot
         it[0] += 1
         gqa.gqa_decode_paged(d, q, gate, k, v, kcs[i], vcs[i], bt, lens, c.page_size,
-                             c.max_context_len, y, ws, rope_theta=c.rope_theta, stream=sh)
+                             c.max_context_len, y, ws, rope_theta=c.rope_theta, k_scale=c.k_scale,
+                             v_scale=c.v_scale, stream=sh)
 
     for _ in range(warmup):
         step()
@@ -617,7 +622,8 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa):
     return {
         "workload": f"gqa_decode_r64: {R} requests, {ctx} cached positions "
                     f"({int(c.context_lens.min())}-{int(c.context_lens.max())} each), pages of "
-                    f"{c.page_size}, 24 query / 4 kv heads x 256, RoPE on 64 dims, bf16 K/V",
+                    f"{c.page_size}, 24 query / 4 kv heads x 256, RoPE on 64 dims, "
+                    + ("fp8 e4m3 K/V (scales 1)" if fp8 else "bf16 K/V"),
         "ms_per_step": round(wall, 4),
         "gpu_ms_per_step": round(gpu, 4),
         "tokens_per_s": round(R / (wall * 1e-3), 1),
@@ -628,7 +634,8 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
                      "traffic": None,
-                     "attn_split_kernel_hbm_bytes": measured_traffic("gqa_attn_split_kernel", "gqa_decode.hip"),
+                     "attn_split_kernel_hbm_bytes": None if fp8 else measured_traffic("gqa_attn_split_kernel",
+                                                                                         "gqa_decode.hip"),
                      "attn_split_kernel_kv_bytes": kv_b},
     }
 

@@ -40,6 +40,7 @@ size_t gqa_decode_workspace_bytes(const gqa_dims *dims, int32_t num_reqs, int32_
 gdn_status gqa_decode_paged(const gqa_dims *dims, const void *q, int64_t q_ld, const void *gate,
                             int64_t gate_ld, const void *k, const void *v, int64_t kv_ld,
                             gdn_dtype act_dt, void *k_cache, void *v_cache, gdn_dtype cache_dt,
+                            float k_scale, float v_scale,
                             const int32_t *block_tables, int32_t max_pages_per_req,
                             const int32_t *context_lens, int32_t num_reqs, int32_t num_pages,
                             int32_t page_size, int32_t max_context_len, double rope_theta, void *y,
@@ -47,7 +48,11 @@ gdn_status gqa_decode_paged(const gqa_dims *dims, const void *q, int64_t q_ld, c
                             void *stream) {
     gdn_status st = check_gqa_dims(dims);
     if (st != GDN_OK) return st;
-    if (!act_dtype(act_dt) || !act_dtype(y_dt) || cache_dt != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!act_dtype(act_dt) || !act_dtype(y_dt) || (cache_dt != GDN_BF16 && cache_dt != GDN_FP8_E4M3))
+        return GDN_ERR_DTYPE;
+    const bool fp8 = cache_dt == GDN_FP8_E4M3;
+    if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+        return GDN_ERR_SHAPE;
     if (num_reqs < 0 || max_pages_per_req < 1 || num_pages < 1 || page_size < 1 || max_context_len < 1)
         return GDN_ERR_SHAPE;
     const int64_t Hq = dims->num_q_heads, Hkv = dims->num_kv_heads, D = dims->head_dim;
@@ -62,7 +67,8 @@ gdn_status gqa_decode_paged(const gqa_dims *dims, const void *q, int64_t q_ld, c
     gdn::GqaArgs a{};
     a.q = q; a.q_ld = q_ld; a.gate = gate; a.gate_ld = gate_ld; a.k = k; a.v = v; a.kv_ld = kv_ld;
     a.act_bf16 = act_dt == GDN_BF16;
-    a.k_cache = k_cache; a.v_cache = v_cache;
+    a.k_cache = k_cache; a.v_cache = v_cache; a.kv_fp8 = fp8;
+    a.k_scale = fp8 ? k_scale : 1.f; a.v_scale = fp8 ? v_scale : 1.f;
     a.bt = block_tables; a.max_pages = max_pages_per_req; a.lens = context_lens;
     a.R = num_reqs; a.Hq = (int32_t)Hq; a.Hkv = (int32_t)Hkv; a.rd = dims->rotary_dim;
     a.P = page_size; a.num_pages = num_pages; a.max_ctx = max_context_len; a.theta = rope_theta;

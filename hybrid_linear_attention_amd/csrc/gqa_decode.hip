@@ -11,7 +11,8 @@
 // Three launches:
 //  1. rope_append: per (request, head), rotates q or k of the new token at
 //     position L - 1 in fp64, keeps q in fp32 for the attention pass and
-//     stores the rotated k (rounded once to bf16) and v into the token's page.
+//     stores the rotated k and v into the token's page: rounded once to bf16,
+//     or (an fp8 cache) the e4m3 codes nearest to k / k_scale and v / v_scale.
 //  2. attn_split: one block per (request, key/value head, run of 256
 //     positions); 4 waves of 64 positions, 16 at a time.  Scores q . K^T on
 //     v_mfma_f32_16x16x32_bf16 (rows: the <= 8 query heads of the group, q
@@ -20,7 +21,10 @@
 //     lanes that hold a head row (DPP), its reference max moved only when a
 //     score passes it by 2^8; then P V on v_mfma_f32_16x16x16_bf16 (p as
 //     bf16 hi + lo) with both operands taken from row-major LDS tiles by the
-//     transposed LDS read.  The block merges its 4 waves and writes one
+//     transposed LDS read.  An fp8 cache is read as e4m3 codes (half the
+//     bytes) and widened to bf16 exactly in registers before the MFMAs (the
+//     K fragments) or the LDS tile (the V rows); k_scale rides on q and
+//     v_scale on the combine.  The block merges its 4 waves and writes one
 //     partial (max, sum, unnormalised o) per query head.
 //  3. combine: per (request, query head), merges the partials of the
 //     request's runs, applies the sigmoid gate and writes y (and o).  (A
@@ -30,6 +34,8 @@
 // The cache traffic (every position's K and V read once per key/value head)
 // is the bound; the arithmetic all sits on the matrix cores, and the
 // loads of the next 16 positions are in flight while a tile computes.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gqa_launch.h"
 
@@ -59,10 +65,29 @@ __device__ __forceinline__ uint16_t bf16_from_f64(double x) {
     return uint16_t(u >> 16);
 }
 
-template <typename TA>
+// fp64 -> OCP e4m3 code nearest to x, ties to even, saturated at +-448 (a NaN
+// gives code 0).  Every step is exact in fp64: the quantum of x's binade is a
+// power of two, so x / quantum is exact and rint rounds it half to even.
+__device__ __forceinline__ uint8_t e4m3_from_f64(double x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs(x);
+    if (!(a > 0.0)) return sign;
+    int e;
+    frexp(a, &e);                                   // a in [2^(e-1), 2^e)
+    const double quantum = ldexp(1.0, max(e - 1, -6) - 3);
+    const double rq = fmin(rint(a / quantum) * quantum, 448.0);
+    if (rq == 0.0) return sign;
+    int er;
+    const double m = frexp(rq, &er);                // rq = m 2^er, m in [0.5, 1)
+    if (er - 1 < -6) return sign | (uint8_t)(rq * 512.0);          // subnormal: k 2^-9
+    return sign | (uint8_t)(((er - 1 + 7) << 3) | (int)((m * 2.0 - 1.0) * 8.0));
+}
+
+// TC: uint16_t (bf16 bits) or uint8_t (e4m3 codes at k_scale, v_scale)
+template <typename TA, typename TC>
 __global__ __launch_bounds__(D) void gqa_rope_append_kernel(
     const TA *__restrict__ q, int64_t q_ld, const TA *__restrict__ k, const TA *__restrict__ v,
-    int64_t kv_ld, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
+    int64_t kv_ld, TC *__restrict__ kc, TC *__restrict__ vc, float k_scale, float v_scale,
     const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens,
     int32_t Hq, int32_t Hkv, int32_t rd, int32_t P, int32_t num_pages, int32_t lmax, double theta,
     float *__restrict__ qrot) {
@@ -94,8 +119,14 @@ __global__ __launch_bounds__(D) void gqa_rope_append_kernel(
     if (pg < 0 || pg >= num_pages) return;  // contract broken: no append
     const int j = hh - Hq;
     const int64_t dst = (((int64_t)pg * Hkv + j) * P + pos % P) * D + d;
-    kc[dst] = bf16_from_f64(val);
-    vc[dst] = to_bf16(to_f32(v[(int64_t)r * kv_ld + j * D + d])).bits;
+    const float vin = to_f32(v[(int64_t)r * kv_ld + j * D + d]);
+    if constexpr (sizeof(TC) == 1) {
+        kc[dst] = e4m3_from_f64(val / (double)k_scale);
+        vc[dst] = e4m3_from_f64((double)vin / (double)v_scale);
+    } else {
+        kc[dst] = bf16_from_f64(val);
+        vc[dst] = to_bf16(vin).bits;
+    }
 }
 
 // max over the 16 lanes of a row (same butterfly as group_sum)
@@ -140,9 +171,21 @@ constexpr int PT_OFF = 16 * VROW;
 constexpr int WREG = PT_OFF + 2 * 16 * 16 * 2;
 constexpr float RESCALE_LOG2 = 8.f;  // keep p below 2^8 before moving the reference max
 
-template <int G>
+// e4m3 -> bf16 for 8 codes: every e4m3 value is exact in bf16, so the top
+// halves of the hardware's fp32 conversions are the bf16 patterns
+template <bool HI> __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+    return make_uint2(fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w));
+}
+
+// FP8: the cache holds e4m3 codes (k_scale folded into qscale by the host,
+// v_scale applied by the combine); otherwise bf16.
+template <int G, bool FP8>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2))) void gqa_attn_split_kernel(
-    const float *__restrict__ qrot, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const float *__restrict__ qrot, const void *__restrict__ kc, const void *__restrict__ vc,
     const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens, int32_t Hq,
     int32_t Hkv, int32_t P, int32_t num_pages, int32_t lmax, int32_t nsplit, float qscale,
     float *__restrict__ po, float2 *__restrict__ pml) {
@@ -220,22 +263,52 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
     // taken them; V rows (lane l holds dims 4 l .. 4 l + 3 of each of the 16
     // positions) go to LDS at the top of a tile, which frees their registers
     // for the next tile's rows.  Either load thus has most of a tile to land.
-    bf16x8_t kf[8];
-    uint2 vraw[16];
-    auto load_k = [&](int t) {
-        const uint16_t *krow = kc + (size_t)rows[t] * D + 8 * kg;
+    // An fp8 cache moves the same 16-byte pieces with half the loads: K, lane
+    // (n, kg) reads dims 64 j + 16 kg .. + 15 of position n for j = 0..3, and
+    // the scores' k-step 2 j + b takes its half b (q's fragments are read in
+    // the same dim order: any order of the contraction works if A and B agree);
+    // V, lanes 0-31 and 32-63 read two positions' rows, 8 dims per lane.  Both
+    // are widened to bf16 exactly, at the MFMA and at the LDS tile.
+    constexpr int NKL = FP8 ? 4 : 8;   // K loads per tile
+    constexpr int NVL = FP8 ? 8 : 16;  // V loads per tile
+    // tiles in flight behind the one being computed: the fp8 tiles' registers
+    // (32 per tile) leave room for two within two waves per SIMD, bf16 (64) for one
+    constexpr int DEPTH = FP8 ? 2 : 1;
+    using KRaw = typename std::conditional<FP8, uint4, bf16x8_t>::type;
+    KRaw kf[DEPTH][NKL];
+    uint2 vraw[DEPTH][NVL];
+    const uint8_t *const kc8 = reinterpret_cast<const uint8_t *>(kc);
+    const uint8_t *const vc8 = reinterpret_cast<const uint8_t *>(vc);
+    auto load_k = [&](int t, int b) {
+        if constexpr (FP8) {
+            const uint8_t *krow = kc8 + (size_t)rows[t] * D + 16 * kg;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t *>(krow + 32 * ks);
-    };
-    auto load_v = [&](int t) {
+            for (int j = 0; j < NKL; ++j) kf[b][j] = *reinterpret_cast<const uint4 *>(krow + 64 * j);
+        } else {
+            const uint8_t *krow = kc8 + ((size_t)rows[t] * D + 8 * kg) * 2;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t ri = __builtin_amdgcn_readlane(rows[t], i);
-            vraw[i] = *reinterpret_cast<const uint2 *>(vc + (size_t)ri * D + 4 * lane);
+            for (int ks = 0; ks < NKL; ++ks) kf[b][ks] = *reinterpret_cast<const bf16x8_t *>(krow + 64 * ks);
         }
     };
-    load_k(0);
-    load_v(0);
+    auto load_v = [&](int t, int b) {
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            if constexpr (FP8) {
+                const uint32_t ra = __builtin_amdgcn_readlane(rows[t], 2 * i);
+                const uint32_t rb = __builtin_amdgcn_readlane(rows[t], 2 * i + 1);
+                const uint32_t ri = lane < 32 ? ra : rb;
+                vraw[b][i] = *reinterpret_cast<const uint2 *>(vc8 + (size_t)ri * D + 8 * (lane & 31));
+            } else {
+                const uint32_t ri = __builtin_amdgcn_readlane(rows[t], i);
+                vraw[b][i] = *reinterpret_cast<const uint2 *>(vc8 + ((size_t)ri * D + 4 * lane) * 2);
+            }
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t) {
+        load_k(t, t);
+        load_v(t, t);
+    }
     // the scheduler keeps the phases below in program order: loads issued
     // early stay early, and no wait for a later load lands in front of one
     // for an earlier load (wait counts complete in order)
@@ -245,19 +318,35 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
     const uint32_t tr_row = (uint32_t)(4 * kg + (n >> 2)), tr_col = (uint32_t)(8 * (n & 3));
 #pragma unroll
     for (int t = 0; t < NTILE; ++t) {
+        const int b = t % DEPTH;
         const int nt = L - (wk0 + 16 * t);  // positions of the tile inside the request (may be <= 0)
-        // scores (log2 units): S[i] = row 4 kg + i, position wk0 + 16 t + n
-        floatx4_t S = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        // scores (log2 units): S[i] = row 4 kg + i, position wk0 + 16 t + n; one
+        // accumulator per q term keeps three independent MFMA chains of 8 in
+        // flight instead of one of 24 (summed smallest first)
+        floatx4_t Sp[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) Sp[p] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
             for (int p = 2; p >= 0; --p) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&qf[p][n][32 * ks + 8 * kg]);
-                S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], S, 0, 0, 0);
+                const int dim0 = FP8 ? 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1) : 32 * ks + 8 * kg;
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&qf[p][n][dim0]);
+                bf16x8_t bk;
+                if constexpr (FP8) {
+                    const uint4 w = kf[b][ks >> 1];
+                    const uint2 lo = fp8x4_to_bf16x4((ks & 1) ? w.z : w.x);
+                    const uint2 hi = fp8x4_to_bf16x4((ks & 1) ? w.w : w.y);
+                    bk = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                } else {
+                    bk = kf[b][ks];
+                }
+                Sp[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bk, Sp[p], 0, 0, 0);
             }
         }
+        const floatx4_t S = (Sp[2] + Sp[1]) + Sp[0];
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 1 < NTILE) load_k(t + 1);
+        if (t + DEPTH < NTILE) load_k(t + DEPTH, b);
         __builtin_amdgcn_sched_barrier(0);
         // online softmax with a lazily moved reference max: p = 2^(s - Mu) stays
         // below 2^8; the reference (and with it O and the sums) moves only when a
@@ -304,9 +393,17 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
         }
         // V rows of this tile to LDS, then the next tile's rows into the registers
 #pragma unroll
-        for (int i = 0; i < 16; ++i) *reinterpret_cast<uint2 *>(vt + i * VROW + 8 * lane) = vraw[i];
+        for (int i = 0; i < NVL; ++i) {
+            if constexpr (FP8) {
+                const uint2 lo = fp8x4_to_bf16x4(vraw[b][i].x), hi = fp8x4_to_bf16x4(vraw[b][i].y);
+                *reinterpret_cast<uint4 *>(vt + (2 * i + (lane >> 5)) * VROW + 16 * (lane & 31)) =
+                    make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                *reinterpret_cast<uint2 *>(vt + i * VROW + 8 * lane) = vraw[b][i];
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 1 < NTILE) load_v(t + 1);
+        if (t + DEPTH < NTILE) load_v(t + DEPTH, b);
         __builtin_amdgcn_sched_barrier(0);
         wave_lds_sync();
         // O += P V on the matrix cores: A = p (heads x 16 positions, hi and lo),
@@ -371,7 +468,7 @@ template <typename TA, typename TY>
 __global__ __launch_bounds__(D) void gqa_combine_kernel(
     const float *__restrict__ po, const float2 *__restrict__ pml, const TA *__restrict__ gate,
     int64_t gate_ld, const int32_t *__restrict__ lens, int32_t Hq, int32_t lmax, int32_t nsplit,
-    TY *__restrict__ y, float *__restrict__ o) {
+    float v_scale, TY *__restrict__ y, float *__restrict__ o) {
     const int rh = blockIdx.x;
     const int r = rh / Hq, h = rh % Hq;
     const int d = threadIdx.x;
@@ -389,22 +486,37 @@ __global__ __launch_bounds__(D) void gqa_combine_kernel(
             den = fmaf(wgt, e.y, den);
             num = fmaf(wgt, po[((int64_t)rh * nsplit + s) * D + d], num);
         }
-        out = num / den;
+        out = num / den * v_scale;
     }
     if (o != nullptr) o[(int64_t)rh * D + d] = out;
     const float gt = to_f32(gate[(int64_t)r * gate_ld + h * D + d]);
     y[(int64_t)rh * D + d] = from_f32<TY>(out / (1.0f + expf(-gt)));
 }
 
-template <int G>
+template <int G, bool FP8>
 static hipError_t launch_attn(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float *qrot,
                               float2 *pml, float *po) {
-    const float qscale = 1.4426950408889634f / sqrtf((float)D);
+    const float qscale = 1.4426950408889634f / sqrtf((float)D) * a.k_scale;
     const int64_t blocks = (int64_t)a.R * a.Hkv * nsplit;
-    hipLaunchKernelGGL(gqa_attn_split_kernel<G>, dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st, qrot,
-                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.bt, a.max_pages, a.lens,
-                       a.Hq, a.Hkv, a.P, a.num_pages, lmax, nsplit, qscale, po, pml);
+    hipLaunchKernelGGL((gqa_attn_split_kernel<G, FP8>), dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st, qrot,
+                       a.k_cache, a.v_cache, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.P, a.num_pages, lmax,
+                       nsplit, qscale, po, pml);
     return hipGetLastError();
+}
+
+template <bool FP8>
+static hipError_t launch_attn_g(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float *qrot,
+                                float2 *pml, float *po) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return launch_attn<1, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 2: return launch_attn<2, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 3: return launch_attn<3, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 4: return launch_attn<4, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 5: return launch_attn<5, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 6: return launch_attn<6, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 7: return launch_attn<7, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        default: return launch_attn<8, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+    }
 }
 
 template <typename TA, typename TY>
@@ -415,24 +527,24 @@ static hipError_t launch_all(const GqaArgs &a, hipStream_t st) {
     float *qrot = (float *)a.ws;
     float2 *pml = (float2 *)((uint8_t *)a.ws + gqa_ws_qrot_bytes(a.R, a.Hq));
     float *po = (float *)((uint8_t *)pml + gqa_ws_ml_bytes(a.R, a.Hq, nsplit));
-    hipLaunchKernelGGL(gqa_rope_append_kernel<TA>, dim3(a.R, a.Hq + a.Hkv), dim3(D), 0, st, (const TA *)a.q, a.q_ld,
-                       (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint16_t *)a.k_cache, (uint16_t *)a.v_cache,
-                       a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages, lmax, a.theta, qrot);
+    const dim3 rgrid(a.R, a.Hq + a.Hkv);
+    if (a.kv_fp8)
+        hipLaunchKernelGGL((gqa_rope_append_kernel<TA, uint8_t>), rgrid, dim3(D), 0, st, (const TA *)a.q, a.q_ld,
+                           (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint8_t *)a.k_cache, (uint8_t *)a.v_cache,
+                           a.k_scale, a.v_scale, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages,
+                           lmax, a.theta, qrot);
+    else
+        hipLaunchKernelGGL((gqa_rope_append_kernel<TA, uint16_t>), rgrid, dim3(D), 0, st, (const TA *)a.q, a.q_ld,
+                           (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint16_t *)a.k_cache, (uint16_t *)a.v_cache,
+                           1.f, 1.f, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages, lmax, a.theta,
+                           qrot);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    switch (a.Hq / a.Hkv) {
-        case 1: e = launch_attn<1>(a, st, lmax, nsplit, qrot, pml, po); break;
-        case 2: e = launch_attn<2>(a, st, lmax, nsplit, qrot, pml, po); break;
-        case 3: e = launch_attn<3>(a, st, lmax, nsplit, qrot, pml, po); break;
-        case 4: e = launch_attn<4>(a, st, lmax, nsplit, qrot, pml, po); break;
-        case 5: e = launch_attn<5>(a, st, lmax, nsplit, qrot, pml, po); break;
-        case 6: e = launch_attn<6>(a, st, lmax, nsplit, qrot, pml, po); break;
-        case 7: e = launch_attn<7>(a, st, lmax, nsplit, qrot, pml, po); break;
-        default: e = launch_attn<8>(a, st, lmax, nsplit, qrot, pml, po); break;
-    }
+    e = a.kv_fp8 ? launch_attn_g<true>(a, st, lmax, nsplit, qrot, pml, po)
+                 : launch_attn_g<false>(a, st, lmax, nsplit, qrot, pml, po);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gqa_combine_kernel<TA, TY>), dim3((unsigned)(a.R * a.Hq)), dim3(D), 0, st, po, pml,
-                       (const TA *)a.gate, a.gate_ld, a.lens, a.Hq, lmax, nsplit, (TY *)a.y, a.o);
+                       (const TA *)a.gate, a.gate_ld, a.lens, a.Hq, lmax, nsplit, a.v_scale, (TY *)a.y, a.o);
     return hipGetLastError();
 }
 

@@ -15,7 +15,9 @@ struct GqaArgs {
     const void *gate; int64_t gate_ld;
     const void *k, *v; int64_t kv_ld;
     bool act_bf16;
-    void *k_cache, *v_cache;            // bf16 [num_pages, Hkv, P, D]
+    void *k_cache, *v_cache;            // bf16 or e4m3 codes [num_pages, Hkv, P, D]
+    bool kv_fp8;
+    float k_scale, v_scale;             // 1 for a bf16 cache
     const int32_t *bt; int32_t max_pages;
     const int32_t *lens;
     int32_t R, Hq, Hkv, rd, P, num_pages, max_ctx;

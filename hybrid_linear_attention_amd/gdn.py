@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_FP8_E4M3 = 2
 
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE",
@@ -75,8 +76,8 @@ _SIGS = {
     "gdn_validate_snapshot_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _i32),
     "gqa_decode_workspace_bytes": ([ctypes.POINTER(GqaDimsC), _i32, _i32], ctypes.c_size_t),
     "gqa_decode_paged": ([ctypes.POINTER(GqaDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
-                          _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp,
-                          _i32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+                          _vp, _i32, _f32, _f32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                          ctypes.c_double, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "gqa_validate_decode_metadata": ([_vp, _i32, _vp, _i32, _i32, _i32, _i32], _i32),
 }
 

@@ -8,7 +8,7 @@ import ctypes
 import numpy as np
 import torch
 
-from .gdn import GDN_BF16, GqaDimsC, _check, _dt, _ptr, _rows, _stream, lib
+from .gdn import GDN_BF16, GDN_FP8_E4M3, GqaDimsC, _check, _dt, _ptr, _rows, _stream, lib
 
 
 def dims_c(dims) -> GqaDimsC:
@@ -25,10 +25,20 @@ def gqa_decode_workspace_bytes(dims, num_reqs, max_context_len):
     return int(lib().gqa_decode_workspace_bytes(ctypes.byref(d), int(num_reqs), int(max_context_len)))
 
 
+def _cache_dt(t):
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return GDN_FP8_E4M3
+    raise TypeError(f"unsupported KV cache dtype {t.dtype}")
+
+
 def gqa_decode_paged(dims, q, gate, k, v, k_cache, v_cache, block_tables, context_lens, page_size,
-                     max_context_len, y, workspace, rope_theta=10000.0, o=None, stream=None):
+                     max_context_len, y, workspace, rope_theta=10000.0, o=None, k_scale=1.0,
+                     v_scale=1.0, stream=None):
     """q, gate [R, >=Hq*D] (or [R, Hq, D]); k, v [R, >=Hkv*D] sharing one row
-    stride; k_cache, v_cache bf16 [num_pages, Hkv, page_size, D];
+    stride; k_cache, v_cache [num_pages, Hkv, page_size, D], bf16 or e4m3 codes
+    (uint8 / float8_e4m3fn, with k_scale, v_scale);
     block_tables int32 [R, max_pages]; context_lens int32 [R];
     y [R, Hq*D]; o optional fp32 [R, Hq, D]; workspace uint8 of
     gqa_decode_workspace_bytes bytes."""
@@ -46,12 +56,13 @@ def gqa_decode_paged(dims, q, gate, k, v, k_cache, v_cache, block_tables, contex
             raise ValueError(f"{name}: must be contiguous")
     if o is not None and (o.dtype != torch.float32 or not o.is_contiguous()):
         raise TypeError("o must be contiguous float32")
-    if k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
-        raise TypeError("the KV cache is bf16")
+    cdt = _cache_dt(k_cache)
+    if _cache_dt(v_cache) != cdt:
+        raise TypeError("k_cache and v_cache share one dtype")
     st = lib().gqa_decode_paged(
         ctypes.byref(d), _ptr(q2, "q"), _rows(q2, "q"), _ptr(g2, "gate"), _rows(g2, "gate"),
         _ptr(k2, "k"), _ptr(v2, "v"), _rows(k2, "k"), _dt(q), _ptr(k_cache, "k_cache"),
-        _ptr(v_cache, "v_cache"), GDN_BF16, _ptr(block_tables, "block_tables"),
+        _ptr(v_cache, "v_cache"), cdt, float(k_scale), float(v_scale), _ptr(block_tables, "block_tables"),
         block_tables.shape[1], _ptr(context_lens, "context_lens"), R, k_cache.shape[0],
         int(page_size), int(max_context_len), float(rope_theta), _ptr(y, "y"), _dt(y),
         _ptr(o, "o"), _ptr(workspace, "workspace"), workspace.numel(), _stream(stream))

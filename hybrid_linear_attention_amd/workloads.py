@@ -304,6 +304,8 @@ class GqaCase:
     page_size: int
     max_context_len: int
     rope_theta: float = 10000.0
+    k_scale: float = 1.0         # an e4m3 cache: code c stands for scale * e4m3(c)
+    v_scale: float = 1.0
 
     @property
     def num_reqs(self) -> int:
@@ -312,10 +314,13 @@ class GqaCase:
 
 def make_gqa_case(seed: int, lens: List[int], page_size: int, dims: GqaDims = GQA_DIMS,
                   spare_pages: int = 3, act_dtype=torch.bfloat16, max_context_len: Optional[int] = None,
-                  std: float = 1.0, rope_theta: float = 10000.0) -> GqaCase:
+                  std: float = 1.0, rope_theta: float = 10000.0, cache_dtype=torch.bfloat16,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> GqaCase:
     """Draw order: q, gate, k, v, k_cache, v_cache (normal, `std` for q, k and
     the K cache, 1 otherwise), then one permutation of the physical pages that
-    deals each request its pages in table order; spare pages stay unused."""
+    deals each request its pages in table order; spare pages stay unused.
+    cache_dtype torch.float8_e4m3fn: the cache draws are converted by torch
+    (nearest-even) and kept as uint8 codes, read at k_scale / v_scale."""
     rng = np.random.default_rng(seed)
     R, Hq, Hkv, D = len(lens), dims.num_q_heads, dims.num_kv_heads, dims.head_dim
     q = _normal(rng, (R, Hq, D), std, act_dtype)
@@ -324,8 +329,12 @@ def make_gqa_case(seed: int, lens: List[int], page_size: int, dims: GqaDims = GQ
     v = _normal(rng, (R, Hkv, D), 1.0, act_dtype)
     need = [(L + page_size - 1) // page_size for L in lens]
     num_pages = sum(need) + spare_pages
-    k_cache = _normal(rng, (num_pages, Hkv, page_size, D), std, torch.bfloat16)
-    v_cache = _normal(rng, (num_pages, Hkv, page_size, D), 1.0, torch.bfloat16)
+    if cache_dtype == torch.float8_e4m3fn:
+        k_cache = _normal(rng, (num_pages, Hkv, page_size, D), std, torch.float32).to(cache_dtype).view(torch.uint8)
+        v_cache = _normal(rng, (num_pages, Hkv, page_size, D), 1.0, torch.float32).to(cache_dtype).view(torch.uint8)
+    else:
+        k_cache = _normal(rng, (num_pages, Hkv, page_size, D), std, torch.bfloat16)
+        v_cache = _normal(rng, (num_pages, Hkv, page_size, D), 1.0, torch.bfloat16)
     perm = rng.permutation(num_pages)
     max_pages = max(need) + 1
     bt = np.full((R, max_pages), -1, np.int32)
@@ -337,7 +346,7 @@ def make_gqa_case(seed: int, lens: List[int], page_size: int, dims: GqaDims = GQ
                    block_tables=torch.from_numpy(bt), context_lens=torch.tensor(lens, dtype=torch.int32),
                    page_size=page_size,
                    max_context_len=max(lens) if max_context_len is None else max_context_len,
-                   rope_theta=rope_theta)
+                   rope_theta=rope_theta, k_scale=k_scale, v_scale=v_scale)
 
 
 def gqa_decode_r64(seed: int = 1240, page_size: int = 16) -> GqaCase:
@@ -349,6 +358,13 @@ def gqa_decode_r64(seed: int = 1240, page_size: int = 16) -> GqaCase:
     return make_gqa_case(seed + 1, lens, page_size)
 
 
+def gqa_decode_r64_fp8(seed: int = 1240, page_size: int = 16) -> GqaCase:
+    """The same 64 requests with an fp8 e4m3 KV cache (the server profile's KV
+    dtype), scales 1."""
+    lens = np.random.default_rng(seed).integers(1024, 3073, 64).tolist()
+    return make_gqa_case(seed + 1, lens, page_size, cache_dtype=torch.float8_e4m3fn)
+
+
 WORKLOADS = {
     "tiny_core": tiny_core,
     "decode_r64": decode_r64,
@@ -357,4 +373,5 @@ WORKLOADS = {
     "layer_mixed": layer_mixed,
     "spec_verify_r64": spec_verify_r64,
     "gqa_decode_r64": gqa_decode_r64,
+    "gqa_decode_r64_fp8": gqa_decode_r64_fp8,
 }

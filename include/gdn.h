@@ -66,7 +66,8 @@ typedef struct gdn_dims {
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
-    GDN_BF16 = 1
+    GDN_BF16 = 1,
+    GDN_FP8_E4M3 = 2 /* OCP e4m3 codes; only the GQA KV cache (gqa.h) takes it */
 } gdn_dtype;
 
 typedef enum gdn_status {

@@ -27,7 +27,7 @@
  * Conventions are those of gdn.h (device pointers owned by the caller, work
  * enqueued on `stream`, host-checkable faults reported before anything is
  * enqueued).  Supported on the GPU: head_dim 256, 1 <= Hq / Hkv <= 8,
- * rotary_dim even in [0, head_dim].
+ * rotary_dim even in [0, head_dim], a bf16 or fp8 e4m3 KV cache.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -60,9 +60,16 @@ size_t gqa_decode_workspace_bytes(const gqa_dims *dims, int32_t num_reqs, int32_
  *   q, gate    [num_reqs, q_ld] / [num_reqs, gate_ld] in act_dt (bf16 or fp32):
  *              query head h at columns h*D .. h*D + D - 1 of the request's row.
  *   k, v       [num_reqs, kv_ld] in act_dt: key/value head j at columns j*D ...
- *   k_cache, v_cache  [num_pages, Hkv, page_size, D] in cache_dt (GDN_BF16 only):
- *              position p of request r lives in page block_tables[r][p / page_size]
- *              at offset p % page_size.  Updated in place at position L - 1 only.
+ *   k_cache, v_cache  [num_pages, Hkv, page_size, D] in cache_dt: position p of
+ *              request r lives in page block_tables[r][p / page_size] at offset
+ *              p % page_size.  Updated in place at position L - 1 only.
+ *              GDN_BF16: the rotated k rounded once to nearest-even, v as given.
+ *              GDN_FP8_E4M3 (the server profile's KV dtype, section 04): OCP e4m3
+ *              codes; code c of the K cache stands for k_scale * e4m3(c), of the V
+ *              cache for v_scale * e4m3(c); the new k and v are stored as the codes
+ *              nearest to (rotated k) / k_scale and v / v_scale, ties to even,
+ *              saturated at +-448.
+ *   k_scale, v_scale  positive finite scales of an fp8 cache (ignored for bf16).
  *   block_tables [num_reqs, max_pages_per_req] int32 (device).
  *   context_lens [num_reqs] int32 (device), new token included.
  *   max_context_len  host bound on every context length (sizes the grid and the
@@ -81,11 +88,14 @@ size_t gqa_decode_workspace_bytes(const gqa_dims *dims, int32_t num_reqs, int32_
  * call.  Out-of-range page ids are clamped into the cache (no fault; the result
  * is then meaningless).  Alignment: q, gate, k, v rows and the caches 16-byte
  * aligned (q_ld, gate_ld, kv_ld multiples of 8 elements).
+ * An fp8 cache holds NaN codes only if the caller put them there; a NaN input
+ * stores code 0 (plus its sign).
  * num_pages * Hkv * page_size must stay below 2^31.
  */
 gdn_status gqa_decode_paged(const gqa_dims *dims, const void *q, int64_t q_ld, const void *gate,
                             int64_t gate_ld, const void *k, const void *v, int64_t kv_ld,
                             gdn_dtype act_dt, void *k_cache, void *v_cache, gdn_dtype cache_dt,
+                            float k_scale, float v_scale,
                             const int32_t *block_tables, int32_t max_pages_per_req,
                             const int32_t *context_lens, int32_t num_reqs, int32_t num_pages,
                             int32_t page_size, int32_t max_context_len, double rope_theta, void *y,

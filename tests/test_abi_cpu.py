@@ -300,13 +300,13 @@ GQA = gdn.GqaDimsC(24, 4, 256, 64)
 
 def gqa_call(d=GQA, **kw):
     args = dict(q=FAKE, qld=24 * 256, gate=FAKE, gld=24 * 256, k=FAKE, v=FAKE, kvld=4 * 256, act=1,
-                kc=FAKE, vc=FAKE, cdt=1, bt=FAKE, maxp=40, lens=FAKE, R=8, npages=400, P=64,
+                kc=FAKE, vc=FAKE, cdt=1, ks=1.0, vs=1.0, bt=FAKE, maxp=40, lens=FAKE, R=8, npages=400, P=64,
                 maxctx=2048, theta=1e4, y=FAKE, ydt=1, o=None, ws=FAKE, wsb=1 << 30)
     args.update(kw)
     return gdn.lib().gqa_decode_paged(
         None if d is None else ctypes.byref(d), args["q"], args["qld"], args["gate"], args["gld"],
         args["k"], args["v"], args["kvld"], args["act"], args["kc"], args["vc"], args["cdt"],
-        args["bt"], args["maxp"], args["lens"], args["R"], args["npages"], args["P"],
+        args["ks"], args["vs"], args["bt"], args["maxp"], args["lens"], args["R"], args["npages"], args["P"],
         args["maxctx"], args["theta"], args["y"], args["ydt"], args["o"], args["ws"], args["wsb"],
         None)
 
@@ -318,7 +318,9 @@ def gqa_call(d=GQA, **kw):
     (dict(d=gdn.GqaDimsC(24, 4, 128, 64)), 2),     # head dim
     (dict(d=gdn.GqaDimsC(24, 4, 256, 63)), 2),     # odd rotary dim
     (dict(d=gdn.GqaDimsC(24, 4, 256, 258)), 2),    # rotary dim > head dim
-    (dict(act=2), 3), (dict(cdt=0), 3), (dict(ydt=5), 3),
+    (dict(act=2), 3), (dict(cdt=0), 3), (dict(cdt=3), 3), (dict(ydt=5), 3), (dict(ydt=2), 3),
+    (dict(cdt=2, ks=0.0), 4), (dict(cdt=2, vs=float("inf")), 4), (dict(cdt=2, ks=float("nan")), 4),
+    (dict(cdt=2, kc=FAKE + 8), 6),
     (dict(R=-1), 4), (dict(P=0), 4), (dict(maxctx=0), 4), (dict(maxp=0), 4),
     (dict(qld=24 * 256 - 1), 4), (dict(kvld=100), 4), (dict(theta=0.0), 4),
     (dict(npages=1 << 20, P=1024), 4),             # cache rows beyond 2^31

@@ -5,7 +5,9 @@ Bars: o (fp32, before the gate) within FP32_TOL rel-L2 (the scores keep fp32
 accuracy: q enters the matrix cores as three bf16 terms against the exact bf16
 K); y within one bf16 ulp where stored as bf16, FP32_TOL where fp32; the K/V
 cache bit for bit (the rotated k is rounded once to bf16 on both sides from
-fp64, v is copied), every position other than the new tokens' untouched."""
+fp64, v is copied; an e4m3 cache gets the codes nearest to k / k_scale and
+v / v_scale, the same on both sides since both round the same fp64 value), every
+position other than the new tokens' untouched."""
 import numpy as np
 import pytest
 import torch
@@ -13,9 +15,21 @@ import torch
 import oracle
 from helpers import FP32_TOL, bf16_ulp_ok, bits, dev, f64, rel_l2
 from hybrid_linear_attention_amd import gqa
-from hybrid_linear_attention_amd.workloads import GqaDims, gqa_decode_r64, make_gqa_case
+from hybrid_linear_attention_amd.workloads import GqaDims, gqa_decode_r64, gqa_decode_r64_fp8, make_gqa_case
 
 pytestmark = pytest.mark.gpu
+
+
+def is_fp8(case):
+    return case.k_cache.dtype == torch.uint8
+
+
+def cache_values(case):
+    """The values the caches hold (fp64), decoded from e4m3 codes for an fp8 cache."""
+    if is_fp8(case):
+        return (case.k_scale * oracle.e4m3_decode(case.k_cache.numpy()),
+                case.v_scale * oracle.e4m3_decode(case.v_cache.numpy()))
+    return f64(case.k_cache), f64(case.v_cache)
 
 
 def run_gpu(case, y_dtype=torch.bfloat16):
@@ -28,7 +42,8 @@ def run_gpu(case, y_dtype=torch.bfloat16):
                      device="cuda")
     gqa.gqa_decode_paged(d, dev(case.q), dev(case.gate), dev(case.k), dev(case.v), kc, vc,
                          dev(case.block_tables), dev(case.context_lens), case.page_size,
-                         case.max_context_len, y, ws, rope_theta=case.rope_theta, o=o)
+                         case.max_context_len, y, ws, rope_theta=case.rope_theta, o=o,
+                         k_scale=case.k_scale, v_scale=case.v_scale)
     torch.cuda.synchronize()
     return y, o, kc, vc
 
@@ -36,10 +51,30 @@ def run_gpu(case, y_dtype=torch.bfloat16):
 def run_oracle(case, reqs=None):
     d = case.dims
     sel = slice(None) if reqs is None else reqs
+    kc, vc = cache_values(case)
+    rounding = {}
+    if is_fp8(case):
+        rounding = dict(cache_round=oracle.fp8_cache_round(case.k_scale),
+                        v_round=oracle.fp8_cache_round(case.v_scale))
     return oracle.gqa_decode_paged(
-        f64(case.q)[sel], f64(case.k)[sel], f64(case.v)[sel], f64(case.gate)[sel], f64(case.k_cache),
-        f64(case.v_cache), case.block_tables.numpy()[sel], case.context_lens.numpy()[sel],
-        case.page_size, d.rotary_dim, case.rope_theta)
+        f64(case.q)[sel], f64(case.k)[sel], f64(case.v)[sel], f64(case.gate)[sel], kc, vc,
+        case.block_tables.numpy()[sel], case.context_lens.numpy()[sel], case.page_size, d.rotary_dim,
+        case.rope_theta, **rounding)
+
+
+def check_fp8_caches(case, kc, vc, kc_ref, vc_ref, reqs):
+    """e4m3 caches: the new tokens' codes equal the oracle's (its stored values
+    encoded back), every other code is untouched."""
+    got_k, got_v = kc.cpu().numpy(), vc.cpu().numpy()
+    exp_k, exp_v = case.k_cache.numpy().copy(), case.v_cache.numpy().copy()
+    P = case.page_size
+    for r in reqs:
+        L = int(case.context_lens[r])
+        p, off = int(case.block_tables[r, (L - 1) // P]), (L - 1) % P
+        exp_k[p, :, off] = oracle.e4m3_encode(kc_ref[p, :, off] / case.k_scale)
+        exp_v[p, :, off] = oracle.e4m3_encode(vc_ref[p, :, off] / case.v_scale)
+    np.testing.assert_array_equal(got_k, exp_k)
+    np.testing.assert_array_equal(got_v, exp_v)
 
 
 def check(case, y, o, kc, vc, y_dtype=torch.bfloat16):
@@ -53,11 +88,18 @@ def check(case, y, o, kc, vc, y_dtype=torch.bfloat16):
         assert bf16_ulp_ok(y, y_ref.reshape(R, -1), ulps=1)
     else:
         assert rel_l2(f64(y), y_ref.reshape(R, -1)) <= FP32_TOL
-    np.testing.assert_array_equal(bits(kc), bits(torch.from_numpy(kc_ref).to(torch.bfloat16)))
-    np.testing.assert_array_equal(bits(vc), bits(torch.from_numpy(vc_ref).to(torch.bfloat16)))
+    if is_fp8(case):
+        check_fp8_caches(case, kc, vc, kc_ref, vc_ref, range(R))
+    else:
+        np.testing.assert_array_equal(bits(kc), bits(torch.from_numpy(kc_ref).to(torch.bfloat16)))
+        np.testing.assert_array_equal(bits(vc), bits(torch.from_numpy(vc_ref).to(torch.bfloat16)))
 
 
-@pytest.mark.parametrize("which", ["pages16", "pages1", "pages100", "g8_f32", "g1_norope"])
+FP8 = torch.float8_e4m3fn
+
+
+@pytest.mark.parametrize("which", ["pages16", "pages1", "pages100", "g8_f32", "g1_norope",
+                                   "fp8_pages16", "fp8_scaled", "fp8_g8_f32"])
 def test_gqa_decode_parity(which):
     y_dtype = torch.bfloat16
     if which == "pages16":     # lengths around the 16-position tiles and 256-position runs
@@ -70,8 +112,16 @@ def test_gqa_decode_parity(which):
         case = make_gqa_case(84, [33, 513, 7], 16, dims=GqaDims(16, 2, 256, 256),
                              act_dtype=torch.float32)
         y_dtype = torch.float32
-    else:                      # one query head per kv head, no rotation
+    elif which == "g1_norope":  # one query head per kv head, no rotation
         case = make_gqa_case(85, [20, 290], 32, dims=GqaDims(8, 8, 256, 0))
+    elif which == "fp8_pages16":  # e4m3 cache at scale 1
+        case = make_gqa_case(87, [1, 2, 15, 16, 17, 255, 256, 257, 700, 64], 16, cache_dtype=FP8)
+    elif which == "fp8_scaled":   # e4m3 cache with per-cache scales, a page size that is no power of two
+        case = make_gqa_case(88, [530, 1, 1200, 99], 100, cache_dtype=FP8, k_scale=0.0625, v_scale=0.75)
+    else:                         # e4m3 cache, 8 query heads per kv head, fp32 activations and y
+        case = make_gqa_case(89, [33, 513, 7], 16, dims=GqaDims(16, 2, 256, 256), act_dtype=torch.float32,
+                             cache_dtype=FP8, k_scale=2.0, v_scale=0.5)
+        y_dtype = torch.float32
     assert gqa.gqa_validate_decode_metadata(case.block_tables, case.context_lens,
                                             case.k_cache.shape[0], case.page_size,
                                             case.max_context_len) == 0
@@ -100,5 +150,12 @@ def test_gqa_decode_full_size():
     """The benchmarked workload (64 requests, 1024-3072 positions, pages of 16),
     launched as the benchmark launches it, against the oracle on every request."""
     case = gqa_decode_r64()
+    y, o, kc, vc = run_gpu(case)
+    check(case, y, o, kc, vc)
+
+
+def test_gqa_decode_full_size_fp8():
+    """The benchmarked fp8 workload (the same 64 requests, e4m3 cache)."""
+    case = gqa_decode_r64_fp8()
     y, o, kc, vc = run_gpu(case)
     check(case, y, o, kc, vc)
