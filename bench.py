@@ -634,8 +634,8 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa, fp8=False):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
                      "traffic": None,
-                     "attn_split_kernel_hbm_bytes": None if fp8 else measured_traffic("gqa_attn_split_kernel",
-                                                                                         "gqa_decode.hip"),
+                     "attn_split_kernel_hbm_bytes": measured_traffic(
+                         "gqa_attn_split_kernel_fp8" if fp8 else "gqa_attn_split_kernel", "gqa_decode.hip"),
                      "attn_split_kernel_kv_bytes": kv_b},
     }
 
