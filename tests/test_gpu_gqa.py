@@ -146,6 +146,19 @@ def test_gqa_skipped_request_and_slack_context_bound():
     assert int(lens[1]) == 5
 
 
+@pytest.mark.parametrize("which", ["long_single", "pages528_fp8"])
+def test_gqa_decode_long_contexts(which):
+    """One request with a 20,000-position context (79 runs merged by the
+    combine) beside a 1-position one; pages of 528 positions (longer than a
+    run, no power of two) on an e4m3 cache."""
+    if which == "long_single":
+        case = make_gqa_case(90, [20000, 1], 64)
+    else:
+        case = make_gqa_case(91, [3000, 528, 529, 1], 528, cache_dtype=FP8, k_scale=0.5, v_scale=1.5)
+    y, o, kc, vc = run_gpu(case)
+    check(case, y, o, kc, vc)
+
+
 def test_gqa_decode_full_size():
     """The benchmarked workload (64 requests, 1024-3072 positions, pages of 16),
     launched as the benchmark launches it, against the oracle on every request."""
