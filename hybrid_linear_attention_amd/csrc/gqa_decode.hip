@@ -13,8 +13,8 @@
 //     position L - 1 in fp64, keeps q in fp32 for the attention pass and
 //     stores the rotated k and v into the token's page: rounded once to bf16,
 //     or (an fp8 cache) the e4m3 codes nearest to k / k_scale and v / v_scale.
-//  2. attn_split: one block per (request, key/value head, run of 256
-//     positions); 4 waves of 64 positions, 16 at a time.  Scores q . K^T on
+//  2. attn_split: one block per (request, key/value head, run of 512
+//     positions); 4 waves of 128 positions, 16 at a time.  Scores q . K^T on
 //     v_mfma_f32_16x16x32_bf16 (rows: the <= 8 query heads of the group, q
 //     split into three bf16 terms so that the scores keep fp32 accuracy
 //     against the exact bf16 K); an online softmax in base 2 across the 16
@@ -43,7 +43,7 @@ namespace gdn {
 namespace gqa {
 
 constexpr int D = 256;          // head dim
-constexpr int SPLIT = 256;      // positions per attention block
+constexpr int SPLIT = 512;      // positions per attention block
 constexpr int NWAVE = 4;
 constexpr int WKEYS = SPLIT / NWAVE;
 constexpr int NTILE = WKEYS / 16;  // 16-position tiles per wave

@@ -47,7 +47,7 @@ typedef struct gqa_dims {
 
 /* Keys one attention block reads; a request's positions are cut into
  * ceil(L / GQA_SPLIT_KEYS) partial softmaxes that a second pass merges. */
-#define GQA_SPLIT_KEYS 256
+#define GQA_SPLIT_KEYS 512
 
 /* Workspace bytes gqa_decode_paged needs for num_reqs requests whose context
  * lengths are at most max_context_len: the rotated queries (fp32 [R, Hq, D])

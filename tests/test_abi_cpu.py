@@ -337,7 +337,7 @@ def test_gqa_empty_batch_and_workspace_query():
     assert gqa_call(R=0, q=None, k=None, ws=None) == 0     # nothing to do: no pointer needed
     lib = gdn.lib()
     ws = lib.gqa_decode_workspace_bytes(ctypes.byref(GQA), 64, 3584)
-    nsplit = (3584 + 255) // 256
+    nsplit = (3584 + 511) // 512      # GQA_SPLIT_KEYS positions per partial
     assert ws == 64 * 24 * 256 * 4 + (64 * 24 * nsplit * 8 + 255) // 256 * 256 + 64 * 24 * nsplit * 256 * 4
     assert lib.gqa_decode_workspace_bytes(ctypes.byref(gdn.GqaDimsC(24, 4, 128, 64)), 64, 10) == 0
     assert lib.gqa_decode_workspace_bytes(ctypes.byref(GQA), 64, 0) == 0
