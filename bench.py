@@ -314,6 +314,9 @@ def main():
         result["layer"] = bench_layer(args.layer_steps, dev, stream, torch, np)
         torch.cuda.empty_cache()
 
+    # --------------------------------------- measured HBM reference rates
+    result["hbm_reference"] = hbm_reference(torch, dev)
+
     # ------------------------------------------------------------ CPU baseline
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
@@ -640,6 +643,30 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa, fp8=False):
     }
 
 
+def hbm_reference(torch, dev, mib=1024, reps=10):
+    """What plain torch kernels reach on this machine beside the 8 TB/s peak: a
+    device-to-device copy (reads and writes `mib` MiB) and a sum (reads them)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("torch_copy_gbs", lambda: dst.copy_(src), 2 * n * 4),
+                             ("torch_sum_read_gbs", lambda: src.sum(), n * 4)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    out["bytes"] = mib * (1 << 20)
+    return out
+
+
 def cpu_baseline(case, seconds):
     """The fp64 oracle (conv1d_update -> decode_step -> gated_norm) on the same
     decode workload, repeated until ~`seconds` of CPU time have passed."""
@@ -655,18 +682,32 @@ def cpu_baseline(case, seconds):
     st = f64(case.state_pool)
     a, b, z, g = f64(case.a), f64(case.b), f64(case.z), f64(case.gamma)
     qsl, slots, hi = case.qsl.numpy(), case.slot_ids.numpy(), case.has_initial.numpy()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        qq, kk, vv, hist = oracle.conv1d_update(x, w, hist, qsl, slots, hi, d.num_k_heads,
-                                                d.num_v_heads, d.head_dim_k, d.head_dim_v, L2_EPS)
-        o, st = oracle.decode_step(qq, kk, vv, a, b, st, slots)
-        oracle.gated_norm(o, z, g, NORM_EPS)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    def sample(secs):
+        nonlocal hist, st
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            qq, kk, vv, hist = oracle.conv1d_update(x, w, hist, qsl, slots, hi, d.num_k_heads,
+                                                    d.num_v_heads, d.head_dim_k, d.head_dim_v, L2_EPS)
+            o, st = oracle.decode_step(qq, kk, vv, a, b, st, slots)
+            oracle.gated_norm(o, z, g, NORM_EPS)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= secs:
+                return reps, el
+
+    threads = oracle.num_threads()
+    reps, el = sample(seconds)
+    oracle.set_num_threads(1)               # the same step on one thread, a shorter sample
+    reps1, el1 = sample(max(2.0, seconds / 4))
+    oracle.set_num_threads(threads)
     state_bytes = 2 * case.num_reqs * d.num_v_heads * d.head_dim_k * d.head_dim_v * 4
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(state_bytes * reps / el / 1e9, 4),
         "unit": "GB/s",
@@ -677,6 +718,9 @@ def cpu_baseline(case, seconds):
                   f"state bytes counted as fp32, as on the GPU",
         "ms_per_step": round(el * 1e3 / reps, 2),
         "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model,
+        "one_thread": {"value": round(state_bytes * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+                       "ms_per_step": round(el1 * 1e3 / reps1, 2), "steps": reps1},
     }
 
 

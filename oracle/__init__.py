@@ -41,6 +41,7 @@ from .oracle import (  # noqa: F401
     residual_add,
     rmsnorm,
     round_bf16,
+    set_num_threads,
     silu,
     spec_verify,
     split_qkv,

@@ -129,3 +129,14 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following parallel regions (n >= 1; for timing the core
+ * on one thread beside all of them). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

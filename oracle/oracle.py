@@ -44,6 +44,8 @@ def _load():
         lib.oracle_gdn_recurrence.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -51,6 +53,11 @@ def _load():
 def num_threads() -> int:
     """Threads the C core's parallel region uses (OMP_NUM_THREADS)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the C core's later parallel regions."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _f64(x):
