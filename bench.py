@@ -112,7 +112,7 @@ def decode_bytes(d, R, act_bytes=4, o_bytes=4):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
