@@ -274,7 +274,7 @@ def main():
         "roofline": {"kernel": "decode_fused_kernel (bf16 state)", "bound": "hbm",
                      "achieved": round(a16, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(a16 / HBM_PEAK_GBS, 4), "bytes_per_launch": b16,
-                     "traffic": None},
+                     "traffic": measured_traffic("decode_fused_kernel_bf16_state", "decode_fused.hip")},
     }
     del states, conv_pools, states16
     torch.cuda.empty_cache()
