@@ -106,31 +106,43 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // ---------------------------------------------------------------------------
 // Large-tile variant for K % 64 == 0: a 512-thread block owns a 256x256 C tile
 // (8 waves as 4 x 2, each 64 x 128 = 4 x 8 MFMA tiles); K advances 64 at a time
-// through a two-stage LDS ring filled by direct-to-LDS 16-byte loads.  A wave
-// tile of 64 x 128 reads 12 fragments per 32 MFMAs, which keeps the LDS well
-// below its bandwidth at full MFMA rate.  LDS rows are 128 bytes (64 bf16) with
-// the 16-byte chunk index XOR-swizzled by row (chunk j of row r stored at
-// j ^ (r & 7)), so the 16 rows of a fragment read fall in different banks; the
-// swizzle is applied on the global side because a direct-to-LDS load places
-// lane l's bytes at base + 16 l.
+// through a two-stage LDS ring filled by direct-to-LDS 16-byte loads.  LDS rows
+// are 128 bytes (64 bf16) with the 16-byte chunk index XOR-swizzled by row
+// (chunk j of row r stored at j ^ (r & 7)), so the 16 rows of a fragment read
+// fall in different banks; the swizzle is applied on the global side because a
+// direct-to-LDS load places lane l's bytes at base + 16 l.
+//
+// Each 64-deep stage is two 32-deep k-slices, and the one barrier per stage sits
+// between them.  Phase A multiplies slice 0 (fragments already in registers)
+// while reading slice 1's; the barrier then certifies that the next stage has
+// landed and that every wave is done with this one; phase B multiplies slice 1
+// while reading the next stage's slice-0 fragments and refilling this stage's
+// buffer with the stage after next.  A wave thus leaves the barrier with a full
+// slice of MFMAs ready instead of waiting for LDS reads that every wave of the
+// block issues at the same moment.  MFMAs run over one B fragment at a time
+// (4 tiles) so that the register of the fragment they finish is refilled next.
 // ---------------------------------------------------------------------------
 constexpr int G2M = 256, G2N = 256;
 constexpr int G2_THREADS = 512;
+constexpr int G2_BK = 64;                          // K per stage (two MFMA k-slices)
+constexpr int G2_CPR = G2_BK / 8;                  // 16-byte chunks per LDS row
+constexpr size_t G2_TILE = (size_t)G2M * G2_BK * 2;  // one operand, one stage
+constexpr size_t G2_STAGE = 2 * G2_TILE;
+constexpr size_t G2_SMEM = 2 * G2_STAGE;           // two stages: 128 KiB
+constexpr int G2_LOADS = G2M * G2_CPR * 2 / G2_THREADS;  // direct-to-LDS loads per thread per stage
+constexpr int G2_GROUP_M = 2;                      // tile rows per group of the tile order
 
-// one operand tile of 256 rows x BK bf16: rows of 2 BK bytes, 16-byte chunk j
-// of row r stored at chunk j ^ (r & (BK / 8 - 1))
-template <int BK>
+// one operand tile of 256 rows x 64 bf16: rows of 128 bytes, 16-byte chunk j
+// of row r stored at chunk j ^ (r & 7)
 __device__ __forceinline__ void g2_copy(const uint16_t *__restrict__ X, int64_t ld, int rows_valid,
                                         int row0, int k0, uint8_t *tile, int tid) {
-    constexpr int CPR = BK / 8;                      // 16-byte chunks per row
-    constexpr int PIECES = G2M * CPR;                // per tile
-    constexpr int PER_THREAD = PIECES / G2_THREADS;
+    constexpr int PER_THREAD = G2M * G2_CPR / G2_THREADS;
     const int wv = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int m = 0; m < PER_THREAD; ++m) {
         const int s = (m * 8 + wv) * 64 + lane;  // wave-contiguous LDS pieces
-        const int r = s / CPR;
-        const int j = (s % CPR) ^ (r & (CPR - 1));
+        const int r = s / G2_CPR;
+        const int j = (s % G2_CPR) ^ (r & (G2_CPR - 1));
         const int rr = min(row0 + r, rows_valid - 1);  // rows past the edge load a valid row, never stored
         const uint16_t *src = X + (int64_t)rr * ld + k0 + 8 * j;
         __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
@@ -139,24 +151,38 @@ __device__ __forceinline__ void g2_copy(const uint16_t *__restrict__ X, int64_t 
     }
 }
 
-template <typename TC, bool RES, int BK, int NST>
+// Tile order.  Workgroups are dealt to the 8 XCDs round-robin (block b on XCD
+// b % 8), so XCD x is handed a contiguous run of the linear tile order (its
+// share of nb, the first nb % 8 XCDs one tile more) and the blocks resident on
+// one XCD at a time work on neighbouring tiles.  The linear order walks groups
+// of G2_GROUP_M tile rows column by column, so the resident blocks of an XCD
+// share A row panels and B column panels through its L2.  The map is a
+// bijection on [0, nbm * nbn) whatever the hardware's dispatch order.
+__device__ __forceinline__ void g2_tile(int b, int nbm, int nbn, int &tm, int &tn) {
+    const int nb = nbm * nbn;
+    const int x = b % 8, base = nb / 8, rem = nb % 8;
+    const int t = x * base + min(x, rem) + b / 8;
+    const int gsz = G2_GROUP_M * nbn;
+    const int r0 = (t / gsz) * G2_GROUP_M;
+    const int gm = min(G2_GROUP_M, nbm - r0);
+    const int local = t - (t / gsz) * gsz;
+    tm = r0 + local % gm;
+    tn = local / gm;
+}
+
+template <typename TC, bool RES>
 __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
     const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
     TC *__restrict__ C, int64_t ldc, const uint16_t *__restrict__ R, int64_t ldr, int M, int N,
     int K) {
-    constexpr int CPR = BK / 8;
-    constexpr size_t TILE = (size_t)G2M * BK * 2;
-    constexpr size_t STAGE = 2 * TILE;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves: rows 64 wm, columns 128 wn
     const int lr = lane & 15, lg = lane >> 4;
-    // XCD-aware tile order: the 8 XCDs take contiguous runs of tiles
     const int nbn = (N + G2N - 1) / G2N, nbm = (M + G2M - 1) / G2M;
-    const int nb = nbn * nbm;
-    int bid = blockIdx.x;
-    if (nb % 8 == 0) bid = (bid % 8) * (nb / 8) + bid / 8;
-    const int m0 = (bid / nbn) * G2M, n0 = (bid % nbn) * G2N;
+    int tm, tn;
+    g2_tile(blockIdx.x, nbm, nbn, tm, tn);
+    const int m0 = tm * G2M, n0 = tn * G2N;
 
     floatx4_t acc[4][8];
 #pragma unroll
@@ -164,54 +190,87 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
-    // NST - 1 k-steps in flight ahead of the one being multiplied
+    // fragment: row lr of a 16-row tile, logical chunk 4 ks + lg (8 bf16)
+    auto frag_a = [&](const uint8_t *At, int ks, int i) {
+        const int r = wm * 64 + i * 16 + lr;
+        const int pc = (4 * ks + lg) ^ (r & (G2_CPR - 1));
+        return *reinterpret_cast<const bf16x8_t *>(At + (size_t)r * (2 * G2_BK) + 16 * pc);
+    };
+    auto frag_b = [&](const uint8_t *Bt, int ks, int j) {
+        const int r = wn * 128 + j * 16 + lr;
+        const int pc = (4 * ks + lg) ^ (r & (G2_CPR - 1));
+        return *reinterpret_cast<const bf16x8_t *>(Bt + (size_t)r * (2 * G2_BK) + 16 * pc);
+    };
+
+    const int nk = K / G2_BK;
+    g2_copy(A, lda, M, m0, 0, smem, tid);
+    g2_copy(B, ldb, N, n0, 0, smem + G2_TILE, tid);
+    if (nk > 1) {
+        g2_copy(A, lda, M, m0, G2_BK, smem + G2_STAGE, tid);
+        g2_copy(B, ldb, N, n0, G2_BK, smem + G2_STAGE + G2_TILE, tid);
+        // stage 0 landed (loads complete in order; vmcnt <= one stage's loads,
+        // expcnt and lgkmcnt not waited on)
+        static_assert(G2_LOADS < 16, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | G2_LOADS);
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    bf16x8_t a0[4], b0[8], a1[4], b1[8];
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p)
-        if (p < nk) {
-            g2_copy<BK>(A, lda, M, m0, p * BK, smem + (size_t)p * STAGE, tid);
-            g2_copy<BK>(B, ldb, N, n0, p * BK, smem + (size_t)p * STAGE + TILE, tid);
-        }
+    for (int i = 0; i < 4; ++i) a0[i] = frag_a(smem, 0, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b0[j] = frag_b(smem + G2_TILE, 0, j);
+
     for (int kt = 0; kt < nk; ++kt) {
-        const uint8_t *cur = smem + (size_t)(kt % NST) * STAGE;
-        // wait until only the copies of the later NST - 2 k-steps are outstanding
-        // (each k-step is BK / 8 load instructions per thread; loads complete in
-        // order); near the end fewer are in flight, so wait for all
-        constexpr int ALLOWED = (NST - 2) * (BK / 8);
-        constexpr int VMCNT_ENC = 0x0F70 | (ALLOWED & 15) | ((ALLOWED >> 4) << 14);  // expcnt, lgkmcnt: no wait
-        static_assert(ALLOWED < 64, "vmcnt range");
-        if (NST == 2 || kt + NST - 2 >= nk) __builtin_amdgcn_s_waitcnt(0);
-        else __builtin_amdgcn_s_waitcnt(VMCNT_ENC);
-        __syncthreads();  // stage kt landed; every wave is done with the stage refilled next
-        if (kt + NST - 1 < nk) {
-            uint8_t *nxt = smem + (size_t)((kt + NST - 1) % NST) * STAGE;
-            g2_copy<BK>(A, lda, M, m0, (kt + NST - 1) * BK, nxt, tid);
-            g2_copy<BK>(B, ldb, N, n0, (kt + NST - 1) * BK, nxt + TILE, tid);
-        }
-        const uint8_t *At = cur, *Bt = cur + TILE;
+        uint8_t *cur = smem + (size_t)(kt & 1) * G2_STAGE;
+        // phase A: k-slice 0 from registers, slice 1 read meanwhile
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            // fragment: row lr of a 16-row tile, logical chunk 4 ks + lg (8 bf16)
-            bf16x8_t af[4], bfr[8];
+        for (int i = 0; i < 4; ++i) a1[i] = frag_a(cur, 1, i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + i * 16 + lr;
-                const int pc = (4 * ks + lg) ^ (r & (CPR - 1));
-                af[i] = *reinterpret_cast<const bf16x8_t *>(At + (size_t)r * (2 * BK) + 16 * pc);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = wn * 128 + j * 16 + lr;
-                const int pc = (4 * ks + lg) ^ (r & (CPR - 1));
-                bfr[j] = *reinterpret_cast<const bf16x8_t *>(Bt + (size_t)r * (2 * BK) + 16 * pc);
-            }
+        for (int j = 0; j < 8; ++j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+            b1[j] = frag_b(cur + G2_TILE, 1, j);
+        }
+        // keep the reads between the MFMAs (mask 0x100: LDS reads, 0x008: MFMA)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // the next stage has landed and every wave is done reading this one
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // phase B: slice 1 from registers; the next stage's slice-0 fragments read
+        // (on the last step: stale, in-bounds LDS, never used) and this buffer
+        // refilled with the stage after next (near the end: the last stage again,
+        // in bounds, never read)
+        const uint8_t *nx = smem + (size_t)((kt + 1) & 1) * G2_STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a0[i] = frag_a(nx, 0, i);
+        const int kc = min(kt + 2, nk - 1) * G2_BK;
+        g2_copy(A, lda, M, m0, kc, cur, tid);
+        g2_copy(B, ldb, N, n0, kc, cur + G2_TILE, tid);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+            b0[j] = frag_b(nx + G2_TILE, 0, j);
+        }
+        // mask 0x020: the direct-to-LDS loads, spread over the first half
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (j < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the last copies land before the block's LDS is released
 
     // accumulator layout: lane holds rows 4 lg + r, column lr of each tile
 #pragma unroll
@@ -231,21 +290,17 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
         }
 }
 
-constexpr int G2_BK = 64, G2_NST = 2;  // K step and pipeline stages of the 256 x 256 kernel
-
 template <typename TC, bool RES>
 static hipError_t launch_gemm_v2(const GemmArgs &a, hipStream_t s) {
-    constexpr size_t smem = (size_t)G2_NST * 2 * G2M * G2_BK * 2;
     static bool set = false;
     if (!set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&gemm_bf16_v2_kernel<TC, RES, G2_BK, G2_NST>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_v2_kernel<TC, RES>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)G2_SMEM);
         if (e != hipSuccess) return e;
         set = true;
     }
     const int nb = ((a.M + G2M - 1) / G2M) * ((a.N + G2N - 1) / G2N);
-    hipLaunchKernelGGL((gemm_bf16_v2_kernel<TC, RES, G2_BK, G2_NST>), dim3(nb), dim3(G2_THREADS), smem, s,
+    hipLaunchKernelGGL((gemm_bf16_v2_kernel<TC, RES>), dim3(nb), dim3(G2_THREADS), G2_SMEM, s,
                        (const uint16_t *)a.A, a.lda, (const uint16_t *)a.B, a.ldb, (TC *)a.C, a.ldc,
                        (const uint16_t *)a.R, a.ldr, a.M, a.N, a.K);
     return hipGetLastError();
@@ -253,7 +308,7 @@ static hipError_t launch_gemm_v2(const GemmArgs &a, hipStream_t s) {
 
 static bool g2_ok(const GemmArgs &a) {
     auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-    return a.K % G2_BK == 0 && a.M > 0 && a.N > 0 && al16(a.A) && al16(a.B) && a.lda % 8 == 0 &&
+    return a.K > 0 && a.K % G2_BK == 0 && a.M > 0 && a.N > 0 && al16(a.A) && al16(a.B) && a.lda % 8 == 0 &&
            a.ldb % 8 == 0;
 }
 
