@@ -568,11 +568,13 @@ def test_rmsnorm_parity(rows, cols, ydt):
 @pytest.mark.parametrize("M,N,K,res", [(300, 200, 5120, False), (129, 136, 264, True),
                                        (1, 8, 8, False), (256, 96, 5120, True),
                                        (513, 264, 64, True), (1000, 520, 640, False),
-                                       (300, 520, 128, False), (257, 264, 192, True)])
+                                       (300, 520, 128, False), (257, 264, 192, True),
+                                       (90 * 256 - 37, 600, 128, False)])
 def test_gemm_parity(M, N, K, res):
     """K a multiple of 64 takes the 256 x 256 tile kernel (edges of M and N not
     multiples of 256 included; one, two and three 64-deep stages, where the
-    refill two stages ahead runs past the end), other K the 128 x 128 one."""
+    refill two stages ahead runs past the end; 270 tiles, more than one per
+    CU, the last row and column partial), other K the 128 x 128 one."""
     rng = np.random.default_rng(M + N + K)
     A = torch.from_numpy(rng.standard_normal((M, K))).to(torch.bfloat16)
     B = torch.from_numpy(rng.standard_normal((N, K)) * 0.02).to(torch.bfloat16)
