@@ -171,14 +171,13 @@ constexpr int PT_OFF = 16 * VROW;
 constexpr int WREG = PT_OFF + 2 * 16 * 16 * 2;
 constexpr float RESCALE_LOG2 = 8.f;  // keep p below 2^8 before moving the reference max
 
-// e4m3 -> bf16 for 8 codes: every e4m3 value is exact in bf16, so the top
-// halves of the hardware's fp32 conversions are the bf16 patterns
-template <bool HI> __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-}
+// e4m3 -> bf16 for 4 codes: every e4m3 value is exact in bf16, and gfx950's
+// scaled fp8 -> bf16 conversion at scale 1 yields those patterns directly, two
+// codes per instruction (OCP decoding, NaN codes and signed zeros included,
+// checked on all 256 codes)
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-    return make_uint2(fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w));
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
 }
 
 // FP8: the cache holds e4m3 codes (k_scale folded into qscale by the host,
