@@ -359,15 +359,18 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
             need |= tmax[i] > Mu[i] + RESCALE_LOG2;
         }
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            floatx4_t alv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float mnew = tmax[i] > Mu[i] + RESCALE_LOG2 ? tmax[i] : Mu[i];
                 const float al = Mu[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mu[i] - mnew);
                 lsum[i] *= al;
-#pragma unroll
-                for (int db = 0; db < 16; ++db) O[db][i] *= al;
+                alv[i] = al;
                 Mu[i] = mnew;
             }
+            // whole accumulators, so that they keep their registers across the branch
+#pragma unroll
+            for (int db = 0; db < 16; ++db) O[db] *= alv;
         }
         float pr[4];
 #pragma unroll
