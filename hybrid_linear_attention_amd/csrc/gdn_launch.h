@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gdn {
 
 struct ConvArgs {
@@ -118,5 +120,21 @@ struct GemmArgs {
     int32_t M, N, K;
 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s);
+
+// Raise a kernel's dynamic-LDS limit once per device (the attribute belongs to
+// the device the call is made on); `done` records the devices already set, as
+// bits of an atomic mask, so concurrent first calls are harmless.
+template <typename K>
+inline hipError_t set_smem_once(K kern, size_t bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_relaxed) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
 
 }  // namespace gdn

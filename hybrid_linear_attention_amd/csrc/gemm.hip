@@ -292,13 +292,9 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
 
 template <typename TC, bool RES>
 static hipError_t launch_gemm_v2(const GemmArgs &a, hipStream_t s) {
-    static bool set = false;
-    if (!set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_bf16_v2_kernel<TC, RES>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)G2_SMEM);
-        if (e != hipSuccess) return e;
-        set = true;
-    }
+    static std::atomic<uint64_t> set{0};
+    hipError_t e = set_smem_once(&gemm_bf16_v2_kernel<TC, RES>, G2_SMEM, set);
+    if (e != hipSuccess) return e;
     const int nb = ((a.M + G2M - 1) / G2M) * ((a.N + G2N - 1) / G2N);
     hipLaunchKernelGGL((gemm_bf16_v2_kernel<TC, RES>), dim3(nb), dim3(G2_THREADS), G2_SMEM, s,
                        (const uint16_t *)a.A, a.lda, (const uint16_t *)a.B, a.ldb, (TC *)a.C, a.ldc,

@@ -1383,15 +1383,6 @@ size_t prefill_chunk_workspace_bytes(int32_t Hk, int32_t Hv, int32_t T, int32_t 
     return ChunkWorkspace(Hk, Hv, T, nreq).total;
 }
 
-template <typename K>
-static hipError_t set_smem(K kern, size_t bytes, bool &done) {
-    if (done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) done = true;
-    return e;
-}
-
 // TA: the type of v (or float for V images); VIMG: v from the V images the
 // prep kernel wrote, and the chain writes the new conv history (of type TX).
 template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS, int NCW>
@@ -1399,9 +1390,9 @@ static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
-    static bool set = false;
+    static std::atomic<uint64_t> set{0};
     const size_t smem = STAGES * STAGE;
-    hipError_t e = set_smem(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS, NCW>, smem, set);
+    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS, NCW>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
@@ -1418,9 +1409,9 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
                                      const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
     constexpr int NW = GRP_NW;
-    static bool set = false;
+    static std::atomic<uint64_t> set{0};
     const size_t smem = STAGES * (KIMG + G * TIMG);
-    hipError_t e = set_smem(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
+    hipError_t e = set_smem_once(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * (int64_t)(D / GRP_ROWS) * ((groups + 7) / 8);
@@ -1449,8 +1440,8 @@ template <typename TA, typename TG, typename TX, typename TW, bool CONV>
 static hipError_t launch_prep(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                               uint8_t *kimg, uint8_t *timg, const PrepConvIn &cv, float *vimg) {
     using namespace chunk;
-    static bool set = false;
-    hipError_t e = set_smem(&prefill_prep_kernel<TA, TG, TX, TW, CONV>, sizeof(PrepSmem), set);
+    static std::atomic<uint64_t> set{0};
+    hipError_t e = set_smem_once(&prefill_prep_kernel<TA, TG, TX, TW, CONV>, sizeof(PrepSmem), set);
     if (e != hipSuccess) return e;
     const int64_t max_chunks = (int64_t)a.T / CH + a.nreq;
     hipLaunchKernelGGL((prefill_prep_kernel<TA, TG, TX, TW, CONV>), dim3((unsigned)(max_chunks * a.Hk)),
