@@ -126,17 +126,20 @@ template <> struct Vec8<bf16> {
 constexpr int RMS_THREADS = 256;
 constexpr int RMS_MAX_VEC = 8;  // up to 256 * 8 * 8 = 16384 columns
 
-template <typename TX, typename TG, typename TY>
+// VEC: 8-element vectors per thread, the fewest that cover the row (the row
+// stays in registers between the sum of squares and the scaling, and a smaller
+// VEC keeps more blocks resident)
+template <typename TX, typename TG, typename TY, int VEC>
 __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(
     const TX *__restrict__ x, const TG *__restrict__ gamma, float eps, int32_t cols,
     TY *__restrict__ y) {
     __shared__ float part[RMS_THREADS / 64];
     const int64_t row = blockIdx.x;
     const int nvec = cols / 8;
-    float buf[RMS_MAX_VEC][8];
+    float buf[VEC][8];
     float ss = 0.f;
 #pragma unroll
-    for (int it = 0; it < RMS_MAX_VEC; ++it) {
+    for (int it = 0; it < VEC; ++it) {
         const int vi = it * RMS_THREADS + threadIdx.x;
         if (vi < nvec) {
             Vec8<TX>::load(x + row * cols + vi * 8, buf[it]);
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_kernel(
     for (int w = 0; w < RMS_THREADS / 64; ++w) tot += part[w];
     const float inv = 1.0f / sqrtf(tot / (float)cols + eps);
 #pragma unroll
-    for (int it = 0; it < RMS_MAX_VEC; ++it) {
+    for (int it = 0; it < VEC; ++it) {
         const int vi = it * RMS_THREADS + threadIdx.x;
         if (vi < nvec) {
             float g[8], out[8];
@@ -219,11 +222,21 @@ hipError_t launch_gated_norm(const GatedNormArgs &a, hipStream_t s) {
     }
 }
 
-template <typename TX, typename TG, typename TY>
-static hipError_t launch_rms_t(const RmsNormArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((rmsnorm_kernel<TX, TG, TY>), dim3(a.rows), dim3(RMS_THREADS), 0, s,
+template <typename TX, typename TG, typename TY, int VEC>
+static hipError_t launch_rms_v(const RmsNormArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((rmsnorm_kernel<TX, TG, TY, VEC>), dim3(a.rows), dim3(RMS_THREADS), 0, s,
                        (const TX *)a.x, (const TG *)a.gamma, a.eps, a.cols, (TY *)a.y);
     return hipGetLastError();
+}
+template <typename TX, typename TG, typename TY>
+static hipError_t launch_rms_t(const RmsNormArgs &a, hipStream_t s) {
+    const int per = (a.cols / 8 + RMS_THREADS - 1) / RMS_THREADS;  // vectors per thread
+    if (per <= 1) return launch_rms_v<TX, TG, TY, 1>(a, s);
+    if (per <= 2) return launch_rms_v<TX, TG, TY, 2>(a, s);
+    if (per <= 3) return launch_rms_v<TX, TG, TY, 3>(a, s);
+    if (per <= 4) return launch_rms_v<TX, TG, TY, 4>(a, s);
+    static_assert(RMS_MAX_VEC == 8, "widest row");
+    return launch_rms_v<TX, TG, TY, 8>(a, s);
 }
 template <typename TX, typename TG>
 static hipError_t launch_rms_y(const RmsNormArgs &a, hipStream_t s) {

@@ -551,8 +551,12 @@ def test_prefill_chain_parity(which):
 # ---------------------------------------------------------------------------
 # RMSNorm and GEMM (layer-block stages)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("rows,cols,ydt", [(37, 5120, torch.bfloat16), (5, 136, torch.float32)])
+@pytest.mark.parametrize("rows,cols,ydt", [(37, 5120, torch.bfloat16), (5, 136, torch.float32),
+                                           (3, 4096, torch.bfloat16), (3, 8184, torch.float32),
+                                           (2, 12000, torch.bfloat16)])
 def test_rmsnorm_parity(rows, cols, ydt):
+    """Rows of 1, 2, 3, 4 and 8 vectors of 8 per thread (the kernel's register
+    footprint is picked from the row width)."""
     rng = np.random.default_rng(cols)
     x = torch.from_numpy(rng.standard_normal((rows, cols))).to(torch.bfloat16)
     g = torch.from_numpy(1 + 0.02 * rng.standard_normal(cols)).to(torch.bfloat16)
