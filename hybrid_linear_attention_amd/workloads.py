@@ -6,15 +6,18 @@ fed the tensors it returns (CPU torch tensors; the oracle widens them exactly to
 fp64, the GPU path copies them to the device).
 
 Generator: ``numpy.random.Generator(PCG64(seed))`` (seed 1234 + workload id for
-the five named workloads).  Normal draws are float32 from that generator, scaled
-by the standard deviation in float32 and rounded to bf16 round-to-nearest-even
-by torch on the CPU where the storage dtype is bf16.  Draw order is fixed and
-documented in ``make_gdn_case``.
+the five named workloads) draws the integers (lengths, permutations) and one
+key per tensor; a tensor's normal values are float32 draws from keyed block
+streams (``_normal``), scaled by the standard deviation in float32 and rounded
+to bf16 round-to-nearest-even by torch on the CPU where the storage dtype is
+bf16.  Draw order is fixed and documented in ``make_gdn_case``.
 
 Shapes follow the tutorial page's data-structure table (section 01): q/k
 [T,16,128], v/z [T,48,128], a/b [T,48], state [R,48,128,128] fp32, conv history
 [R,10240,3].
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
@@ -75,17 +78,41 @@ class GdnCase:
         return int(self.state_pool.shape[0])
 
 
-def _normal(rng, shape, std, dtype):
-    """float32 normal draws scaled by std, stored as ``dtype`` (RNE for bf16)."""
+_BLOCK = 1 << 22          # normal draws per keyed block
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _normal(rng, shape, std, dtype, mean=0.0):
+    """Normal draws N(mean, std) of one tensor, stored as ``dtype`` (RNE for
+    bf16).
+
+    The tensor takes one 63-bit key from the workload's stream ``rng``; its
+    elements, in blocks of 2^22, are float32 standard normals from
+    ``PCG64(SeedSequence([key, block]))``, scaled by std and shifted by mean in
+    float32.  The blocks are independent streams, so they are filled by a
+    thread pool and the values do not depend on the thread count."""
+    key = int(rng.integers(0, 2 ** 63 - 1))
     n = int(np.prod(shape)) if len(shape) else 1
     out = torch.empty(n, dtype=dtype)
-    step = 1 << 24  # bounded temporaries for the multi-GB workloads
-    for s in range(0, n, step):
-        e = min(n, s + step)
-        blk = rng.standard_normal(e - s, dtype=np.float32)
+
+    def fill(j):
+        s = j * _BLOCK
+        e = min(n, s + _BLOCK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([key, j])))
+        blk = g.standard_normal(e - s, dtype=np.float32)
         if std != 1.0:
             blk *= np.float32(std)
+        if mean != 0.0:
+            blk += np.float32(mean)
         out[s:e] = torch.from_numpy(blk).to(dtype)
+
+    nblk = (n + _BLOCK - 1) // _BLOCK
+    if nblk <= 1:
+        for j in range(nblk):
+            fill(j)
+    else:
+        with ThreadPoolExecutor(min(_THREADS, nblk)) as ex:
+            list(ex.map(fill, range(nblk)))
     return out.reshape(shape)
 
 
@@ -103,16 +130,20 @@ def make_gdn_case(seed: int, dims: GdnDims, lengths: Optional[List[int]] = None,
                   permute_slots: bool = False, act_dtype=torch.bfloat16,
                   pool_dtype=None, weight_dtype=None, state_std: float = 0.0,
                   hist_std: float = 0.0, has_initial: Optional[bool] = None,
-                  conv_w_std: float = 0.5, gamma_std: float = 0.0) -> GdnCase:
+                  conv_w_std: float = 0.5, gamma_std: float = 0.0,
+                  target_total=None, a_mean: float = 0.0) -> GdnCase:
     """Build one seeded GDN-core workload.
 
     Draw order from one PCG64 stream:
       1. request lengths (only if ``random_lengths=(n, lo, hi)``: integers in
-         [lo, hi] inclusive),
+         [lo, hi] inclusive; with ``target_total=(total, frac)`` the n lengths
+         are drawn again, from the same stream, until their sum lies within
+         frac of total),
       2. slot permutation of range(num_slots) (only if ``permute_slots``),
       3. initial state of each used slot, in request order (if state_std > 0),
       4. conv history of each used slot, in request order (if hist_std > 0),
-      5. x_qkv [T, Cqkv], 6. z [T, Hv, dv], 7. a [T, Hv], 8. b [T, Hv] ~ N(0,1),
+      5. x_qkv [T, Cqkv], 6. z [T, Hv, dv] ~ N(0,1), 7. a [T, Hv] ~ N(a_mean, 1),
+         8. b [T, Hv] ~ N(0,1),
       9. conv_w [Cqkv, taps] ~ N(0, conv_w_std),
      10. gamma = 1 + N(0, gamma_std) (only if gamma_std > 0, else exactly 1).
     Unused slots carry a NaN sentinel bit pattern.
@@ -120,7 +151,10 @@ def make_gdn_case(seed: int, dims: GdnDims, lengths: Optional[List[int]] = None,
     rng = np.random.Generator(np.random.PCG64(seed))
     if random_lengths is not None:
         n, lo, hi = random_lengths
-        lengths = [int(x) for x in rng.integers(lo, hi + 1, n)]
+        while True:
+            lengths = [int(x) for x in rng.integers(lo, hi + 1, n)]
+            if target_total is None or abs(sum(lengths) - target_total[0]) <= target_total[1] * target_total[0]:
+                break
     assert lengths is not None
     nreq = len(lengths)
     if num_slots is None:
@@ -157,7 +191,7 @@ def make_gdn_case(seed: int, dims: GdnDims, lengths: Optional[List[int]] = None,
 
     x_qkv = _normal(rng, (T, C), 1.0, act_dtype)
     z = _normal(rng, (T, Hv, dv), 1.0, act_dtype)
-    a = _normal(rng, (T, Hv), 1.0, act_dtype)
+    a = _normal(rng, (T, Hv), 1.0, act_dtype, mean=a_mean)
     b = _normal(rng, (T, Hv), 1.0, act_dtype)
     conv_w = _normal(rng, (C, dims.conv_taps), conv_w_std, weight_dtype)
     if gamma_std > 0:
@@ -197,13 +231,18 @@ def prefill_4096(seed: int = 1236) -> GdnCase:
     return make_gdn_case(seed, FULL_DIMS, [4096])
 
 
+VARLEN16_TOTAL = 66000  # the packed batch's stated size, about 66k tokens
+
+
 def prefill_varlen16(seed: int = 1237) -> GdnCase:
-    """Packed varlen prefill: 16 requests of lengths uniform in [256, 8192],
-    slots a seeded permutation of a 64-slot pool, nonzero initial state
+    """Packed varlen prefill: 16 requests of lengths uniform in [256, 8192]
+    whose total is about 66k tokens (length vectors are redrawn from the stream
+    until the sum is within 2% of 66,000; this seed: 66,292 tokens on the 20th
+    draw), slots a seeded permutation of a 64-slot pool, nonzero initial state
     ~ N(0, 0.02) and conv history ~ N(0, 1) per used slot."""
     return make_gdn_case(seed, FULL_DIMS, random_lengths=(16, 256, 8192),
-                         num_slots=64, permute_slots=True, state_std=0.02,
-                         hist_std=1.0)
+                         target_total=(VARLEN16_TOTAL, 0.02), num_slots=64,
+                         permute_slots=True, state_std=0.02, hist_std=1.0)
 
 
 def spec_verify_r64(seed: int = 1239, tokens: int = 4) -> GdnCase:
@@ -216,6 +255,58 @@ def spec_verify_r64(seed: int = 1239, tokens: int = 4) -> GdnCase:
     case = make_gdn_case(seed, FULL_DIMS, [tokens] * R, num_slots=R * (tokens + 1),
                          state_std=0.02, hist_std=1.0)
     case.meta["spec_slots"] = (R + torch.arange(R * tokens, dtype=torch.int32)).reshape(R, tokens)
+    return case
+
+
+# gate values whose maps saturate in float32 and in fp64 alike: softplus(-30)
+# and sigmoid(-30) are ~1e-13, so alpha -> 1 and beta -> 0 (and the reverse at +30)
+GATE_SATURATE = 30.0
+EDGE_KINDS = ("frozen", "write", "forget", "zero_qk", "weak_decay")
+
+
+def edge_case(kind: str, seed: int, lengths: List[int], num_slots: Optional[int] = None,
+              dims: GdnDims = FULL_DIMS) -> GdnCase:
+    """Workloads at the gates' and inputs' extremes (the regimes of the tutorial
+    page's GDN state lab: a small decay erases the state, a large one keeps
+    it; the delta write stores the prediction error).  Built on make_gdn_case
+    (state ~ N(0, 0.02), history ~ N(0, 1), slots permuted), then:
+
+      frozen      a = b = -30 everywhere: alpha ~ 1, beta ~ 0 (nothing written)
+      write       b = +30: beta ~ 1 (a full delta write of a unit k)
+      forget      a = +30: alpha ~ 0 (only the newest write survives)
+      zero_qk     the q and k conv inputs of every token of the first request,
+                  and of its history, are zero, and its a is lowered by 4 (a weak
+                  decay, so that the pure decay it undergoes stays well inside
+                  float32's range); in every other request, the q and k inputs
+                  of a run of tokens from a quarter to three quarters of its
+                  length are zero (q = k = 0 from the run's fourth token on)
+      weak_decay  a ~ N(-4, 1): alpha ~ 0.98, a long memory
+    """
+    if kind not in EDGE_KINDS:
+        raise ValueError(kind)
+    case = make_gdn_case(seed, dims, list(lengths), num_slots=num_slots or len(lengths) + 3,
+                         permute_slots=True, state_std=0.02, hist_std=1.0,
+                         a_mean=-4.0 if kind == "weak_decay" else 0.0)
+    if kind == "frozen":
+        case.a.fill_(-GATE_SATURATE)
+        case.b.fill_(-GATE_SATURATE)
+    elif kind == "write":
+        case.b.fill_(GATE_SATURATE)
+    elif kind == "forget":
+        case.a.fill_(GATE_SATURATE)
+    elif kind == "zero_qk":
+        nqk = 2 * dims.num_k_heads * dims.head_dim_k
+        qsl = case.qsl.tolist()
+        for r in range(case.num_reqs):
+            t0, t1 = qsl[r], qsl[r + 1]
+            if r == 0:
+                case.x_qkv[t0:t1, :nqk] = 0
+                case.conv_pool[case.used_slots[0], :nqk] = 0
+                case.a[t0:t1] -= 4.0
+            else:
+                L = t1 - t0
+                case.x_qkv[t0 + L // 4:t0 + (3 * L) // 4, :nqk] = 0
+    case.meta["edge"] = kind
     return case
 
 

@@ -1,0 +1,202 @@
+"""Composition and determinism on the GPU, through the C ABI.
+
+Composition: a request's state and conv history persist in its slot between
+calls until it ends (tutorial page, section 01 data-structure table), and the
+engine may prefill a long request in pieces over several steps (section 05,
+chunked prefill).  So gdn_prefill_fused over the first T1 tokens of each
+request followed by a second call over the rest must give what one call over
+all T1 + T2 tokens gives: the same y rows, the same final state (both within
+the chunked arithmetic's error of the fp64 oracle) and the same history bit for
+bit.  The cut T1 = 77 is not a multiple of the 32-token chunk, so chunk
+boundaries fall differently in the two runs.  With a bf16 state the first call
+rounds the state once more (at the cut): the split run is compared with the
+oracle run in the same two pieces, with that rounding in between.
+
+Determinism: the decode, single-sequence and varlen workloads run twice on
+fresh copies of their inputs; every output, state and history bit must repeat
+(no kernel on these paths accumulates through atomics or in a
+schedule-dependent order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (OUT_TOL, STATE_TOL, bits, check_bf16_state, check_y_rows, dev, f64, rel_l2)
+from hybrid_linear_attention_amd import gdn
+from hybrid_linear_attention_amd.workloads import (FULL_DIMS, GdnCase, decode_r64, make_gdn_case,
+                                                   prefill_4096, prefill_varlen16)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+L2_EPS = 1e-6
+NORM_EPS = 1e-6
+
+
+def piece(case, cuts, first):
+    """The first cuts[r] tokens of every request (first=True) or the rest."""
+    qsl = case.qsl.numpy()
+    rows, lens = [], []
+    for r in range(case.num_reqs):
+        t0, t1 = int(qsl[r]), int(qsl[r + 1])
+        c = min(int(cuts[r]), t1 - t0)
+        rr = np.arange(t0, t0 + c) if first else np.arange(t0 + c, t1)
+        rows.append(rr)
+        lens.append(len(rr))
+    rows = np.concatenate(rows).astype(np.int64)
+    new_qsl = torch.zeros(case.num_reqs + 1, dtype=torch.int32)
+    new_qsl[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    hi = case.has_initial.clone()
+    if not first:  # a request whose first piece ran continues from its slot
+        hi = torch.tensor([1 if min(int(cuts[r]), int(qsl[r + 1] - qsl[r])) > 0 else int(hi[r])
+                           for r in range(case.num_reqs)], dtype=torch.uint8)
+    idx = torch.from_numpy(rows)
+    return GdnCase(dims=case.dims, x_qkv=case.x_qkv[idx], z=case.z[idx], a=case.a[idx],
+                   b=case.b[idx], conv_w=case.conv_w, gamma=case.gamma, conv_pool=case.conv_pool,
+                   state_pool=case.state_pool, qsl=new_qsl, slot_ids=case.slot_ids,
+                   has_initial=hi, used_slots=case.used_slots), rows
+
+
+def prefill(case, pool, state):
+    """gdn_prefill_fused on device pools; returns y on the host."""
+    d = case.dims
+    T = case.num_tokens
+    y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    if T == 0:
+        return y.cpu()
+    ws = torch.empty(gdn.gdn_prefill_fused_workspace_bytes(d, T, case.num_reqs), dtype=torch.uint8,
+                     device="cuda")
+    gdn.gdn_prefill_fused(d, dev(case.x_qkv), dev(case.z), dev(case.a), dev(case.b),
+                          dev(case.conv_w), dev(case.gamma), pool, state, dev(case.qsl),
+                          dev(case.slot_ids), dev(case.has_initial), y, ws, l2_eps=L2_EPS,
+                          norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def oracle_run(case, state_pool, hist_pool):
+    """conv -> recurrence -> gated norm in fp64 from the given pools; returns
+    (o, y, state, history)."""
+    d = case.dims
+    qr, kr, vr, pr = oracle.conv1d_update(f64(case.x_qkv), f64(case.conv_w), hist_pool,
+                                          case.qsl.numpy(), case.slot_ids.numpy(),
+                                          case.has_initial.numpy(), d.num_k_heads, d.num_v_heads,
+                                          d.head_dim_k, d.head_dim_v, L2_EPS)
+    o, st = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b), state_pool,
+                                    case.qsl.numpy(), case.slot_ids.numpy(),
+                                    case.has_initial.numpy())
+    z = f64(case.z).reshape(case.num_tokens, d.num_v_heads, d.head_dim_v)
+    return o, oracle.gated_norm(o, z, f64(case.gamma), NORM_EPS), st, pr
+
+
+CASES = {
+    # one 4096-token request: 32-row chain blocks
+    "rows_4096": ([4096], [77]),
+    # eight requests: key-head group blocks; cuts at, around and off the chunk
+    "group_eight": ([300, 77, 64, 500, 33, 129, 2, 260], [77, 77, 32, 33, 0, 100, 1, 250]),
+}
+
+
+@pytest.mark.parametrize("state_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("which", list(CASES))
+def test_prefill_split_equals_whole(which, state_dt):
+    lengths, cuts = CASES[which]
+    case = make_gdn_case(600 + len(lengths), FULL_DIMS, lengths, num_slots=len(lengths) + 4,
+                         permute_slots=True, state_std=0.02, hist_std=1.0, gamma_std=0.1)
+    case.has_initial = torch.tensor([r % 4 != 3 for r in range(case.num_reqs)], dtype=torch.uint8)
+    if state_dt == "bf16":
+        case.state_pool = case.state_pool.to(torch.bfloat16)
+    print(f"{which} {state_dt}: lengths {lengths}, cuts {cuts}", flush=True)
+    d = case.dims
+    D = d.head_dim_v
+    # one call over everything
+    pool_w, state_w = dev(case.conv_pool), dev(case.state_pool)
+    y_w = prefill(case, pool_w, state_w)
+    # two calls: the first pieces, then the rest from the slots they left
+    first, rows1 = piece(case, cuts, True)
+    rest, rows2 = piece(case, cuts, False)
+    pool_s, state_s = dev(case.conv_pool), dev(case.state_pool)
+    y1 = prefill(first, pool_s, state_s)
+    state_cut = state_s.cpu()  # the state each request's slot holds between the calls
+    y2 = prefill(rest, pool_s, state_s)
+    y_s = torch.empty_like(y_w)
+    y_s[torch.from_numpy(rows1)] = y1
+    y_s[torch.from_numpy(rows2)] = y2
+    slots = sorted(int(s) for s in case.slot_ids)
+    unused = sorted(set(range(case.num_slots)) - set(slots))
+
+    # history: both runs leave the same raw inputs, bit for bit
+    np.testing.assert_array_equal(bits(pool_s.cpu()), bits(pool_w.cpu()))
+    np.testing.assert_array_equal(bits(state_s.cpu())[unused], bits(case.state_pool)[unused])
+
+    # the split run against the oracle run in the same pieces.  With an fp32
+    # state the oracle carries its own state through the cut (so this is the
+    # whole run).  With a bf16 state each call is checked on its own: the stored
+    # state after the first call is the rounding of the oracle's, and the second
+    # piece starts, on both sides, from the bf16 state the GPU stored (two
+    # roundings of nearly equal values differ by one ulp now and then, and that
+    # difference would otherwise carry into the second call).
+    st0, h0 = f64(case.state_pool), f64(case.conv_pool)
+    o1, y1r, st1, h1 = oracle_run(first, st0, h0)
+    if state_dt == "bf16":
+        check_bf16_state(state_cut, st1, slots, 1e-2, abs_rel=3e-5)
+        st1 = f64(state_cut)
+    o2, y2r, st2, _ = oracle_run(rest, st1, h1)
+    y_ref = np.empty((case.num_tokens, d.num_v_heads * D))
+    y_ref[rows1], y_ref[rows2] = y1r, y2r
+    o_ref = np.empty((case.num_tokens, d.num_v_heads, D))
+    o_ref[rows1], o_ref[rows2] = o1, o2
+    z = f64(case.z).reshape(case.num_tokens, d.num_v_heads, D)
+    e = dict(y_split=rel_l2(f64(y_s), y_ref))
+    e["y_row_split"] = check_y_rows(f64(y_s), y_ref, o_ref, z, f64(case.gamma), D)
+    if state_dt == "f32":
+        e["y_whole"] = rel_l2(f64(y_w), y_ref)
+        e["y_split_vs_whole"] = rel_l2(f64(y_s), f64(y_w))
+        e["state_split"] = rel_l2(f64(state_s.cpu())[slots], st2[slots])
+        e["state_whole"] = rel_l2(f64(state_w.cpu())[slots], st2[slots])
+        e["state_split_vs_whole"] = rel_l2(f64(state_s.cpu())[slots], f64(state_w.cpu())[slots])
+    else:
+        _, yw_ref, stw_ref, _ = oracle_run(case, st0, h0)
+        e["y_whole"] = rel_l2(f64(y_w), yw_ref)
+    print("  ".join(f"{k} {v:.2e}" for k, v in e.items()))
+    assert e["y_split"] <= OUT_TOL and e["y_whole"] <= OUT_TOL
+    if state_dt == "f32":
+        assert e["y_split_vs_whole"] <= OUT_TOL
+        assert e["state_split"] <= STATE_TOL and e["state_whole"] <= STATE_TOL
+        # both within the chunked arithmetic's ~1e-5 of the exact state
+        assert e["state_split_vs_whole"] <= 1e-4
+    else:
+        # each run's stored state is the rounding of its fp64 counterpart
+        check_bf16_state(state_s.cpu(), st2, slots, 1e-2, abs_rel=3e-5)
+        check_bf16_state(state_w.cpu(), stw_ref, slots, 1e-2, abs_rel=3e-5)
+
+
+def run_decode(case):
+    d = case.dims
+    R = case.num_reqs
+    pool, state = dev(case.conv_pool), dev(case.state_pool)
+    y = torch.empty((R, d.num_v_heads * d.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((R, d.num_v_heads, d.head_dim_v), device="cuda")
+    gdn.gdn_decode_fused(d, dev(case.x_qkv), dev(case.z), dev(case.a), dev(case.b), dev(case.conv_w),
+                         dev(case.gamma), pool, state, dev(case.slot_ids), y,
+                         has_initial=dev(case.has_initial), o=o, l2_eps=L2_EPS, norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    return [y.cpu(), o.cpu(), pool.cpu(), state.cpu()]
+
+
+def run_prefill(case):
+    pool, state = dev(case.conv_pool), dev(case.state_pool)
+    y = prefill(case, pool, state)
+    return [y, pool.cpu(), state.cpu()]
+
+
+@pytest.mark.parametrize("which", ["decode_r64", "prefill_4096", "prefill_varlen16"])
+def test_bitwise_repeatable(which):
+    case = {"decode_r64": decode_r64, "prefill_4096": prefill_4096,
+            "prefill_varlen16": prefill_varlen16}[which]()
+    run = run_decode if which == "decode_r64" else run_prefill
+    first = run(case)
+    second = run(case)
+    for a, b in zip(first, second):
+        np.testing.assert_array_equal(bits(a), bits(b))
+    print(f"{which}: {len(first)} outputs repeat bit for bit")

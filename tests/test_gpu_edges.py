@@ -1,0 +1,234 @@
+"""GPU parity at the method's edge cases, through the C ABI.
+
+The regimes of the tutorial page's GDN state lab (a small alpha erases the
+state, a large one keeps it; the delta write stores the prediction error), at
+full head shapes (16 key heads, 48 value heads, d = 128), each through
+  * gdn_prefill_fused with one request (32-row chain blocks) and with eight
+    requests (key-head group blocks),
+  * gdn_prefill_varlen (o visible), and
+  * gdn_decode_fused, one token per request per step over several steps.
+Inputs come from workloads.edge_case: saturated gates (a, b = +-30, where
+alpha and beta reach 0 or 1 to within 1e-13), tokens whose q and k are exactly
+zero, and the weak-decay regime alpha ~ 0.98 over a 4096-token request.
+Every result is compared with the fp64 oracle at the usual tolerances (output
+2e-3, state 1e-3 rel-L2, row bounds, history bit for bit); in addition each
+case's closed form is checked on the GPU's own result:
+  frozen  (alpha = 1, beta = 0): every state is its initial state;
+  write   (beta = 1, |k| = 1):   S k = v for each request's last token;
+  forget  (alpha = 0):           S = beta v k^T of each request's last token;
+  zero_qk (q = k = 0):           o and y are exactly zero on those tokens, and
+                                 the all-zero request's state is
+                                 prod(alpha) S0, a pure decay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (FP32_TOL, OUT_TOL, STATE_TOL, bits, check_o_rows, check_y_rows, dev, f64,
+                     rel_l2)
+from hybrid_linear_attention_amd import gdn
+from hybrid_linear_attention_amd.workloads import edge_case
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
+
+L2_EPS = 1e-6
+NORM_EPS = 1e-6
+SAT_KINDS = ["frozen", "write", "forget", "zero_qk"]
+ONE_REQ = [301]                                  # 10 chunks, a ragged last one
+EIGHT_REQS = [77, 300, 1, 0, 64, 129, 33, 250]   # 8 x 48 heads >= 256 units: group blocks
+
+
+def oracle_chain(case):
+    d = case.dims
+    qr, kr, vr, pr = oracle.conv1d_update(f64(case.x_qkv), f64(case.conv_w), f64(case.conv_pool),
+                                          case.qsl.numpy(), case.slot_ids.numpy(),
+                                          case.has_initial.numpy(), d.num_k_heads, d.num_v_heads,
+                                          d.head_dim_k, d.head_dim_v, L2_EPS)
+    o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
+                                            f64(case.state_pool), case.qsl.numpy(),
+                                            case.slot_ids.numpy(), case.has_initial.numpy())
+    z = f64(case.z).reshape(case.num_tokens, d.num_v_heads, d.head_dim_v)
+    y_ref = oracle.gated_norm(o_ref, z, f64(case.gamma), NORM_EPS)
+    return dict(q=qr, k=kr, v=vr, o=o_ref, y=y_ref, z=z, state=st_ref, pool=pr)
+
+
+def run_prefill_fused(case):
+    d = case.dims
+    T = case.num_tokens
+    pool = dev(case.conv_pool)
+    state = dev(case.state_pool)
+    y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_fused_workspace_bytes(d, T, case.num_reqs), dtype=torch.uint8,
+                     device="cuda")
+    gdn.gdn_prefill_fused(d, dev(case.x_qkv), dev(case.z), dev(case.a), dev(case.b), dev(case.conv_w),
+                          dev(case.gamma), pool, state, dev(case.qsl), dev(case.slot_ids),
+                          dev(case.has_initial), y, ws, l2_eps=L2_EPS, norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    return dict(o=None, y=y.cpu(), pool=pool.cpu(), state=state.cpu())
+
+
+def run_prefill_separate(case):
+    d = case.dims
+    T = case.num_tokens
+    D = d.head_dim_k
+    q = torch.empty((T, d.num_k_heads, D), device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, d.num_v_heads, D), device="cuda")
+    o = torch.empty((T, d.num_v_heads, D), device="cuda")
+    y = torch.empty((T, d.num_v_heads * D), dtype=torch.bfloat16, device="cuda")
+    pool = dev(case.conv_pool)
+    state = dev(case.state_pool)
+    qsl, slots, hi = dev(case.qsl), dev(case.slot_ids), dev(case.has_initial)
+    gdn.gdn_conv1d_update(d, dev(case.x_qkv), dev(case.conv_w), pool, qsl, slots, hi, q, k, v,
+                          l2_eps=L2_EPS)
+    nbytes = gdn.gdn_prefill_workspace_bytes(d, T, case.num_reqs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gdn.gdn_prefill_varlen(d, q, k, v, dev(case.a), dev(case.b), state, qsl, slots, hi, o, ws)
+    gdn.gdn_gated_norm(d, o, dev(case.z), dev(case.gamma), y, eps=NORM_EPS)
+    torch.cuda.synchronize()
+    return dict(o=o.cpu(), y=y.cpu(), pool=pool.cpu(), state=state.cpu())
+
+
+def run_decode_steps(case):
+    """Every request has the same number of tokens; step j feeds token j of each
+    request to gdn_decode_fused (state and history carried in the pools)."""
+    d = case.dims
+    R = case.num_reqs
+    lens = np.diff(case.qsl.numpy())
+    n = int(lens[0])
+    assert np.all(lens == n)
+    pool = dev(case.conv_pool)
+    state = dev(case.state_pool)
+    Hv, D = d.num_v_heads, d.head_dim_v
+    y = torch.empty((R * n, Hv * D), dtype=torch.bfloat16)
+    o = torch.empty((R * n, Hv, D))
+    yj = torch.empty((R, Hv * D), dtype=torch.bfloat16, device="cuda")
+    oj = torch.empty((R, Hv, D), device="cuda")
+    slots = dev(case.slot_ids)
+    hi = dev(case.has_initial)
+    ones = torch.ones(R, dtype=torch.uint8, device="cuda")
+    for j in range(n):
+        rows = np.arange(R) * n + j
+        gdn.gdn_decode_fused(d, dev(case.x_qkv[rows]), dev(case.z[rows]), dev(case.a[rows]),
+                             dev(case.b[rows]), dev(case.conv_w), dev(case.gamma), pool, state, slots,
+                             yj, has_initial=hi if j == 0 else ones, o=oj, l2_eps=L2_EPS,
+                             norm_eps=NORM_EPS)
+        torch.cuda.synchronize()
+        y[rows] = yj.cpu()
+        o[rows] = oj.cpu()
+    return dict(o=o, y=y, pool=pool.cpu(), state=state.cpu())
+
+
+def check_against_oracle(case, run, ref, state_tol=STATE_TOL, out_tol=OUT_TOL, rows=True):
+    d = case.dims
+    D = d.head_dim_v
+    lens = np.diff(case.qsl.numpy())
+    touched = [int(s) for s, L in zip(case.slot_ids, lens) if L > 0]
+    e = dict(y=rel_l2(f64(run["y"]), ref["y"]),
+             state=rel_l2(f64(run["state"])[touched], ref["state"][touched]))
+    if rows:
+        e["y_row"] = check_y_rows(f64(run["y"]), ref["y"], ref["o"], ref["z"], f64(case.gamma), D)
+    if run["o"] is not None:
+        e["o"] = rel_l2(f64(run["o"]), ref["o"])
+        if rows:
+            e["o_row"] = check_o_rows(f64(run["o"]), ref["o"], D)
+    print("  ".join(f"{k} {v:.2e}" for k, v in e.items()))
+    assert e.get("o", 0.0) <= out_tol and e["y"] <= OUT_TOL and e["state"] <= state_tol, e
+    # history bit for bit; untouched slots keep their bits
+    gb, ib = bits(run["pool"]), bits(case.conv_pool)
+    for s in range(case.num_slots):
+        if s in touched:
+            refh = torch.from_numpy(ref["pool"][s]).to(case.conv_pool.dtype)
+            np.testing.assert_array_equal(gb[s], bits(refh), err_msg=f"history slot {s}")
+        else:
+            np.testing.assert_array_equal(gb[s], ib[s], err_msg=f"untouched history slot {s}")
+    untouched = sorted(set(range(case.num_slots)) - set(touched))
+    np.testing.assert_array_equal(bits(run["state"])[untouched], bits(case.state_pool)[untouched])
+
+
+def check_closed_form(case, run, ref):
+    """The kind's closed form on the GPU's own result (see the module notes)."""
+    kind = case.meta["edge"]
+    d = case.dims
+    g = d.num_v_heads // d.num_k_heads
+    qsl = case.qsl.numpy()
+    lens = np.diff(qsl)
+    got = f64(run["state"])
+    for r, s in enumerate(case.slot_ids.numpy()):
+        L = int(lens[r])
+        if L == 0:
+            continue
+        t = int(qsl[r + 1]) - 1                      # the request's last token
+        S = got[s]                                   # [Hv, dv, dk]
+        S0 = f64(case.state_pool[s])
+        kt = np.repeat(ref["k"][t], g, axis=0)       # [Hv, dk]
+        vt = ref["v"][t]                             # [Hv, dv]
+        if kind == "frozen":
+            err = rel_l2(S, S0)
+            assert err <= 1e-6, f"request {r}: state moved by {err:.2e}"
+        elif kind == "write":
+            Sk = np.einsum("hij,hj->hi", S, kt)
+            err = rel_l2(Sk, vt)
+            assert err <= 1e-4, f"request {r}: S k vs v {err:.2e}"
+        elif kind == "forget":
+            _, beta = oracle.gates(f64(case.a[t]), f64(case.b[t]))
+            outer = beta[:, None, None] * vt[:, :, None] * kt[:, None, :]
+            err = rel_l2(S, outer)
+            assert err <= 1e-4, f"request {r}: S vs beta v k^T {err:.2e}"
+        elif kind == "zero_qk":
+            t0 = int(qsl[r])
+            if r == 0:
+                alpha, _ = oracle.gates(f64(case.a[t0:t0 + L]), f64(case.b[t0:t0 + L]))
+                decay = np.prod(alpha, axis=0)       # [Hv]
+                err = rel_l2(S, decay[:, None, None] * S0)
+                assert err <= 1e-5, f"pure decay {err:.2e}"
+                zero = np.arange(t0, t0 + L)
+            else:
+                zero = np.arange(t0 + L // 4 + 3, t0 + (3 * L) // 4)
+            assert np.all(f64(run["y"][zero]) == 0), f"request {r}: y not zero where q = k = 0"
+            if run["o"] is not None:
+                assert np.all(f64(run["o"][zero]) == 0), f"request {r}: o not zero where q = k = 0"
+    print(f"{kind}: closed form holds")
+
+
+@pytest.mark.parametrize("path", ["fused_one", "fused_eight", "separate_eight"])
+@pytest.mark.parametrize("kind", SAT_KINDS)
+def test_prefill_edges(kind, path):
+    lengths = ONE_REQ if path == "fused_one" else EIGHT_REQS
+    case = edge_case(kind, 500 + SAT_KINDS.index(kind), lengths)
+    print(f"prefill {kind} {path}: lengths {lengths}", flush=True)
+    run = run_prefill_fused(case) if path.startswith("fused") else run_prefill_separate(case)
+    ref = oracle_chain(case)
+    check_against_oracle(case, run, ref)
+    check_closed_form(case, run, ref)
+
+
+@pytest.mark.parametrize("kind", SAT_KINDS + ["weak_decay"])
+def test_decode_edges(kind):
+    """Eight decode steps of 24 requests at the edge gates (and 48 steps of the
+    weak-decay regime), one gdn_decode_fused launch per step; fp32 arithmetic,
+    so the fp32 bars apply."""
+    R, n = (24, 8) if kind != "weak_decay" else (16, 48)
+    case = edge_case(kind, 520 + (SAT_KINDS + ["weak_decay"]).index(kind), [n] * R)
+    print(f"decode {kind}: {R} requests x {n} steps", flush=True)
+    run = run_decode_steps(case)
+    ref = oracle_chain(case)
+    check_against_oracle(case, run, ref, state_tol=FP32_TOL, out_tol=FP32_TOL, rows=False)
+    if kind != "weak_decay":
+        check_closed_form(case, run, ref)
+
+
+@pytest.mark.parametrize("path", ["fused_one", "fused_six", "separate_one"])
+def test_prefill_weak_decay_long(path):
+    """alpha ~ 0.98 (a ~ N(-4, 1)): the state keeps ~50 tokens of memory, so
+    every chunk's carried term matters, over a 4096-token request (row blocks)
+    and over six requests up to 4096 tokens (group blocks)."""
+    lengths = [4096] if path.endswith("one") else [4096, 1000, 2000, 37, 3000, 512]
+    case = edge_case("weak_decay", 540, lengths)
+    print(f"weak decay {path}: lengths {lengths}", flush=True)
+    run = run_prefill_fused(case) if path.startswith("fused") else run_prefill_separate(case)
+    ref = oracle_chain(case)
+    alpha, _ = oracle.gates(f64(case.a), f64(case.b))
+    print(f"mean alpha {alpha.mean():.4f}, mean chunk decay {np.mean(alpha ** 32):.3f}")
+    check_against_oracle(case, run, ref)

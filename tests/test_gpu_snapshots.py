@@ -7,10 +7,9 @@ import pytest
 import torch
 
 import oracle
-from helpers import OUT_TOL, STATE_TOL, bits, dev, f64, rel_l2
+from helpers import OUT_TOL, STATE_TOL, bits, check_bf16_state, dev, f64, rel_l2
 from hybrid_linear_attention_amd import gdn
 from hybrid_linear_attention_amd.workloads import TINY_DIMS, GdnDims, make_gdn_case
-from test_gpu_state_bf16 import check_bf16_state
 
 pytestmark = pytest.mark.gpu
 

@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import FP32_TOL, OUT_TOL, bf16_ulp_ok, bits, dev, f64, rel_l2
+from helpers import FP32_TOL, OUT_TOL, bf16_ulp_ok, bits, check_bf16_state, dev, f64, rel_l2
 from hybrid_linear_attention_amd import gdn
 from hybrid_linear_attention_amd.workloads import (TINY_DIMS, GdnDims, decode_r64, make_gdn_case,
                                                    spec_verify_r64)
@@ -30,35 +30,6 @@ pytestmark = pytest.mark.gpu
 
 L2_EPS = 1e-6
 NORM_EPS = 1e-6
-
-
-def ulp_diff(got_bits, ref_bits):
-    """bf16 ulps between two bit patterns of equal sign handling (sign-magnitude
-    mapped onto a monotonic integer line)."""
-    def mono(b):
-        b = b.astype(np.int64) & 0xFFFF
-        m = b & 0x7FFF
-        return np.where(b & 0x8000, -m, m)
-    return np.abs(mono(got_bits) - mono(ref_bits))
-
-
-def check_bf16_state(got, ref_f64, slots, max_mismatch, abs_rel=1e-6):
-    """Stored bf16 states of `slots` against the rounded oracle states: within
-    one ulp, except that elements whose exact value nearly cancels (|x| far
-    below the state's rms) may be off by the GPU's absolute arithmetic error,
-    abs_rel x rms, which can be many ulps of a tiny number."""
-    ref = ref_f64[slots]
-    g = bits(got)[slots]
-    r = bits(torch.from_numpy(oracle.round_bf16(ref)).to(torch.bfloat16))
-    d = ulp_diff(g, r)
-    gv = f64(got)[slots]
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    near_zero_ok = np.abs(gv - ref) <= abs_rel * rms + 2.0 ** -8 * np.abs(ref)
-    frac = float(np.mean(d != 0))
-    bad = (d > 1) & ~near_zero_ok
-    print(f"bf16 state: {frac:.2e} of elements differ, {int(np.sum(d > 1))} by > 1 ulp "
-          f"(largest |x| among them {float(np.max(np.abs(ref[d > 1]), initial=0.0)):.2e}, rms {rms:.2e})")
-    assert not bad.any() and frac <= max_mismatch
 
 
 def bf16_case(case):
