@@ -231,9 +231,14 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // fused prefill scratch: fp32 q, k, v and o of every token, then the
-// workspace of the prefill kernels
+// workspace of the prefill kernels.  At d = 128 the chunked prefill reads q and
+// k only in its prep kernel, before its chain writes o, so q and k share o's
+// region (and when the prep kernel forms q and k from x itself, they are not
+// used at all); the sequential kernel (d < 128) reads q and k while it writes
+// o, so there they have regions of their own.
 struct FusedPrefillWs {
     size_t q, k, v, o, pre, total;
+    size_t q_off, k_off, v_off, o_off, pre_off;
     FusedPrefillWs(const gdn_dims *d, int32_t T, int32_t nreq) {
         const size_t D = d->head_dim_k;
         q = align256((size_t)T * d->num_k_heads * D * 4);
@@ -243,7 +248,21 @@ struct FusedPrefillWs {
         v = align256(((size_t)T / 32 + (size_t)nreq) * 32 * d->num_v_heads * D * 4);
         o = align256((size_t)T * d->num_v_heads * D * 4);
         pre = align256(gdn::prefill_workspace_bytes(d->head_dim_k, d->num_k_heads, d->num_v_heads, T, nreq));
-        total = q + k + v + o + pre;
+        if (D == 128) {
+            const size_t o_region = o > q + k ? o : q + k;
+            o_off = 0;
+            q_off = 0;
+            k_off = q;
+            v_off = o_region;
+            pre_off = v_off + v;
+        } else {
+            q_off = 0;
+            k_off = q;
+            v_off = q + k;
+            o_off = v_off + v;
+            pre_off = o_off + o;
+        }
+        total = pre_off + pre;
     }
 };
 }  // namespace
@@ -294,11 +313,11 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
         !aligned(y, 2 * dt_size(y_dt)) || !aligned(workspace, 256))
         return GDN_ERR_ALIGN;
     uint8_t *w = static_cast<uint8_t *>(workspace);
-    float *q = reinterpret_cast<float *>(w);
-    float *k = reinterpret_cast<float *>(w + wl.q);
-    float *v = reinterpret_cast<float *>(w + wl.q + wl.k);
-    float *o = reinterpret_cast<float *>(w + wl.q + wl.k + wl.v);
-    uint8_t *pre = w + wl.q + wl.k + wl.v + wl.o;
+    float *q = reinterpret_cast<float *>(w + wl.q_off);
+    float *k = reinterpret_cast<float *>(w + wl.k_off);
+    float *v = reinterpret_cast<float *>(w + wl.v_off);
+    float *o = reinterpret_cast<float *>(w + wl.o_off);
+    uint8_t *pre = w + wl.pre_off;
     hipStream_t s = static_cast<hipStream_t>(stream);
     gdn::ConvArgs ca{D, x_qkv, x_ld, act_dt == GDN_BF16, conv_w, w_dt == GDN_BF16, conv_pool,
                      query_start_loc, slot_ids, has_initial, num_reqs, num_tokens, C, nq,
