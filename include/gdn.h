@@ -233,7 +233,9 @@ gdn_status gdn_spec_verify(const gdn_dims *dims, const void *x_qkv, int64_t x_ld
 /*
  * gdn_prefill_workspace_bytes — device workspace gdn_prefill_varlen needs for
  * a batch of at most num_tokens tokens in at most num_reqs requests.
- * Returns 0 for unsupported dims.
+ * Returns 0 for unsupported dims.  The chunk length is not an argument: the
+ * chunked prefill (d = 128) always runs 32-token chunks (one MFMA k-step per
+ * chunk), and the sequential kernel (d < 128) has none.
  */
 size_t gdn_prefill_workspace_bytes(const gdn_dims *dims, int32_t num_tokens,
                                    int32_t num_reqs);
@@ -367,14 +369,6 @@ gdn_status gdn_validate_metadata(const int32_t *query_start_loc_host,
                                  int32_t num_tokens, int32_t num_slots);
 
 /*
- * gdn_validate_spec_metadata — HOST-side check of host copies of the metadata
- * of gdn_spec_verify: everything gdn_validate_metadata checks, every request at
- * most max_tokens long, and the slots a call writes (spec_slot_ids[r][j] for j
- * below the request's length) in range, distinct, and distinct from the other
- * requests' input slots (spec_slot_ids[r][0] == slot_ids[r] is allowed).
- * Enqueues nothing; GDN_ERR_METADATA on violation.
- */
-/*
  * gdn_validate_snapshot_metadata — HOST-side check of host copies of
  * gdn_prefill_fused's snapshot metadata: everything gdn_validate_metadata
  * checks, snap_interval a positive multiple of GDN_SNAPSHOT_QUANTUM, and the
@@ -389,6 +383,14 @@ gdn_status gdn_validate_snapshot_metadata(const int32_t *query_start_loc_host,
                                           int32_t num_reqs, int32_t num_tokens,
                                           int32_t num_slots);
 
+/*
+ * gdn_validate_spec_metadata — HOST-side check of host copies of the metadata
+ * of gdn_spec_verify: everything gdn_validate_metadata checks, every request at
+ * most max_tokens long, and the slots a call writes (spec_slot_ids[r][j] for j
+ * below the request's length) in range, distinct, and distinct from the other
+ * requests' input slots (spec_slot_ids[r][0] == slot_ids[r] is allowed).
+ * Enqueues nothing; GDN_ERR_METADATA on violation.
+ */
 gdn_status gdn_validate_spec_metadata(const int32_t *query_start_loc_host,
                                       const int32_t *slot_ids_host,
                                       const int32_t *spec_slot_ids_host,
