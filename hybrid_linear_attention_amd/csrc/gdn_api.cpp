@@ -6,8 +6,16 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "gdn_launch.h"
+
+// Static scratch of gdn_prefill_fused_noalloc: each GPU the library runs on
+// holds its own copy for the life of the process.  In host code `scratch` only
+// names the symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to a kernel.
+static __device__ __align__(256) uint8_t scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -44,6 +52,7 @@ const char *gdn_status_string(gdn_status s) {
         case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer misaligned";
         case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP launch error";
         case GDN_ERR_METADATA: return "GDN_ERR_METADATA: bad query_start_loc or slot ids";
+        case GDN_ERR_SCRATCH: return "GDN_ERR_SCRATCH: batch needs more than the library's static scratch";
     }
     return "GDN_ERR_UNKNOWN";
 }
@@ -272,16 +281,44 @@ size_t gdn_prefill_fused_workspace_bytes(const gdn_dims *dims, int32_t num_token
     return FusedPrefillWs(dims, num_tokens, num_reqs).total;
 }
 
-gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
-                             int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
-                             gdn_dtype act_dt, const void *conv_w, const void *gamma,
-                             gdn_dtype w_dt, void *conv_pool, void *state_pool,
-                             gdn_dtype state_dt, const int32_t *query_start_loc, const int32_t *slot_ids,
-                             const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
-                             int32_t num_slots, const int32_t *snap_slot_ids, int32_t max_snaps,
-                             int32_t snap_interval, float l2_eps, float norm_eps, void *y,
-                             gdn_dtype y_dt, void *workspace, size_t workspace_bytes,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device).
+gdn_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return GDN_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return GDN_OK;
+}
+
+// The whole fused prefill step, shared by gdn_prefill_fused (on the caller's
+// workspace) and gdn_prefill_fused_noalloc (static_scratch: on the library's
+// scratch array, whose address is looked up only after every host check).
+gdn_status prefill_fused_impl(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
+                              int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
+                              gdn_dtype act_dt, const void *conv_w, const void *gamma,
+                              gdn_dtype w_dt, void *conv_pool, void *state_pool,
+                              gdn_dtype state_dt, const int32_t *query_start_loc,
+                              const int32_t *slot_ids, const uint8_t *has_initial,
+                              int32_t num_reqs, int32_t num_tokens, int32_t num_slots,
+                              const int32_t *snap_slot_ids, int32_t max_snaps,
+                              int32_t snap_interval, float l2_eps, float norm_eps, void *y,
+                              gdn_dtype y_dt, void *workspace, size_t workspace_bytes,
+                              bool static_scratch, void *stream) {
     gdn_status st = check_dims(dims);
     if (st != GDN_OK) return st;
     if (!valid_dtype(act_dt) || !valid_dtype(w_dt) || !valid_dtype(y_dt) || !valid_dtype(state_dt))
@@ -304,14 +341,28 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
         !query_start_loc || !slot_ids || !y)
         return GDN_ERR_NULL;
     const FusedPrefillWs wl(dims, num_tokens, num_reqs);
-    if (!workspace || workspace_bytes < wl.total) return GDN_ERR_WORKSPACE;
+    if (static_scratch) {
+        if (wl.total > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+    } else if (!workspace || workspace_bytes < wl.total) {
+        return GDN_ERR_WORKSPACE;
+    }
     const size_t e = dt_size(act_dt);
     if (x_ld % 2 != 0 || z_ld % 2 != 0 || !aligned(x_qkv, 2 * e) || !aligned(z, 2 * e) ||
         !aligned(a, e) || !aligned(b, e) || !aligned(conv_pool, e) ||
         !aligned(conv_w, dt_size(w_dt)) || !aligned(gamma, 2 * dt_size(w_dt)) ||
         !aligned(state_pool, 16) || !aligned(query_start_loc, 4) || !aligned(slot_ids, 4) ||
-        !aligned(y, 2 * dt_size(y_dt)) || !aligned(workspace, 256))
+        !aligned(y, 2 * dt_size(y_dt)) || (!static_scratch && !aligned(workspace, 256)))
         return GDN_ERR_ALIGN;
+    // d = 128 with 16-byte rows: the prefill's prep kernel forms q and k from x
+    // itself and its chain forms v, so no conv pass runs
+    const bool prep_conv = D == 128 && x_ld % (int64_t)(16 / e) == 0 && aligned(x_qkv, 16) &&
+                           aligned(conv_w, 16);
+    // a bf16 state at d = 128 needs the prep-conv path (16-byte conv rows)
+    if (state_dt == GDN_BF16 && D == 128 && !prep_conv) return GDN_ERR_ALIGN;
+    if (static_scratch) {
+        const gdn_status sst = scratch_address(&workspace);
+        if (sst != GDN_OK) return sst;
+    }
     uint8_t *w = static_cast<uint8_t *>(workspace);
     float *q = reinterpret_cast<float *>(w + wl.q_off);
     float *k = reinterpret_cast<float *>(w + wl.k_off);
@@ -325,12 +376,6 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
     gdn::PrefillArgs pa{D, q, k, v, false, a, b, gate_ld, act_dt == GDN_BF16, state_pool,
                         query_start_loc, slot_ids, has_initial, num_reqs, num_tokens,
                         dims->num_k_heads, dims->num_v_heads, o, false, pre, wl.pre};
-    // d = 128 with 16-byte rows: the prefill's prep kernel forms q and k from x
-    // itself and its chain forms v, so no conv pass runs
-    const bool prep_conv = D == 128 && x_ld % (int64_t)(16 / e) == 0 && aligned(x_qkv, 16) &&
-                           aligned(conv_w, 16);
-    // a bf16 state at d = 128 needs the prep-conv path (16-byte conv rows)
-    if (state_dt == GDN_BF16 && D == 128 && !prep_conv) return GDN_ERR_ALIGN;
     pa.state_bf16 = state_dt == GDN_BF16;
     if (prep_conv) {
         pa.x = x_qkv;
@@ -360,6 +405,45 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
                                                        query_start_loc, snap_slot_ids, snap_interval,
                                                        max_snaps, num_reqs, C, s));
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_ld, const void *z,
+                             int64_t z_ld, const void *a, const void *b, int64_t gate_ld,
+                             gdn_dtype act_dt, const void *conv_w, const void *gamma,
+                             gdn_dtype w_dt, void *conv_pool, void *state_pool,
+                             gdn_dtype state_dt, const int32_t *query_start_loc, const int32_t *slot_ids,
+                             const uint8_t *has_initial, int32_t num_reqs, int32_t num_tokens,
+                             int32_t num_slots, const int32_t *snap_slot_ids, int32_t max_snaps,
+                             int32_t snap_interval, float l2_eps, float norm_eps, void *y,
+                             gdn_dtype y_dt, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    return prefill_fused_impl(dims, x_qkv, x_ld, z, z_ld, a, b, gate_ld, act_dt, conv_w, gamma, w_dt,
+                              conv_pool, state_pool, state_dt, query_start_loc, slot_ids,
+                              has_initial, num_reqs, num_tokens, num_slots, snap_slot_ids,
+                              max_snaps, snap_interval, l2_eps, norm_eps, y, y_dt, workspace,
+                              workspace_bytes, false, stream);
+}
+
+gdn_status gdn_prefill_fused_noalloc(const gdn_dims *dims, const void *x_qkv, int64_t x_ld,
+                                     const void *z, int64_t z_ld, const void *a, const void *b,
+                                     int64_t gate_ld, gdn_dtype act_dt, const void *conv_w,
+                                     const void *gamma, gdn_dtype w_dt, void *conv_pool,
+                                     void *state_pool, gdn_dtype state_dt,
+                                     const int32_t *query_start_loc, const int32_t *slot_ids,
+                                     const uint8_t *has_initial, int32_t num_reqs,
+                                     int32_t num_tokens, int32_t num_slots,
+                                     const int32_t *snap_slot_ids, int32_t max_snaps,
+                                     int32_t snap_interval, float l2_eps, float norm_eps, void *y,
+                                     gdn_dtype y_dt, void *stream) {
+    return prefill_fused_impl(dims, x_qkv, x_ld, z, z_ld, a, b, gate_ld, act_dt, conv_w, gamma, w_dt,
+                              conv_pool, state_pool, state_dt, query_start_loc, slot_ids,
+                              has_initial, num_reqs, num_tokens, num_slots, snap_slot_ids,
+                              max_snaps, snap_interval, l2_eps, norm_eps, y, y_dt, nullptr, 0,
+                              true, stream);
 }
 
 gdn_status gdn_gated_norm(const gdn_dims *dims, const void *o, gdn_dtype o_dt, const void *z,

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_F32 = 0
 GDN_BF16 = 1
 GDN_FP8_E4M3 = 2
+GDN_NOALLOC_SCRATCH_BYTES = 256 << 20  # include/gdn.h: the static scratch of gdn_prefill_fused_noalloc
 
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_DIMS", 3: "GDN_ERR_DTYPE",
     4: "GDN_ERR_SHAPE", 5: "GDN_ERR_WORKSPACE", 6: "GDN_ERR_ALIGN", 7: "GDN_ERR_HIP",
-    8: "GDN_ERR_METADATA",
+    8: "GDN_ERR_METADATA", 9: "GDN_ERR_SCRATCH",
 }
 
 
@@ -64,6 +65,9 @@ _SIGS = {
     "gdn_prefill_fused": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _vp,
                            _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32,
                            _i32, _f32, _f32, _vp, _i32, _vp, ctypes.c_size_t, _vp], _i32),
+    "gdn_prefill_fused_noalloc": ([ctypes.POINTER(GdnDimsC), _vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32,
+                                   _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                   _vp, _i32, _i32, _f32, _f32, _vp, _i32, _vp], _i32),
     "gdn_prefill_varlen": ([ctypes.POINTER(GdnDimsC), _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64,
                             _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, ctypes.c_size_t,
                             _vp], _i32),
@@ -276,15 +280,10 @@ def gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs):
                                                        int(num_reqs)))
 
 
-def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, query_start_loc,
-                      slot_ids, has_initial, y, workspace, l2_eps=1e-6, norm_eps=1e-6,
-                      snap_slot_ids=None, snap_interval=0, stream=None):
-    """A whole prefill step (conv update -> recurrence -> gated norm) over a packed
-    batch; x, z, a, b share one dtype and give their row strides; state_pool fp32
-    or bf16; y [T, Hv*dv];
-    workspace a uint8 device tensor of gdn_prefill_fused_workspace_bytes(...);
-    snap_slot_ids int32 [R, max_snaps] with snap_interval (tokens, a multiple of
-    32) keeps prefix-cache snapshots."""
+def _prefill_fused_args(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, query_start_loc,
+                        slot_ids, has_initial, y, l2_eps, norm_eps, snap_slot_ids, snap_interval):
+    """The arguments gdn_prefill_fused and gdn_prefill_fused_noalloc share, up to
+    and including y_dt, after the binding's own checks."""
     d = dims_c(dims)
     if a.stride() != b.stride() or not (x.dtype == z.dtype == a.dtype == b.dtype == conv_pool.dtype):
         raise ValueError("x, z, a, b and conv_pool share one dtype; a and b share strides")
@@ -300,16 +299,42 @@ def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, qu
         if snap_slot_ids.dim() != 2 or snap_slot_ids.shape[0] != slot_ids.numel():
             raise ValueError("snap_slot_ids must be [num_reqs, max_snaps]")
         max_snaps = snap_slot_ids.shape[1]
-    st = lib().gdn_prefill_fused(
-        ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"), _ptr(a, "a"),
-        _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"), _ptr(gamma, "gamma"),
-        _dt(conv_w), _ptr(conv_pool, "conv_pool"), _ptr(state_pool, "state_pool"),
-        _dt(state_pool), _ptr(query_start_loc, "qsl"), _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"),
-        slot_ids.numel(), x.shape[0], state_pool.shape[0], _ptr(snap_slot_ids, "snap_slot_ids"),
-        max_snaps, int(snap_interval), float(l2_eps), float(norm_eps),
-        _ptr(y, "y"), _dt(y), _ptr(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+    return (ctypes.byref(d), _ptr(x, "x"), _rows(x, "x"), _ptr(zz, "z"), _rows(zz, "z"),
+            _ptr(a, "a"), _ptr(b, "b"), _rows(a, "a"), _dt(x), _ptr(conv_w, "conv_w"),
+            _ptr(gamma, "gamma"), _dt(conv_w), _ptr(conv_pool, "conv_pool"),
+            _ptr(state_pool, "state_pool"), _dt(state_pool), _ptr(query_start_loc, "qsl"),
+            _ptr(slot_ids, "slot_ids"), _ptr(has_initial, "has_initial"), slot_ids.numel(),
+            x.shape[0], state_pool.shape[0], _ptr(snap_slot_ids, "snap_slot_ids"), max_snaps,
+            int(snap_interval), float(l2_eps), float(norm_eps), _ptr(y, "y"), _dt(y))
+
+
+def gdn_prefill_fused(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool, query_start_loc,
+                      slot_ids, has_initial, y, workspace, l2_eps=1e-6, norm_eps=1e-6,
+                      snap_slot_ids=None, snap_interval=0, stream=None):
+    """A whole prefill step (conv update -> recurrence -> gated norm) over a packed
+    batch; x, z, a, b share one dtype and give their row strides; state_pool fp32
+    or bf16; y [T, Hv*dv];
+    workspace a uint8 device tensor of gdn_prefill_fused_workspace_bytes(...);
+    snap_slot_ids int32 [R, max_snaps] with snap_interval (tokens, a multiple of
+    32) keeps prefix-cache snapshots."""
+    args = _prefill_fused_args(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool,
+                               query_start_loc, slot_ids, has_initial, y, l2_eps, norm_eps,
+                               snap_slot_ids, snap_interval)
+    st = lib().gdn_prefill_fused(*args, _ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "gdn_prefill_fused")
+
+
+def gdn_prefill_fused_noalloc(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool,
+                              query_start_loc, slot_ids, has_initial, y, l2_eps=1e-6,
+                              norm_eps=1e-6, snap_slot_ids=None, snap_interval=0, stream=None):
+    """gdn_prefill_fused on the library's static scratch (no workspace, nothing
+    allocated); raises GdnError (GDN_ERR_SCRATCH) for a batch larger than it."""
+    args = _prefill_fused_args(dims, x, z, a, b, conv_w, gamma, conv_pool, state_pool,
+                               query_start_loc, slot_ids, has_initial, y, l2_eps, norm_eps,
+                               snap_slot_ids, snap_interval)
+    st = lib().gdn_prefill_fused_noalloc(*args, _stream(stream))
+    _check(st, "gdn_prefill_fused_noalloc")
 
 
 def gdn_gated_norm(dims, o, z, gamma, y, eps=1e-6, stream=None):

@@ -79,7 +79,9 @@ typedef enum gdn_status {
     GDN_ERR_WORKSPACE = 5, /* workspace missing or too small                 */
     GDN_ERR_ALIGN = 6,     /* pointer not aligned as documented              */
     GDN_ERR_HIP = 7,       /* the HIP runtime reported an error on launch    */
-    GDN_ERR_METADATA = 8   /* gdn_validate_metadata: bad qsl or slot ids     */
+    GDN_ERR_METADATA = 8,  /* gdn_validate_metadata: bad qsl or slot ids     */
+    GDN_ERR_SCRATCH = 9    /* gdn_prefill_fused_noalloc: the batch needs more
+                              than GDN_NOALLOC_SCRATCH_BYTES of scratch      */
 } gdn_status;
 
 /* Human-readable name of a status code (static storage). */
@@ -313,6 +315,35 @@ gdn_status gdn_prefill_fused(const gdn_dims *dims, const void *x_qkv, int64_t x_
                              int32_t snap_interval, float l2_eps, float norm_eps,
                              void *y, gdn_dtype y_dt, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_fused_noalloc — gdn_prefill_fused without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The call
+ * allocates nothing: its scratch is a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES in the library, one per GPU the library runs on,
+ * held from the first call on that GPU until the process ends.  Arguments,
+ * results and alignment are those of gdn_prefill_fused; the same kernels run.
+ * A batch whose gdn_prefill_fused_workspace_bytes(dims, num_tokens, num_reqs)
+ * exceeds GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_SCRATCH before anything is
+ * enqueued (at d = 128 a token takes ~86 KiB and a request ~2 MiB more: about
+ * 2,900 tokens in 4 requests, or 2,000 tokens in 40).  Every call on one GPU
+ * uses that GPU's one array, whose contents need no clearing (each call writes
+ * what it reads): calls that overlap on one GPU (several streams, or several
+ * host threads) race and must be serialised by the caller.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (256u << 20)
+gdn_status gdn_prefill_fused_noalloc(const gdn_dims *dims, const void *x_qkv, int64_t x_ld,
+                                     const void *z, int64_t z_ld, const void *a, const void *b,
+                                     int64_t gate_ld, gdn_dtype act_dt, const void *conv_w,
+                                     const void *gamma, gdn_dtype w_dt, void *conv_pool,
+                                     void *state_pool, gdn_dtype state_dt,
+                                     const int32_t *query_start_loc, const int32_t *slot_ids,
+                                     const uint8_t *has_initial, int32_t num_reqs,
+                                     int32_t num_tokens, int32_t num_slots,
+                                     const int32_t *snap_slot_ids, int32_t max_snaps,
+                                     int32_t snap_interval, float l2_eps, float norm_eps, void *y,
+                                     gdn_dtype y_dt, void *stream);
 
 /*
  * gdn_gated_norm — Ogate = RMSNorm(o) * SiLU(Z) (operator table, gated-output

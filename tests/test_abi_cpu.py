@@ -354,3 +354,28 @@ def test_gqa_validate_metadata_host():
     shared = np.array([[3, 0, -1], [3, 2, -1]], np.int32)
     assert gqa.gqa_validate_decode_metadata(shared, [5, 8], 5, 4, 12) == 0       # shared read-only prefix page
     assert gqa.gqa_validate_decode_metadata(shared, [3, 8], 5, 4, 12) == 8       # request 0 appends into it
+
+
+def test_prefill_fused_noalloc_rejects_on_the_host():
+    """The no-allocation prefill validates like gdn_prefill_fused and refuses a
+    batch beyond its static scratch (GDN_ERR_SCRATCH) before any HIP call."""
+    lib = gdn.lib()
+
+    def call(d, T, R, **kw):
+        args = dict(x=FAKE, y=FAKE, act=1)
+        args.update(kw)
+        return lib.gdn_prefill_fused_noalloc(
+            None if d is None else ctypes.byref(d), args["x"], 10240, FAKE, 6144, FAKE, FAKE, 48,
+            args["act"], FAKE, FAKE, 1, FAKE, FAKE, 0, FAKE, FAKE, None, R, T, 64, None, 0, 0,
+            1e-6, 1e-6, args["y"], 1, None)
+    assert gdn.gdn_prefill_fused_workspace_bytes(FULL, 4096, 1) > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    assert gdn.gdn_prefill_fused_workspace_bytes(FULL, 2000, 40) <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    assert call(FULL, 4096, 1) == 9                  # GDN_ERR_SCRATCH
+    assert call(None, 100, 2) == 1
+    assert call(dims(16, 48, 96, 96, 4), 100, 2) == 2
+    assert call(FULL, 100, 2, act=5) == 3
+    assert call(FULL, 100, 0) == 4
+    assert call(FULL, 100, 2, y=None) == 1
+    assert call(FULL, 100, 2, x=FAKE + 2) == 6       # misaligned conv rows
+    assert call(FULL, 0, 0, x=None) == 0             # empty batch: nothing to do
+    assert gdn.lib().gdn_status_string(9).startswith(b"GDN_ERR_SCRATCH")
