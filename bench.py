@@ -84,6 +84,35 @@ def measured_traffic(kernel, source):
     return int(float(vals["hbm_bytes_per_launch"]))
 
 
+def step_counters(name):
+    """Counter summary of a multi-kernel step (profiles/<name>_counters.txt:
+    per-kernel HBM bytes from FETCH_SIZE / WRITE_SIZE scaled by a plain copy's
+    reading, MFMA busy cycles and issued MFMA flops), or None when it is missing
+    or any source file it names has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals, kernels = {}, []
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#"):
+                continue
+            if line.startswith("kernel:"):
+                kernels.append(line.split()[1])
+                continue
+            if line.startswith("source_sha256_16 "):
+                src, digest = line[len("source_sha256_16 "):].split(":")
+                if source_digest(os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc",
+                                              src.strip())) != digest.strip():
+                    return None
+                continue
+            if ":" in line:
+                key, val = line.split(":", 1)
+                vals[key.strip()] = float(val.strip())
+    vals["kernels"] = kernels
+    return vals
+
+
 def fused_decode_bytes(d, R, act_bytes=2, y_bytes=2, state_bytes=4):
     """Algorithmic HBM bytes of one gdn_decode_fused launch: the state read and
     written once; the token's conv inputs, z and gates read once; its conv
@@ -287,11 +316,14 @@ def main():
         pre = {}
         for name, make in legs:
             c = make()
-            pre[name] = bench_prefill(c, args.prefill_steps, dev, stream, torch, gdn, np)
+            pre[name] = bench_prefill(c, args.prefill_steps, dev, stream, torch, gdn, np, name=name)
             if name == "prefill_varlen16":
                 # the same step keeping a prefix-cache snapshot every 512 tokens
                 pre[name]["with_snapshots"] = bench_prefill(c, args.prefill_steps, dev, stream,
                                                             torch, gdn, np, snap_interval=512)
+            if not args.no_cpu:
+                pre[name]["cpu_baseline"] = (cpu_prefill_baseline(c, 1024, 128) if c.num_reqs == 1
+                                             else cpu_prefill_baseline(c, 64, 8))
             del c
             torch.cuda.empty_cache()
         result["prefill"] = pre
@@ -313,6 +345,8 @@ def main():
     if not args.no_layer:
         result["layer"] = bench_layer(args.layer_steps, dev, stream, torch, np)
         torch.cuda.empty_cache()
+        if not args.no_cpu:
+            result["layer"]["cpu_baseline"] = cpu_layer_baseline()
 
     # --------------------------------------- measured HBM reference rates
     result["hbm_reference"] = hbm_reference(torch, dev)
@@ -423,7 +457,7 @@ def fused_prefill_bytes(d, T, nreq, n_init, act_bytes=2, y_bytes=2):
     return per_tok * T + state * (nreq + n_init) + hist * nreq
 
 
-def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0):
+def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0, name=None):
     """One prefill step (gdn_prefill_fused: conv update -> recurrence -> gated
     norm) over one packed batch.  State and history are re-seeded from device
     copies before every step, outside the timed events.  With snap_interval,
@@ -484,9 +518,21 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0):
     else:
         roof.update(bound="mfma", achieved=round(tflops, 2), peak=BF16_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(tflops / BF16_PEAK_TFLOPS, 4))
-    roof.update(bytes_per_launch=nbytes, flops_per_launch=flops, traffic=None,
+    cnt = step_counters(name) if name else None
+    roof.update(bytes_per_launch=nbytes, flops_per_launch=flops,
+                traffic=int(cnt["hbm_bytes_per_step"]) if cnt else None,
                 mfma_tflops=round(tflops, 2),
-                mfma_util=round(tflops / BF16_PEAK_TFLOPS, 4))
+                mfma_util_algorithmic=round(tflops / BF16_PEAK_TFLOPS, 4))
+    if cnt:
+        # from the counters: the MFMA work the step issues (bf16x3: three products
+        # per algorithmic one) over the step time, and the chain kernel's MFMA-busy
+        # share of its own cycles
+        issued = cnt["mfma_bf16_flops_issued_per_step"] / (ms * 1e-3) / 1e12
+        roof.update(traffic_per_token=int(cnt["hbm_bytes_per_token"]),
+                    mfma_issued_tflops=round(issued, 1),
+                    mfma_issued_util=round(issued / BF16_PEAK_TFLOPS, 4),
+                    chain_mfma_busy=cnt["chain_mfma_busy"],
+                    counters=f"profiles/{name}_counters.txt")
     return {
         "roofline": roof,
         "tokens": T,
@@ -722,6 +768,130 @@ def cpu_baseline(case, seconds):
         "one_thread": {"value": round(state_bytes * reps1 / el1 / 1e9, 4), "unit": "GB/s",
                        "ms_per_step": round(el1 * 1e3 / reps1, 2), "steps": reps1},
     }
+
+
+def _cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return model
+
+
+def _sub_batch(c, take):
+    """Rows of the first take[r] tokens of every request, with their qsl."""
+    import numpy as np
+    qsl = c.qsl.numpy()
+    rows, lens = [], []
+    for r in range(c.num_reqs):
+        n = int(min(take[r], qsl[r + 1] - qsl[r]))
+        rows.append(np.arange(qsl[r], qsl[r] + n))
+        lens.append(n)
+    return np.concatenate(rows), np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def _oracle_core(c, rows, sub_qsl):
+    """conv1d_update -> gated_delta_rule -> gated_norm, fp64, on the given rows
+    (the whole step of gdn_prefill_fused); returns seconds."""
+    import oracle
+    d = c.dims
+    slots, hi = c.slot_ids.numpy(), c.has_initial.numpy()
+    x = c.x_qkv[rows].double().numpy()
+    a, b = c.a[rows].double().numpy(), c.b[rows].double().numpy()
+    z = c.z[rows].double().numpy()
+    hist, st = c.conv_pool.double().numpy(), c.state_pool.double().numpy()
+    w, g = c.conv_w.double().numpy(), c.gamma.double().numpy()
+    t0 = time.perf_counter()
+    q, k, v, _ = oracle.conv1d_update(x, w, hist, sub_qsl, slots, hi, d.num_k_heads, d.num_v_heads,
+                                      d.head_dim_k, d.head_dim_v, L2_EPS)
+    o, _ = oracle.gated_delta_rule(q, k, v, a, b, st, sub_qsl, slots, hi)
+    oracle.gated_norm(o, z, g, NORM_EPS)
+    return time.perf_counter() - t0
+
+
+def cpu_prefill_baseline(c, per_req, per_req_one):
+    """The fp64 oracle of one prefill step (conv update, recurrence, gated norm)
+    on a bounded sample of the same workload: every request cut to its first
+    per_req tokens, all heads, on all the host threads; and every request cut to
+    per_req_one tokens on one thread.  Tokens/s over the sample."""
+    import oracle
+    rows, sq = _sub_batch(c, [per_req] * c.num_reqs)
+    el = _oracle_core(c, rows, sq)
+    rows1, sq1 = _sub_batch(c, [per_req_one] * c.num_reqs)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    el1 = _oracle_core(c, rows1, sq1)
+    oracle.set_num_threads(threads)
+    return {"value": round(len(rows) / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} tokens (each of the {c.num_reqs} requests cut to its first "
+                      f"{per_req}), all 48 heads, conv + recurrence + gated norm in fp64: {el:.2f} s",
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_info(),
+            "one_thread": {"value": round(len(rows1) / el1, 1), "unit": "tokens/s",
+                           "sample": f"{len(rows1)} tokens (first {per_req_one} of each request): "
+                                     f"{el1:.2f} s"}}
+
+
+def cpu_layer_baseline(n_prefill_tokens=512, n_decode=16):
+    """The fp64 oracle of the layer block (RMSNorm, in-projection by numpy fp64
+    matmul, conv, recurrence, gated norm, out-projection + residual) on a
+    sub-batch of the mixed workload: the first prefill request (its first
+    n_prefill_tokens tokens) and the first n_decode decode requests, per stage."""
+    import numpy as np
+    import oracle
+    from hybrid_linear_attention_amd.workloads import layer_mixed
+    case = layer_mixed()
+    core = case.core
+    d = core.dims
+    qsl = core.qsl.numpy()
+    reqs = [0] + list(range(case.num_prefill, case.num_prefill + n_decode))
+    take = {0: n_prefill_tokens}
+    rows = np.concatenate([np.arange(qsl[r], qsl[r] + min(take.get(r, 1), qsl[r + 1] - qsl[r]))
+                           for r in reqs])
+    lens = [min(take.get(r, 1), int(qsl[r + 1] - qsl[r])) for r in reqs]
+    sq = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = core.slot_ids.numpy()[reqs]
+    hi = core.has_initial.numpy()[reqs]
+    X = case.X[torch_rows(rows)].double().numpy()
+    W_in = np.concatenate([case.W_qkvz.double().numpy(), case.W_ba.double().numpy()], axis=1)
+    W_o = case.W_o.double().numpy()
+    Hk, Hv, D = d.num_k_heads, d.num_v_heads, d.head_dim_k
+    cq = 2 * Hk * D + Hv * D
+    T = len(rows)
+    st = {}
+    t = time.perf_counter()
+    U = oracle.rmsnorm(X, case.gamma_in.double().numpy(), NORM_EPS)
+    st["rmsnorm"] = time.perf_counter() - t
+    t = time.perf_counter()
+    P = oracle.linear(U, W_in)
+    st["in_proj"] = time.perf_counter() - t
+    t = time.perf_counter()
+    q, k, v, _ = oracle.conv1d_update(P[:, :cq], core.conv_w.double().numpy(),
+                                      core.conv_pool.double().numpy()[slots], sq,
+                                      np.arange(len(reqs), dtype=np.int32), hi, Hk, Hv, D, D, L2_EPS)
+    o, _ = oracle.gated_delta_rule(q, k, v, P[:, cq + Hv * D + Hv:], P[:, cq + Hv * D:cq + Hv * D + Hv],
+                                   core.state_pool.double().numpy()[slots], sq,
+                                   np.arange(len(reqs), dtype=np.int32), hi)
+    y = oracle.gated_norm(o, P[:, cq:cq + Hv * D].reshape(T, Hv, D), core.gamma.double().numpy(),
+                          NORM_EPS)
+    st["core"] = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.residual_add(X, oracle.linear(y, W_o))
+    st["out_proj"] = time.perf_counter() - t
+    total = sum(st.values())
+    return {"value": round(T / total, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{T} tokens: the first {n_prefill_tokens} of prefill request 0 and {n_decode} "
+                      f"decode requests, the whole layer block in fp64 (numpy BLAS for the "
+                      f"projections): {total:.2f} s",
+            "stage_s": {k_: round(v_, 3) for k_, v_ in st.items()},
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_info()}
+
+
+def torch_rows(rows):
+    import torch
+    return torch.from_numpy(rows)
 
 
 if __name__ == "__main__":
