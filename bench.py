@@ -322,8 +322,8 @@ def main():
                 pre[name]["with_snapshots"] = bench_prefill(c, args.prefill_steps, dev, stream,
                                                             torch, gdn, np, snap_interval=512)
             if not args.no_cpu:
-                pre[name]["cpu_baseline"] = (cpu_prefill_baseline(c, 1024, 128) if c.num_reqs == 1
-                                             else cpu_prefill_baseline(c, 64, 8))
+                pre[name]["cpu_baseline"] = (cpu_prefill_baseline(c, 4096, 1024) if c.num_reqs == 1
+                                             else cpu_prefill_baseline(c, 512, 64))
             del c
             torch.cuda.empty_cache()
         result["prefill"] = pre
@@ -833,7 +833,7 @@ def cpu_prefill_baseline(c, per_req, per_req_one):
                                      f"{el1:.2f} s"}}
 
 
-def cpu_layer_baseline(n_prefill_tokens=512, n_decode=16):
+def cpu_layer_baseline(n_prefill_tokens=2048, n_decode=64):
     """The fp64 oracle of the layer block (RMSNorm, in-projection by numpy fp64
     matmul, conv, recurrence, gated norm, out-projection + residual) on a
     sub-batch of the mixed workload: the first prefill request (its first

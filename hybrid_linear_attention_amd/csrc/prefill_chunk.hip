@@ -65,14 +65,14 @@ constexpr int AP = CH + 4;  // padded fp32 row of 32x32 work matrices
 // byte 16 l, holding the eight bf16 values of one MFMA A operand in k-slot
 // order (see the chain kernel's layout note).
 constexpr int FRAG = 1024;
-// K image: K and Q as (plane hi/lo, row tile tau, k-step ks), K^T as (plane, jt)
-constexpr int FK = 0, FQ = 16, FKT = 32, KIMG_FRAGS = 48;
+// K image: K and Q as (plane hi/lo, row tile tau, k-step ks).  The chain's K^T
+// operands are read from the K planes with the transposed LDS read.
+constexpr int FK = 0, FQ = 16, KIMG_FRAGS = 32;
 // T image: T and P as (plane, tau), then three float[32] token vectors
 constexpr int FT = 0, FP = 4, TIMG_FRAGS = 9;
 constexpr int T_GAM = 8 * FRAG, T_REV = T_GAM + 128, T_BETA = T_REV + 128;
-constexpr size_t KIMG = (size_t)KIMG_FRAGS * FRAG;  // 49,152 bytes
+constexpr size_t KIMG = (size_t)KIMG_FRAGS * FRAG;  // 32,768 bytes
 constexpr size_t TIMG = (size_t)TIMG_FRAGS * FRAG;  //  9,216 bytes
-constexpr size_t STAGE = KIMG + TIMG;               // LDS per chunk in the chain
 
 constexpr int PLAN_SORT_MAX = 4096;  // longest-first order for up to this many requests
 
@@ -120,6 +120,37 @@ __device__ __forceinline__ void split_pack(const float (&x)[8], uint4 &hi, uint4
 
 __device__ __forceinline__ bf16x8_t frag(const uint8_t *p) {
     return *reinterpret_cast<const bf16x8_t *>(p);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
+// lane i receives element i % 4 of the 8-byte words read by lanes 4 j + i / 4,
+// j = 0..3, in order of j.
+__device__ __forceinline__ s16x4_t lds_read_tr(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t *)((__attribute__((address_space(3))) uint8_t *)(p)));
+}
+
+// This lane's byte offset for the K^T reads: lane (lr, lg) supplies the four
+// channels 16 jt + 4 (lr % 4) .. + 3 of token 4 lg + lr / 4 (second read: of
+// token 16 + 4 lg + lr / 4), which sit in K fragment (tau, ks = jt / 2) at lane
+// (token % 16) + 16 (lr % 4), half jt % 2.
+__device__ __forceinline__ uint32_t kt_lane_off(int lr, int lg) {
+    return 16u * (uint32_t)((4 * lg + (lr >> 2)) + 16 * (lr & 3));
+}
+
+// The K^T operand (rows 16 jt + lr of K^T, i.e. channels; k-slots the tokens in
+// the chain's slot order) of plane `plane` (0 hi, 1 lo) from the staged K
+// image: lane i of 16-lane group lg then holds K[4 lg + j][16 jt + i] for
+// j = 0..3 (first read) and K[16 + 4 lg + j][16 jt + i] (second read).
+__device__ __forceinline__ bf16x8_t kt_frag(const uint8_t *kimg_lane, int plane, int jt) {
+    const uint8_t *p = kimg_lane + ((FK + plane * 8 + (jt >> 1)) * FRAG + 8 * (jt & 1));
+    const s16x4_t a = lds_read_tr(p);             // tau = 0: tokens 4 lg + j
+    const s16x4_t b = lds_read_tr(p + 4 * FRAG);  // tau = 1: tokens 16 + 4 lg + j
+    const s16x4_t ab[2] = {a, b};
+    return __builtin_bit_cast(bf16x8_t, ab);
 }
 
 // acc += a * b with a = ah + al, b = bh + bl (the lo*lo term is below fp32 noise).
@@ -281,7 +312,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const TA *__restrict__ q, const TA *__restrict__ k, const TG *__restrict__ ga,
     const TG *__restrict__ gb, int64_t gate_ld, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ chunk_off, int32_t nreq, int32_t Hk, int32_t Hv,
-    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg, PrepConvIn cv, float *__restrict__ vimg) {
+    uint8_t *__restrict__ kimg, uint8_t *__restrict__ timg, PrepConvIn cv) {
     using namespace chunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     PrepSmem &sm = *reinterpret_cast<PrepSmem *>(smem_raw);
@@ -324,9 +355,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         }
     } else {
         // The conv inputs of the chunk are staged in LDS with coalesced 16-byte
-        // loads, NCH channels per pass: first the key head's q and k channels
-        // (bf16: one pass; fp32: q, then k), then (V images requested) the v
-        // channels of its value heads.  Staged row rr holds token tb - 3 + rr;
+        // loads, NCH channels per pass: the key head's q and k channels (bf16:
+        // one pass; fp32: q, then k).  Staged row rr holds token tb - 3 + rr;
         // rows before the request start come from its history (zeros without
         // one); rows past the chunk's last token are zeros.  The next pass's
         // rows are loaded while the current pass computes: every lane issues
@@ -343,19 +373,11 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         const int t0 = qsl[r];
         const TX *x = static_cast<const TX *>(cv.x);
         TX(*xs)[XSP * 2 / (int)sizeof(TX)] = reinterpret_cast<TX(*)[XSP * 2 / (int)sizeof(TX)]>(&sm.xs[0][0]);
-        const int nvc = group * D;                  // v channels of the key head
-        const int vbase = 2 * Hk * D + kh * nvc;
-        const int nvpass = vimg != nullptr ? (nvc + NCH - 1) / NCH : 0;
-        const int npass_all = NPASS + nvpass;
-        // channel of column cq of pass ps (q: 0 .. D-1, k: D .. 2D-1 over the q / k
-        // passes; then the v channels), or -1 past the last v channel
+        constexpr int npass_all = NPASS;
+        // channel of column cq of pass ps (q: 0 .. D-1, k: D .. 2D-1 over the passes)
         auto pass_chan = [&](int ps, int cq) -> int {
-            if (ps < NPASS) {
-                const int c2 = ps * NCH + cq;
-                return (c2 >= D ? Hk * D : 0) + kh * D + (c2 & (D - 1));
-            }
-            const int vc = (ps - NPASS) * NCH + cq;
-            return vc < nvc ? vbase + vc : -1;
+            const int c2 = ps * NCH + cq;
+            return (c2 >= D ? Hk * D : 0) + kh * D + (c2 & (D - 1));
         };
         auto load_pass = [&](uint4 (&pv)[NM], int ps) {
 #pragma unroll
@@ -364,7 +386,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 const int rr = pi >> 5, seg = pi & 31;
                 const int tok = tb - 3 + rr;
                 const int ch = pass_chan(ps, EPP * seg);
-                const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc && ch >= 0;
+                const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc;
                 pv[m] = *reinterpret_cast<const uint4 *>(x + (ok ? (int64_t)tok * cv.x_ld + ch : (int64_t)0));
             }
         };
@@ -375,7 +397,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 const int rr = pi >> 5, seg = pi & 31;
                 const int tok = tb - 3 + rr;
                 const int ch = pass_chan(ps, EPP * seg);
-                const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc && ch >= 0;
+                const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc;
                 if (pi < NPIECE && tok >= t0)
                     *reinterpret_cast<uint4 *>(&xs[rr][EPP * seg]) = ok ? pv[m] : make_uint4(0u, 0u, 0u, 0u);
             }
@@ -388,7 +410,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                     const int idx = tid + 256 * j;
                     const int rr = idx / NCH, cc = idx % NCH;
                     const int ch = pass_chan(ps, cc);
-                    if (rr < 3 && ch >= 0) xs[rr][cc] = hi ? pool[(hbase + ch) * 3 + rr] : TX{};
+                    if (rr < 3) xs[rr][cc] = hi ? pool[(hbase + ch) * 3 + rr] : TX{};
                 }
             }
         };
@@ -402,9 +424,9 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
             stage_pass(pv, ps);
             __syncthreads();
             const int ch0 = pass_chan(ps, 8 * cgi);
-            float wf[32];  // w[channel + e][i] at 4 e + i (unconditional loads, see above)
+            float wf[32];  // w[channel + e][i] at 4 e + i
             {
-                const TW *wp = static_cast<const TW *>(cv.w) + (int64_t)max(ch0, 0) * 4;
+                const TW *wp = static_cast<const TW *>(cv.w) + (int64_t)ch0 * 4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     Raw8<TW> wr;
@@ -421,7 +443,6 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
             __builtin_amdgcn_sched_barrier(0);
             load_pass(pv, min(ps + 1, npass_all - 1));
             __builtin_amdgcn_sched_barrier(0);
-            if (ch0 < 0) continue;  // past the last v channel (no barrier below)
             float y[TPT][8];
 #pragma unroll
             for (int j = 0; j < TPT; ++j)
@@ -443,7 +464,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                     }
                 }
             }
-            if (ps < NPASS) {
+            {
                 // q or k: SiLU, L2 norm over the head, hi / lo planes
                 const int cq = ps * NCH + 8 * cgi;
                 const bool isk = cq >= D;
@@ -464,70 +485,31 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                     split4_store(y[j][0] * inv, y[j][1] * inv, y[j][2] * inv, y[j][3] * inv, ph, pl);
                     split4_store(y[j][4] * inv, y[j][5] * inv, y[j][6] * inv, y[j][7] * inv, ph + 4, pl + 4);
                 }
-            } else {
-                // v: SiLU, straight into the V image the chain reads: per (chunk,
-                // value head) 32 tokens x 128 rows fp32, ordered so that chain lane
-                // (lr, lg) of row tile rt finds tokens 16 tau + 4 lg + 0..3 of row
-                // 16 rt + lr as one 16-byte piece: float (((rt 2 + tau) 4 + lg) 16 + lr) 4 + e
-                const int vc = (ps - NPASS) * NCH + 8 * cgi;
-                const int hh = vc / D, row0 = vc % D;
-                float *vh = vimg + ((size_t)c * Hv + kh * group + hh) * (CH * D);
-                const int t0g = TPT * tg;  // first token; TPT (2 or 4) divides 4
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = row0 + e;
-                    float vals[TPT];
-#pragma unroll
-                    for (int j = 0; j < TPT; ++j) vals[j] = t0g + j < Lc ? silu_f(y[j][e]) : 0.f;
-                    float *dst = vh + ((((row >> 4) * 2 + (t0g >> 4)) * 4 + ((t0g >> 2) & 3)) * 16 + (row & 15)) * 4 +
-                                 (t0g & 3);
-                    if constexpr (TPT == 4)
-                        *reinterpret_cast<float4 *>(dst) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-                    else
-                        *reinterpret_cast<float2 *>(dst) = make_float2(vals[0], vals[1]);
-                }
             }
         }
     }
     __syncthreads();
 
-    // K image: 48 fragment blocks x 64 lanes = 12 pieces per thread, each a
+    // K image: 32 fragment blocks x 64 lanes = 8 pieces per thread, each a
     // coalesced 16-byte store
     {
         uint8_t *kim = kimg + ((size_t)c * Hk + kh) * KIMG;
 #pragma unroll 4
-        for (int m = 0; m < 12; ++m) {
+        for (int m = 0; m < 8; ++m) {
             const int pi = tid + 256 * m;
             const int f = pi >> 6;
             const int l = pi & 63;
             const int plr = l & 15, plg = l >> 4;
-            uint4 val;
-            if (f < FKT) {
-                // K or Q rows 16 tau + lr, channels 32 ks + 4 lg + {0..3, 16..19}
-                const int ff = f & 15;
-                const int plane = ff >> 3, tau = (ff >> 2) & 1, ks = ff & 3;
-                const bool isQ = f >= FQ;
-                const uint16_t *row = isQ ? (plane ? sm.Ql[16 * tau + plr] : sm.Qh[16 * tau + plr])
-                                          : (plane ? sm.Kl[16 * tau + plr] : sm.Kh[16 * tau + plr]);
-                const int c0 = 32 * ks + 4 * plg;
-                const uint2 a = *reinterpret_cast<const uint2 *>(row + c0);
-                const uint2 b = *reinterpret_cast<const uint2 *>(row + c0 + 16);
-                val = make_uint4(a.x, a.y, b.x, b.y);
-            } else {
-                // K^T row j = 16 jt + lr, tokens 4 lg + {0..3, 16..19}
-                const int ff = f - FKT;
-                const int plane = ff >> 3, jt = ff & 7;
-                const int j = 16 * jt + plr;
-                uint16_t e[8];
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const int t = 16 * (p >> 2) + 4 * plg + (p & 3);
-                    e[p] = plane ? sm.Kl[t][j] : sm.Kh[t][j];
-                }
-                val = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
-                                 pack2(e[6], e[7]));
-            }
-            *reinterpret_cast<uint4 *>(kim + (size_t)f * FRAG + 16 * l) = val;
+            // K or Q rows 16 tau + lr, channels 32 ks + 4 lg + {0..3, 16..19}
+            const int ff = f & 15;
+            const int plane = ff >> 3, tau = (ff >> 2) & 1, ks = ff & 3;
+            const bool isQ = f >= FQ;
+            const uint16_t *row = isQ ? (plane ? sm.Ql[16 * tau + plr] : sm.Qh[16 * tau + plr])
+                                      : (plane ? sm.Kl[16 * tau + plr] : sm.Kh[16 * tau + plr]);
+            const int c0 = 32 * ks + 4 * plg;
+            const uint2 a = *reinterpret_cast<const uint2 *>(row + c0);
+            const uint2 b = *reinterpret_cast<const uint2 *>(row + c0 + 16);
+            *reinterpret_cast<uint4 *>(kim + (size_t)f * FRAG + 16 * l) = make_uint4(a.x, a.y, b.x, b.y);
         }
     }
 
@@ -717,22 +699,30 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 //   X = K S0^T, OQ = Q S0^T        (A: K / Q fragments, B: state registers)
 //   Delta = T (beta E)             (A: T fragments,     B: E registers)
 //   O = gamma OQ + P Delta         (A: P fragments,     B: Delta registers)
-//   S^T = gamma_C S^T + K^T Delta~ (A: K^T fragments,   B: Delta registers)
+//   S^T = gamma_C S^T + K^T Delta~ (A: K^T operands,    B: Delta registers)
 // An accumulator lane holds rows 4 lg + e of a 16-row tile; feeding it back
 // as the B operand of the next product uses the k-slot order
 //   slot (lg, p) -> 32 ks + 16 (p / 4) + 4 lg + p % 4,
 // and the prep kernel wrote the A fragments in that same order, so no register
-// ever crosses lanes.
+// ever crosses lanes.  The K^T operands come from the staged K planes through
+// the transposed LDS read (kt_frag).
+//
+// In the fused prefill (XCONV) the chain also forms v: its rows of state are
+// value channels, so each block stages the raw conv inputs of its own v
+// channels (35 rows of x per chunk, the 3 before it included) in LDS beside
+// the chunk's images, and every lane convolves its channel for its tokens.
 //
 // Blocks map to (request, key head) groups so that the blocks sharing a K
 // image run on one XCD (workgroups are dealt to the 8 XCDs round-robin) and
 // the longest requests' groups are dispatched first.
 // ---------------------------------------------------------------------------
-// Conv inputs the chain needs in its fused mode, where the prep kernel has
-// formed v into V images: the chain writes the request's new conv history
-// once the old one has been read (q / k and v by the prep kernel).
+// Conv inputs of the chain in the fused prefill: x and the conv taps of the v
+// channels, and the history pool (read for the v channels' first chunk, then
+// rewritten for every channel once the request's last chunk is done: the
+// prep kernel has read the q / k history by then).
 struct ChainConvIn {
     const void *x; int64_t x_ld;
+    const void *w; bool w_bf16;  // conv taps [C, 4]
     void *pool;
     int32_t C;   // conv channels q | k | v
     int32_t nq;  // Hk * D
@@ -747,54 +737,133 @@ struct ChainSnap {
 };
 
 // v for the tokens a lane holds in the accumulator layout, 16 tau + 4 lg + e
-// of a chunk: either four scalar loads per tau from v [T, Hv, D] (VIMG false),
-// or one 16-byte load per tau from the chunk's V image (VIMG true; the prep
-// kernel wrote zeros past the chunk's last token).  Loads stay raw until the
-// next chunk uses them.
-template <int RT, bool VIMG, typename TA>
+// of a chunk, from v [T, Hv, D] (the unfused prefill): four scalar loads per
+// tau, kept raw until the next chunk uses them.
+template <int RT, typename TA>
 struct ChainVLoads {
     chunk::Raw1<TA> r[RT][2][4];
-    float4 r4[RT][2];
 
-    __device__ __forceinline__ void load(const TA *v, const int (&irow)[RT], int h, int Hv, int tb,
-                                         int chunk_idx, int Lc, int lane) {
+    __device__ __forceinline__ void load(const TA *v, const int (&irow)[RT], int h, int Hv, int tb, int Lc,
+                                         int lane) {
         using namespace chunk;
         const int lg = lane >> 4;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int tau = 0; tau < 2; ++tau) {
-                if constexpr (!VIMG) {
+            for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * tau + 4 * lg + e;
-                        if (t < Lc) r[rt][tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow[rt]);
-                        else r[rt][tau][e].zero();
-                    }
-                } else {
-                    const float *img = reinterpret_cast<const float *>(v) + ((size_t)chunk_idx * Hv + h) * (CH * D);
-                    r4[rt][tau] = *reinterpret_cast<const float4 *>(img + (((irow[rt] >> 4) * 2 + tau) * 64 + lane) * 4);
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tau + 4 * lg + e;
+                    if (t < Lc) r[rt][tau][e].load(v + ((int64_t)(tb + t) * Hv + h) * D + irow[rt]);
+                    else r[rt][tau][e].zero();
                 }
-            }
     }
 
     __device__ __forceinline__ void get(float (&vc)[RT][2][4]) const {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int tau = 0; tau < 2; ++tau) {
-                if constexpr (!VIMG) {
+            for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vc[rt][tau][e] = r[rt][tau][e].get();
-                } else {
-                    vc[rt][tau][0] = r4[rt][tau].x;
-                    vc[rt][tau][1] = r4[rt][tau].y;
-                    vc[rt][tau][2] = r4[rt][tau].z;
-                    vc[rt][tau][3] = r4[rt][tau].w;
-                }
-            }
+                for (int e = 0; e < 4; ++e) vc[rt][tau][e] = r[rt][tau][e].get();
     }
 };
+
+// The conv inputs a fused chain block stages per chunk: for each of its NH
+// heads, XR rows (tokens tb - 3 .. tb + 31) of its IBH v channels of x, each
+// row followed by one unused 16-byte slot, so that lanes reading rows 4 apart
+// (the 4 lane groups of an accumulator) fall in different LDS banks.
+template <typename TX, int NH, int IBH> struct XRows {
+    static constexpr int PIECES = IBH * (int)sizeof(TX) / 16;  // 16-byte pieces per row
+    static constexpr int ROWB = (PIECES + 1) * 16;
+    static constexpr int HEADB = chunk::XR * ROWB;
+    static constexpr int BYTES = NH * HEADB;
+    static constexpr int SLOTS = NH * chunk::XR * (PIECES + 1);
+    static constexpr int NCOPY = (SLOTS + 63) / 64;            // 64-lane copies per chunk
+};
+
+// This wave's share (copies w, w + NWC, ...) of the direct-to-LDS copies that
+// stage one chunk's x rows at LDS address xs: copy m fills slots 64 m .. + 63,
+// slot -> (head, row, piece).  Head hd's channels are cb + hd D .. + IBH - 1.
+// Row rr is token tb - 3 + rr; rows past the request's last token repeat it
+// (their v is never used); padding slots are skipped, and so are rows 0..2 of
+// the request's first chunk (first: those come from the slot's history).
+template <typename TX, int NH, int IBH, int NWC>
+__device__ __forceinline__ void issue_xrows(uint32_t xs, const ChainConvIn &cv, int cb, int tb, int tok_last,
+                                            bool first, int w, int lane) {
+    using namespace chunk;
+    using XRW = XRows<TX, NH, IBH>;
+    constexpr int RS = XRW::PIECES + 1;  // slots per row
+    const int base_row = first ? tb : tb - 3;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(static_cast<const TX *>(cv.x) +
+                                                              (int64_t)base_row * cv.x_ld);
+#pragma unroll
+    for (int m = w; m < XRW::NCOPY; m += NWC) {
+        const int slot = 64 * m + lane;
+        const int hd = slot / (XR * RS);
+        const int rem = slot - hd * (XR * RS);
+        const int rr = rem / RS;
+        const int pc = rem - rr * RS;
+        if (slot < XRW::SLOTS && pc < XRW::PIECES && (!first || rr >= 3)) {
+            const int grow = min(tb - 3 + rr, tok_last);
+            const int64_t el = (int64_t)(grow - base_row) * cv.x_ld + cb + hd * D + pc * (16 / (int)sizeof(TX));
+            copy_frag(base, xs + 1024u * (uint32_t)m, (uint32_t)(el * (int64_t)sizeof(TX)));
+        }
+    }
+}
+
+// The three history rows of one staged channel for the request's first chunk
+// (zeros without a history), written by the lane that owns the channel.
+template <typename TX>
+__device__ __forceinline__ void stage_history(uint8_t *xs_col, int rowb, const ChainConvIn &cv, int c, int slot,
+                                              bool hi) {
+    const TX *hp = static_cast<const TX *>(cv.pool) + ((int64_t)slot * cv.C + c) * 3;
+#pragma unroll
+    for (int rr = 0; rr < 3; ++rr) *reinterpret_cast<TX *>(xs_col + rr * rowb) = hi ? hp[rr] : TX{};
+}
+
+// The conv taps of channel c, widened to fp32.
+__device__ __forceinline__ void load_taps(const ChainConvIn &cv, int c, float (&wt)[4]) {
+    if (cv.w_bf16) {
+        const float4 f = ld4(static_cast<const bf16 *>(cv.w) + (int64_t)c * 4);
+        wt[0] = f.x; wt[1] = f.y; wt[2] = f.z; wt[3] = f.w;
+    } else {
+        const float4 f = ld4(static_cast<const float *>(cv.w) + (int64_t)c * 4);
+        wt[0] = f.x; wt[1] = f.y; wt[2] = f.z; wt[3] = f.w;
+    }
+}
+
+template <typename TX> __device__ __forceinline__ float lds_x(const uint8_t *p);
+template <> __device__ __forceinline__ float lds_x<float>(const uint8_t *p) {
+    return *reinterpret_cast<const float *>(p);
+}
+template <> __device__ __forceinline__ float lds_x<bf16>(const uint8_t *p) {
+    return __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t *>(p)) << 16);
+}
+
+// v = SiLU(sum_i w_i x_{t-i}) of this lane's channel for its tokens 16 tau +
+// 4 lg + e of the chunk (0 past the chunk's last token), from the staged rows
+// of its channel (xs_col: row 0 of the channel's column; row rr is token
+// tb - 3 + rr, so tap i of token t sits in row t + 3 - i).  The taps are
+// summed from the oldest input on, as the other channels' conv does.
+template <typename TX, int ROWB>
+__device__ __forceinline__ void conv_v(const uint8_t *xs_col, const float (&wt)[4], int lg, int Lc,
+                                       float (&vc)[2][4]) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        const int t0 = 16 * tau + 4 * lg;
+        float xr[7];  // rows t0 .. t0 + 6: tokens t0 - 3 .. t0 + 3
+#pragma unroll
+        for (int j = 0; j < 7; ++j) xr[j] = lds_x<TX>(xs_col + (t0 + j) * ROWB);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float y = 0.f;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) y += wt[i] * xr[e + 3 - i];
+            vc[tau][e] = t0 + e < Lc ? silu_f(y) : 0.f;
+        }
+    }
+}
 
 // New conv history of channel c: the last 3 entries of the window [history,
 // the request's L rows] (raw copies; zeros stand in for a missing history).
@@ -833,11 +902,18 @@ __device__ __forceinline__ void issue_images(uint32_t stage, const uint8_t *kim,
     }
 }
 
-// NCW extra waves only copy the images (STAGES == 2): a wave issues
-// direct-to-LDS copies at a limited rate, so a block of few compute waves
-// spends more time issuing a chunk's copies than computing it unless other
-// waves share that work.
-template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS, int NCW>
+// LDS of one stage of the per-head chain: the chunk's K image, its T image and
+// (fused) its staged x rows; two stages alternate.
+template <int NW, bool XCONV, typename TX>
+constexpr size_t chain_stage_bytes() {
+    return chunk::KIMG + chunk::TIMG + (XCONV ? (size_t)XRows<TX, 1, 16 * NW>::BYTES : 0);
+}
+
+// NCW extra waves only copy (images and x rows): a wave issues direct-to-LDS
+// copies at a limited rate, so a block of few compute waves spends more time
+// issuing a chunk's copies than computing it unless other waves share that
+// work.
+template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, int NCW>
 __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
@@ -847,6 +923,9 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     using namespace chunk;
     constexpr int IB = 16 * NW;  // state rows per block
     constexpr int NRB = D / IB;  // blocks per (request, head)
+    using XRW = XRows<TX, 1, IB>;
+    constexpr uint32_t XOFF = (uint32_t)(KIMG + TIMG);  // staged x rows within a stage
+    constexpr uint32_t STG = (uint32_t)chain_stage_bytes<NW, XCONV, TX>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lds0 = lds_addr(smem);
@@ -872,22 +951,28 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
     const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
     const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
+    const int tok_last = tok0 + L - 1;
+    const int cb = 2 * cv.nq + h * D + IB * rb;  // the block's first v channel (fused)
     if constexpr (NCW > 0) {
-        static_assert(STAGES == 2, "copy waves fill the two-stage ring");
         if (w >= NW) {
-            // copy wave: chunk cc + 1's images go into the free stage while the
-            // compute waves work on chunk cc; one barrier per chunk, as theirs
+            // copy wave: chunk cc + 1's images and x rows go into the free stage
+            // while the compute waves work on chunk cc; one barrier per chunk, as
+            // theirs
             const int cw = w - NW;
 #pragma unroll
             for (int part = 0; part < NPART; ++part) issue_images<NCW>(lds0, kim0, tim0, cw, lane, part);
+            if constexpr (XCONV) issue_xrows<TX, 1, IB, NCW>(lds0 + XOFF, cv, cb, tok0, tok_last, true, cw, lane);
             for (int cc = 0; cc < nch; ++cc) {
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
                 if (cc + 1 < nch) {
-                    const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * (uint32_t)STAGE;
+                    const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * STG;
 #pragma unroll
                     for (int part = 0; part < NPART; ++part)
                         issue_images<NCW>(nstg, kim0 + (cc + 1) * kstep, tim0 + (cc + 1) * tstep, cw, lane, part);
+                    if constexpr (XCONV)
+                        issue_xrows<TX, 1, IB, NCW>(nstg + XOFF, cv, cb, tok0 + (cc + 1) * CH, tok_last, false,
+                                                    cw, lane);
                 }
             }
             return;
@@ -910,38 +995,55 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
         }
     }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    const uint32_t kt_off = kt_lane_off(lr, lg);
+    const int xcol = (16 * w + lr) * (int)sizeof(TX);  // this lane's column of the staged rows
 
-    // v of this lane's row for tokens 16 tau + 4 lg + e of chunk cc
-    ChainVLoads<1, VIMG, TA> vr;
-    auto load_v = [&](int cc) { vr.load(v, irows, h, Hv, tok0 + cc * CH, c_first + cc, min(CH, L - cc * CH), lane); };
+    float wt[4] = {0.f, 0.f, 0.f, 0.f};
+    ChainVLoads<1, TA> vr;
+    auto load_v = [&](int cc) { vr.load(v, irows, h, Hv, tok0 + cc * CH, min(CH, L - cc * CH), lane); };
 
+    if constexpr (XCONV) {
+        load_taps(cv, cb + 16 * w + lr, wt);
+        if (lg == 0) stage_history<TX>(smem + XOFF + xcol, XRW::ROWB, cv, cb + 16 * w + lr, slot, hi_init);
+    }
     if constexpr (NCW == 0) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, kim0, tim0, w, lane, part);
+        if constexpr (XCONV) issue_xrows<TX, 1, IB, NW>(lds0 + XOFF, cv, cb, tok0, tok_last, true, w, lane);
     }
-    load_v(0);
+    if constexpr (!XCONV) load_v(0);
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
     __builtin_amdgcn_s_waitcnt(0);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
-        const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * STAGE : 0);
-        const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * (uint32_t)STAGE;
-        const bool more = STAGES == 2 && cc + 1 < nch;   // chunk cc + 1's v loads
-        const bool prefetch = NCW == 0 && more;          // and its copies, by this wave
+        const uint8_t *stg = smem + (size_t)(cc & 1) * STG;
+        const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * STG;
+        const bool more = cc + 1 < nch;          // chunk cc + 1's v loads
+        const bool prefetch = NCW == 0 && more;  // and its copies, by this wave
         const uint8_t *nkim = kim0 + (cc + 1) * kstep, *ntim = tim0 + (cc + 1) * tstep;
         // this wave's copies and loads of chunk cc have landed (issued before the
         // previous chunk's 8 o stores, which may stay in flight); after the
-        // barrier every wave's have, and (two stages) every wave is done with
-        // chunk cc - 1
-        if (STAGES == 2 && cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+        // barrier every wave's have, and every wave is done with chunk cc - 1
+        if (cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        float vcur1[1][2][4];
-        vr.get(vcur1);
-        float(&vcur)[2][4] = vcur1[0];
-        if (prefetch) issue_images<NW>(nstg, nkim, ntim, w, lane, 0);
+        float vcur[2][4];
+        if constexpr (XCONV) {
+            conv_v<TX, XRW::ROWB>(stg + XOFF + xcol, wt, lg, Lc, vcur);
+        } else {
+            float vcur1[1][2][4];
+            vr.get(vcur1);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vcur[tau][e] = vcur1[0][tau][e];
+        }
+        if (prefetch) {
+            issue_images<NW>(nstg, nkim, ntim, w, lane, 0);
+            if constexpr (XCONV) issue_xrows<TX, 1, IB, NW>(nstg + XOFF, cv, cb, tb + CH, tok_last, false, w, lane);
+        }
         const uint8_t *kst = stg + 16 * lane;          // this lane's piece of each K fragment
         const uint8_t *tst = stg + KIMG + 16 * lane;   // and of each T fragment
 
@@ -972,7 +1074,7 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
                 mma3(OQ[tau], qh_, ql_, sbh, sbl);
             }
         }
-        if (more) load_v(cc + 1);
+        if (!XCONV && more) load_v(cc + 1);
         // per-token gamma, e^{G_C - G_t}, beta for this lane's tokens
         const uint8_t *tvec = stg + KIMG;
         float4 gam[2], rev[2], bet[2];
@@ -1026,10 +1128,11 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
             mma3(OQ[tau], frag(tst + (FP + tau) * FRAG), frag(tst + (FP + 2 + tau) * FRAG), dbh, dbl);
+        const uint8_t *ktl = stg + kt_off;
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
             ST[jt] *= gC;
-            mma3(ST[jt], frag(kst + (FKT + jt) * FRAG), frag(kst + (FKT + 8 + jt) * FRAG), tbh, tbl);
+            mma3(ST[jt], kt_frag(ktl, 0, jt), kt_frag(ktl, 1, jt), tbh, tbl);
         }
         {
             const __amdgpu_buffer_rsrc_t orr = wave_rsrc(o + ((int64_t)tb * Hv + h) * D,
@@ -1050,24 +1153,17 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
             for (int jt = 0; jt < 8; ++jt)
                 st4(sp + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
         }
-        if (STAGES == 1) {
-            __syncthreads();  // every wave is done reading the stage
-            if (cc + 1 < nch) {
-#pragma unroll
-                for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, nkim, ntim, w, lane, part);
-                load_v(cc + 1);
-            }
-        }
     }
 
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt)
         st4(sbase + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
-    if constexpr (VIMG) {
-        // new history (the prep kernel has read the old one): this lane's v
+    if constexpr (XCONV) {
+        // new history (every reader of the old one is done: the prep kernel for
+        // q / k, this block's prologue for its v channels): this lane's v
         // channel, and the key head's q / k channels from one block of the key
         // head's first value head
-        if (lg == 0) chain_write_history<TX>(cv, 2 * cv.nq + h * D + irow, slot, hi_init, tok0, L);
+        if (lg == 0) chain_write_history<TX>(cv, cb + 16 * w + lr, slot, hi_init, tok0, L);
         if (h % group == 0 && rb == 0)
             for (int j = threadIdx.x; j < 2 * D; j += 64 * NW)
                 chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
@@ -1077,19 +1173,23 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
 // ---------------------------------------------------------------------------
 // chain, group variant for large batches: one block per (request, key head,
 // block of 64 state rows) covering the 3 value heads that read the key head,
-// so the chunk's 48 KiB K image is staged once for them.  The 12 row tiles of
-// 16 rows go to 8 waves: four waves hold two tiles of one head (every K / Q /
-// K^T fragment read feeds both) and four hold one, so that with waves dealt
-// to the 4 SIMDs in turn each SIMD carries one of each, 3 tiles (6 waves of
-// two tiles left two SIMDs with twice the work of the others, and the block
-// waited for them at every chunk).  Same per-row algebra and operand layout
-// as above.
+// so the chunk's K image is staged once for them.  The 12 row tiles of 16 rows
+// go to 8 waves: four waves hold two tiles of one head (every K / Q / K^T
+// operand read feeds both) and four hold one, so that with waves dealt to the
+// 4 SIMDs in turn each SIMD carries one of each, 3 tiles (6 waves of two
+// tiles left two SIMDs with twice the work of the others, and the block waited
+// for them at every chunk).  Same per-row algebra and operand layout as above.
 // ---------------------------------------------------------------------------
 constexpr int GRP_ROWS = 64;          // state rows per head per block
 constexpr int GRP_RPW = 2;            // 16-row tiles per wave, at most
 constexpr int GRP_NW = 8;             // waves per block
 
-template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
+template <int G, bool XCONV, typename TX>
+constexpr size_t group_stage_bytes() {
+    return chunk::KIMG + G * chunk::TIMG + (XCONV ? (size_t)XRows<TX, G, GRP_ROWS>::BYTES : 0);
+}
+
+template <int G, typename TA, typename TO, bool XCONV, typename TX, typename TS>
 __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
@@ -1101,7 +1201,9 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     constexpr int NW = GRP_NW;
     constexpr int NRB = D / GRP_ROWS;               // row blocks per head
     constexpr int NFRAG = KIMG_FRAGS + G * TIMG_FRAGS;
-    constexpr size_t GSTAGE = KIMG + G * TIMG;
+    using XRW = XRows<TX, G, GRP_ROWS>;
+    constexpr uint32_t XOFF = (uint32_t)(KIMG + G * TIMG);
+    constexpr uint32_t GSTG = (uint32_t)group_stage_bytes<G, XCONV, TX>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lds0 = lds_addr(smem);
@@ -1128,13 +1230,19 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     const int nch = (L + CH - 1) / CH;
     const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
+    const int tok_last = tok0 + L - 1;
     // a one-tile wave's second tile repeats its first: loads stay in bounds and
     // every store of it is dropped or skipped
-    int irow[GRP_RPW];
+    int irow[GRP_RPW], ci[GRP_RPW];
 #pragma unroll
-    for (int rt = 0; rt < GRP_RPW; ++rt) irow[rt] = GRP_ROWS * rb + 16 * (tile0 + (rt < nt ? rt : 0)) + lr;
+    for (int rt = 0; rt < GRP_RPW; ++rt) {
+        ci[rt] = 16 * (tile0 + (rt < nt ? rt : 0)) + lr;  // row within the block's 64 of head hh
+        irow[rt] = GRP_ROWS * rb + ci[rt];
+    }
     const int slot = slots[r];
     TS *sbase = state + ((int64_t)slot * Hv + h) * D * D;
+    // fused: the group's v channels of this row block, head hd at cb + hd D
+    const int cb = 2 * cv.nq + kh * G * D + GRP_ROWS * rb;
 
     floatx4_t ST[GRP_RPW][8];
 #pragma unroll
@@ -1148,14 +1256,15 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
             }
         }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    const uint32_t kt_off = kt_lane_off(lr, lg);
 
     const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
     const uint8_t *tim0 = timg + ((size_t)c_first * Hv + kh * G) * TIMG;  // the group's G heads are adjacent
     const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
 
-    // this wave's copies of chunk cc's images, in NPART slices so that they can be
-    // spread over the previous chunk's MFMA phases instead of stalling the wave
-    // on a full memory queue in one burst
+    // this wave's copies of chunk cc's images (and, with part 0, x rows), in
+    // NPART slices so that they can be spread over the previous chunk's MFMA
+    // phases instead of stalling the wave on a full memory queue in one burst
     constexpr int PER_WAVE = (NFRAG + NW - 1) / NW;
     auto issue = [&](uint32_t stage, int cc, int part) {
         const uint8_t *kim = kim0 + cc * kstep;
@@ -1168,28 +1277,49 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
                 copy_frag(src, stage + (uint32_t)f * FRAG, 16u * lane);
             }
         }
+        if constexpr (XCONV) {
+            if (part == 0) issue_xrows<TX, G, GRP_ROWS, NW>(stage + XOFF, cv, cb, tok0 + cc * CH, tok_last, cc == 0,
+                                                            w, lane);
+        }
     };
-    ChainVLoads<GRP_RPW, VIMG, TA> vr;
-    auto load_v = [&](int cc) { vr.load(v, irow, h, Hv, tok0 + cc * CH, c_first + cc, min(CH, L - cc * CH), lane); };
+    float wt[GRP_RPW][4];
+    ChainVLoads<GRP_RPW, TA> vr;
+    auto load_v = [&](int cc) { vr.load(v, irow, h, Hv, tok0 + cc * CH, min(CH, L - cc * CH), lane); };
 
+    if constexpr (XCONV) {
+#pragma unroll
+        for (int rt = 0; rt < GRP_RPW; ++rt) {
+            load_taps(cv, cb + hh * D + ci[rt], wt[rt]);
+            if (lg == 0)
+                stage_history<TX>(smem + XOFF + hh * XRW::HEADB + ci[rt] * (int)sizeof(TX), XRW::ROWB, cv,
+                                  cb + hh * D + ci[rt], slot, hi_init);
+        }
+    }
 #pragma unroll
     for (int part = 0; part < NPART; ++part) issue(lds0, 0, part);
-    load_v(0);
+    if constexpr (!XCONV) load_v(0);
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
     __builtin_amdgcn_s_waitcnt(0);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
-        const uint8_t *stg = smem + (STAGES == 2 ? (size_t)(cc & 1) * GSTAGE : 0);
-        const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * (uint32_t)GSTAGE;
-        const bool prefetch = STAGES == 2 && cc + 1 < nch;
+        const uint8_t *stg = smem + (size_t)(cc & 1) * GSTG;
+        const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * GSTG;
+        const bool prefetch = cc + 1 < nch;
         // as in the per-head chain: the previous chunk's o stores stay in flight
-        if (STAGES == 2 && cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * GRP_RPW));
+        if (cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * GRP_RPW));
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float vcur[GRP_RPW][2][4];
-        vr.get(vcur);
+        if constexpr (XCONV) {
+#pragma unroll
+            for (int rt = 0; rt < GRP_RPW; ++rt)
+                conv_v<TX, XRW::ROWB>(stg + XOFF + hh * XRW::HEADB + ci[rt] * (int)sizeof(TX), wt[rt], lg, Lc,
+                                      vcur[rt]);
+        } else {
+            vr.get(vcur);
+        }
         if (prefetch) issue(nstg, cc + 1, 0);
         const uint8_t *kst = stg + 16 * lane;
         const uint8_t *tst = stg + KIMG + (size_t)hh * TIMG + 16 * lane;
@@ -1230,7 +1360,7 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
                 }
             }
         }
-        if (prefetch) load_v(cc + 1);
+        if (!XCONV && prefetch) load_v(cc + 1);
         float4 gam[2], rev[2], bet[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
@@ -1291,15 +1421,16 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
                 mma3(OQ[rt][1], ph1, pl1, dbh, dbl);
             }
         }
+        const uint8_t *ktl = stg + kt_off;
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-            const bf16x8_t kth = frag(kst + (FKT + jt) * FRAG);
-            const bf16x8_t ktl = frag(kst + (FKT + 8 + jt) * FRAG);
+            const bf16x8_t kth = kt_frag(ktl, 0, jt);
+            const bf16x8_t ktlo = kt_frag(ktl, 1, jt);
 #pragma unroll
             for (int rt = 0; rt < GRP_RPW; ++rt) {
                 if (rt < nt) {
                     ST[rt][jt] *= gC;
-                    mma3(ST[rt][jt], kth, ktl, tbh[rt], tbl[rt]);
+                    mma3(ST[rt][jt], kth, ktlo, tbh[rt], tbl[rt]);
                 }
             }
         }
@@ -1332,14 +1463,6 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
                         st4(sp + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
                             make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
         }
-        if (STAGES == 1) {
-            __syncthreads();
-            if (cc + 1 < nch) {
-#pragma unroll
-                for (int part = 0; part < NPART; ++part) issue(lds0, cc + 1, part);
-                load_v(cc + 1);
-            }
-        }
     }
 #pragma unroll
     for (int rt = 0; rt < GRP_RPW; ++rt)
@@ -1348,13 +1471,13 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
             for (int jt = 0; jt < 8; ++jt)
                 st4(sbase + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
                     make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
-    if constexpr (VIMG) {
-        // new history (the prep kernel has read the old one): this lane's v
+    if constexpr (XCONV) {
+        // new history (every reader of the old one is done): this lane's v
         // channels, and the key head's q / k channels from the first row block
         if (lg == 0)
 #pragma unroll
             for (int rt = 0; rt < GRP_RPW; ++rt)
-                if (rt < nt) chain_write_history<TX>(cv, 2 * cv.nq + h * D + irow[rt], slot, hi_init, tok0, L);
+                if (rt < nt) chain_write_history<TX>(cv, cb + hh * D + ci[rt], slot, hi_init, tok0, L);
         if (rb == 0)
             for (int j = threadIdx.x; j < 2 * D; j += 64 * NW)
                 chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
@@ -1383,62 +1506,67 @@ size_t prefill_chunk_workspace_bytes(int32_t Hk, int32_t Hv, int32_t T, int32_t 
     return ChunkWorkspace(Hk, Hv, T, nreq).total;
 }
 
-// TA: the type of v (or float for V images); VIMG: v from the V images the
-// prep kernel wrote, and the chain writes the new conv history (of type TX).
-template <int NW, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS, int NCW>
+// TA: the type of v (the unfused prefill); XCONV: the fused prefill, where the
+// chain forms v from x (of type TX) and writes the new conv history.
+template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, int NCW>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
     static std::atomic<uint64_t> set{0};
-    const size_t smem = STAGES * STAGE;
-    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS, NCW>, smem, set);
+    constexpr size_t smem = 2 * chain_stage_bytes<NW, XCONV, TX>();
+    static_assert(smem <= 160 * 1024, "two chain stages must fit in LDS");
+    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS, NCW>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, STAGES, TA, TO, VIMG, TX, TS, NCW>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS, NCW>), dim3((unsigned)blocks),
                        dim3(64 * (NW + NCW)), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
     return hipGetLastError();
 }
 
-template <int G, int STAGES, typename TA, typename TO, bool VIMG, typename TX, typename TS>
+template <int G, typename TA, typename TO, bool XCONV, typename TX, typename TS>
 static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                      const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                      const ChainConvIn &cv, const ChainSnap &sn) {
     using namespace chunk;
     constexpr int NW = GRP_NW;
     static std::atomic<uint64_t> set{0};
-    const size_t smem = STAGES * (KIMG + G * TIMG);
-    hipError_t e = set_smem_once(&prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>, smem, set);
+    constexpr size_t smem = 2 * group_stage_bytes<G, XCONV, TX>();
+    static_assert(smem <= 160 * 1024, "two chain stages must fit in LDS");
+    hipError_t e = set_smem_once(&prefill_chain_group_kernel<G, TA, TO, XCONV, TX, TS>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * (int64_t)(D / GRP_ROWS) * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_group_kernel<G, STAGES, TA, TO, VIMG, TX, TS>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((prefill_chain_group_kernel<G, TA, TO, XCONV, TX, TS>), dim3((unsigned)blocks),
                        dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
     return hipGetLastError();
 }
 
 // Block shape: large batches take key-head group blocks (the K image staged
-// once for the group's 3 value heads); else per-head blocks, a whole head
-// (8 waves) when there are enough (request, head) units to fill the chip,
-// else 32 rows.
-template <typename TA, typename TO, bool VIMG, typename TX, typename TS>
+// once for the group's 3 value heads; in the fused prefill only with bf16 x,
+// whose staged rows leave two stages within LDS); else per-head blocks, a
+// whole head (8 waves) when there are enough (request, head) units to fill the
+// chip, else 32 rows.
+template <typename TA, typename TO, bool XCONV, typename TX, typename TS>
 static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                    const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                    const ChainConvIn &cv, const ChainSnap &sn) {
     const int64_t units = (int64_t)a.nreq * a.Hv;
-    if (units >= 256 && a.Hv == 3 * a.Hk)
-        return launch_chain_group<3, 2, TA, TO, VIMG, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
-    return units >= 256 ? launch_chain<8, 2, TA, TO, VIMG, TX, TS, 0>(a, s, chunk_off, order, kimg, timg, cv, sn)
-                        : launch_chain<2, 2, TA, TO, VIMG, TX, TS, 6>(a, s, chunk_off, order, kimg, timg, cv, sn);
+    if constexpr (!XCONV || std::is_same<TX, bf16>::value) {
+        if (units >= 256 && a.Hv == 3 * a.Hk)
+            return launch_chain_group<3, TA, TO, XCONV, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
+    }
+    return units >= 256 ? launch_chain<8, TA, TO, XCONV, TX, TS, 0>(a, s, chunk_off, order, kimg, timg, cv, sn)
+                        : launch_chain<2, TA, TO, XCONV, TX, TS, 6>(a, s, chunk_off, order, kimg, timg, cv, sn);
 }
 
 template <typename TA, typename TG, typename TX, typename TW, bool CONV>
 static hipError_t launch_prep(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
-                              uint8_t *kimg, uint8_t *timg, const PrepConvIn &cv, float *vimg) {
+                              uint8_t *kimg, uint8_t *timg, const PrepConvIn &cv) {
     using namespace chunk;
     static std::atomic<uint64_t> set{0};
     hipError_t e = set_smem_once(&prefill_prep_kernel<TA, TG, TX, TW, CONV>, sizeof(PrepSmem), set);
@@ -1447,7 +1575,7 @@ static hipError_t launch_prep(const PrefillArgs &a, hipStream_t s, const int32_t
     hipLaunchKernelGGL((prefill_prep_kernel<TA, TG, TX, TW, CONV>), dim3((unsigned)(max_chunks * a.Hk)),
                        dim3(256), sizeof(PrepSmem), s, (const TA *)a.q, (const TA *)a.k,
                        (const TG *)a.a, (const TG *)a.b, a.gate_ld, a.qsl, chunk_off, a.nreq, a.Hk,
-                       a.Hv, kimg, timg, cv, vimg);
+                       a.Hv, kimg, timg, cv);
     return hipGetLastError();
 }
 
@@ -1470,17 +1598,15 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     const ChainSnap sn{a.max_snaps > 0 ? a.snap_slots : nullptr, a.max_snaps > 0 ? a.snap_interval / CH : 1,
                        a.max_snaps};
     if (a.x) {
-        // conv mode: the prep kernel forms q and k (into the K images) and v
-        // (into V images at a.v, one per chunk and value head) from x; the chain
-        // reads the V images and writes the new history of every channel; o is
-        // fp32 scratch in this mode
-        float *vimg = static_cast<float *>(const_cast<void *>(a.v));
-        e = a.x_bf16 ? (a.w_bf16 ? launch_prep<TA, TG, bf16, bf16, true>(a, s, chunk_off, kimg, timg, cv, vimg)
-                                 : launch_prep<TA, TG, bf16, float, true>(a, s, chunk_off, kimg, timg, cv, vimg))
-                     : (a.w_bf16 ? launch_prep<TA, TG, float, bf16, true>(a, s, chunk_off, kimg, timg, cv, vimg)
-                                 : launch_prep<TA, TG, float, float, true>(a, s, chunk_off, kimg, timg, cv, vimg));
+        // conv mode: the prep kernel forms q and k (into the K images) from x;
+        // the chain forms v from x itself and writes the new history of every
+        // channel; o is fp32 scratch in this mode
+        e = a.x_bf16 ? (a.w_bf16 ? launch_prep<TA, TG, bf16, bf16, true>(a, s, chunk_off, kimg, timg, cv)
+                                 : launch_prep<TA, TG, bf16, float, true>(a, s, chunk_off, kimg, timg, cv))
+                     : (a.w_bf16 ? launch_prep<TA, TG, float, bf16, true>(a, s, chunk_off, kimg, timg, cv)
+                                 : launch_prep<TA, TG, float, float, true>(a, s, chunk_off, kimg, timg, cv));
         if (e != hipSuccess) return e;
-        const ChainConvIn ci{a.x, a.x_ld, a.pool, 2 * a.Hk * D + a.Hv * D, a.Hk * D};
+        const ChainConvIn ci{a.x, a.x_ld, a.conv_w, a.w_bf16, a.pool, 2 * a.Hk * D + a.Hv * D, a.Hk * D};
         if constexpr (std::is_same<TO, float>::value) {
             if (a.state_bf16)
                 e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn)
@@ -1492,7 +1618,7 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
             return hipErrorInvalidValue;
         }
     } else {
-        e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv, nullptr);
+        e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv);
         if (e != hipSuccess) return e;
         if (a.state_bf16) return hipErrorInvalidValue;  // the unfused prefill keeps an fp32 state
         e = launch_chain_any<TA, TO, false, float, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{}, sn);
