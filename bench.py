@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--prefill-steps", type=int, default=5)
+    p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-varlen", action="store_true")
     p.add_argument("--no-layer", action="store_true")

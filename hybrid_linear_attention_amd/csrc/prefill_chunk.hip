@@ -769,48 +769,63 @@ struct ChainVLoads {
     }
 };
 
-// The conv inputs a fused chain block stages per chunk: for each of its NH
-// heads, XR rows (tokens tb - 3 .. tb + 31) of its IBH v channels of x, each
-// row followed by one unused 16-byte slot, so that lanes reading rows 4 apart
-// (the 4 lane groups of an accumulator) fall in different LDS banks.
-template <typename TX, int NH, int IBH> struct XRows {
-    static constexpr int PIECES = IBH * (int)sizeof(TX) / 16;  // 16-byte pieces per row
+// The conv inputs a compute wave of a fused chain block stages per chunk: XR
+// rows (tokens tb - 3 .. tb + 31) of x over the v channels of its own row
+// tiles (16 NT channels), each row followed by one unused 16-byte slot, so
+// that lanes reading rows 4 apart (the 4 lane groups of an accumulator) fall
+// in different LDS banks.  The wave copies these rows itself, so once its own
+// copies have landed it can convolve them without waiting for the block.
+template <typename TX, int NT> struct XWave {
+    static constexpr int PIECES = 16 * NT * (int)sizeof(TX) / 16;  // 16-byte pieces per row
     static constexpr int ROWB = (PIECES + 1) * 16;
-    static constexpr int HEADB = chunk::XR * ROWB;
-    static constexpr int BYTES = NH * HEADB;
-    static constexpr int SLOTS = NH * chunk::XR * (PIECES + 1);
-    static constexpr int NCOPY = (SLOTS + 63) / 64;            // 64-lane copies per chunk
+    static constexpr int SLOTS = chunk::XR * (PIECES + 1);
+    static constexpr int BYTES = SLOTS * 16;
+    static constexpr int NCOPY = (SLOTS + 63) / 64;               // 64-lane copies per chunk
 };
 
-// This wave's share (copies w, w + NWC, ...) of the direct-to-LDS copies that
-// stage one chunk's x rows at LDS address xs: copy m fills slots 64 m .. + 63,
-// slot -> (head, row, piece).  Head hd's channels are cb + hd D .. + IBH - 1.
-// Row rr is token tb - 3 + rr; rows past the request's last token repeat it
-// (their v is never used); padding slots are skipped, and so are rows 0..2 of
-// the request's first chunk (first: those come from the slot's history).
-template <typename TX, int NH, int IBH, int NWC>
-__device__ __forceinline__ void issue_xrows(uint32_t xs, const ChainConvIn &cv, int cb, int tb, int tok_last,
-                                            bool first, int w, int lane) {
-    using namespace chunk;
-    using XRW = XRows<TX, NH, IBH>;
-    constexpr int RS = XRW::PIECES + 1;  // slots per row
-    const int base_row = first ? tb : tb - 3;
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(static_cast<const TX *>(cv.x) +
-                                                              (int64_t)base_row * cv.x_ld);
+// The lane's part of a wave's x-row copies (the same for every chunk, so it
+// is decoded once): copy i fills slots 64 i .. + 63 of the wave's rows, slot
+// -> (row, piece).  The wave owns nt <= NTMAX tiles (16 nt channels).
+template <typename TX, int NTMAX>
+struct XCopyPlan {
+    static constexpr int NCOPY = XWave<TX, NTMAX>::NCOPY;
+    int rr[NCOPY];   // staged row (token tb - 3 + rr), or -1: no copy by this lane
+    int col[NCOPY];  // element offset of the piece within a row of x
+
+    // c0: the first of the wave's 16 nt channels
+    __device__ __forceinline__ void init(int c0, int nt, int lane) {
+        using namespace chunk;
+        const int pieces = nt * (int)sizeof(TX);  // 16 nt channels in 16-byte pieces
+        const int rs = pieces + 1;                // slots per row
 #pragma unroll
-    for (int m = w; m < XRW::NCOPY; m += NWC) {
-        const int slot = 64 * m + lane;
-        const int hd = slot / (XR * RS);
-        const int rem = slot - hd * (XR * RS);
-        const int rr = rem / RS;
-        const int pc = rem - rr * RS;
-        if (slot < XRW::SLOTS && pc < XRW::PIECES && (!first || rr >= 3)) {
-            const int grow = min(tb - 3 + rr, tok_last);
-            const int64_t el = (int64_t)(grow - base_row) * cv.x_ld + cb + hd * D + pc * (16 / (int)sizeof(TX));
-            copy_frag(base, xs + 1024u * (uint32_t)m, (uint32_t)(el * (int64_t)sizeof(TX)));
+        for (int i = 0; i < NCOPY; ++i) {
+            const int slot = 64 * i + lane;
+            const int row = slot / rs;
+            const int pc = slot - row * rs;
+            rr[i] = row < XR && pc < pieces ? row : -1;
+            col[i] = c0 + pc * (16 / (int)sizeof(TX));
         }
     }
-}
+
+    // Issue the copies of the chunk starting at token tb into the wave's rows at
+    // LDS address xs.  Rows past the request's last token repeat it (their v is
+    // never used); rows 0..2 of the request's first chunk (first) are not
+    // copied: they come from the slot's history.
+    __device__ __forceinline__ void issue(uint32_t xs, const ChainConvIn &cv, int tb, int tok_last,
+                                          bool first) const {
+        const int base_row = first ? tb : tb - 3;
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(static_cast<const TX *>(cv.x) +
+                                                                  (int64_t)base_row * cv.x_ld);
+#pragma unroll
+        for (int i = 0; i < NCOPY; ++i) {
+            if (rr[i] >= (first ? 3 : 0)) {
+                const int grow = min(tb - 3 + rr[i], tok_last);
+                const uint32_t off = (uint32_t)(((int64_t)(grow - base_row) * cv.x_ld + col[i]) * (int64_t)sizeof(TX));
+                chunk::copy_frag(base, xs + 1024u * (uint32_t)i, off);
+            }
+        }
+    }
+};
 
 // The three history rows of one staged channel for the request's first chunk
 // (zeros without a history), written by the lane that owns the channel.
@@ -846,21 +861,21 @@ template <> __device__ __forceinline__ float lds_x<bf16>(const uint8_t *p) {
 // of its channel (xs_col: row 0 of the channel's column; row rr is token
 // tb - 3 + rr, so tap i of token t sits in row t + 3 - i).  The taps are
 // summed from the oldest input on, as the other channels' conv does.
-template <typename TX, int ROWB>
-__device__ __forceinline__ void conv_v(const uint8_t *xs_col, const float (&wt)[4], int lg, int Lc,
+template <typename TX>
+__device__ __forceinline__ void conv_v(const uint8_t *xs_col, int rowb, const float (&wt)[4], int lg, int Lc,
                                        float (&vc)[2][4]) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
         const int t0 = 16 * tau + 4 * lg;
         float xr[7];  // rows t0 .. t0 + 6: tokens t0 - 3 .. t0 + 3
 #pragma unroll
-        for (int j = 0; j < 7; ++j) xr[j] = lds_x<TX>(xs_col + (t0 + j) * ROWB);
+        for (int j = 0; j < 7; ++j) xr[j] = lds_x<TX>(xs_col + (t0 + j) * rowb);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float y = 0.f;
 #pragma unroll
             for (int i = 3; i >= 0; --i) y += wt[i] * xr[e + 3 - i];
-            vc[tau][e] = t0 + e < Lc ? silu_f(y) : 0.f;
+            vc[tau][e] = t0 + e < Lc ? silu_fast(y) : 0.f;
         }
     }
 }
@@ -903,16 +918,16 @@ __device__ __forceinline__ void issue_images(uint32_t stage, const uint8_t *kim,
 }
 
 // LDS of one stage of the per-head chain: the chunk's K image, its T image and
-// (fused) its staged x rows; two stages alternate.
+// (fused) the compute waves' staged x rows; two stages alternate.
 template <int NW, bool XCONV, typename TX>
 constexpr size_t chain_stage_bytes() {
-    return chunk::KIMG + chunk::TIMG + (XCONV ? (size_t)XRows<TX, 1, 16 * NW>::BYTES : 0);
+    return chunk::KIMG + chunk::TIMG + (XCONV ? (size_t)NW * XWave<TX, 1>::BYTES : 0);
 }
 
-// NCW extra waves only copy (images and x rows): a wave issues direct-to-LDS
-// copies at a limited rate, so a block of few compute waves spends more time
-// issuing a chunk's copies than computing it unless other waves share that
-// work.
+// NCW extra waves only copy the images: a wave issues direct-to-LDS copies at a
+// limited rate, so a block of few compute waves spends more time issuing a
+// chunk's copies than computing it unless other waves share that work.  (Each
+// compute wave copies the x rows of its own channels.)
 template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, int NCW>
 __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
@@ -923,7 +938,7 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     using namespace chunk;
     constexpr int IB = 16 * NW;  // state rows per block
     constexpr int NRB = D / IB;  // blocks per (request, head)
-    using XRW = XRows<TX, 1, IB>;
+    using XW = XWave<TX, 1>;
     constexpr uint32_t XOFF = (uint32_t)(KIMG + TIMG);  // staged x rows within a stage
     constexpr uint32_t STG = (uint32_t)chain_stage_bytes<NW, XCONV, TX>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -955,13 +970,11 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     const int cb = 2 * cv.nq + h * D + IB * rb;  // the block's first v channel (fused)
     if constexpr (NCW > 0) {
         if (w >= NW) {
-            // copy wave: chunk cc + 1's images and x rows go into the free stage
-            // while the compute waves work on chunk cc; one barrier per chunk, as
-            // theirs
+            // copy wave: chunk cc + 1's images go into the free stage while the
+            // compute waves work on chunk cc; one barrier per chunk, as theirs
             const int cw = w - NW;
 #pragma unroll
             for (int part = 0; part < NPART; ++part) issue_images<NCW>(lds0, kim0, tim0, cw, lane, part);
-            if constexpr (XCONV) issue_xrows<TX, 1, IB, NCW>(lds0 + XOFF, cv, cb, tok0, tok_last, true, cw, lane);
             for (int cc = 0; cc < nch; ++cc) {
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
@@ -970,9 +983,6 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
 #pragma unroll
                     for (int part = 0; part < NPART; ++part)
                         issue_images<NCW>(nstg, kim0 + (cc + 1) * kstep, tim0 + (cc + 1) * tstep, cw, lane, part);
-                    if constexpr (XCONV)
-                        issue_xrows<TX, 1, IB, NCW>(nstg + XOFF, cv, cb, tok0 + (cc + 1) * CH, tok_last, false,
-                                                    cw, lane);
                 }
             }
             return;
@@ -996,25 +1006,32 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
     const uint32_t kt_off = kt_lane_off(lr, lg);
-    const int xcol = (16 * w + lr) * (int)sizeof(TX);  // this lane's column of the staged rows
+    // this wave's staged x rows (fused) and this lane's column in them
+    const uint32_t xw_off = XOFF + (uint32_t)(w * XW::BYTES);
+    const int xcol = lr * (int)sizeof(TX);
 
     float wt[4] = {0.f, 0.f, 0.f, 0.f};
     ChainVLoads<1, TA> vr;
     auto load_v = [&](int cc) { vr.load(v, irows, h, Hv, tok0 + cc * CH, min(CH, L - cc * CH), lane); };
+    XCopyPlan<TX, 1> xp;
+    float vnext[2][4];  // (fused) v of the next chunk, formed at the end of the current one
+    (void)vnext;
 
     if constexpr (XCONV) {
         load_taps(cv, cb + 16 * w + lr, wt);
-        if (lg == 0) stage_history<TX>(smem + XOFF + xcol, XRW::ROWB, cv, cb + 16 * w + lr, slot, hi_init);
+        xp.init(cb + 16 * w, 1, lane);
+        if (lg == 0) stage_history<TX>(smem + xw_off + xcol, XW::ROWB, cv, cb + 16 * w + lr, slot, hi_init);
+        xp.issue(lds0 + xw_off, cv, tok0, tok_last, true);
     }
     if constexpr (NCW == 0) {
 #pragma unroll
         for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, kim0, tim0, w, lane, part);
-        if constexpr (XCONV) issue_xrows<TX, 1, IB, NW>(lds0 + XOFF, cv, cb, tok0, tok_last, true, w, lane);
     }
     if constexpr (!XCONV) load_v(0);
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (XCONV) conv_v<TX>(smem + xw_off + xcol, XW::ROWB, wt, lg, min(CH, L), vnext);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
@@ -1031,7 +1048,11 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
         __syncthreads();
         float vcur[2][4];
         if constexpr (XCONV) {
-            conv_v<TX, XRW::ROWB>(stg + XOFF + xcol, wt, lg, Lc, vcur);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vcur[tau][e] = vnext[tau][e];
+            if (more) xp.issue(nstg + xw_off, cv, tb + CH, tok_last, false);
         } else {
             float vcur1[1][2][4];
             vr.get(vcur1);
@@ -1040,10 +1061,7 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[tau][e] = vcur1[0][tau][e];
         }
-        if (prefetch) {
-            issue_images<NW>(nstg, nkim, ntim, w, lane, 0);
-            if constexpr (XCONV) issue_xrows<TX, 1, IB, NW>(nstg + XOFF, cv, cb, tb + CH, tok_last, false, w, lane);
-        }
+        if (prefetch) issue_images<NW>(nstg, nkim, ntim, w, lane, 0);
         const uint8_t *kst = stg + 16 * lane;          // this lane's piece of each K fragment
         const uint8_t *tst = stg + KIMG + 16 * lane;   // and of each T fragment
 
@@ -1075,6 +1093,14 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
             }
         }
         if (!XCONV && more) load_v(cc + 1);
+        // the K^T operands of the state update, read while the LDS is idle
+        bf16x8_t kth[8], ktlo[8];
+        const uint8_t *ktl = stg + kt_off;
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+            kth[jt] = kt_frag(ktl, 0, jt);
+            ktlo[jt] = kt_frag(ktl, 1, jt);
+        }
         // per-token gamma, e^{G_C - G_t}, beta for this lane's tokens
         const uint8_t *tvec = stg + KIMG;
         float4 gam[2], rev[2], bet[2];
@@ -1128,11 +1154,21 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
             mma3(OQ[tau], frag(tst + (FP + tau) * FRAG), frag(tst + (FP + 2 + tau) * FRAG), dbh, dbl);
-        const uint8_t *ktl = stg + kt_off;
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
             ST[jt] *= gC;
-            mma3(ST[jt], kt_frag(ktl, 0, jt), kt_frag(ktl, 1, jt), tbh, tbl);
+            mma3(ST[jt], kth[jt], ktlo[jt], tbh, tbl);
+        }
+        if constexpr (XCONV) {
+            // v of the next chunk, from this wave's own copies of its rows (landed
+            // once its memory counter drains), beside the state update's MFMAs
+            // (measured: here, ahead of the o stores, the single-sequence chain
+            // is ~3% faster than with it after them; the group chain the reverse)
+            if (more) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                conv_v<TX>(smem + (size_t)((cc + 1) & 1) * STG + xw_off + xcol, XW::ROWB, wt, lg,
+                           min(CH, L - (cc + 1) * CH), vnext);
+            }
         }
         {
             const __amdgpu_buffer_rsrc_t orr = wave_rsrc(o + ((int64_t)tb * Hv + h) * D,
@@ -1184,9 +1220,12 @@ constexpr int GRP_ROWS = 64;          // state rows per head per block
 constexpr int GRP_RPW = 2;            // 16-row tiles per wave, at most
 constexpr int GRP_NW = 8;             // waves per block
 
+// LDS of one stage of the group chain: the chunk's K image, its G T images and
+// (fused) the waves' staged x rows: waves 0-3 hold two row tiles, 4-7 one.
 template <int G, bool XCONV, typename TX>
 constexpr size_t group_stage_bytes() {
-    return chunk::KIMG + G * chunk::TIMG + (XCONV ? (size_t)XRows<TX, G, GRP_ROWS>::BYTES : 0);
+    return chunk::KIMG + G * chunk::TIMG +
+           (XCONV ? 4 * (size_t)(XWave<TX, 2>::BYTES + XWave<TX, 1>::BYTES) : 0);
 }
 
 template <int G, typename TA, typename TO, bool XCONV, typename TX, typename TS>
@@ -1201,7 +1240,6 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     constexpr int NW = GRP_NW;
     constexpr int NRB = D / GRP_ROWS;               // row blocks per head
     constexpr int NFRAG = KIMG_FRAGS + G * TIMG_FRAGS;
-    using XRW = XRows<TX, G, GRP_ROWS>;
     constexpr uint32_t XOFF = (uint32_t)(KIMG + G * TIMG);
     constexpr uint32_t GSTG = (uint32_t)group_stage_bytes<G, XCONV, TX>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1241,8 +1279,12 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     }
     const int slot = slots[r];
     TS *sbase = state + ((int64_t)slot * Hv + h) * D * D;
-    // fused: the group's v channels of this row block, head hd at cb + hd D
+    // fused: the group's v channels of this row block, head hd at cb + hd D; this
+    // wave's staged x rows (its nt tiles' channels) and their row stride
     const int cb = 2 * cv.nq + kh * G * D + GRP_ROWS * rb;
+    const uint32_t xw_off = XOFF + (uint32_t)(w < 4 ? w * XWave<TX, 2>::BYTES
+                                                    : 4 * XWave<TX, 2>::BYTES + (w - 4) * XWave<TX, 1>::BYTES);
+    const int xrowb = nt == 2 ? XWave<TX, 2>::ROWB : XWave<TX, 1>::ROWB;
 
     floatx4_t ST[GRP_RPW][8];
 #pragma unroll
@@ -1262,9 +1304,11 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     const uint8_t *tim0 = timg + ((size_t)c_first * Hv + kh * G) * TIMG;  // the group's G heads are adjacent
     const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
 
-    // this wave's copies of chunk cc's images (and, with part 0, x rows), in
-    // NPART slices so that they can be spread over the previous chunk's MFMA
-    // phases instead of stalling the wave on a full memory queue in one burst
+    XCopyPlan<TX, 2> xp;
+    if constexpr (XCONV) xp.init(cb + hh * D + 16 * tile0, nt, lane);
+    // this wave's copies of chunk cc's images, in NPART slices so that they can
+    // be spread over the previous chunk's MFMA phases instead of stalling the
+    // wave on a full memory queue in one burst
     constexpr int PER_WAVE = (NFRAG + NW - 1) / NW;
     auto issue = [&](uint32_t stage, int cc, int part) {
         const uint8_t *kim = kim0 + cc * kstep;
@@ -1277,23 +1321,35 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
                 copy_frag(src, stage + (uint32_t)f * FRAG, 16u * lane);
             }
         }
-        if constexpr (XCONV) {
-            if (part == 0) issue_xrows<TX, G, GRP_ROWS, NW>(stage + XOFF, cv, cb, tok0 + cc * CH, tok_last, cc == 0,
-                                                            w, lane);
-        }
     };
     float wt[GRP_RPW][4];
     ChainVLoads<GRP_RPW, TA> vr;
     auto load_v = [&](int cc) { vr.load(v, irow, h, Hv, tok0 + cc * CH, min(CH, L - cc * CH), lane); };
+    // (fused) v of the next chunk, formed at the end of the current one from this
+    // wave's own rows; a one-tile wave's second tile repeats its first
+    float vnext[GRP_RPW][2][4];
+    auto conv_next = [&](int cn) {
+        const uint8_t *xs = smem + (size_t)(cn & 1) * GSTG + xw_off;
+        const int Lc = min(CH, L - cn * CH);
+        conv_v<TX>(xs + lr * (int)sizeof(TX), xrowb, wt[0], lg, Lc, vnext[0]);
+        if (nt > 1) conv_v<TX>(xs + (16 + lr) * (int)sizeof(TX), xrowb, wt[1], lg, Lc, vnext[1]);
+        else {
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vnext[1][tau][e] = vnext[0][tau][e];
+        }
+    };
 
     if constexpr (XCONV) {
 #pragma unroll
         for (int rt = 0; rt < GRP_RPW; ++rt) {
             load_taps(cv, cb + hh * D + ci[rt], wt[rt]);
-            if (lg == 0)
-                stage_history<TX>(smem + XOFF + hh * XRW::HEADB + ci[rt] * (int)sizeof(TX), XRW::ROWB, cv,
-                                  cb + hh * D + ci[rt], slot, hi_init);
+            if (lg == 0 && rt < nt)
+                stage_history<TX>(smem + xw_off + (16 * rt + lr) * (int)sizeof(TX), xrowb, cv, cb + hh * D + ci[rt],
+                                  slot, hi_init);
         }
+        xp.issue(lds0 + xw_off, cv, tok0, tok_last, true);
     }
 #pragma unroll
     for (int part = 0; part < NPART; ++part) issue(lds0, 0, part);
@@ -1301,6 +1357,7 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (XCONV) conv_next(0);
     for (int cc = 0; cc < nch; ++cc) {
         const int tb = tok0 + cc * CH;
         const int Lc = min(CH, L - cc * CH);
@@ -1315,8 +1372,11 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
         if constexpr (XCONV) {
 #pragma unroll
             for (int rt = 0; rt < GRP_RPW; ++rt)
-                conv_v<TX, XRW::ROWB>(stg + XOFF + hh * XRW::HEADB + ci[rt] * (int)sizeof(TX), wt[rt], lg, Lc,
-                                      vcur[rt]);
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vcur[rt][tau][e] = vnext[rt][tau][e];
+            if (prefetch) xp.issue(nstg + xw_off, cv, tb + CH, tok_last, false);
         } else {
             vr.get(vcur);
         }
@@ -1462,6 +1522,14 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
                     for (int jt = 0; jt < 8; ++jt)
                         st4(sp + (int64_t)irow[rt] * D + 16 * jt + 4 * lg,
                             make_float4(ST[rt][jt][0], ST[rt][jt][1], ST[rt][jt][2], ST[rt][jt][3]));
+        }
+        if constexpr (XCONV) {
+            // v of the next chunk, from this wave's own copies of its rows: they
+            // have landed once no more than this chunk's o stores are in flight
+            if (prefetch) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * GRP_RPW));
+                conv_next(cc + 1);
+            }
         }
     }
 #pragma unroll
