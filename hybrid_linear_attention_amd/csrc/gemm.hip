@@ -122,21 +122,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // block issues at the same moment.  MFMAs run over one B fragment at a time
 // (4 tiles) so that the register of the fragment they finish is refilled next.
 // ---------------------------------------------------------------------------
-constexpr int G2M = 256, G2N = 256;
+constexpr int G2N = 256;
 constexpr int G2_THREADS = 512;
 constexpr int G2_BK = 64;                          // K per stage (two MFMA k-slices)
 constexpr int G2_CPR = G2_BK / 8;                  // 16-byte chunks per LDS row
-constexpr size_t G2_TILE = (size_t)G2M * G2_BK * 2;  // one operand, one stage
-constexpr size_t G2_STAGE = 2 * G2_TILE;
-constexpr size_t G2_SMEM = 2 * G2_STAGE;           // two stages: 128 KiB
-constexpr int G2_LOADS = G2M * G2_CPR * 2 / G2_THREADS;  // direct-to-LDS loads per thread per stage
 constexpr int G2_GROUP_M = 2;                      // tile rows per group of the tile order
+// tile rows TM (256, or 192 where it quantises the tiles into rounds of the
+// chip's CUs better): one operand stage of TM or 256 rows x 64 bf16, two stages
+template <int TM> struct G2 {
+    static constexpr int MI = TM / 64;                      // 16-row MFMA tiles per wave (4 waves in M)
+    static constexpr size_t TILE_A = (size_t)TM * G2_BK * 2;
+    static constexpr size_t TILE_B = (size_t)G2N * G2_BK * 2;
+    static constexpr size_t STAGE = TILE_A + TILE_B;
+    static constexpr size_t SMEM = 2 * STAGE;               // 128 or 112 KiB
+    static constexpr int LOADS = (TM + G2N) * G2_CPR / G2_THREADS;  // direct-to-LDS loads per thread per stage
+};
 
-// one operand tile of 256 rows x 64 bf16: rows of 128 bytes, 16-byte chunk j
+// one operand tile of ROWS rows x 64 bf16: rows of 128 bytes, 16-byte chunk j
 // of row r stored at chunk j ^ (r & 7)
+template <int ROWS>
 __device__ __forceinline__ void g2_copy(const uint16_t *__restrict__ X, int64_t ld, int rows_valid,
                                         int row0, int k0, uint8_t *tile, int tid) {
-    constexpr int PER_THREAD = G2M * G2_CPR / G2_THREADS;
+    constexpr int PER_THREAD = ROWS * G2_CPR / G2_THREADS;
     const int wv = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int m = 0; m < PER_THREAD; ++m) {
@@ -170,29 +177,31 @@ __device__ __forceinline__ void g2_tile(int b, int nbm, int nbn, int &tm, int &t
     tn = local / gm;
 }
 
-template <typename TC, bool RES>
+template <int TM, typename TC, bool RES>
 __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
     const uint16_t *__restrict__ A, int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
     TC *__restrict__ C, int64_t ldc, const uint16_t *__restrict__ R, int64_t ldr, int M, int N,
     int K) {
+    using P = G2<TM>;
+    constexpr int MI = P::MI;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves: rows 64 wm, columns 128 wn
+    const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves: rows 16 MI wm, columns 128 wn
     const int lr = lane & 15, lg = lane >> 4;
-    const int nbn = (N + G2N - 1) / G2N, nbm = (M + G2M - 1) / G2M;
+    const int nbn = (N + G2N - 1) / G2N, nbm = (M + TM - 1) / TM;
     int tm, tn;
     g2_tile(blockIdx.x, nbm, nbn, tm, tn);
-    const int m0 = tm * G2M, n0 = tn * G2N;
+    const int m0 = tm * TM, n0 = tn * G2N;
 
-    floatx4_t acc[4][8];
+    floatx4_t acc[MI][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     // fragment: row lr of a 16-row tile, logical chunk 4 ks + lg (8 bf16)
     auto frag_a = [&](const uint8_t *At, int ks, int i) {
-        const int r = wm * 64 + i * 16 + lr;
+        const int r = wm * 16 * MI + i * 16 + lr;
         const int pc = (4 * ks + lg) ^ (r & (G2_CPR - 1));
         return *reinterpret_cast<const bf16x8_t *>(At + (size_t)r * (2 * G2_BK) + 16 * pc);
     };
@@ -203,42 +212,42 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
     };
 
     const int nk = K / G2_BK;
-    g2_copy(A, lda, M, m0, 0, smem, tid);
-    g2_copy(B, ldb, N, n0, 0, smem + G2_TILE, tid);
+    g2_copy<TM>(A, lda, M, m0, 0, smem, tid);
+    g2_copy<G2N>(B, ldb, N, n0, 0, smem + P::TILE_A, tid);
     if (nk > 1) {
-        g2_copy(A, lda, M, m0, G2_BK, smem + G2_STAGE, tid);
-        g2_copy(B, ldb, N, n0, G2_BK, smem + G2_STAGE + G2_TILE, tid);
+        g2_copy<TM>(A, lda, M, m0, G2_BK, smem + P::STAGE, tid);
+        g2_copy<G2N>(B, ldb, N, n0, G2_BK, smem + P::STAGE + P::TILE_A, tid);
         // stage 0 landed (loads complete in order; vmcnt <= one stage's loads,
         // expcnt and lgkmcnt not waited on)
-        static_assert(G2_LOADS < 16, "vmcnt field");
-        __builtin_amdgcn_s_waitcnt(0x0F70 | G2_LOADS);
+        static_assert(P::LOADS < 16, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | P::LOADS);
     } else {
         __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
-    bf16x8_t a0[4], b0[8], a1[4], b1[8];
+    bf16x8_t a0[MI], b0[8], a1[MI], b1[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a0[i] = frag_a(smem, 0, i);
+    for (int i = 0; i < MI; ++i) a0[i] = frag_a(smem, 0, i);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b0[j] = frag_b(smem + G2_TILE, 0, j);
+    for (int j = 0; j < 8; ++j) b0[j] = frag_b(smem + P::TILE_A, 0, j);
 
     for (int kt = 0; kt < nk; ++kt) {
-        uint8_t *cur = smem + (size_t)(kt & 1) * G2_STAGE;
+        uint8_t *cur = smem + (size_t)(kt & 1) * P::STAGE;
         // phase A: k-slice 0 from registers, slice 1 read meanwhile
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a1[i] = frag_a(cur, 1, i);
+        for (int i = 0; i < MI; ++i) a1[i] = frag_a(cur, 1, i);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-            b1[j] = frag_b(cur + G2_TILE, 1, j);
+            b1[j] = frag_b(cur + P::TILE_A, 1, j);
         }
         // keep the reads between the MFMAs (mask 0x100: LDS reads, 0x008: MFMA)
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MI, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         // the next stage has landed and every wave is done reading this one
@@ -248,40 +257,42 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
         // (on the last step: stale, in-bounds LDS, never used) and this buffer
         // refilled with the stage after next (near the end: the last stage again,
         // in bounds, never read)
-        const uint8_t *nx = smem + (size_t)((kt + 1) & 1) * G2_STAGE;
+        const uint8_t *nx = smem + (size_t)((kt + 1) & 1) * P::STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a0[i] = frag_a(nx, 0, i);
+        for (int i = 0; i < MI; ++i) a0[i] = frag_a(nx, 0, i);
         const int kc = min(kt + 2, nk - 1) * G2_BK;
-        g2_copy(A, lda, M, m0, kc, cur, tid);
-        g2_copy(B, ldb, N, n0, kc, cur + G2_TILE, tid);
+        g2_copy<TM>(A, lda, M, m0, kc, cur, tid);
+        g2_copy<G2N>(B, ldb, N, n0, kc, cur + P::TILE_A, tid);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MI; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-            b0[j] = frag_b(nx + G2_TILE, 0, j);
+            b0[j] = frag_b(nx + P::TILE_A, 0, j);
         }
-        // mask 0x020: the direct-to-LDS loads, spread over the first half
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // mask 0x020: the direct-to-LDS loads, two at a time over the first B
+        // fragments
+        __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MI, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (j < 4) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            if (j < P::LOADS / 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            else if (j == P::LOADS / 2 && (P::LOADS & 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the last copies land before the block's LDS is released
 
     // accumulator layout: lane holds rows 4 lg + r, column lr of each tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int col = n0 + wn * 128 + j * 16 + lr;
             if (col >= N) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 64 + i * 16 + 4 * lg + r;
+                const int row = m0 + wm * 16 * MI + i * 16 + 4 * lg + r;
                 if (row >= M) continue;
                 float val = acc[i][j][r];
                 if (RES) val += __uint_as_float(uint32_t(R[(int64_t)row * ldr + col]) << 16);
@@ -290,16 +301,45 @@ __global__ __launch_bounds__(G2_THREADS) void gemm_bf16_v2_kernel(
         }
 }
 
-template <typename TC, bool RES>
+template <int TM, typename TC, bool RES>
 static hipError_t launch_gemm_v2(const GemmArgs &a, hipStream_t s) {
     static std::atomic<uint64_t> set{0};
-    hipError_t e = set_smem_once(&gemm_bf16_v2_kernel<TC, RES>, G2_SMEM, set);
+    hipError_t e = set_smem_once(&gemm_bf16_v2_kernel<TM, TC, RES>, G2<TM>::SMEM, set);
     if (e != hipSuccess) return e;
-    const int nb = ((a.M + G2M - 1) / G2M) * ((a.N + G2N - 1) / G2N);
-    hipLaunchKernelGGL((gemm_bf16_v2_kernel<TC, RES>), dim3(nb), dim3(G2_THREADS), G2_SMEM, s,
+    const int nb = ((a.M + TM - 1) / TM) * ((a.N + G2N - 1) / G2N);
+    hipLaunchKernelGGL((gemm_bf16_v2_kernel<TM, TC, RES>), dim3(nb), dim3(G2_THREADS), G2<TM>::SMEM, s,
                        (const uint16_t *)a.A, a.lda, (const uint16_t *)a.B, a.ldb, (TC *)a.C, a.ldc,
                        (const uint16_t *)a.R, a.ldr, a.M, a.N, a.K);
     return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Tile rows for a shape: one tile per CU at a time, so the time goes as the
+// rounds of tiles times the rows of a tile; 192-row tiles are taken only where
+// that product is at least 8% below that of 256-row ones (they reuse each
+// fragment read over fewer MFMAs).
+static int g2_rows(const GemmArgs &a) {
+    const int64_t cus = device_cus();
+    const int64_t nbn = (a.N + G2N - 1) / G2N;
+    auto cost = [&](int64_t tm) { return (((a.M + tm - 1) / tm) * nbn + cus - 1) / cus * tm; };
+    return cost(192) * 100 <= cost(256) * 92 ? 192 : 256;
+}
+
+template <typename TC, bool RES>
+static hipError_t launch_gemm_v2_any(const GemmArgs &a, hipStream_t s) {
+    return g2_rows(a) == 192 ? launch_gemm_v2<192, TC, RES>(a, s) : launch_gemm_v2<256, TC, RES>(a, s);
 }
 
 static bool g2_ok(const GemmArgs &a) {
@@ -319,8 +359,8 @@ static hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s) {
     if (g2_ok(a)) {
-        if (a.c_bf16) return a.R ? launch_gemm_v2<bf16, true>(a, s) : launch_gemm_v2<bf16, false>(a, s);
-        return a.R ? launch_gemm_v2<float, true>(a, s) : launch_gemm_v2<float, false>(a, s);
+        if (a.c_bf16) return a.R ? launch_gemm_v2_any<bf16, true>(a, s) : launch_gemm_v2_any<bf16, false>(a, s);
+        return a.R ? launch_gemm_v2_any<float, true>(a, s) : launch_gemm_v2_any<float, false>(a, s);
     }
     if (a.c_bf16)
         return a.R ? launch_gemm_t<bf16, true>(a, s) : launch_gemm_t<bf16, false>(a, s);
