@@ -113,6 +113,32 @@ def step_counters(name):
     return vals
 
 
+def gemm_counters():
+    """MFMA-busy share and calibrated HBM bytes of the layer's two GEMMs from
+    profiles/layer_gemm_counters.txt, or None when it is missing or gemm.hip has
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "layer_gemm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    out, cur = {}, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("gemm:"):
+                cur = "in_proj" if "in-projection" in line else "out_proj"
+            elif line.startswith("  mfma_busy") and cur:
+                out[cur + "_mfma_busy"] = float(line.split()[1])
+            elif line.startswith("  fetch_bytes") and cur:
+                t = line.split()
+                out[cur + "_hbm_bytes"] = int(float(t[1]) + float(t[3]))
+            elif line.startswith("source_sha256_16 "):
+                src, digest = line[len("source_sha256_16 "):].split(":")
+                if source_digest(os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc",
+                                              src.strip())) != digest.strip():
+                    return None
+    out["counters"] = "profiles/layer_gemm_counters.txt"
+    return out
+
+
 def fused_decode_bytes(d, R, act_bytes=2, y_bytes=2, state_bytes=4):
     """Algorithmic HBM bytes of one gdn_decode_fused launch: the state read and
     written once; the token's conv inputs, z and gates read once; its conv
@@ -439,6 +465,7 @@ def bench_layer(steps, dev, stream, torch, np):
         "stage_ms": {n: round(v, 4) for n, v in med.items()},
         "in_proj_tflops": round(f_in / (med["in_proj"] * 1e-3) / 1e12, 1),
         "out_proj_tflops": round(f_out / (med["out_proj"] * 1e-3) / 1e12, 1),
+        "gemm_counters": gemm_counters(),
     }
     del layer, w, X, pool, state
     return out
