@@ -34,16 +34,22 @@
 //          hi/lo planes, K K^T and Q K^T on MFMA, then one wave per value head:
 //          the gates' cumulative decay, T = (I + A)^-1 and P.  It writes every
 //          MFMA A operand the chain needs, already split and in the exact
-//          per-lane fragment order, as "images": a 48 KiB K image per (chunk,
-//          key head) holding K, Q and K^T, and a 9 KiB T image per (chunk, value
+//          per-lane fragment order, as "images": a 32 KiB K image per (chunk,
+//          key head) holding K and Q (the chain reads K^T out of the K planes
+//          with the transposed LDS read), and a 9 KiB T image per (chunk, value
 //          head) holding T, P and the per-token gamma, e^{G_C-G_t} and beta.
-//   chain  one block per (request, value head, block of state rows), sequential
-//          over the request's chunks: only the state-dependent products.  Each
-//          chunk's images are copied global -> LDS with direct-to-LDS loads
-//          (global_load_lds_dwordx4) into a two-stage ring while the previous
-//          chunk computes; every operand fragment is then one conflict-free
-//          16-byte LDS read.  State rows evolve independently given
-//          (k, beta, alpha), so the row blocks of a head never communicate.
+//   chain  sequential over each request's chunks: only the state-dependent
+//          products.  Each chunk's images are copied global -> LDS with
+//          direct-to-LDS loads (global_load_lds_dwordx4) into a ring of stages
+//          while earlier chunks compute; every operand fragment is then one
+//          conflict-free 16-byte LDS read.  State rows evolve independently
+//          given (k, beta, alpha), so the row blocks of a head never
+//          communicate.  Three block layouts: per (request, key head, 64 rows)
+//          over the key head's 3 value heads (large batches), per (request,
+//          value head, 128 rows) (large batches of other head ratios), and per
+//          (request, value head, 32 rows) with the recurrence and the output
+//          on separate waves (few requests, where one block's chunk latency is
+//          the kernel's time).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -924,12 +930,10 @@ constexpr size_t chain_stage_bytes() {
     return chunk::KIMG + chunk::TIMG + (XCONV ? (size_t)NW * XWave<TX, 1>::BYTES : 0);
 }
 
-// NCW extra waves only copy the images: a wave issues direct-to-LDS copies at a
-// limited rate, so a block of few compute waves spends more time issuing a
-// chunk's copies than computing it unless other waves share that work.  (Each
-// compute wave copies the x rows of its own channels.)
-template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, int NCW>
-__global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
+// Every wave computes a 16-row tile and copies its share of the next chunk's
+// images (and the x rows of its own channels) while it computes the current.
+template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS>
+__global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
@@ -968,26 +972,6 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
     const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
     const int tok_last = tok0 + L - 1;
     const int cb = 2 * cv.nq + h * D + IB * rb;  // the block's first v channel (fused)
-    if constexpr (NCW > 0) {
-        if (w >= NW) {
-            // copy wave: chunk cc + 1's images go into the free stage while the
-            // compute waves work on chunk cc; one barrier per chunk, as theirs
-            const int cw = w - NW;
-#pragma unroll
-            for (int part = 0; part < NPART; ++part) issue_images<NCW>(lds0, kim0, tim0, cw, lane, part);
-            for (int cc = 0; cc < nch; ++cc) {
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                if (cc + 1 < nch) {
-                    const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * STG;
-#pragma unroll
-                    for (int part = 0; part < NPART; ++part)
-                        issue_images<NCW>(nstg, kim0 + (cc + 1) * kstep, tim0 + (cc + 1) * tstep, cw, lane, part);
-                }
-            }
-            return;
-        }
-    }
     const int irow = IB * rb + 16 * w + lr;  // this lane's state row (value channel)
     const int irows[1] = {irow};
     const int slot = slots[r];
@@ -1023,10 +1007,8 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
         if (lg == 0) stage_history<TX>(smem + xw_off + xcol, XW::ROWB, cv, cb + 16 * w + lr, slot, hi_init);
         xp.issue(lds0 + xw_off, cv, tok0, tok_last, true);
     }
-    if constexpr (NCW == 0) {
 #pragma unroll
-        for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, kim0, tim0, w, lane, part);
-    }
+    for (int part = 0; part < NPART; ++part) issue_images<NW>(lds0, kim0, tim0, w, lane, part);
     if constexpr (!XCONV) load_v(0);
     // everything above (state rows, chunk 0's copies and v) lands before the
     // loop, so that no wait for the state rows' loads is left inside it
@@ -1037,8 +1019,8 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
         const int Lc = min(CH, L - cc * CH);
         const uint8_t *stg = smem + (size_t)(cc & 1) * STG;
         const uint32_t nstg = lds0 + (uint32_t)((cc + 1) & 1) * STG;
-        const bool more = cc + 1 < nch;          // chunk cc + 1's v loads
-        const bool prefetch = NCW == 0 && more;  // and its copies, by this wave
+        const bool more = cc + 1 < nch;  // chunk cc + 1's v loads
+        const bool prefetch = more;      // and its copies
         const uint8_t *nkim = kim0 + (cc + 1) * kstep, *ntim = tim0 + (cc + 1) * tstep;
         // this wave's copies and loads of chunk cc have landed (issued before the
         // previous chunk's 8 o stores, which may stay in flight); after the
@@ -1066,31 +1048,48 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
         const uint8_t *tst = stg + KIMG + 16 * lane;   // and of each T fragment
 
         // ---------------- X = K S0^T and OQ = Q S0^T  (tokens x this wave's rows)
+        // The K / Q fragments of k-step ks + 1 are read while the MFMAs of
+        // k-step ks run (scheduling barriers keep the compiler from sinking
+        // the reads to their uses, where each MFMA group would wait out a full
+        // LDS latency), and the state's bf16 split, plain VALU work on
+        // registers, fills the wait for the first k-step's reads.
         floatx4_t X[2], OQ[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             X[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             OQ[tau] = X[tau];
         }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (prefetch && ks > 0) issue_images<NW>(nstg, nkim, ntim, w, lane, ks);
-            bf16x8_t sbh, sbl;
-            {
-                float sv[8];
-#pragma unroll
-                for (int p = 0; p < 8; ++p) sv[p] = ST[2 * ks + (p >> 2)][p & 3];
-                split_vals(sv, sbh, sbl);
-            }
+        bf16x8_t kq[2][8];  // [k-step parity][4 tau + (K hi, K lo, Q hi, Q lo)]
+        auto read_kq = [&](int ks, bf16x8_t (&f)[8]) {
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
-                const bf16x8_t kh_ = frag(kst + (FK + (0 + tau) * 4 + ks) * FRAG);
-                const bf16x8_t kl_ = frag(kst + (FK + (2 + tau) * 4 + ks) * FRAG);
-                const bf16x8_t qh_ = frag(kst + (FQ + (0 + tau) * 4 + ks) * FRAG);
-                const bf16x8_t ql_ = frag(kst + (FQ + (2 + tau) * 4 + ks) * FRAG);
-                mma3(X[tau], kh_, kl_, sbh, sbl);
-                mma3(OQ[tau], qh_, ql_, sbh, sbl);
+                f[4 * tau + 0] = frag(kst + (FK + (0 + tau) * 4 + ks) * FRAG);
+                f[4 * tau + 1] = frag(kst + (FK + (2 + tau) * 4 + ks) * FRAG);
+                f[4 * tau + 2] = frag(kst + (FQ + (0 + tau) * 4 + ks) * FRAG);
+                f[4 * tau + 3] = frag(kst + (FQ + (2 + tau) * 4 + ks) * FRAG);
             }
+        };
+        read_kq(0, kq[0]);
+        bf16x8_t sbh[4], sbl[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float sv[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) sv[p] = ST[2 * ks + (p >> 2)][p & 3];
+            split_vals(sv, sbh[ks], sbl[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) read_kq(ks + 1, kq[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (prefetch && ks > 0) issue_images<NW>(nstg, nkim, ntim, w, lane, ks);
+            const bf16x8_t(&f)[8] = kq[ks & 1];
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                mma3(X[tau], f[4 * tau + 0], f[4 * tau + 1], sbh[ks], sbl[ks]);
+                mma3(OQ[tau], f[4 * tau + 2], f[4 * tau + 3], sbh[ks], sbl[ks]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (!XCONV && more) load_v(cc + 1);
         // the K^T operands of the state update, read while the LDS is idle
@@ -1203,6 +1202,368 @@ __global__ __launch_bounds__(64 * (NW + NCW)) void prefill_chain_kernel(
         if (h % group == 0 && rb == 0)
             for (int j = threadIdx.x; j < 2 * D; j += 64 * NW)
                 chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chain, paired variant for few (request, head) units, e.g. one long
+// sequence, where each block's critical path per chunk sets the kernel's
+// time.  Each 16-row tile of the per-head block gets two waves.  The state
+// wave carries the recurrence: X = K S^T, E, Delta = T E and the state
+// update.  The output wave keeps its own copy of the state, advanced by the
+// same MFMAs on the same operands (so the two copies stay bit-identical), and
+// forms the output one chunk behind: gamma Q S^T + P Delta, from the Delta
+// splits the state wave leaves in LDS, and the o stores.  (Fused) two of the
+// copy waves convolve the x rows of the tiles' v channels a chunk ahead and
+// leave v in LDS.  The recurrence then waits on neither the output products,
+// the stores nor the conv.  Waves 0-1: state waves of tiles 0-1; 2-3: their
+// output waves; 4-7 copy the images, and 6-7 (on the output waves' SIMDs,
+// which have more room) convolve for tiles 0-1.  Three image stages rotate:
+// while the state waves work on chunk c, the output waves read chunk c - 1's
+// images and chunk c + 1's land.
+// ---------------------------------------------------------------------------
+constexpr int PAIR_TILES = 2;  // 16-row tiles per block
+constexpr int PAIR_NCW = 4;    // copy waves
+constexpr int PAIR_WAVES = 2 * PAIR_TILES + PAIR_NCW;
+
+// LDS of the paired chain: three image stages, the Delta splits of two chunks
+// (4 fragments per tile) and (fused) the conv waves' x rows and the v they
+// form (2 fragments of fp32 per tile), both for two chunks.
+constexpr uint32_t PAIR_VTILE = 2 * chunk::FRAG;
+template <bool XCONV, typename TX>
+constexpr size_t pair_smem_bytes() {
+    return 3 * (chunk::KIMG + chunk::TIMG) + 2 * (size_t)PAIR_TILES * 4 * chunk::FRAG +
+           (XCONV ? 2 * (size_t)PAIR_TILES * (XWave<TX, 1>::BYTES + PAIR_VTILE) : 0);
+}
+
+template <typename TA, typename TO, bool XCONV, typename TX, typename TS>
+__global__ __launch_bounds__(64 * PAIR_WAVES) void prefill_chain_pair_kernel(
+    const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
+    const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
+    const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
+    int32_t Hv, TO *__restrict__ o, ChainConvIn cv, ChainSnap snap) {
+    using namespace chunk;
+    constexpr int IB = 16 * PAIR_TILES;  // state rows per block
+    constexpr int NRB = D / IB;          // blocks per (request, head)
+    using XW = XWave<TX, 1>;
+    constexpr uint32_t STG = (uint32_t)(KIMG + TIMG);  // one image stage
+    constexpr uint32_t DTILE = 4 * FRAG;               // dbh, dbl, tbh, tbl of one tile
+    constexpr uint32_t DBASE = 3 * STG;                // Delta [chunk parity][tile]
+    constexpr uint32_t XBASE = DBASE + 2 * PAIR_TILES * DTILE;  // (fused) x rows [parity][tile]
+    constexpr uint32_t VBASE = XBASE + 2 * PAIR_TILES * XW::BYTES;  // (fused) v [parity][tile]
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds0 = lds_addr(smem);
+    const int lr = lane & 15, lg = lane >> 4;
+
+    const int group = Hv / Hk;
+    const int per_group = group * NRB;
+    const int xcd = blockIdx.x & 7;
+    const int qd = blockIdx.x >> 3;
+    const int gi = 8 * (qd / per_group) + xcd;  // (request rank, key head) group
+    const int jj = qd % per_group;
+    if (gi >= nreq * Hk) return;
+    const int r = order[gi / Hk];
+    const int kh = gi % Hk;
+    const int h = kh * group + jj / NRB;
+    const int rb = jj % NRB;
+    const int tok0 = qsl[r];
+    const int L = qsl[r + 1] - tok0;
+    if (L <= 0) return;  // empty request: slot untouched
+    const int nch = (L + CH - 1) / CH;
+    const int c_first = chunk_off[r];
+    const bool hi_init = has_init == nullptr || has_init[r] != 0;
+    const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
+    const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
+    const size_t kstep = (size_t)Hk * KIMG, tstep = (size_t)Hv * TIMG;
+    const int tok_last = tok0 + L - 1;
+    const int cb = 2 * cv.nq + h * D + IB * rb;  // the block's first v channel (fused)
+    const int slot = slots[r];
+
+    // Every wave passes nch + 1 barriers: barrier i opens iteration i, in which
+    // the state waves take chunk i (i < nch) and the output waves chunk i - 1
+    // (i > 0).
+    if (w >= 2 * PAIR_TILES) {
+        // copy wave: chunk i + 1's images go into stage (i + 1) % 3, last read by
+        // the output waves in iteration i - 1.  A conv wave also forms chunk
+        // i + 1's v in iteration i, from x rows it copied in iteration i - 1,
+        // into the v buffer the state wave read in iteration i - 1.
+        const int cw = w - 2 * PAIR_TILES;
+        const int ctile = cw - (PAIR_NCW - PAIR_TILES);
+        const bool conv_wave = XCONV && ctile >= 0;
+        const int xcol = lr * (int)sizeof(TX);
+        const uint32_t xw_off = XBASE + (uint32_t)(ctile * XW::BYTES);  // + parity * XPAR
+        constexpr uint32_t XPAR = (uint32_t)(PAIR_TILES * XW::BYTES);
+        const uint32_t vw_off = VBASE + (uint32_t)ctile * PAIR_VTILE + 16u * (uint32_t)lane;  // + parity, + tau
+        constexpr uint32_t VPAR = PAIR_TILES * PAIR_VTILE;
+        float wt[4] = {0.f, 0.f, 0.f, 0.f};
+        XCopyPlan<TX, 1> xp;
+        auto conv_to_lds = [&](int cn) {
+            float vc[2][4];
+            conv_v<TX>(smem + xw_off + (uint32_t)(cn & 1) * XPAR + xcol, XW::ROWB, wt, lg, min(CH, L - cn * CH), vc);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+                *reinterpret_cast<float4 *>(smem + vw_off + (uint32_t)(cn & 1) * VPAR + (uint32_t)tau * FRAG) =
+                    make_float4(vc[tau][0], vc[tau][1], vc[tau][2], vc[tau][3]);
+        };
+        if (conv_wave) {
+            load_taps(cv, cb + 16 * ctile + lr, wt);
+            xp.init(cb + 16 * ctile, 1, lane);
+            if (lg == 0) stage_history<TX>(smem + xw_off + xcol, XW::ROWB, cv, cb + 16 * ctile + lr, slot, hi_init);
+            xp.issue(lds0 + xw_off, cv, tok0, tok_last, true);
+            if (nch > 1) xp.issue(lds0 + xw_off + XPAR, cv, tok0 + CH, tok_last, false);
+        }
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) issue_images<PAIR_NCW>(lds0, kim0, tim0, cw, lane, part);
+        if (conv_wave) {
+            __builtin_amdgcn_s_waitcnt(0);
+            conv_to_lds(0);
+        }
+        for (int it = 0; it <= nch; ++it) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (it + 1 < nch) {
+                const uint32_t nstg = lds0 + (uint32_t)((it + 1) % 3) * STG;
+#pragma unroll
+                for (int part = 0; part < NPART; ++part)
+                    issue_images<PAIR_NCW>(nstg, kim0 + (it + 1) * kstep, tim0 + (it + 1) * tstep, cw, lane, part);
+                if (conv_wave) {
+                    // chunk it + 2's rows go into the buffer chunk it's conv read
+                    // in iteration it - 1
+                    if (it + 2 < nch)
+                        xp.issue(lds0 + xw_off + (uint32_t)(it & 1) * XPAR, cv, tok0 + (it + 2) * CH, tok_last, false);
+                    conv_to_lds(it + 1);
+                }
+            }
+        }
+        // new history of this conv wave's v channels (their old history was
+        // read in its prologue)
+        if (conv_wave && lg == 0) chain_write_history<TX>(cv, cb + 16 * ctile + lr, slot, hi_init, tok0, L);
+        return;
+    }
+    const bool state_wave = w < PAIR_TILES;
+    const int tile = state_wave ? w : w - PAIR_TILES;
+    const int irow = IB * rb + 16 * tile + lr;  // this lane's state row (value channel)
+    TS *sbase = state + ((int64_t)slot * Hv + h) * D * D;
+
+    // state rows of this lane, transposed accumulator layout:
+    // ST[jt][e] = S[irow][16 jt + 4 lg + e]
+    floatx4_t ST[8];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+        ST[jt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        if (hi_init) {
+            const float4 s4 = ld4(sbase + (int64_t)irow * D + 16 * jt + 4 * lg);
+            ST[jt] = floatx4_t{s4.x, s4.y, s4.z, s4.w};
+        }
+    }
+    const uint32_t kt_off = kt_lane_off(lr, lg);
+    const uint32_t dt_off = DBASE + (uint32_t)tile * DTILE + 16u * (uint32_t)lane;  // + parity, + plane
+    // (fused) this lane's v of its 8 tokens: [parity][tile][tau][lane] float4
+    const uint32_t vt_off = VBASE + (uint32_t)tile * PAIR_VTILE + 16u * (uint32_t)lane;  // + parity, + tau
+    constexpr uint32_t VPAR = PAIR_TILES * PAIR_VTILE;
+    (void)vt_off;
+
+    // the state update of one chunk on this wave's copy: S = gC S + (K^T)(tDelta)
+    auto state_update = [&](const uint8_t *stg, float gC, const bf16x8_t &tbh, const bf16x8_t &tbl) {
+        bf16x8_t kth[8], ktlo[8];
+        const uint8_t *ktl = stg + kt_off;
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+            kth[jt] = kt_frag(ktl, 0, jt);
+            ktlo[jt] = kt_frag(ktl, 1, jt);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+            ST[jt] *= gC;
+            mma3(ST[jt], kth[jt], ktlo[jt], tbh, tbl);
+        }
+    };
+    // A S^T for the 32 x 128 operand A of K-image plane pair f0 (hi: f0, lo:
+    // f0 + 8), all four k-steps; the fragments of k-step ks + 1 are read while
+    // k-step ks's MFMAs run (scheduling barriers keep the compiler from sinking
+    // the reads to their uses), the state's bf16 split fills the first wait
+    auto contract_state = [&](const uint8_t *kst, int f0, floatx4_t (&acc)[2]) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) acc[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        bf16x8_t fr[2][4];  // [k-step parity][2 tau + plane]
+        auto read = [&](int ks, bf16x8_t (&f)[4]) {
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                f[2 * tau + 0] = frag(kst + (f0 + (0 + tau) * 4 + ks) * FRAG);
+                f[2 * tau + 1] = frag(kst + (f0 + (2 + tau) * 4 + ks) * FRAG);
+            }
+        };
+        read(0, fr[0]);
+        bf16x8_t sbh[4], sbl[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float sv[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) sv[p] = ST[2 * ks + (p >> 2)][p & 3];
+            split_vals(sv, sbh[ks], sbl[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) read(ks + 1, fr[(ks + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+                mma3(acc[tau], fr[ks & 1][2 * tau + 0], fr[ks & 1][2 * tau + 1], sbh[ks], sbl[ks]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (state_wave) {
+        ChainVLoads<1, TA> vr;
+        const int irows[1] = {irow};
+        auto load_v = [&](int cc) { vr.load(v, irows, h, Hv, tok0 + cc * CH, min(CH, L - cc * CH), lane); };
+        if constexpr (!XCONV) load_v(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        for (int cc = 0; cc <= nch; ++cc) {
+            __syncthreads();
+            if (cc == nch) break;
+            const uint8_t *stg = smem + (size_t)(cc % 3) * STG;
+            const bool more = cc + 1 < nch;
+            float vcur[2][4];
+            if constexpr (XCONV) {
+                // v of chunk cc, formed by a conv wave in iteration cc - 1
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau) {
+                    const float4 f = *reinterpret_cast<const float4 *>(
+                        smem + vt_off + (uint32_t)(cc & 1) * VPAR + (uint32_t)tau * FRAG);
+                    vcur[tau][0] = f.x;
+                    vcur[tau][1] = f.y;
+                    vcur[tau][2] = f.z;
+                    vcur[tau][3] = f.w;
+                }
+            } else {
+                float vcur1[1][2][4];
+                vr.get(vcur1);
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vcur[tau][e] = vcur1[0][tau][e];
+            }
+            // X = K S^T (tokens x this tile's rows)
+            floatx4_t X[2];
+            contract_state(stg + 16 * lane, FK, X);
+            if (!XCONV && more) load_v(cc + 1);
+            const uint8_t *tvec = stg + KIMG;
+            const uint8_t *tst = stg + KIMG + 16 * lane;
+            float4 gam[2], rev[2], bet[2];
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const int t0 = 16 * tau + 4 * lg;
+                gam[tau] = *reinterpret_cast<const float4 *>(tvec + T_GAM + 4 * t0);
+                rev[tau] = *reinterpret_cast<const float4 *>(tvec + T_REV + 4 * t0);
+                bet[tau] = *reinterpret_cast<const float4 *>(tvec + T_BETA + 4 * t0);
+            }
+            const float gC = *reinterpret_cast<const float *>(tvec + T_GAM + 4 * (CH - 1));
+            // E = beta (V - gamma X), then Delta = T E
+            bf16x8_t ebh, ebl;
+            {
+                float ev[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int tau = p >> 2, e = p & 3;
+                    const float g = e == 0 ? gam[tau].x : e == 1 ? gam[tau].y : e == 2 ? gam[tau].z : gam[tau].w;
+                    const float b = e == 0 ? bet[tau].x : e == 1 ? bet[tau].y : e == 2 ? bet[tau].z : bet[tau].w;
+                    ev[p] = b * (vcur[tau][e] - g * X[tau][e]);
+                }
+                split_vals(ev, ebh, ebl);
+            }
+            floatx4_t Dl[2];
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                Dl[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                mma3(Dl[tau], frag(tst + (FT + tau) * FRAG), frag(tst + (FT + 2 + tau) * FRAG), ebh, ebl);
+            }
+            bf16x8_t dbh, dbl, tbh, tbl;
+            {
+                const float r8[8] = {rev[0].x, rev[0].y, rev[0].z, rev[0].w,
+                                     rev[1].x, rev[1].y, rev[1].z, rev[1].w};
+                float dv[8], dtv[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    dv[p] = Dl[p >> 2][p & 3];
+                    dtv[p] = dv[p] * r8[p];
+                }
+                split_vals(dv, dbh, dbl);
+                split_vals(dtv, tbh, tbl);
+            }
+            // Delta's splits for the output wave (read after the next barrier)
+            {
+                uint8_t *dp = smem + dt_off + (uint32_t)(cc & 1) * (PAIR_TILES * DTILE);
+                *reinterpret_cast<bf16x8_t *>(dp + 0 * FRAG) = dbh;
+                *reinterpret_cast<bf16x8_t *>(dp + 1 * FRAG) = dbl;
+                *reinterpret_cast<bf16x8_t *>(dp + 2 * FRAG) = tbh;
+                *reinterpret_cast<bf16x8_t *>(dp + 3 * FRAG) = tbl;
+            }
+            state_update(stg, gC, tbh, tbl);
+            // prefix-cache snapshot after this chunk (full chunks only)
+            if (snap.slots != nullptr && (cc + 1) % snap.every == 0 && (cc + 1) * CH <= L &&
+                (cc + 1) / snap.every <= snap.max) {
+                TS *sp = state + ((int64_t)snap.slots[(int64_t)r * snap.max + (cc + 1) / snap.every - 1] * Hv + h) * D * D;
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt)
+                    st4(sp + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
+            }
+        }
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt)
+            st4(sbase + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
+        if constexpr (XCONV) {
+            // new history of the key head's q / k channels (their old history
+            // was read by the prep kernel), from one block of the key head's
+            // first value head
+            if (h % group == 0 && rb == 0)
+                for (int j = threadIdx.x; j < 2 * D; j += 64 * PAIR_TILES)
+                    chain_write_history<TX>(cv, (j < D ? 0 : cv.nq) + kh * D + (j & (D - 1)), slot, hi_init, tok0, L);
+        }
+    } else {
+        // output wave: chunk cc - 1's output in iteration cc
+        const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+        __builtin_amdgcn_s_waitcnt(0);
+        for (int cc = 0; cc <= nch; ++cc) {
+            __syncthreads();
+            if (cc == 0) continue;
+            const int c = cc - 1;
+            const int tb = tok0 + c * CH;
+            const int Lc = min(CH, L - c * CH);
+            const uint8_t *stg = smem + (size_t)(c % 3) * STG;
+            const uint8_t *tst = stg + KIMG + 16 * lane;
+            // OQ = gamma Q S^T + P Delta
+            floatx4_t OQ[2];
+            contract_state(stg + 16 * lane, FQ, OQ);
+            const uint8_t *tvec = stg + KIMG;
+            const uint8_t *dp = smem + dt_off + (uint32_t)(c & 1) * (PAIR_TILES * DTILE);
+            const bf16x8_t dbh = frag(dp + 0 * FRAG), dbl = frag(dp + 1 * FRAG);
+            const bf16x8_t tbh = frag(dp + 2 * FRAG), tbl = frag(dp + 3 * FRAG);
+            const float gC = *reinterpret_cast<const float *>(tvec + T_GAM + 4 * (CH - 1));
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const float4 g = *reinterpret_cast<const float4 *>(tvec + T_GAM + 4 * (16 * tau + 4 * lg));
+                OQ[tau][0] *= g.x;
+                OQ[tau][1] *= g.y;
+                OQ[tau][2] *= g.z;
+                OQ[tau][3] *= g.w;
+                mma3(OQ[tau], frag(tst + (FP + tau) * FRAG), frag(tst + (FP + 2 + tau) * FRAG), dbh, dbl);
+            }
+            {
+                const __amdgpu_buffer_rsrc_t orr = wave_rsrc(o + ((int64_t)tb * Hv + h) * D,
+                                                             (uint32_t)((Lc - 1) * Hv + 1) * D * sizeof(TO));
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * tau + 4 * lg + e;
+                        store_o<TO>(orr, (uint32_t)(t * Hv * D + irow), OQ[tau][e] * inv_sqrt_d);
+                    }
+            }
+            if (cc < nch) state_update(stg, gC, tbh, tbl);  // the state chunk cc's output starts from
+        }
     }
 }
 
@@ -1576,7 +1937,7 @@ size_t prefill_chunk_workspace_bytes(int32_t Hk, int32_t Hv, int32_t T, int32_t 
 
 // TA: the type of v (the unfused prefill); XCONV: the fused prefill, where the
 // chain forms v from x (of type TX) and writes the new conv history.
-template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, int NCW>
+template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                const ChainConvIn &cv, const ChainSnap &sn) {
@@ -1584,13 +1945,13 @@ static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_
     static std::atomic<uint64_t> set{0};
     constexpr size_t smem = 2 * chain_stage_bytes<NW, XCONV, TX>();
     static_assert(smem <= 160 * 1024, "two chain stages must fit in LDS");
-    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS, NCW>, smem, set);
+    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS, NCW>), dim3((unsigned)blocks),
-                       dim3(64 * (NW + NCW)), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS>), dim3((unsigned)blocks),
+                       dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
                        a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
     return hipGetLastError();
 }
@@ -1620,6 +1981,25 @@ static hipError_t launch_chain_group(const PrefillArgs &a, hipStream_t s, const 
 // whole head (8 waves) when there are enough (request, head) units to fill the
 // chip, else 32 rows.
 template <typename TA, typename TO, bool XCONV, typename TX, typename TS>
+static hipError_t launch_chain_pair(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
+                                    const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
+                                    const ChainConvIn &cv, const ChainSnap &sn) {
+    using namespace chunk;
+    static std::atomic<uint64_t> set{0};
+    constexpr size_t smem = pair_smem_bytes<XCONV, TX>();
+    static_assert(smem <= 160 * 1024, "the paired chain's stages must fit in LDS");
+    hipError_t e = set_smem_once(&prefill_chain_pair_kernel<TA, TO, XCONV, TX, TS>, smem, set);
+    if (e != hipSuccess) return e;
+    const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * PAIR_TILES));
+    const int64_t groups = (int64_t)a.nreq * a.Hk;
+    const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
+    hipLaunchKernelGGL((prefill_chain_pair_kernel<TA, TO, XCONV, TX, TS>), dim3((unsigned)blocks),
+                       dim3(64 * PAIR_WAVES), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
+    return hipGetLastError();
+}
+
+template <typename TA, typename TO, bool XCONV, typename TX, typename TS>
 static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                    const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
                                    const ChainConvIn &cv, const ChainSnap &sn) {
@@ -1628,8 +2008,8 @@ static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const in
         if (units >= 256 && a.Hv == 3 * a.Hk)
             return launch_chain_group<3, TA, TO, XCONV, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
     }
-    return units >= 256 ? launch_chain<8, TA, TO, XCONV, TX, TS, 0>(a, s, chunk_off, order, kimg, timg, cv, sn)
-                        : launch_chain<2, TA, TO, XCONV, TX, TS, 6>(a, s, chunk_off, order, kimg, timg, cv, sn);
+    return units >= 256 ? launch_chain<8, TA, TO, XCONV, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn)
+                        : launch_chain_pair<TA, TO, XCONV, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
 }
 
 template <typename TA, typename TG, typename TX, typename TW, bool CONV>
