@@ -82,46 +82,43 @@ constexpr size_t TIMG = (size_t)TIMG_FRAGS * FRAG;  //  9,216 bytes
 
 constexpr int PLAN_SORT_MAX = 4096;  // longest-first order for up to this many requests
 
-__device__ __forceinline__ uint16_t bits_of(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
-
-// x = hi + lo with hi = RNE_bf16(x), lo = RNE_bf16(x - hi).
-__device__ __forceinline__ void split(float x, uint16_t &h, uint16_t &l) {
-    const __bf16 hb = (__bf16)x;
-    const float hf = (float)hb;
-    h = bits_of(hb);
-    l = bits_of((__bf16)(x - hf));
+// x = hi + lo with hi = RNE_bf16(x), lo = RNE_bf16(x - hi), two values at a
+// time into packed bf16 pairs: one two-value conversion gives both hi parts,
+// whose fp32 values are the pair's low half shifted up and its high half
+// masked, so each lo costs a subtract and half a conversion (three VALU
+// operations per value).
+typedef float float2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &l) {
+    h = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v_t{x0, x1}, bf16x2_t));
+    const float h0 = __uint_as_float(h << 16), h1 = __uint_as_float(h & 0xffff0000u);
+    l = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v_t{x0 - h0, x1 - h1}, bf16x2_t));
 }
-
-__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return a | (uint32_t(b) << 16); }
 
 __device__ __forceinline__ void split4_store(float a, float b, float c, float d, uint16_t *ph,
                                              uint16_t *pl) {
-    uint16_t h[4], l[4];
-    split(a, h[0], l[0]);
-    split(b, h[1], l[1]);
-    split(c, h[2], l[2]);
-    split(d, h[3], l[3]);
-    *reinterpret_cast<uint2 *>(ph) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-    *reinterpret_cast<uint2 *>(pl) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
-}
-
-// eight values (MFMA k-slot order) -> hi/lo operands
-__device__ __forceinline__ void split_vals(const float (&x)[8], bf16x8_t &hi, bf16x8_t &lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 hb = (__bf16)x[e];
-        hi[e] = hb;
-        lo[e] = (__bf16)(x[e] - (float)hb);
-    }
+    uint32_t h0, l0, h1, l1;
+    split2(a, b, h0, l0);
+    split2(c, d, h1, l1);
+    *reinterpret_cast<uint2 *>(ph) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2 *>(pl) = make_uint2(l0, l1);
 }
 
 // eight values -> two 16-byte hi/lo fragment pieces
 __device__ __forceinline__ void split_pack(const float (&x)[8], uint4 &hi, uint4 &lo) {
-    uint16_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split(x[e], h[e], l[e]);
-    hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-    lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+    for (int p = 0; p < 4; ++p) split2(x[2 * p], x[2 * p + 1], h[p], l[p]);
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// eight values (MFMA k-slot order) -> hi/lo operands
+__device__ __forceinline__ void split_vals(const float (&x)[8], bf16x8_t &hi, bf16x8_t &lo) {
+    uint4 h, l;
+    split_pack(x, h, l);
+    hi = __builtin_bit_cast(bf16x8_t, h);
+    lo = __builtin_bit_cast(bf16x8_t, l);
 }
 
 __device__ __forceinline__ bf16x8_t frag(const uint8_t *p) {
@@ -1381,13 +1378,15 @@ __global__ __launch_bounds__(64 * PAIR_WAVES) void prefill_chain_pair_kernel(
         }
     };
     // A S^T for the 32 x 128 operand A of K-image plane pair f0 (hi: f0, lo:
-    // f0 + 8), all four k-steps; the fragments of k-step ks + 1 are read while
-    // k-step ks's MFMAs run (scheduling barriers keep the compiler from sinking
-    // the reads to their uses), the state's bf16 split fills the first wait
+    // f0 + 8), all four k-steps.  While k-step ks's six MFMAs run, the wave
+    // reads k-step ks + 1's fragments and splits its slice of the state
+    // (scheduling groups interleave the split's VALU work between the MFMAs
+    // and keep the compiler from sinking the reads to their uses).
     auto contract_state = [&](const uint8_t *kst, int f0, floatx4_t (&acc)[2]) {
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) acc[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         bf16x8_t fr[2][4];  // [k-step parity][2 tau + plane]
+        bf16x8_t sbh[2], sbl[2];
         auto read = [&](int ks, bf16x8_t (&f)[4]) {
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
@@ -1395,22 +1394,32 @@ __global__ __launch_bounds__(64 * PAIR_WAVES) void prefill_chain_pair_kernel(
                 f[2 * tau + 1] = frag(kst + (f0 + (2 + tau) * 4 + ks) * FRAG);
             }
         };
-        read(0, fr[0]);
-        bf16x8_t sbh[4], sbl[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        auto split_state = [&](int ks) {
             float sv[8];
 #pragma unroll
             for (int p = 0; p < 8; ++p) sv[p] = ST[2 * ks + (p >> 2)][p & 3];
-            split_vals(sv, sbh[ks], sbl[ks]);
-        }
+            split_vals(sv, sbh[ks & 1], sbl[ks & 1]);
+        };
+        read(0, fr[0]);
+        split_state(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if (ks + 1 < 4) read(ks + 1, fr[(ks + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < 4) {
+                read(ks + 1, fr[(ks + 1) & 1]);
+                split_state(ks + 1);
+            }
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau)
-                mma3(acc[tau], fr[ks & 1][2 * tau + 0], fr[ks & 1][2 * tau + 1], sbh[ks], sbl[ks]);
+                mma3(acc[tau], fr[ks & 1][2 * tau + 0], fr[ks & 1][2 * tau + 1], sbh[ks & 1], sbl[ks & 1]);
+            if (ks + 1 < 4) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the four reads first
+#pragma unroll
+                for (int m = 0; m < 6; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU of the split
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
