@@ -26,10 +26,12 @@
 // Chunks are C = 32 tokens: one MFMA k-step spans a chunk and the triangular
 // inverse is 32x32.
 //
-// Three launches:
+// Three launches (two for at most 64 requests):
 //   plan   one block: chunk offsets per request (prefix sum of ceil(L/C)) and
 //          the requests in order of decreasing length, on the device so the
-//          host never waits for query_start_loc.
+//          host never waits for query_start_loc.  For at most 64 requests the
+//          prep and chain waves compute the same figures themselves, in-wave,
+//          and the plan launch (and the wait for it) is skipped.
 //   prep   one block per (chunk, key head), fully parallel: splits K and Q into
 //          hi/lo planes, K K^T and Q K^T on MFMA, then one wave per value head:
 //          the gates' cumulative decay, T = (I + A)^-1 and P.  It writes every
@@ -275,6 +277,46 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t *__res
     }
 }
 
+// The same plan inside a wave, for at most PLAN_WAVE_MAX requests: the launch
+// of the plan kernel and the wait for it cost more than every wave of the
+// prep and chain blocks working it out for itself (no LDS, no barrier).  Lane
+// t holds request t's length and the inclusive prefix sum of the chunk counts.
+constexpr int PLAN_WAVE_MAX = 64;
+struct WavePlan {
+    int len, incl;
+};
+__device__ __forceinline__ WavePlan wave_plan(const int32_t *__restrict__ qsl, int nreq, int lane) {
+    WavePlan p{0, 0};
+    if (lane < nreq) p.len = qsl[lane + 1] - qsl[lane];
+    p.incl = (p.len + chunk::CH - 1) / chunk::CH;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(p.incl, off, 64);
+        if (lane >= off) p.incl += u;
+    }
+    return p;
+}
+// chunk c's request (and its first chunk), as find_request over the offsets;
+// total: every request's chunks
+__device__ __forceinline__ int wave_plan_chunk(const WavePlan &p, int nreq, int c, int &c_first, int &total) {
+    total = __builtin_amdgcn_readfirstlane(__shfl(p.incl, nreq - 1, 64));
+    const int r = __builtin_amdgcn_readfirstlane(__popcll(__ballot(p.incl <= c) & (nreq >= 64 ? ~0ull : ((1ull << nreq) - 1))));
+    c_first = r > 0 ? __builtin_amdgcn_readfirstlane(__shfl(p.incl, r - 1, 64)) : 0;
+    return r;
+}
+// the request of rank k in the plan's order (longest first, ties by index)
+// and its first chunk
+__device__ __forceinline__ int wave_plan_rank(const WavePlan &p, int nreq, int lane, int k, int &c_first) {
+    int rank = 0;
+    for (int u = 0; u < nreq; ++u) {
+        const int lu = __shfl(p.len, u, 64);
+        rank += (lu > p.len) || (lu == p.len && u < lane);
+    }
+    const int r = __builtin_amdgcn_readfirstlane(__ffsll((long long)__ballot(lane < nreq && rank == k)) - 1);
+    c_first = r > 0 ? __builtin_amdgcn_readfirstlane(__shfl(p.incl, r - 1, 64)) : 0;
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // prep: per (chunk, key head): the K image, then one wave per value head for
 // its T image
@@ -324,9 +366,18 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 
     const int c = blockIdx.x / Hk;
     const int kh = blockIdx.x - c * Hk;
-    if (c >= chunk_off[nreq]) return;
-    const int r = find_request(chunk_off, nreq, c);
-    const int tb = qsl[r] + CH * (c - chunk_off[r]);
+    // without chunk offsets (few requests) every wave works out the plan
+    int r, c_first;
+    if (chunk_off == nullptr) {
+        int total;
+        r = wave_plan_chunk(wave_plan(qsl, nreq, lane), nreq, c, c_first, total);
+        if (c >= total) return;
+    } else {
+        if (c >= chunk_off[nreq]) return;
+        r = find_request(chunk_off, nreq, c);
+        c_first = chunk_off[r];
+    }
+    const int tb = qsl[r] + CH * (c - c_first);
     const int Lc = min(CH, qsl[r + 1] - tb);
     const int group = Hv / Hk;
 
@@ -954,7 +1005,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const int gi = 8 * (qd / per_group) + xcd;  // (request rank, key head) group
     const int jj = qd % per_group;
     if (gi >= nreq * Hk) return;
-    const int r = order[gi / Hk];
+    int c_first;
+    const int r = order != nullptr ? order[gi / Hk] : wave_plan_rank(wave_plan(qsl, nreq, lane), nreq, lane, gi / Hk, c_first);
+    if (order != nullptr) c_first = chunk_off[r];
     const int kh = gi % Hk;
     const int h = kh * group + jj / NRB;
     const int rb = jj % NRB;
@@ -962,7 +1015,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const int L = qsl[r + 1] - tok0;
     if (L <= 0) return;  // empty request: slot untouched
     const int nch = (L + CH - 1) / CH;
-    const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
     const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
     const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
@@ -1261,7 +1313,9 @@ __global__ __launch_bounds__(64 * PAIR_WAVES) void prefill_chain_pair_kernel(
     const int gi = 8 * (qd / per_group) + xcd;  // (request rank, key head) group
     const int jj = qd % per_group;
     if (gi >= nreq * Hk) return;
-    const int r = order[gi / Hk];
+    int c_first;
+    const int r = order != nullptr ? order[gi / Hk] : wave_plan_rank(wave_plan(qsl, nreq, lane), nreq, lane, gi / Hk, c_first);
+    if (order != nullptr) c_first = chunk_off[r];
     const int kh = gi % Hk;
     const int h = kh * group + jj / NRB;
     const int rb = jj % NRB;
@@ -1269,7 +1323,6 @@ __global__ __launch_bounds__(64 * PAIR_WAVES) void prefill_chain_pair_kernel(
     const int L = qsl[r + 1] - tok0;
     if (L <= 0) return;  // empty request: slot untouched
     const int nch = (L + CH - 1) / CH;
-    const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
     const uint8_t *kim0 = kimg + ((size_t)c_first * Hk + kh) * KIMG;
     const uint8_t *tim0 = timg + ((size_t)c_first * Hv + h) * TIMG;
@@ -1623,7 +1676,9 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     const int gi = 8 * (qd / NRB) + xcd;
     const int rb = qd % NRB;
     if (gi >= nreq * Hk) return;
-    const int r = order[gi / Hk];
+    int c_first;
+    const int r = order != nullptr ? order[gi / Hk] : wave_plan_rank(wave_plan(qsl, nreq, lane), nreq, lane, gi / Hk, c_first);
+    if (order != nullptr) c_first = chunk_off[r];
     const int kh = gi % Hk;
     // this wave's head within the group, first tile and tile count: waves 0-2
     // tiles 0-1 of heads 0-2, wave 3 tiles 2-3 of head 0, waves 4-7 tile 2 or 3
@@ -1636,7 +1691,6 @@ __global__ __launch_bounds__(64 * GRP_NW) void prefill_chain_group_kernel(
     const int L = qsl[r + 1] - tok0;
     if (L <= 0) return;
     const int nch = (L + CH - 1) / CH;
-    const int c_first = chunk_off[r];
     const bool hi_init = has_init == nullptr || has_init[r] != 0;
     const int tok_last = tok0 + L - 1;
     // a one-tile wave's second tile repeats its first: loads stay in bounds and
@@ -2046,9 +2100,16 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
     uint8_t *kimg = base + wl.meta;
     uint8_t *timg = kimg + wl.kimg;
 
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, s, a.qsl, a.nreq, chunk_off, order);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (a.nreq <= PLAN_WAVE_MAX) {
+        // few requests: the prep and chain waves work the plan out themselves
+        chunk_off = nullptr;
+        order = nullptr;
+    } else {
+        hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, s, a.qsl, a.nreq, chunk_off, order);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     const PrepConvIn cv{a.x, a.x_ld, a.conv_w, a.pool, a.slots, a.has_init,
                         2 * a.Hk * D + a.Hv * D, a.l2_eps};
