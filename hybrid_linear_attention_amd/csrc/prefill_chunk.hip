@@ -978,21 +978,48 @@ constexpr size_t chain_stage_bytes() {
     return chunk::KIMG + chunk::TIMG + (XCONV ? (size_t)NW * XWave<TX, 1>::BYTES : 0);
 }
 
+// Gated output formed by the per-head chain itself ("Qwen3.8-27B: from model
+// structure to the vLLM inference dataflow", section 01 operator table,
+// gated-output row: y = o / rms(o) * gamma * SiLU(z), the RMS over the d_v
+// channels of one head and token).  A whole-head block holds every channel of
+// its head, so the RMS is a reduction inside the block: each chunk's o goes to
+// LDS (fp32, one padded row per token), and after the next chunk-top barrier
+// every wave normalises 4 of its tokens, a lane 8 channels, with z read and y
+// written as 16-byte pieces of whole rows.  z and y are bf16.
+struct ChainNorm {
+    const bf16 *z; int64_t z_ld;
+    const void *gamma; bool gamma_bf16;
+    float eps;
+    bf16 *y;
+};
+constexpr int NORM_ROW = chunk::D + 4;  // padded fp32 row of the staged o (528 bytes)
+constexpr size_t NORM_BUF = (size_t)chunk::CH * NORM_ROW * 4;  // one chunk's o
+// LDS of the per-head chain: two stages, and two chunks' staged o with the
+// gated output
+template <int NW, bool XCONV, typename TX, bool NORM>
+constexpr size_t chain_smem_bytes() {
+    return 2 * chain_stage_bytes<NW, XCONV, TX>() + (NORM ? 2 * NORM_BUF : 0);
+}
+
 // Every wave computes a 16-row tile and copies its share of the next chunk's
 // images (and the x rows of its own channels) while it computes the current.
-template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS>
+// NORM (whole-head blocks of the fused prefill): the gated output is formed
+// here, one chunk behind, and o is not written.
+template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, bool NORM>
 __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     const TA *__restrict__ v, TS *__restrict__ state, const int32_t *__restrict__ qsl,
     const int32_t *__restrict__ slots, const uint8_t *__restrict__ has_init,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
     const uint8_t *__restrict__ kimg, const uint8_t *__restrict__ timg, int32_t nreq, int32_t Hk,
-    int32_t Hv, TO *__restrict__ o, ChainConvIn cv, ChainSnap snap) {
+    int32_t Hv, TO *__restrict__ o, ChainConvIn cv, ChainSnap snap, ChainNorm nm) {
     using namespace chunk;
     constexpr int IB = 16 * NW;  // state rows per block
     constexpr int NRB = D / IB;  // blocks per (request, head)
+    static_assert(!NORM || (NRB == 1 && XCONV), "the gated output needs whole-head blocks of the fused prefill");
     using XW = XWave<TX, 1>;
     constexpr uint32_t XOFF = (uint32_t)(KIMG + TIMG);  // staged x rows within a stage
     constexpr uint32_t STG = (uint32_t)chain_stage_bytes<NW, XCONV, TX>();
+    constexpr uint32_t OBASE = 2 * STG;  // (NORM) the two staged o chunks
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lds0 = lds_addr(smem);
@@ -1050,6 +1077,60 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
     float vnext[2][4];  // (fused) v of the next chunk, formed at the end of the current one
     (void)vnext;
 
+    // (NORM) this lane's share of a chunk's gated output: token ntt, channels
+    // nc8 .. nc8 + 7 of head h; gamma of those channels; z of the previous
+    // chunk (zp) and of the current one (zc, loaded a chunk ahead of its use)
+    const int ntt = 4 * w + lg, nc8 = 8 * lr;
+    float gmv[8];
+    Raw8<bf16> zp, zc;
+    uint4 ypk = make_uint4(0, 0, 0, 0);  // the previous chunk's y, stored at the end of this one
+    if constexpr (NORM) {
+        if (nm.gamma_bf16) {
+            Raw8<bf16> g;
+            g.load(static_cast<const bf16 *>(nm.gamma) + nc8);
+            g.get(gmv);
+        } else {
+            Raw8<float> g;
+            g.load(static_cast<const float *>(nm.gamma) + nc8);
+            g.get(gmv);
+        }
+        zc.zero();
+    }
+    (void)gmv;
+    auto load_z = [&](int tbc, int Lcc) {
+        if (ntt < Lcc) zc.load(nm.z + (int64_t)(tbc + ntt) * nm.z_ld + (int64_t)h * D + nc8);
+        else zc.zero();
+    };
+    // y of chunk cn's token ntt from its staged o and z, rounded to bf16
+    // (nearest-even).  Straight-line code with the hardware reciprocal square
+    // root and reciprocal (about 1 ulp of fp32 each), so that it can be
+    // interleaved with the state update's MFMAs.
+    auto gated = [&](int cn, const Raw8<bf16> &zr) {
+        const float *orow = reinterpret_cast<const float *>(smem + OBASE + (size_t)(cn & 1) * NORM_BUF +
+                                                            ((size_t)ntt * NORM_ROW + nc8) * 4);
+        const float4 oa = reinterpret_cast<const float4 *>(orow)[0], ob = reinterpret_cast<const float4 *>(orow)[1];
+        const float of[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+        float zf[8];
+        zr.get(zf);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += of[e] * of[e];
+        ss = group_sum<16>(ss);
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + nm.eps);
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float y0 = of[2 * i] * inv * gmv[2 * i] * silu_fast(zf[2 * i]);
+            const float y1 = of[2 * i + 1] * inv * gmv[2 * i + 1] * silu_fast(zf[2 * i + 1]);
+            pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v_t{y0, y1}, bf16x2_t));
+        }
+        return make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    };
+    auto store_y = [&](int tbn, int Lcn, const uint4 &yv) {
+        if (ntt < Lcn)
+            *reinterpret_cast<uint4 *>(nm.y + ((int64_t)(tbn + ntt) * Hv + h) * D + nc8) = yv;
+    };
+
     if constexpr (XCONV) {
         load_taps(cv, cb + 16 * w + lr, wt);
         xp.init(cb + 16 * w, 1, lane);
@@ -1077,6 +1158,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
         if (cc > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if constexpr (NORM) {
+            // z of chunk cc, first: it has long landed when the wait for the
+            // next chunk's copies comes
+            zp = zc;
+            load_z(tb, Lc);
+        }
         float vcur[2][4];
         if constexpr (XCONV) {
 #pragma unroll
@@ -1207,6 +1294,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
             ST[jt] *= gC;
             mma3(ST[jt], kth[jt], ktlo[jt], tbh, tbl);
         }
+        // (NORM) the previous chunk's gated output (a full chunk: only the last
+        // is ragged) under the state update's MFMAs; on the first chunk it is
+        // formed from the other, not yet written, o buffer and never stored
+        if constexpr (NORM) ypk = gated(cc - 1, zp);
         if constexpr (XCONV) {
             // v of the next chunk, from this wave's own copies of its rows (landed
             // once its memory counter drains), beside the state update's MFMAs
@@ -1218,7 +1309,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
                            min(CH, L - (cc + 1) * CH), vnext);
             }
         }
-        {
+        if constexpr (NORM) {
+            // this chunk's o to its LDS rows (read after the next chunk-top
+            // barrier; the buffer is rewritten two chunks on, after every wave
+            // has passed the barrier in between); the previous chunk's y out
+            float *ob = reinterpret_cast<float *>(smem + OBASE + (size_t)(cc & 1) * NORM_BUF);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ob[(16 * tau + 4 * lg + e) * NORM_ROW + irow] = OQ[tau][e] * inv_sqrt_d;
+            if (cc > 0) store_y(tb - CH, CH, ypk);
+        } else {
             const __amdgpu_buffer_rsrc_t orr = wave_rsrc(o + ((int64_t)tb * Hv + h) * D,
                                                          (uint32_t)((Lc - 1) * Hv + 1) * D * sizeof(TO));
 #pragma unroll
@@ -1242,6 +1344,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_chain_kernel(
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt)
         st4(sbase + (int64_t)irow * D + 16 * jt + 4 * lg, make_float4(ST[jt][0], ST[jt][1], ST[jt][2], ST[jt][3]));
+    if constexpr (NORM) {
+        // the last chunk's gated output: its z has landed and every wave's o
+        // rows are in LDS
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int cl = nch - 1;
+        store_y(tok0 + cl * CH, L - cl * CH, gated(cl, zc));
+    }
     if constexpr (XCONV) {
         // new history (every reader of the old one is done: the prep kernel for
         // q / k, this block's prologue for its v channels): this lane's v
@@ -2000,22 +2110,22 @@ size_t prefill_chunk_workspace_bytes(int32_t Hk, int32_t Hv, int32_t T, int32_t 
 
 // TA: the type of v (the unfused prefill); XCONV: the fused prefill, where the
 // chain forms v from x (of type TX) and writes the new conv history.
-template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS>
+template <int NW, typename TA, typename TO, bool XCONV, typename TX, typename TS, bool NORM = false>
 static hipError_t launch_chain(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
-                               const ChainConvIn &cv, const ChainSnap &sn) {
+                               const ChainConvIn &cv, const ChainSnap &sn, const ChainNorm &nm = ChainNorm{}) {
     using namespace chunk;
     static std::atomic<uint64_t> set{0};
-    constexpr size_t smem = 2 * chain_stage_bytes<NW, XCONV, TX>();
-    static_assert(smem <= 160 * 1024, "two chain stages must fit in LDS");
-    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS>, smem, set);
+    constexpr size_t smem = chain_smem_bytes<NW, XCONV, TX, NORM>();
+    static_assert(smem <= 160 * 1024, "the chain's stages (and staged o) must fit in LDS");
+    hipError_t e = set_smem_once(&prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS, NORM>, smem, set);
     if (e != hipSuccess) return e;
     const int64_t per_group = (int64_t)(a.Hv / a.Hk) * (D / (16 * NW));
     const int64_t groups = (int64_t)a.nreq * a.Hk;
     const int64_t blocks = 8 * per_group * ((groups + 7) / 8);
-    hipLaunchKernelGGL((prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((prefill_chain_kernel<NW, TA, TO, XCONV, TX, TS, NORM>), dim3((unsigned)blocks),
                        dim3(64 * NW), smem, s, (const TA *)a.v, (TS *)a.state, a.qsl, a.slots,
-                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn);
+                       a.has_init, chunk_off, order, kimg, timg, a.nreq, a.Hk, a.Hv, (TO *)a.o, cv, sn, nm);
     return hipGetLastError();
 }
 
@@ -2065,8 +2175,21 @@ static hipError_t launch_chain_pair(const PrefillArgs &a, hipStream_t s, const i
 template <typename TA, typename TO, bool XCONV, typename TX, typename TS>
 static hipError_t launch_chain_any(const PrefillArgs &a, hipStream_t s, const int32_t *chunk_off,
                                    const int32_t *order, const uint8_t *kimg, const uint8_t *timg,
-                                   const ChainConvIn &cv, const ChainSnap &sn) {
+                                   const ChainConvIn &cv, const ChainSnap &sn, bool *normed) {
     const int64_t units = (int64_t)a.nreq * a.Hv;
+    *normed = false;
+    if constexpr (XCONV && std::is_same<TX, bf16>::value) {
+        // enough units for whole-head blocks and a bf16 gated output in 16-byte
+        // pieces: the chain forms y itself (no o round trip, no norm pass)
+        auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+        if (units >= 256 && a.y != nullptr && a.y_bf16 && a.z_bf16 && a.z_ld % 8 == 0 && al16(a.z) &&
+            al16(a.y) && al16(a.gamma)) {
+            *normed = true;
+            const ChainNorm nm{static_cast<const bf16 *>(a.z), a.z_ld, a.gamma, a.gamma_bf16, a.norm_eps,
+                               static_cast<bf16 *>(a.y)};
+            return launch_chain<8, TA, TO, XCONV, TX, TS, true>(a, s, chunk_off, order, kimg, timg, cv, sn, nm);
+        }
+    }
     if constexpr (!XCONV || std::is_same<TX, bf16>::value) {
         if (units >= 256 && a.Hv == 3 * a.Hk)
             return launch_chain_group<3, TA, TO, XCONV, TX, TS>(a, s, chunk_off, order, kimg, timg, cv, sn);
@@ -2115,6 +2238,7 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
                         2 * a.Hk * D + a.Hv * D, a.l2_eps};
     const ChainSnap sn{a.max_snaps > 0 ? a.snap_slots : nullptr, a.max_snaps > 0 ? a.snap_interval / CH : 1,
                        a.max_snaps};
+    bool normed = false;  // the chain formed the gated output itself
     if (a.x) {
         // conv mode: the prep kernel forms q and k (into the K images) from x;
         // the chain forms v from x itself and writes the new history of every
@@ -2127,11 +2251,11 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
         const ChainConvIn ci{a.x, a.x_ld, a.conv_w, a.w_bf16, a.pool, 2 * a.Hk * D + a.Hv * D, a.Hk * D};
         if constexpr (std::is_same<TO, float>::value) {
             if (a.state_bf16)
-                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn)
-                             : launch_chain_any<float, float, true, float, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn);
+                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn, &normed)
+                             : launch_chain_any<float, float, true, float, bf16>(a, s, chunk_off, order, kimg, timg, ci, sn, &normed);
             else
-                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, float>(a, s, chunk_off, order, kimg, timg, ci, sn)
-                             : launch_chain_any<float, float, true, float, float>(a, s, chunk_off, order, kimg, timg, ci, sn);
+                e = a.x_bf16 ? launch_chain_any<float, float, true, bf16, float>(a, s, chunk_off, order, kimg, timg, ci, sn, &normed)
+                             : launch_chain_any<float, float, true, float, float>(a, s, chunk_off, order, kimg, timg, ci, sn, &normed);
         } else {
             return hipErrorInvalidValue;
         }
@@ -2139,12 +2263,11 @@ static hipError_t launch_chunk_t(const PrefillArgs &a, hipStream_t s) {
         e = launch_prep<TA, TG, float, float, false>(a, s, chunk_off, kimg, timg, cv);
         if (e != hipSuccess) return e;
         if (a.state_bf16) return hipErrorInvalidValue;  // the unfused prefill keeps an fp32 state
-        e = launch_chain_any<TA, TO, false, float, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{}, sn);
+        e = launch_chain_any<TA, TO, false, float, float>(a, s, chunk_off, order, kimg, timg, ChainConvIn{}, sn, &normed);
     }
-    if (e != hipSuccess || !a.y) return e;
-    // gated output: a separate HBM-streaming pass over o (folding it into the
-    // chain's chunk loop measured slower: its per-token reductions sit on the
-    // chain's critical path)
+    if (e != hipSuccess || !a.y || normed) return e;
+    // gated output of the other block shapes (whose blocks hold part of a
+    // head): a separate HBM-streaming pass over o
     GatedNormArgs g{D, a.o, a.o_bf16, a.z, a.z_ld, a.z_bf16, a.gamma, a.gamma_bf16, a.norm_eps,
                     a.T, a.Hv, a.y, a.y_bf16};
     return launch_gated_norm(g, s);

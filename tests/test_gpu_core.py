@@ -446,24 +446,29 @@ def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16, x_pad=0):
     return y, pool, state
 
 
-@pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d32_seq",
+@pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d128_group_f32y", "d32_seq",
                                    "d128_unaligned_rows", "d128_many_requests"])
 def test_prefill_fused_parity(which):
     """One prefill step through gdn_prefill_fused against the fp64 oracle chain:
-    32-row chain blocks (few heads x requests), key-head group blocks (>= 256
-    heads x requests), the sequential kernel for d = 32, and x rows that are not
-    16-byte aligned (the conv pass then forms q and k before the prep kernel
-    instead of the prep kernel forming them from x)."""
+    32-row chain blocks (few heads x requests); whole-head blocks that form the
+    gated output themselves (>= 256 (request, head) units, bf16 y); key-head
+    group blocks with the separate gated-norm pass (the same units, fp32 y); the
+    sequential kernel for d = 32; and x rows that are not 16-byte aligned (the
+    conv pass then forms q and k before the prep kernel instead of the prep
+    kernel forming them from x)."""
     x_pad = 0
+    y_dtype = torch.bfloat16
     if which == "d128_split_rows":
         case = varlen_case(41, lengths=(1, 2, 5, 37, 0, 130, 3), num_slots=10)
     elif which == "d128_unaligned_rows":
         case = varlen_case(44, lengths=(3, 50, 0, 2, 91), num_slots=7)
         x_pad = 2
-    elif which == "d128_whole_heads":
+    elif which in ("d128_whole_heads", "d128_group_f32y"):
         rng = np.random.default_rng(42)
         lens = [int(x) for x in rng.integers(0, 70, 48)]
         case = varlen_case(42, lengths=lens, num_slots=60)
+        if which == "d128_group_f32y":
+            y_dtype = torch.float32
     elif which == "d128_many_requests":
         # more than 64 requests: the chunk plan comes from the plan kernel
         rng = np.random.default_rng(45)
@@ -471,7 +476,7 @@ def test_prefill_fused_parity(which):
         case = varlen_case(45, lengths=lens, num_slots=104)
     else:
         case = varlen_case(43, D=32, Hk=2, Hv=4, lengths=(3, 40, 1, 77), num_slots=6)
-    y, pool, state = run_prefill_fused_gpu(case, x_pad=x_pad)
+    y, pool, state = run_prefill_fused_gpu(case, y_dtype=y_dtype, x_pad=x_pad)
     d = case.dims
     qr, kr, vr, pr = oracle_conv(case)
     o_ref, st_ref = oracle.gated_delta_rule(qr, kr, vr, f64(case.a), f64(case.b),
