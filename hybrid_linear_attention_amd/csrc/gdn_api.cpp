@@ -481,9 +481,21 @@ gdn_status gdn_rmsnorm(const void *x, gdn_dtype x_dt, const void *gamma, gdn_dty
     return hip_status(gdn::launch_rmsnorm(ra, static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_gemm_bf16_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    return gdn::gemm_bf16_workspace_bytes(M, N, K);
+}
+
 gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
                          int64_t ldc, gdn_dtype c_dt, const void *residual, int64_t ldr,
                          int32_t M, int32_t N, int32_t K, void *stream) {
+    return gdn_gemm_bf16_ws(A, lda, B, ldb, C, ldc, c_dt, residual, ldr, M, N, K, nullptr, 0, stream);
+}
+
+gdn_status gdn_gemm_bf16_ws(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                            int64_t ldc, gdn_dtype c_dt, const void *residual, int64_t ldr,
+                            int32_t M, int32_t N, int32_t K, void *workspace,
+                            size_t workspace_bytes, void *stream) {
     if (!valid_dtype(c_dt)) return GDN_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || N % 8 != 0 || K % 8 != 0) return GDN_ERR_SHAPE;
     if (lda < K || ldb < K || ldc < N || (residual && ldr < N)) return GDN_ERR_SHAPE;
@@ -492,7 +504,10 @@ gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb,
     if (!A || !B || !C) return GDN_ERR_NULL;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || (residual && !aligned(residual, 16)))
         return GDN_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
     gdn::GemmArgs g{A, lda, B, ldb, C, ldc, c_dt == GDN_BF16, residual, ldr, M, N, K};
+    g.ws = workspace;
+    g.ws_bytes = workspace ? workspace_bytes : 0;
     return hip_status(gdn::launch_gemm_bf16(g, static_cast<hipStream_t>(stream)));
 }
 

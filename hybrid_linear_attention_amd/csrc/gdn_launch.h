@@ -118,8 +118,12 @@ struct GemmArgs {
     void *C; int64_t ldc; bool c_bf16;
     const void *R; int64_t ldr;
     int32_t M, N, K;
+    // optional workspace for the split tail (gemm_bf16_workspace_bytes; 256-byte
+    // aligned): without it, or when it is too small, no tile is split
+    void *ws = nullptr; size_t ws_bytes = 0;
 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, hipStream_t s);
+size_t gemm_bf16_workspace_bytes(int M, int N, int K);  // on the current device; 0: no split
 
 // Raise a kernel's dynamic-LDS limit once per device (the attribute belongs to
 // the device the call is made on); `done` records the devices already set, as

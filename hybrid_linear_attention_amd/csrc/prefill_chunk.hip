@@ -450,7 +450,6 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 const int pi = tid + 256 * m;
                 const int rr = pi >> 5, seg = pi & 31;
                 const int tok = tb - 3 + rr;
-                const int ch = pass_chan(ps, EPP * seg);
                 const bool ok = pi < NPIECE && tok >= t0 && rr - 3 < Lc;
                 if (pi < NPIECE && tok >= t0)
                     *reinterpret_cast<uint4 *>(&xs[rr][EPP * seg]) = ok ? pv[m] : make_uint4(0u, 0u, 0u, 0u);

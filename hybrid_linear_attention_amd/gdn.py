@@ -75,6 +75,9 @@ _SIGS = {
                         _vp, _i32, _vp], _i32),
     "gdn_rmsnorm": ([_vp, _i32, _vp, _i32, _f32, _i32, _i32, _vp, _i32, _vp], _i32),
     "gdn_gemm_bf16": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _i32, _vp], _i32),
+    "gdn_gemm_bf16_ws": ([_vp, _i64, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _i32, _vp,
+                          ctypes.c_size_t, _vp], _i32),
+    "gdn_gemm_bf16_workspace_bytes": ([_i32, _i32, _i32], ctypes.c_size_t),
     "gdn_validate_metadata": ([_vp, _vp, _i32, _i32, _i32], _i32),
     "gdn_validate_spec_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32], _i32),
     "gdn_validate_snapshot_metadata": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32], _i32),
@@ -358,9 +361,17 @@ def gdn_rmsnorm(x, gamma, y, eps=1e-6, stream=None):
     _check(st, "gdn_rmsnorm")
 
 
-def gdn_gemm_bf16(A, B, C, residual=None, stream=None):
+def gdn_gemm_bf16_workspace_bytes(M, N, K):
+    """Workspace bytes gdn_gemm_bf16 can use for this shape on the current device
+    (0: it would split nothing)."""
+    return int(lib().gdn_gemm_bf16_workspace_bytes(int(M), int(N), int(K)))
+
+
+def gdn_gemm_bf16(A, B, C, residual=None, stream=None, workspace=None):
     """C[M,N] = A[M,K] @ B[N,K]^T (+ residual); A, B, residual bf16; row strides taken
-    from the tensors (innermost dimension contiguous)."""
+    from the tensors (innermost dimension contiguous).  With a workspace (uint8
+    device tensor of gdn_gemm_bf16_workspace_bytes(M, N, K) bytes) the last,
+    partly filled round of tiles is split along K (gdn_gemm_bf16_ws)."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K or C.shape[0] != M or C.shape[1] != N:
@@ -372,10 +383,17 @@ def gdn_gemm_bf16(A, B, C, residual=None, stream=None):
         if residual.dtype != torch.bfloat16 or tuple(residual.shape) != (M, N):
             raise ValueError("residual must be bf16 [M, N]")
         r_ptr, ldr = _ptr(residual, "residual"), _rows(residual, "residual")
-    st = lib().gdn_gemm_bf16(_ptr(A, "A"), _rows(A, "A"), _ptr(B, "B"), _rows(B, "B"),
-                             _ptr(C, "C"), _rows(C, "C"), _dt(C), r_ptr, ldr, M, N, K,
-                             _stream(stream))
-    _check(st, "gdn_gemm_bf16")
+    if workspace is None:
+        st = lib().gdn_gemm_bf16(_ptr(A, "A"), _rows(A, "A"), _ptr(B, "B"), _rows(B, "B"),
+                                 _ptr(C, "C"), _rows(C, "C"), _dt(C), r_ptr, ldr, M, N, K,
+                                 _stream(stream))
+        _check(st, "gdn_gemm_bf16")
+        return
+    st = lib().gdn_gemm_bf16_ws(_ptr(A, "A"), _rows(A, "A"), _ptr(B, "B"), _rows(B, "B"),
+                                _ptr(C, "C"), _rows(C, "C"), _dt(C), r_ptr, ldr, M, N, K,
+                                _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check(st, "gdn_gemm_bf16_ws")
 
 
 def gdn_validate_metadata(query_start_loc, slot_ids, num_tokens, num_slots):

@@ -85,6 +85,10 @@ class GdnLayer:
             self.o = torch.empty((T, Hv, dv), device=device)
             nbytes = gdn.gdn_prefill_workspace_bytes(dims, self.T_pf, self.n_pf) if self.n_pf else 0
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+        # the projections' split-tail workspace (one buffer: the launches run in order)
+        gb = max(gdn.gdn_gemm_bf16_workspace_bytes(T, n_in, hidden),
+                 gdn.gdn_gemm_bf16_workspace_bytes(T, hidden, Hv * dv))
+        self.gemm_ws = torch.empty(gb, dtype=torch.uint8, device=device) if gb else None
 
     # views of the projection output
     def x_qkv(self):
@@ -108,7 +112,8 @@ class GdnLayer:
         a, b = self.a(), self.b()
         out = [
             ("rmsnorm", lambda: gdn.gdn_rmsnorm(X, w.gamma_in, self.U, self.norm_eps, stream)),
-            ("in_proj", lambda: gdn.gdn_gemm_bf16(self.U, w.W_in, self.P, stream=stream)),
+            ("in_proj", lambda: gdn.gdn_gemm_bf16(self.U, w.W_in, self.P, stream=stream,
+                                                 workspace=self.gemm_ws)),
         ]
         if self.fused:
             x, z = self.x_qkv(), self.z()
@@ -123,7 +128,7 @@ class GdnLayer:
                     state_pool, slot_ids[n_pf:], self.y[T_pf:], has_initial=has_initial[n_pf:],
                     l2_eps=self.l2_eps, norm_eps=self.norm_eps, stream=stream)))
             out.append(("out_proj", lambda: gdn.gdn_gemm_bf16(self.y, w.W_out, self.Y, residual=X,
-                                                              stream=stream)))
+                                                              stream=stream, workspace=self.gemm_ws)))
             return out
         out += [
             ("conv1d", lambda: gdn.gdn_conv1d_update(
@@ -143,7 +148,7 @@ class GdnLayer:
             ("gated_norm", lambda: gdn.gdn_gated_norm(d, self.o, self.z(), w.gamma_out, self.y,
                                                       self.norm_eps, stream)),
             ("out_proj", lambda: gdn.gdn_gemm_bf16(self.y, w.W_out, self.Y, residual=X,
-                                                   stream=stream)),
+                                                   stream=stream, workspace=self.gemm_ws)),
         ]
         return out
 

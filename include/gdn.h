@@ -390,6 +390,33 @@ gdn_status gdn_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb,
                          int32_t N, int32_t K, void *stream);
 
 /*
+ * gdn_gemm_bf16_ws — gdn_gemm_bf16 with a workspace (the same operation, the
+ * same arguments and checks).  The output tiles of 256 x 256 fill the chip in
+ * rounds of one tile per compute unit; when the last round is only partly
+ * filled (or there are fewer tiles than compute units), its tiles' K stages
+ * are dealt out evenly to up to one block per compute unit, each block taking
+ * a contiguous run that covers at most the end of one tile and the start of
+ * the next, and a second launch adds each tile's runs in a fixed order (the
+ * result is the same on every run; it may differ from the unsplit sum in the
+ * last bits).
+ *   workspace        device memory of at least
+ *                    gdn_gemm_bf16_workspace_bytes(M, N, K) bytes, 256-byte
+ *                    aligned (else GDN_ERR_ALIGN), owned by the caller, free
+ *                    to reuse once the call's work on `stream` is done; NULL,
+ *                    or fewer bytes than asked for: nothing is split.
+ * gdn_gemm_bf16_workspace_bytes — the workspace that shape asks for on the
+ *   current device (two 256 KiB slots per block: at most 128 MiB on 256
+ *   compute units); 0 when nothing of it would be split (K not a multiple of
+ *   64, a full last round, or no more blocks of at least 256 of K than tiles).
+ */
+gdn_status gdn_gemm_bf16_ws(const void *A, int64_t lda, const void *B, int64_t ldb,
+                            void *C, int64_t ldc, gdn_dtype c_dt,
+                            const void *residual, int64_t ldr, int32_t M,
+                            int32_t N, int32_t K, void *workspace,
+                            size_t workspace_bytes, void *stream);
+size_t gdn_gemm_bf16_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/*
  * gdn_validate_metadata — HOST-side check of host copies of the varlen
  * metadata: qsl[0] == 0, qsl non-decreasing, qsl[num_reqs] == num_tokens,
  * slot ids in range and distinct.  Enqueues nothing; GDN_ERR_METADATA on

@@ -131,6 +131,25 @@ def test_norm_and_gemm_reject_bad_args():
     assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 128, 0, None, 0, 0, 128, 64, None) == 0
     assert lib.gdn_gemm_bf16(P, 64, P, 32, P, 128, 0, None, 0, 0, 128, 64, None) == 4
     assert lib.gdn_gemm_bf16(P, 64, P, 64, P, 64, 0, None, 0, 0, 64, 64, None) == 0
+    # the workspace variant: same checks, then a 256-byte aligned workspace
+    assert lib.gdn_gemm_bf16_ws(P, 64, P, 64, P, 64, 0, None, 0, 10, 64, 60, None, 0, None) == 4
+    assert lib.gdn_gemm_bf16_ws(P, 64, P, 64, P, 64, 0, None, 0, 10, 64, 64, P + 16, 1 << 20, None) == 6
+    assert lib.gdn_gemm_bf16_ws(P, 64, P, 64, P, 64, 0, None, 0, 0, 64, 64, P, 1 << 20, None) == 0
+
+
+def test_gemm_workspace_bytes():
+    """The split tail's workspace: none for K not a multiple of 64, for empty
+    shapes or when blocks of at least 4 stages would not outnumber the tail
+    tiles; else two 256 x 256 fp32 slots per block, at most one block per
+    compute unit (128 MiB at 256)."""
+    lib = gdn.lib()
+    slot = 256 * 256 * 4
+    assert lib.gdn_gemm_bf16_workspace_bytes(300, 200, 5000) == 0      # K % 64
+    assert lib.gdn_gemm_bf16_workspace_bytes(0, 200, 5120) == 0
+    assert lib.gdn_gemm_bf16_workspace_bytes(300, 200, 192) == 0       # 2 tiles x 3 stages: no 3 blocks of 4
+    for M, N, K in ((300, 200, 5120), (16640, 5120, 6144), (4300, 4000, 1024), (256, 16480, 5120)):
+        n = lib.gdn_gemm_bf16_workspace_bytes(M, N, K)
+        assert n % (2 * slot) == 0 and 4 * slot <= n <= 512 * slot, (M, N, K, n)
 
 
 def fused_call(d, **kw):

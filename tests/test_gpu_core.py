@@ -603,3 +603,44 @@ def test_gemm_parity(M, N, K, res):
     Cb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     gdn.gdn_gemm_bf16(dev(A), dev(B), Cb, residual=dev(R) if res else None)
     assert bf16_ulp_ok(Cb, ref, ulps=1)
+
+
+@pytest.mark.parametrize("M,N,K,res", [(300, 200, 5120, False), (4300, 4000, 1024, True),
+                                       (256, 16480, 5120, False), (16640, 5120, 6144, True)])
+def test_gemm_split_tail(M, N, K, res):
+    """gdn_gemm_bf16 with a workspace: the K stages of the tiles of the last,
+    partly filled round (or of all tiles, when there are fewer than compute
+    units) are dealt out to up to one block per compute unit and a second
+    launch adds each tile's runs.  Shapes: 2 tiles over 40 blocks; 272 tiles
+    (16 tail tiles with partial rows and columns, over 64 blocks); 65 tiles over
+    256 blocks (runs that cross tile ends); the out-projection of the
+    16,640-token layer batch (20 tail tiles over 256 blocks).  Checked against
+    the fp64 oracle on every row (the large shapes: their first and their tail
+    tile rows), for fp32 and bf16 C; a second call repeats the first bit for
+    bit."""
+    nbytes = gdn.gdn_gemm_bf16_workspace_bytes(M, N, K)
+    assert nbytes > 0, "the shape should be split"
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(M + 7 * N + K)
+    A = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to(torch.bfloat16)
+    B = torch.from_numpy(rng.standard_normal((N, K), dtype=np.float32) * 0.02).to(torch.bfloat16)
+    R = torch.from_numpy(rng.standard_normal((M, N), dtype=np.float32)).to(torch.bfloat16) if res else None
+    Ad, Bd = dev(A), dev(B)
+    Rd = dev(R) if res else None
+    last = 256 * ((M - 1) // 256)
+    rows = np.arange(M) if M * N * K <= 4e9 else np.unique(np.concatenate([np.arange(256), np.arange(last, M)]))
+    ref = oracle.linear(f64(A[rows]), f64(B).T)
+    if res:
+        ref = oracle.residual_add(f64(R[rows]), ref)
+    for cdt in (torch.float32, torch.bfloat16):
+        C = torch.empty((M, N), dtype=cdt, device="cuda")
+        gdn.gdn_gemm_bf16(Ad, Bd, C, residual=Rd, workspace=ws)
+        C2 = torch.full((M, N), float("nan"), dtype=cdt, device="cuda")
+        gdn.gdn_gemm_bf16(Ad, Bd, C2, residual=Rd, workspace=ws)
+        np.testing.assert_array_equal(bits(C.cpu()), bits(C2.cpu()))
+        got = C.cpu()[torch.from_numpy(rows)]
+        if cdt == torch.float32:
+            assert rel_l2(f64(got), ref) <= FP32_TOL
+        else:
+            assert bf16_ulp_ok(got, ref, ulps=1)
+    print(f"{M}x{N}x{K}: {nbytes >> 19} split blocks")
