@@ -412,13 +412,23 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float *__r
             s[4 * v + 3] += f.w;
         }
     }
+    // two 8-column pieces (N % 8 == 0: a piece is all in or all out)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int col = tn * G2N + c0 + e;
+    for (int h = 0; h < 2; ++h) {
+        const int col = tn * G2N + c0 + 8 * h;
         if (col >= N) continue;
-        float val = s[e];
-        if (RES) val += __uint_as_float(uint32_t(R[(int64_t)row * ldr + col]) << 16);
-        st(C + (int64_t)row * ldc + col, val);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = s[8 * h + e];
+        if (RES) {
+            Raw8<bf16> rr;
+            rr.load(reinterpret_cast<const bf16 *>(R + (int64_t)row * ldr + col));
+            float rf[8];
+            rr.get(rf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += rf[e];
+        }
+        store8(C + (int64_t)row * ldc + col, v);
     }
 }
 
