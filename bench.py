@@ -484,6 +484,13 @@ def fused_prefill_bytes(d, T, nreq, n_init, act_bytes=2, y_bytes=2):
     return per_tok * T + state * (nreq + n_init) + hist * nreq
 
 
+def cnt_kernels(name):
+    """The kernels a step's counter summary lists, in dispatch order ([] when
+    there is no current summary)."""
+    cnt = step_counters(name)
+    return cnt["kernels"] if cnt else []
+
+
 def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0, name=None):
     """One prefill step (gdn_prefill_fused: conv update -> recurrence -> gated
     norm) over one packed batch.  State and history are re-seeded from device
@@ -538,7 +545,10 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0, name=N
     gbs = nbytes / (ms * 1e-3) / 1e9
     # the binding resource is the one whose peak needs longer for this work
     hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12)
-    roof = {"kernel": "prefill step (gdn_prefill_fused: conv, plan, prep, chain, norm)"}
+    # the launches of the step, as its counter summary lists them
+    roof = {"kernel": "prefill step (gdn_prefill_fused: " + (
+        ", ".join(k.split("<")[0] for k in cnt_kernels(name)) if name and cnt_kernels(name) else
+        "prep, chain, gated norm") + ")"}
     if hbm_bound:
         roof.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(gbs / HBM_PEAK_GBS, 4))
