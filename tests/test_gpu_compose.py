@@ -92,7 +92,8 @@ def oracle_run(case, state_pool, hist_pool):
 CASES = {
     # one 4096-token request: 32-row chain blocks
     "rows_4096": ([4096], [77]),
-    # eight requests: key-head group blocks; cuts at, around and off the chunk
+    # eight requests: whole-head blocks forming the gated output; cuts at, around
+    # and off the chunk
     "group_eight": ([300, 77, 64, 500, 33, 129, 2, 260], [77, 77, 32, 33, 0, 100, 1, 250]),
 }
 

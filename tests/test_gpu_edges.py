@@ -3,9 +3,9 @@
 The regimes of the tutorial page's GDN state lab (a small alpha erases the
 state, a large one keeps it; the delta write stores the prediction error), at
 full head shapes (16 key heads, 48 value heads, d = 128), each through
-  * gdn_prefill_fused with one request (32-row chain blocks) and with eight
-    requests (key-head group blocks),
-  * gdn_prefill_varlen (o visible), and
+  * gdn_prefill_fused with one request (32-row paired chain blocks) and with
+    eight requests (whole-head chain blocks that form the gated output),
+  * gdn_prefill_varlen (o visible; eight requests run key-head group blocks), and
   * gdn_decode_fused, one token per request per step over several steps.
 Inputs come from workloads.edge_case: saturated gates (a, b = +-30, where
 alpha and beta reach 0 or 1 to within 1e-13), tokens whose q and k are exactly
@@ -36,7 +36,7 @@ L2_EPS = 1e-6
 NORM_EPS = 1e-6
 SAT_KINDS = ["frozen", "write", "forget", "zero_qk"]
 ONE_REQ = [301]                                  # 10 chunks, a ragged last one
-EIGHT_REQS = [77, 300, 1, 0, 64, 129, 33, 250]   # 8 x 48 heads >= 256 units: group blocks
+EIGHT_REQS = [77, 300, 1, 0, 64, 129, 33, 250]   # 8 x 48 heads >= 256 units: whole-head / group blocks
 
 
 def oracle_chain(case):
@@ -223,7 +223,7 @@ def test_decode_edges(kind):
 def test_prefill_weak_decay_long(path):
     """alpha ~ 0.98 (a ~ N(-4, 1)): the state keeps ~50 tokens of memory, so
     every chunk's carried term matters, over a 4096-token request (row blocks)
-    and over six requests up to 4096 tokens (group blocks)."""
+    and over six requests up to 4096 tokens (whole-head blocks)."""
     lengths = [4096] if path.endswith("one") else [4096, 1000, 2000, 37, 3000, 512]
     case = edge_case("weak_decay", 540, lengths)
     print(f"weak decay {path}: lengths {lengths}", flush=True)

@@ -1,7 +1,10 @@
 """GPU parity of gdn_prefill_fused's prefix-cache snapshots against the fp64
 oracle (oracle.prefill_snapshots), through the C ABI: outputs, final states,
 the state after every snap_interval tokens in its snapshot slot, snapshot
-histories bit-exact, every other slot untouched."""
+histories bit-exact, every other slot untouched.  Every chain block shape takes
+snapshots: whole-head blocks forming the gated output (>= 256 (request, head)
+units, bf16 y), key-head group blocks (the same units with an fp32 y), 32-row
+paired blocks (few units) and the sequential kernel (d = 16)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +21,7 @@ NORM_EPS = 1e-6
 
 
 def snap_case(which):
-    if which == "d128_group":     # >= 256 (request, head) units: key-head group blocks
+    if which in ("d128_group", "d128_group_f32y"):  # >= 256 (request, head) units
         dims, lens, interval, max_snaps, seed = GdnDims(4, 12, 128, 128, 4), [200, 64, 31, 96, 130] * 5, 64, 3, 71
     elif which == "d128_rows":    # few units: 32-row per-head blocks
         dims, lens, interval, max_snaps, seed = GdnDims(2, 6, 128, 128, 4), [100, 64, 32, 5], 32, 4, 72
@@ -36,10 +39,13 @@ def snap_case(which):
     return case, snaps, interval
 
 
-def run(case, snaps, interval):
+def run(case, snaps, interval, f32y=False):
+    """gdn_prefill_fused with snapshots; a bf16 y for bf16 inputs unless f32y
+    (an fp32 y sends >= 256 units to the key-head group blocks and the separate
+    gated-norm pass instead of whole-head blocks)."""
     d = case.dims
     T = case.num_tokens
-    ydt = torch.bfloat16 if case.x_qkv.dtype == torch.bfloat16 else torch.float32
+    ydt = torch.bfloat16 if case.x_qkv.dtype == torch.bfloat16 and not f32y else torch.float32
     pool, state = dev(case.conv_pool), dev(case.state_pool)
     y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=ydt, device="cuda")
     ws = torch.empty(gdn.gdn_prefill_fused_workspace_bytes(d, T, case.num_reqs), dtype=torch.uint8,
@@ -65,12 +71,13 @@ def written(case, snaps, interval):
                   for j in range(min(lens[r] // interval, snaps.shape[1])))
 
 
-@pytest.mark.parametrize("which", ["d128_group", "d128_rows", "d16_seq"])
+@pytest.mark.parametrize("which", ["d128_group", "d128_group_f32y", "d128_rows", "d16_seq"])
 def test_prefill_snapshots_parity(which):
     case, snaps, interval = snap_case(which)
     assert gdn.gdn_validate_snapshot_metadata(case.qsl, case.slot_ids, snaps, interval,
                                               case.num_tokens, case.num_slots) == 0
-    (y, pool, state), (y_ref, o_ref, hist_ref, st_ref) = run(case, snaps, interval)
+    (y, pool, state), (y_ref, o_ref, hist_ref, st_ref) = run(case, snaps, interval,
+                                                             f32y=which.endswith("f32y"))
     used = sorted(int(s) for s in case.slot_ids)
     ws = written(case, snaps, interval)
     assert ws, "the case must take snapshots"
@@ -88,10 +95,13 @@ def test_prefill_snapshots_parity(which):
     np.testing.assert_array_equal(bits(state)[rest], bits(case.state_pool)[rest])
 
 
-def test_prefill_snapshots_bf16_state():
+@pytest.mark.parametrize("f32y", [False, True])
+def test_prefill_snapshots_bf16_state(f32y):
+    """A bf16 state with snapshots: whole-head blocks (bf16 y) and key-head
+    group blocks (fp32 y)."""
     case, snaps, interval = snap_case("d128_group")
     case.state_pool = case.state_pool.to(torch.bfloat16)
-    (y, pool, state), (y_ref, o_ref, hist_ref, st_ref) = run(case, snaps, interval)
+    (y, pool, state), (y_ref, o_ref, hist_ref, st_ref) = run(case, snaps, interval, f32y=f32y)
     assert rel_l2(f64(y), y_ref) <= OUT_TOL
     ws = written(case, snaps, interval)
     used = sorted(int(s) for s in case.slot_ids)

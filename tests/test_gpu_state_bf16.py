@@ -113,11 +113,13 @@ def test_spec_verify_bf16_state():
         np.testing.assert_array_equal(bits(pool)[s], bits(torch.from_numpy(hist_ref[s]).to(torch.bfloat16)))
 
 
-@pytest.mark.parametrize("which", ["d128_group", "d128_rows", "d16_seq"])
+@pytest.mark.parametrize("which", ["d128_group", "d128_group_f32y", "d128_rows", "d16_seq"])
 def test_prefill_fused_bf16_state(which):
-    """Packed prefill with a bf16 state: the three block shapes of the chunked
-    chain (key-head groups, 32-row blocks) and the sequential kernel (d = 16)."""
-    if which == "d128_group":   # >= 256 (request, head) units: group blocks
+    """Packed prefill with a bf16 state: the block shapes of the chunked chain
+    (whole-head blocks forming the gated output for >= 256 (request, head) units
+    with a bf16 y; key-head group blocks for the same units with an fp32 y;
+    32-row paired blocks for few units) and the sequential kernel (d = 16)."""
+    if which in ("d128_group", "d128_group_f32y"):  # >= 256 (request, head) units
         case = make_gdn_case(61, GdnDims(4, 12, 128, 128, 4), [40, 1, 77, 33] * 6, num_slots=30,
                              permute_slots=True, state_std=0.02, hist_std=1.0, gamma_std=0.1)
     elif which == "d128_rows":  # few units: 32-row per-head blocks
@@ -130,7 +132,8 @@ def test_prefill_fused_bf16_state(which):
     case = bf16_case(case)
     d = case.dims
     T = case.num_tokens
-    ydt = torch.bfloat16 if case.x_qkv.dtype == torch.bfloat16 else torch.float32
+    f32y = which.endswith("f32y")
+    ydt = torch.bfloat16 if case.x_qkv.dtype == torch.bfloat16 and not f32y else torch.float32
     pool, state = dev(case.conv_pool), dev(case.state_pool)
     y = torch.empty((T, d.num_v_heads * d.head_dim_v), dtype=ydt, device="cuda")
     ws = torch.empty(gdn.gdn_prefill_fused_workspace_bytes(d, T, case.num_reqs), dtype=torch.uint8,

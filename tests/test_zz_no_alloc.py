@@ -40,7 +40,8 @@ def run(case, noalloc):
 
 def test_noalloc_matches_workspace_call_twice():
     # first a large batch (32-row chain blocks: 3 requests x 48 heads < 256),
-    # then a smaller one in more requests (key-head group blocks)
+    # then a smaller one in more requests (whole-head chain blocks that form the
+    # gated output)
     cases = [make_gdn_case(701, FULL_DIMS, [1200, 77, 700], num_slots=6, permute_slots=True,
                            state_std=0.02, hist_std=1.0, gamma_std=0.1),
              make_gdn_case(702, FULL_DIMS, [40, 5, 0, 33, 1, 64], num_slots=9, permute_slots=True,
