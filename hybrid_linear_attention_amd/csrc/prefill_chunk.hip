@@ -324,22 +324,23 @@ __device__ __forceinline__ int wave_plan_rank(const WavePlan &p, int nreq, int l
 namespace chunk {
 constexpr int XR = CH + 3;      // staged conv rows: the 3 tokens before the chunk, then its own
 constexpr int XSP = 2 * D + 8;  // padded staged row: q channels, then k channels (bf16)
+// One region, three lives: the staged conv input rows (read by the conv, whose
+// results wait in registers until every read is done), then the hi / lo planes
+// of K and Q (dead once the K image is written and the K K^T / Q K^T tiles,
+// which also wait in registers, are formed), then those tiles and the per-wave
+// work matrices.  34,816 bytes, so four blocks share a CU.
 struct PrepSmem {
-    // the hi / lo planes of K and Q are dead once the K image and the K K^T /
-    // Q K^T tiles are written: the per-wave work matrices then take their place
     union {
+        uint16_t xs[XR][XSP];
         struct { uint16_t Kh[CH][KP], Kl[CH][KP], Qh[CH][KP], Ql[CH][KP]; };
         struct {
+            float KK[CH][AP], QK[CH][AP];
             float A[4][CH][AP];   // per-wave work matrix: A, then T = (I + A)^-1
             float G[4][CH], Beta[4][CH];
         };
     };
-    // the conv input rows are dead once the planes are written
-    union {
-        uint16_t xs[XR][XSP];
-        struct { float KK[CH][AP], QK[CH][AP]; };
-    };
 };
+static_assert(sizeof(PrepSmem) == 4 * CH * KP * 2, "the prep kernel's LDS is the K / Q planes' size");
 }  // namespace chunk
 
 // Conv inputs of the prep kernel's conv mode: q and k of the chunk are formed
@@ -471,7 +472,11 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         // the 16 groups of one token's q (or k) are 16 aligned adjacent lanes
         const int tg = tid / NCG, cgi = tid % NCG;
         uint4 pv[NM];
+        // normalised q / k of this thread's tokens and channels, per pass, kept
+        // until every thread is done reading the staged rows
+        float qk[NPASS][TPT][8];
         load_pass(pv, 0);
+#pragma unroll
         for (int ps = 0; ps < npass_all; ++ps) {
             if (ps) __syncthreads();  // the previous pass is done with the staged rows
             stage_pass(pv, ps);
@@ -518,10 +523,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 }
             }
             {
-                // q or k: SiLU, L2 norm over the head, hi / lo planes
-                const int cq = ps * NCH + 8 * cgi;
-                const bool isk = cq >= D;
-                const int col = cq & (D - 1);
+                // q or k: SiLU, L2 norm over the head
 #pragma unroll
                 for (int j = 0; j < TPT; ++j) {
                     const int t = TPT * tg + j;
@@ -533,11 +535,25 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                     }
                     ss = group_sum<16>(ss);
                     const float inv = 1.0f / sqrtf(ss + cv.l2_eps);
-                    uint16_t *ph = isk ? &sm.Kh[t][col] : &sm.Qh[t][col];
-                    uint16_t *pl = isk ? &sm.Kl[t][col] : &sm.Ql[t][col];
-                    split4_store(y[j][0] * inv, y[j][1] * inv, y[j][2] * inv, y[j][3] * inv, ph, pl);
-                    split4_store(y[j][4] * inv, y[j][5] * inv, y[j][6] * inv, y[j][7] * inv, ph + 4, pl + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qk[ps][j][e] = y[j][e] * inv;
                 }
+            }
+        }
+        // every read of the staged rows is done: q and k into their hi / lo planes
+        __syncthreads();
+#pragma unroll
+        for (int ps = 0; ps < npass_all; ++ps) {
+            const int cq = ps * NCH + 8 * cgi;
+            const bool isk = cq >= D;
+            const int col = cq & (D - 1);
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                const int t = TPT * tg + j;
+                uint16_t *ph = isk ? &sm.Kh[t][col] : &sm.Qh[t][col];
+                uint16_t *pl = isk ? &sm.Kl[t][col] : &sm.Ql[t][col];
+                split4_store(qk[ps][j][0], qk[ps][j][1], qk[ps][j][2], qk[ps][j][3], ph, pl);
+                split4_store(qk[ps][j][4], qk[ps][j][5], qk[ps][j][6], qk[ps][j][7], ph + 4, pl + 4);
             }
         }
     }
@@ -566,27 +582,45 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         }
     }
 
-    // K K^T and Q K^T on the three lower-triangular 16x16 tiles of each
-    for (int item = w; item < 6; item += 4) {
-        const bool isQ = item >= 3;
-        const int n = isQ ? item - 3 : item;
-        const int tm = n == 0 ? 0 : 1;
-        const int tn = n == 2 ? 1 : 0;
-        floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // K K^T and Q K^T on the three lower-triangular 16x16 tiles of each (items
+    // w and w + 4 of this wave), kept in registers until every wave is done
+    // with the planes, whose space the tiles then take
+    floatx4_t kacc[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int off = 32 * ks + 8 * lg;
-            const uint16_t *arow_h = isQ ? sm.Qh[16 * tm + lr] : sm.Kh[16 * tm + lr];
-            const uint16_t *arow_l = isQ ? sm.Ql[16 * tm + lr] : sm.Kl[16 * tm + lr];
-            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(arow_h + off);
-            const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(arow_l + off);
-            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&sm.Kh[16 * tn + lr][off]);
-            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&sm.Kl[16 * tn + lr][off]);
-            mma3(acc, ah, al, bh, bl);
+    for (int ii = 0; ii < 2; ++ii) {
+        const int item = w + 4 * ii;
+        kacc[ii] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        if (item < 6) {
+            const bool isQ = item >= 3;
+            const int n = isQ ? item - 3 : item;
+            const int tm = n == 0 ? 0 : 1;
+            const int tn = n == 2 ? 1 : 0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = 32 * ks + 8 * lg;
+                const uint16_t *arow_h = isQ ? sm.Qh[16 * tm + lr] : sm.Kh[16 * tm + lr];
+                const uint16_t *arow_l = isQ ? sm.Ql[16 * tm + lr] : sm.Kl[16 * tm + lr];
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(arow_h + off);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(arow_l + off);
+                const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&sm.Kh[16 * tn + lr][off]);
+                const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&sm.Kl[16 * tn + lr][off]);
+                mma3(kacc[ii], ah, al, bh, bl);
+            }
         }
-        float(*dst)[AP] = isQ ? sm.QK : sm.KK;
+    }
+    __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[16 * tm + 4 * lg + e][16 * tn + lr] = acc[e];
+    for (int ii = 0; ii < 2; ++ii) {
+        const int item = w + 4 * ii;
+        if (item < 6) {
+            const bool isQ = item >= 3;
+            const int n = isQ ? item - 3 : item;
+            const int tm = n == 0 ? 0 : 1;
+            const int tn = n == 2 ? 1 : 0;
+            float(*dst)[AP] = isQ ? sm.QK : sm.KK;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[16 * tm + 4 * lg + e][16 * tn + lr] = kacc[ii][e];
+        }
     }
     __syncthreads();
 
