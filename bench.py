@@ -419,9 +419,9 @@ def prefill_bytes(d, T, nreq, n_init, act_bytes=4, gate_bytes=2, o_bytes=4):
 
 def bench_layer(steps, dev, stream, torch, np):
     """The full layer block on the mixed batch (8 x 2048 prefill tokens + 256
-    decode tokens, hidden 5120): RMSNorm -> in-projection -> conv1d_update ->
-    prefill_varlen + decode_step -> gated_norm -> out-projection + residual, with
-    every launch timed by events on the stream."""
+    decode tokens, hidden 5120): RMSNorm -> in-projection -> gdn_prefill_fused
+    (prefill requests) and gdn_decode_fused (decode requests) -> out-projection +
+    residual, with every launch timed by events on the stream."""
     from hybrid_linear_attention_amd.layer import GdnLayer, stack_weights
     from hybrid_linear_attention_amd.workloads import layer_mixed
 

@@ -121,7 +121,7 @@ class GdnLayer:
                 out.append(("prefill", lambda: gdn.gdn_prefill_fused(
                     d, x[:T_pf], z[:T_pf], a[:T_pf], b[:T_pf], w.conv_w, w.gamma_out, conv_pool,
                     state_pool, qsl[:n_pf + 1], slot_ids[:n_pf], has_initial[:n_pf], self.y[:T_pf],
-                    self.ws, self.l2_eps, self.norm_eps, stream)))
+                    self.ws, l2_eps=self.l2_eps, norm_eps=self.norm_eps, stream=stream)))
             if self.n_dec:
                 out.append(("decode", lambda: gdn.gdn_decode_fused(
                     d, x[T_pf:], z[T_pf:], a[T_pf:], b[T_pf:], w.conv_w, w.gamma_out, conv_pool,

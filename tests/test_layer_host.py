@@ -58,3 +58,37 @@ def test_layer_rejects_inconsistent_batch():
                         torch.ones(d.head_dim_v), device="cpu")
     with pytest.raises(ValueError):
         GdnLayer(d, bad, 10, 1, 8, 2, device="cpu")
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+def test_every_stage_gets_the_stream(monkeypatch, fused):
+    """Each launch of GdnLayer.stages binds the stream it is given to the entry
+    point's `stream` parameter (an argument passed by position into the wrong
+    slot would go unnoticed with the default stream)."""
+    import inspect
+
+    from hybrid_linear_attention_amd import gdn
+
+    d = TINY_DIMS
+    hidden, T = 24, 5
+    cq = 2 * d.num_k_heads * d.head_dim_k + d.num_v_heads * d.head_dim_v
+    cz = d.num_v_heads * d.head_dim_v
+    w = stack_weights(d, torch.zeros(hidden, cq + cz), torch.zeros(hidden, 2 * d.num_v_heads),
+                      torch.zeros(cz, hidden), torch.zeros(cq, 4), torch.ones(hidden),
+                      torch.ones(d.head_dim_v), device="cpu")
+    layer = GdnLayer(d, w, T, 1, T - 2, 2, device="cpu", fused=fused)
+    seen = []
+    for name in ("gdn_rmsnorm", "gdn_gemm_bf16", "gdn_prefill_fused", "gdn_decode_fused",
+                 "gdn_conv1d_update", "gdn_prefill_varlen", "gdn_decode_step", "gdn_gated_norm"):
+        orig = getattr(gdn, name)
+
+        def rec(*args, _orig=orig, _name=name, **kw):
+            bound = inspect.signature(_orig).bind(*args, **kw)
+            seen.append((_name, bound.arguments.get("stream")))
+        monkeypatch.setattr(gdn, name, rec)
+    sentinel = object()
+    meta = torch.zeros(4, dtype=torch.int32)
+    for _, fn in layer.stages(torch.zeros(T, hidden), None, None, meta, meta, meta, sentinel):
+        fn()
+    assert len(seen) == (5 if fused else 7)
+    assert all(s is sentinel for _, s in seen), seen
