@@ -447,15 +447,17 @@ def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16, x_pad=0):
 
 
 @pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d128_group_f32y", "d32_seq",
-                                   "d128_unaligned_rows", "d128_many_requests"])
+                                   "d128_unaligned_rows", "d128_many_requests", "d128_f32x_rows",
+                                   "d128_f32x_heads"])
 def test_prefill_fused_parity(which):
     """One prefill step through gdn_prefill_fused against the fp64 oracle chain:
     32-row chain blocks (few heads x requests); whole-head blocks that form the
     gated output themselves (>= 256 (request, head) units, bf16 y); key-head
     group blocks with the separate gated-norm pass (the same units, fp32 y); the
-    sequential kernel for d = 32; and x rows that are not 16-byte aligned (the
+    sequential kernel for d = 32; x rows that are not 16-byte aligned (the
     conv pass then forms q and k before the prep kernel instead of the prep
-    kernel forming them from x)."""
+    kernel forming them from x); and fp32 activations (the prep kernel convolves
+    the q and k channels in two passes), with few units and with >= 256."""
     x_pad = 0
     y_dtype = torch.bfloat16
     if which == "d128_split_rows":
@@ -469,6 +471,14 @@ def test_prefill_fused_parity(which):
         case = varlen_case(42, lengths=lens, num_slots=60)
         if which == "d128_group_f32y":
             y_dtype = torch.float32
+    elif which == "d128_f32x_rows":
+        case = varlen_case(46, lengths=(1, 2, 5, 37, 0, 130, 3), num_slots=10, dtype=torch.float32)
+        y_dtype = torch.float32
+    elif which == "d128_f32x_heads":
+        rng = np.random.default_rng(47)
+        lens = [int(x) for x in rng.integers(0, 70, 48)]
+        case = varlen_case(47, lengths=lens, num_slots=60, dtype=torch.float32)
+        y_dtype = torch.float32
     elif which == "d128_many_requests":
         # more than 64 requests: the chunk plan comes from the plan kernel
         rng = np.random.default_rng(45)
