@@ -6,7 +6,8 @@ full head shapes (16 key heads, 48 value heads, d = 128), each through
   * gdn_prefill_fused with one request (32-row paired chain blocks) and with
     eight requests (whole-head chain blocks that form the gated output),
   * gdn_prefill_varlen (o visible; eight requests run key-head group blocks), and
-  * gdn_decode_fused, one token per request per step over several steps.
+  * gdn_decode_fused, one token per request per step over several steps, and
+  * gdn_spec_verify, four tokens per request with every token's state kept.
 Inputs come from workloads.edge_case: saturated gates (a, b = +-30, where
 alpha and beta reach 0 or 1 to within 1e-13), tokens whose q and k are exactly
 zero, and the weak-decay regime alpha ~ 0.98 over a 4096-token request.
@@ -232,3 +233,32 @@ def test_prefill_weak_decay_long(path):
     alpha, _ = oracle.gates(f64(case.a), f64(case.b))
     print(f"mean alpha {alpha.mean():.4f}, mean chunk decay {np.mean(alpha ** 32):.3f}")
     check_against_oracle(case, run, ref)
+
+
+@pytest.mark.parametrize("kind", SAT_KINDS + ["weak_decay"])
+def test_spec_verify_edges(kind):
+    """gdn_spec_verify at the edge gates: 24 requests x 4 tokens (the last accepted
+    token and three drafts), the state and history after every token in a slot of
+    its own, against the oracle at the fp32 bars (the verify kernel's arithmetic is
+    the decode step's), and the kind's closed form on the state after each
+    request's last token."""
+    from test_gpu_spec import check as spec_check
+    from test_gpu_spec import run_gpu as spec_run
+
+    R, n = 24, 4
+    kinds = SAT_KINDS + ["weak_decay"]
+    case = edge_case(kind, 560 + kinds.index(kind), [n] * R, num_slots=R * (n + 1) + 3)
+    used = set(int(s) for s in case.slot_ids)
+    free = [s for s in range(case.num_slots) if s not in used]
+    spec = torch.tensor(free[:R * n], dtype=torch.int32).reshape(R, n)
+    assert gdn.gdn_validate_spec_metadata(case.qsl, case.slot_ids, spec, case.num_tokens,
+                                          case.num_slots) == 0
+    print(f"spec verify {kind}: {R} requests x {n} tokens", flush=True)
+    y, o, pool, state = spec_run(case, spec, torch.bfloat16)
+    spec_check(case, spec, torch.bfloat16, y, o, pool, state)
+    if kind != "weak_decay":
+        # the state after each request's last token, placed in the request's slot
+        final = state.cpu().clone()
+        for r, s in enumerate(case.slot_ids.tolist()):
+            final[s] = state[int(spec[r, n - 1])].cpu()
+        check_closed_form(case, dict(state=final, y=y.cpu(), o=o.cpu()), oracle_chain(case))
