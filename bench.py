@@ -714,9 +714,9 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa, fp8=False):
         "gpu_ms_per_step": round(gpu, 4),
         "tokens_per_s": round(R / (wall * 1e-3), 1),
         "kv_gbs": round(kv_b / (gpu * 1e-3) / 1e9, 1),
-        # call level (three launches between the events); the counters are the
+        # call level (two launches between the events); the counters are the
         # attention kernel's alone, which moves all but ~3 MB of the call's bytes
-        "roofline": {"kernel": "gqa_decode_paged (rope_append, attn_split, combine)", "bound": "hbm",
+        "roofline": {"kernel": "gqa_decode_paged (attn_split with RoPE and append, combine)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
                      "traffic": None,

@@ -8,13 +8,16 @@
 // and values live in fixed-size pages reached through a per-request block
 // table.
 //
-// Three launches:
-//  1. rope_append: per (request, head), rotates q or k of the new token at
-//     position L - 1 in fp64, keeps q in fp32 for the attention pass and
-//     stores the rotated k and v into the token's page: rounded once to bf16,
-//     or (an fp8 cache) the e4m3 codes nearest to k / k_scale and v / v_scale.
-//  2. attn_split: one block per (request, key/value head, run of 512
-//     positions); 4 waves of 128 positions, 16 at a time.  Scores q . K^T on
+// Two launches:
+//  1. attn_split: one block per (request, key/value head, run of 512
+//     positions); 4 waves of 128 positions, 16 at a time.  Each block first
+//     rotates q of the new token (position L - 1) in fp64 for its group of
+//     query heads (one angle per dim, shared by the group) and rounds it to
+//     fp32; the block whose run holds position L - 1 also rotates k and stores
+//     the rotated k and v into the token's page before it reads any position:
+//     rounded once to bf16, or (an fp8 cache) the e4m3 codes nearest to
+//     k / k_scale and v / v_scale.  No other block reads that row (another
+//     run, request or key/value head reads other rows).  Scores q . K^T on
 //     v_mfma_f32_16x16x32_bf16 (rows: the <= 8 query heads of the group, q
 //     split into three bf16 terms so that the scores keep fp32 accuracy
 //     against the exact bf16 K); an online softmax in base 2 across the 16
@@ -26,7 +29,7 @@
 //     K fragments) or the LDS tile (the V rows); k_scale rides on q and
 //     v_scale on the combine.  The block merges its 4 waves and writes one
 //     partial (max, sum, unnormalised o) per query head.
-//  3. combine: per (request, query head), merges the partials of the
+//  2. combine: per (request, query head), merges the partials of the
 //     request's runs, applies the sigmoid gate and writes y (and o).  (A
 //     separate launch: merging in the last block of each group would need a
 //     device-scope release per block, which writes back the L2 of every
@@ -83,52 +86,6 @@ __device__ __forceinline__ uint8_t e4m3_from_f64(double x) {
     return sign | (uint8_t)(((er - 1 + 7) << 3) | (int)((m * 2.0 - 1.0) * 8.0));
 }
 
-// TC: uint16_t (bf16 bits) or uint8_t (e4m3 codes at k_scale, v_scale)
-template <typename TA, typename TC>
-__global__ __launch_bounds__(D) void gqa_rope_append_kernel(
-    const TA *__restrict__ q, int64_t q_ld, const TA *__restrict__ k, const TA *__restrict__ v,
-    int64_t kv_ld, TC *__restrict__ kc, TC *__restrict__ vc, float k_scale, float v_scale,
-    const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens,
-    int32_t Hq, int32_t Hkv, int32_t rd, int32_t P, int32_t num_pages, int32_t lmax, double theta,
-    float *__restrict__ qrot) {
-    // block (request r, head hh): hh < Hq a query head, else key/value head hh - Hq
-    const int r = blockIdx.x;
-    const int hh = blockIdx.y;
-    const int d = threadIdx.x;
-    const int L = lens[r];
-    if (L < 1 || L > lmax) return;  // skipped request
-    const int pos = L - 1;
-    const int half = rd / 2;
-    const bool is_q = hh < Hq;
-    const TA *row = is_q ? q + (int64_t)r * q_ld + hh * D : k + (int64_t)r * kv_ld + (hh - Hq) * D;
-    // x'_d = x_d cos + sgn x_partner sin over the rotated dims
-    double val = to_f32(row[d]);
-    if (d < rd) {
-        const int i = d < half ? d : d - half;
-        const int partner = d < half ? d + half : d - half;
-        double c, s;
-        sincos((double)pos * pow(theta, -2.0 * i / rd), &s, &c);
-        const double xp = to_f32(row[partner]);
-        val = d < half ? val * c - xp * s : val * c + xp * s;
-    }
-    if (is_q) {
-        qrot[((int64_t)r * Hq + hh) * D + d] = (float)val;
-        return;
-    }
-    const int pg = bt[(int64_t)r * max_pages + pos / P];
-    if (pg < 0 || pg >= num_pages) return;  // contract broken: no append
-    const int j = hh - Hq;
-    const int64_t dst = (((int64_t)pg * Hkv + j) * P + pos % P) * D + d;
-    const float vin = to_f32(v[(int64_t)r * kv_ld + j * D + d]);
-    if constexpr (sizeof(TC) == 1) {
-        kc[dst] = e4m3_from_f64(val / (double)k_scale);
-        vc[dst] = e4m3_from_f64((double)vin / (double)v_scale);
-    } else {
-        kc[dst] = bf16_from_f64(val);
-        vc[dst] = to_bf16(vin).bits;
-    }
-}
-
 // max over the 16 lanes of a row (same butterfly as group_sum)
 __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f(v, 0));
@@ -182,12 +139,13 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
 
 // FP8: the cache holds e4m3 codes (k_scale folded into qscale by the host,
 // v_scale applied by the combine); otherwise bf16.
-template <int G, bool FP8>
+template <int G, bool FP8, typename TA>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2))) void gqa_attn_split_kernel(
-    const float *__restrict__ qrot, const void *__restrict__ kc, const void *__restrict__ vc,
+    const TA *__restrict__ q, int64_t q_ld, const TA *__restrict__ knew, const TA *__restrict__ vnew,
+    int64_t kv_ld, void *__restrict__ kc, void *__restrict__ vc, float k_scale, float v_scale,
     const int32_t *__restrict__ bt, int32_t max_pages, const int32_t *__restrict__ lens, int32_t Hq,
-    int32_t Hkv, int32_t P, int32_t num_pages, int32_t lmax, int32_t nsplit, float qscale,
-    float *__restrict__ po, float2 *__restrict__ pml) {
+    int32_t Hkv, int32_t rd, int32_t P, int32_t num_pages, int32_t lmax, int32_t nsplit, double theta,
+    float qscale, float *__restrict__ po, float2 *__restrict__ pml) {
     static_assert(G >= 1 && G <= GMAX, "query heads per key/value head");
     static_assert(G * D * 4 <= WREG, "the merge reuses a wave's region");
     // q terms (bf16 bits) for all 16 MFMA rows (rows >= G zero); rows padded by
@@ -210,20 +168,55 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
     uint8_t *const vt = wreg[w];
     uint8_t *const pt = wreg[w] + PT_OFF;
 
-    // rotated q of the group, scaled by log2(e) / sqrt(D), as hi + mid + lo bf16
+    // RoPE of the new token (position L - 1) in fp64: x'_d = x_d cos + sgn
+    // x_partner sin over the first rd dims, the angle of dim d shared by every
+    // head of the group.  The group's q values are loaded first; the angle and
+    // the rotation wait until the first tiles' cache loads are in flight.
+    const int pos = L - 1;
+    const int half = rd / 2;
+    const bool rot = tid < rd;
+    const int partner = rot ? (tid < half ? tid + half : tid - half) : tid;
+    float qv[G], qp[G];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const float x = m < G ? qrot[((int64_t)r * Hq + g * G + m) * D + tid] * qscale : 0.f;
-        const uint16_t h0 = bf16_rne_bits(x);
-        const float r1 = x - __uint_as_float(uint32_t(h0) << 16);
-        const uint16_t h1 = bf16_rne_bits(r1);
-        const float r2 = r1 - __uint_as_float(uint32_t(h1) << 16);
-        qf[0][m][tid] = h0;
-        qf[1][m][tid] = h1;
-        qf[2][m][tid] = bf16_rne_bits(r2);
+    for (int m = 0; m < G; ++m) {
+        const TA *row = q + (int64_t)r * q_ld + (g * G + m) * D;
+        qv[m] = to_f32(row[tid]);
+        qp[m] = to_f32(row[partner]);
     }
-    // p rows of heads 8 .. 15 are never written: zero them once
-    for (int e = lane; e < 2 * 16 * 16 / 2; e += 64) reinterpret_cast<uint32_t *>(pt)[e] = 0u;
+    double cs = 1.0, sn = 0.0;
+    auto angle = [&]() {
+        if (rot) {
+            const int i = tid < half ? tid : tid - half;
+            sincos((double)pos * pow(theta, -2.0 * i / rd), &sn, &cs);
+        }
+    };
+    auto rope = [&](float x, float xp) -> double {
+        double val = x;
+        if (rot) val = tid < half ? val * cs - (double)xp * sn : val * cs + (double)xp * sn;
+        return val;
+    };
+    // the run holding the new token appends its rotated k and its v before it
+    // reads any position (the barrier below orders the stores before the loads
+    // of every wave)
+    const bool appender = s == pos / SPLIT;
+    if (appender) {
+        angle();
+        const int pg = bt[(int64_t)r * max_pages + pos / P];
+        if (pg >= 0 && pg < num_pages) {  // else the contract is broken: no append
+            const TA *krow = knew + (int64_t)r * kv_ld + g * D;
+            const double kval = rope(to_f32(krow[tid]), to_f32(krow[partner]));
+            const float vin = to_f32(vnew[(int64_t)r * kv_ld + g * D + tid]);
+            const int64_t dst = (((int64_t)pg * Hkv + g) * P + pos % P) * D + tid;
+            if constexpr (FP8) {
+                static_cast<uint8_t *>(kc)[dst] = e4m3_from_f64(kval / (double)k_scale);
+                static_cast<uint8_t *>(vc)[dst] = e4m3_from_f64((double)vin / (double)v_scale);
+            } else {
+                static_cast<uint16_t *>(kc)[dst] = bf16_from_f64(kval);
+                static_cast<uint16_t *>(vc)[dst] = to_bf16(vin).bits;
+            }
+        }
+        __threadfence_block();
+    }
     __syncthreads();
 
     const int wk0 = k0 + w * WKEYS;
@@ -311,6 +304,24 @@ __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
     // the scheduler keeps the phases below in program order: loads issued
     // early stay early, and no wait for a later load lands in front of one
     // for an earlier load (wait counts complete in order)
+    __builtin_amdgcn_sched_barrier(0);
+    // rotated q of the group (rounded to fp32), scaled by log2(e) / sqrt(D), as
+    // hi + mid + lo bf16, while the first tiles land
+    if (!appender) angle();
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const float x = m < G ? (float)rope(qv[m], qp[m]) * qscale : 0.f;
+        const uint16_t h0 = bf16_rne_bits(x);
+        const float r1 = x - __uint_as_float(uint32_t(h0) << 16);
+        const uint16_t h1 = bf16_rne_bits(r1);
+        const float r2 = r1 - __uint_as_float(uint32_t(h1) << 16);
+        qf[0][m][tid] = h0;
+        qf[1][m][tid] = h1;
+        qf[2][m][tid] = bf16_rne_bits(r2);
+    }
+    // p rows of heads 8 .. 15 are never written: zero them once
+    for (int e = lane; e < 2 * 16 * 16 / 2; e += 64) reinterpret_cast<uint32_t *>(pt)[e] = 0u;
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     // transposed-read offsets: lane 4j + q of group kg reads row 4 kg + j,
     // columns 4q .. 4q + 3
@@ -495,29 +506,31 @@ __global__ __launch_bounds__(D) void gqa_combine_kernel(
     y[(int64_t)rh * D + d] = from_f32<TY>(out / (1.0f + expf(-gt)));
 }
 
-template <int G, bool FP8>
-static hipError_t launch_attn(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float *qrot,
-                              float2 *pml, float *po) {
-    const float qscale = 1.4426950408889634f / sqrtf((float)D) * a.k_scale;
+template <int G, bool FP8, typename TA>
+static hipError_t launch_attn(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float2 *pml,
+                              float *po) {
+    // an fp8 cache: k_scale rides on q (the MFMAs see the codes), v_scale on the combine
+    const float qscale = 1.4426950408889634f / sqrtf((float)D) * (FP8 ? a.k_scale : 1.f);
     const int64_t blocks = (int64_t)a.R * a.Hkv * nsplit;
-    hipLaunchKernelGGL((gqa_attn_split_kernel<G, FP8>), dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st, qrot,
-                       a.k_cache, a.v_cache, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.P, a.num_pages, lmax,
-                       nsplit, qscale, po, pml);
+    hipLaunchKernelGGL((gqa_attn_split_kernel<G, FP8, TA>), dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st,
+                       (const TA *)a.q, a.q_ld, (const TA *)a.k, (const TA *)a.v, a.kv_ld, a.k_cache, a.v_cache,
+                       FP8 ? a.k_scale : 1.f, FP8 ? a.v_scale : 1.f, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv,
+                       a.rd, a.P, a.num_pages, lmax, nsplit, a.theta, qscale, po, pml);
     return hipGetLastError();
 }
 
-template <bool FP8>
-static hipError_t launch_attn_g(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float *qrot,
-                                float2 *pml, float *po) {
+template <bool FP8, typename TA>
+static hipError_t launch_attn_g(const GqaArgs &a, hipStream_t st, int32_t lmax, int32_t nsplit, float2 *pml,
+                                float *po) {
     switch (a.Hq / a.Hkv) {
-        case 1: return launch_attn<1, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        case 2: return launch_attn<2, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        case 3: return launch_attn<3, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        case 4: return launch_attn<4, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        case 5: return launch_attn<5, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        case 6: return launch_attn<6, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        case 7: return launch_attn<7, FP8>(a, st, lmax, nsplit, qrot, pml, po);
-        default: return launch_attn<8, FP8>(a, st, lmax, nsplit, qrot, pml, po);
+        case 1: return launch_attn<1, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        case 2: return launch_attn<2, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        case 3: return launch_attn<3, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        case 4: return launch_attn<4, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        case 5: return launch_attn<5, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        case 6: return launch_attn<6, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        case 7: return launch_attn<7, FP8, TA>(a, st, lmax, nsplit, pml, po);
+        default: return launch_attn<8, FP8, TA>(a, st, lmax, nsplit, pml, po);
     }
 }
 
@@ -526,24 +539,10 @@ static hipError_t launch_all(const GqaArgs &a, hipStream_t st) {
     const int64_t lmax64 = std::min<int64_t>(a.max_ctx, (int64_t)a.max_pages * a.P);
     const int32_t lmax = (int32_t)lmax64;
     const int32_t nsplit = (a.max_ctx + SPLIT - 1) / SPLIT;
-    float *qrot = (float *)a.ws;
-    float2 *pml = (float2 *)((uint8_t *)a.ws + gqa_ws_qrot_bytes(a.R, a.Hq));
+    float2 *pml = (float2 *)a.ws;
     float *po = (float *)((uint8_t *)pml + gqa_ws_ml_bytes(a.R, a.Hq, nsplit));
-    const dim3 rgrid(a.R, a.Hq + a.Hkv);
-    if (a.kv_fp8)
-        hipLaunchKernelGGL((gqa_rope_append_kernel<TA, uint8_t>), rgrid, dim3(D), 0, st, (const TA *)a.q, a.q_ld,
-                           (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint8_t *)a.k_cache, (uint8_t *)a.v_cache,
-                           a.k_scale, a.v_scale, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages,
-                           lmax, a.theta, qrot);
-    else
-        hipLaunchKernelGGL((gqa_rope_append_kernel<TA, uint16_t>), rgrid, dim3(D), 0, st, (const TA *)a.q, a.q_ld,
-                           (const TA *)a.k, (const TA *)a.v, a.kv_ld, (uint16_t *)a.k_cache, (uint16_t *)a.v_cache,
-                           1.f, 1.f, a.bt, a.max_pages, a.lens, a.Hq, a.Hkv, a.rd, a.P, a.num_pages, lmax, a.theta,
-                           qrot);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = a.kv_fp8 ? launch_attn_g<true>(a, st, lmax, nsplit, qrot, pml, po)
-                 : launch_attn_g<false>(a, st, lmax, nsplit, qrot, pml, po);
+    hipError_t e = a.kv_fp8 ? launch_attn_g<true, TA>(a, st, lmax, nsplit, pml, po)
+                            : launch_attn_g<false, TA>(a, st, lmax, nsplit, pml, po);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gqa_combine_kernel<TA, TY>), dim3((unsigned)(a.R * a.Hq)), dim3(D), 0, st, po, pml,
                        (const TA *)a.gate, a.gate_ld, a.lens, a.Hq, lmax, nsplit, a.v_scale, (TY *)a.y, a.o);
@@ -552,13 +551,12 @@ static hipError_t launch_all(const GqaArgs &a, hipStream_t st) {
 
 }  // namespace gqa
 
-size_t gqa_ws_qrot_bytes(int64_t R, int64_t Hq) { return (size_t)(R * Hq * gqa::D * 4); }
 size_t gqa_ws_ml_bytes(int64_t R, int64_t Hq, int64_t nsplit) {
     return (size_t)((R * Hq * nsplit * 8 + 255) / 256 * 256);
 }
 size_t gqa_ws_bytes(int64_t R, int64_t Hq, int64_t max_ctx) {
     const int64_t nsplit = (max_ctx + gqa::SPLIT - 1) / gqa::SPLIT;
-    return gqa_ws_qrot_bytes(R, Hq) + gqa_ws_ml_bytes(R, Hq, nsplit) + (size_t)(R * Hq * nsplit * gqa::D * 4);
+    return gqa_ws_ml_bytes(R, Hq, nsplit) + (size_t)(R * Hq * nsplit * gqa::D * 4);
 }
 
 hipError_t launch_gqa_decode(const GqaArgs &a, hipStream_t s) {

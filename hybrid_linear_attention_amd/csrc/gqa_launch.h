@@ -27,9 +27,8 @@ struct GqaArgs {
     void *ws;
 };
 
-// workspace: rotated q (fp32 [R, Hq, 256]) | partial (max, sum) per (request,
-// query head, run of positions) | partial o (fp32, 256 per partial)
-size_t gqa_ws_qrot_bytes(int64_t R, int64_t Hq);
+// workspace: partial (max, sum) per (request, query head, run of positions) |
+// partial o (fp32, 256 per partial)
 size_t gqa_ws_ml_bytes(int64_t R, int64_t Hq, int64_t nsplit);
 size_t gqa_ws_bytes(int64_t R, int64_t Hq, int64_t max_ctx);
 

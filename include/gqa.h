@@ -50,8 +50,8 @@ typedef struct gqa_dims {
 #define GQA_SPLIT_KEYS 512
 
 /* Workspace bytes gqa_decode_paged needs for num_reqs requests whose context
- * lengths are at most max_context_len: the rotated queries (fp32 [R, Hq, D])
- * and one partial result per (request, query head, block of GQA_SPLIT_KEYS
+ * lengths are at most max_context_len: one partial result (max, sum and
+ * unnormalised o) per (request, query head, block of GQA_SPLIT_KEYS
  * positions).  0 for invalid arguments. */
 size_t gqa_decode_workspace_bytes(const gqa_dims *dims, int32_t num_reqs, int32_t max_context_len);
 

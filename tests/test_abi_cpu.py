@@ -357,7 +357,8 @@ def test_gqa_empty_batch_and_workspace_query():
     lib = gdn.lib()
     ws = lib.gqa_decode_workspace_bytes(ctypes.byref(GQA), 64, 3584)
     nsplit = (3584 + 511) // 512      # GQA_SPLIT_KEYS positions per partial
-    assert ws == 64 * 24 * 256 * 4 + (64 * 24 * nsplit * 8 + 255) // 256 * 256 + 64 * 24 * nsplit * 256 * 4
+    # partial (max, sum) per (request, query head, run), 256-byte aligned, then the partial o
+    assert ws == (64 * 24 * nsplit * 8 + 255) // 256 * 256 + 64 * 24 * nsplit * 256 * 4
     assert lib.gqa_decode_workspace_bytes(ctypes.byref(gdn.GqaDimsC(24, 4, 128, 64)), 64, 10) == 0
     assert lib.gqa_decode_workspace_bytes(ctypes.byref(GQA), 64, 0) == 0
 
