@@ -441,17 +441,21 @@ def bench_layer(steps, dev, stream, torch, np):
     stages = layer.stages(X, pool, state, qsl, slots, hinit)
     names = [n for n, _ in stages]
     per, tot = {n: [] for n in names}, []
+    # every step enqueued before the one synchronisation, so that no step's events
+    # also time the host launching onto an idle GPU
+    evs = []
     for it in range(steps + 1):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
         ev[0].record(stream)
         for i, (_, fn) in enumerate(stages):
             fn()
             ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        if it > 0:
-            for i, n in enumerate(names):
-                per[n].append(ev[i].elapsed_time(ev[i + 1]))
-            tot.append(ev[0].elapsed_time(ev[-1]))
+        evs.append(ev)
+    torch.cuda.synchronize()
+    for ev in evs[1:]:  # the first step is warm-up
+        for i, n in enumerate(names):
+            per[n].append(ev[i].elapsed_time(ev[i + 1]))
+        tot.append(ev[0].elapsed_time(ev[-1]))
     med = {n: float(np.median(v)) for n, v in per.items()}
     ms = float(np.median(tot))
     hidden = X.shape[1]
@@ -522,7 +526,10 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0, name=N
     ws = torch.empty(gdn.gdn_prefill_fused_workspace_bytes(d, T, c.num_reqs), dtype=torch.uint8,
                      device=dev)
     sh = stream.cuda_stream
-    times = []
+    # every step (re-seed copies, then the timed call) is enqueued before the one
+    # synchronisation: the events time the call's kernels, not the host launching
+    # them onto an idle GPU
+    evs = []
     for it in range(steps + 1):
         pool.copy_(pool0)
         state.copy_(state0)
@@ -532,9 +539,9 @@ def bench_prefill(c, steps, dev, stream, torch, gdn, np, snap_interval=0, name=N
                               l2_eps=L2_EPS, norm_eps=NORM_EPS, snap_slot_ids=snaps,
                               snap_interval=snap_interval, stream=sh)
         e1.record(stream)
-        torch.cuda.synchronize()
-        if it > 0:  # first pass is warm-up
-            times.append(e0.elapsed_time(e1))
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    times = [e0.elapsed_time(e1) for e0, e1 in evs[1:]]  # the first step is warm-up
     ms = float(np.median(times))
     if snap_interval:
         return {"snap_interval": snap_interval, "snapshots": nsnap, "ms_per_step": round(ms, 4),
