@@ -102,8 +102,9 @@ FP8 = torch.float8_e4m3fn
                                    "fp8_pages16", "fp8_scaled", "fp8_g8_f32"])
 def test_gqa_decode_parity(which):
     y_dtype = torch.bfloat16
-    if which == "pages16":     # lengths around the 16-position tiles and 256-position runs
-        case = make_gqa_case(81, [1, 2, 15, 16, 17, 255, 256, 257, 700, 64], 16)
+    if which == "pages16":     # lengths around the 16-position tiles and 512-position runs (the
+        # new token alone in its run at 513 and 1025: that block appends, then reads only it)
+        case = make_gqa_case(81, [1, 2, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1025, 700, 64], 16)
     elif which == "pages1":    # every position on a page of its own
         case = make_gqa_case(82, [1, 3, 40, 300], 1)
     elif which == "pages100":  # a page size that is no power of two, a tile straddling pages
@@ -115,7 +116,8 @@ def test_gqa_decode_parity(which):
     elif which == "g1_norope":  # one query head per kv head, no rotation
         case = make_gqa_case(85, [20, 290], 32, dims=GqaDims(8, 8, 256, 0))
     elif which == "fp8_pages16":  # e4m3 cache at scale 1
-        case = make_gqa_case(87, [1, 2, 15, 16, 17, 255, 256, 257, 700, 64], 16, cache_dtype=FP8)
+        case = make_gqa_case(87, [1, 2, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1025, 700, 64], 16,
+                             cache_dtype=FP8)
     elif which == "fp8_scaled":   # e4m3 cache with per-cache scales, a page size that is no power of two
         case = make_gqa_case(88, [530, 1, 1200, 99], 100, cache_dtype=FP8, k_scale=0.0625, v_scale=0.75)
     else:                         # e4m3 cache, 8 query heads per kv head, fp32 activations and y
