@@ -723,12 +723,13 @@ def bench_gqa(steps, warmup, dev, stream, torch, gqa, fp8=False):
         "kv_gbs": round(kv_b / (gpu * 1e-3) / 1e9, 1),
         # call level (two launches between the events); the counters are the
         # attention kernel's alone, which moves all but ~3 MB of the call's bytes
+        # (the combine's partials and y are not in `traffic`)
         "roofline": {"kernel": "gqa_decode_paged (attn_split with RoPE and append, combine)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
-                     "traffic": None,
-                     "attn_split_kernel_hbm_bytes": measured_traffic(
+                     "traffic": measured_traffic(
                          "gqa_attn_split_kernel_fp8" if fp8 else "gqa_attn_split_kernel", "gqa_decode.hip"),
+                     "traffic_kernel": "gqa_attn_split_kernel",
                      "attn_split_kernel_kv_bytes": kv_b},
     }
 
