@@ -485,24 +485,49 @@ __global__ __launch_bounds__(D) void gqa_combine_kernel(
     const int rh = blockIdx.x;
     const int r = rh / Hq, h = rh % Hq;
     const int d = threadIdx.x;
+    // the gate and, for up to NSR runs, every partial are loaded together (one
+    // round trip after the length instead of three)
+    constexpr int NSR = 8;
+    const float gt = to_f32(gate[(int64_t)r * gate_ld + h * D + d]);
     const int L = lens[r];
     float out = 0.f;
     if (L >= 1 && L <= lmax) {
         const int ns = (L + SPLIT - 1) / SPLIT;
         const float2 *ml = pml + (int64_t)rh * nsplit;
-        float mx = -INFINITY;
-        for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[s].x);
+        const float *pd = po + (int64_t)rh * nsplit * D + d;
         float num = 0.f, den = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const float2 e = ml[s];
-            const float wgt = __builtin_amdgcn_exp2f(e.x - mx);
-            den = fmaf(wgt, e.y, den);
-            num = fmaf(wgt, po[((int64_t)rh * nsplit + s) * D + d], num);
+        if (ns <= NSR) {
+            float2 e[NSR];
+            float pv[NSR];
+#pragma unroll
+            for (int s = 0; s < NSR; ++s) {
+                e[s] = s < ns ? ml[s] : make_float2(-INFINITY, 0.f);
+                pv[s] = s < ns ? pd[(int64_t)s * D] : 0.f;
+            }
+            float mx = e[0].x;
+#pragma unroll
+            for (int s = 1; s < NSR; ++s) mx = fmaxf(mx, e[s].x);
+#pragma unroll
+            for (int s = 0; s < NSR; ++s) {
+                if (s < ns) {
+                    const float wgt = __builtin_amdgcn_exp2f(e[s].x - mx);
+                    den = fmaf(wgt, e[s].y, den);
+                    num = fmaf(wgt, pv[s], num);
+                }
+            }
+        } else {
+            float mx = -INFINITY;
+            for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[s].x);
+            for (int s = 0; s < ns; ++s) {
+                const float2 e = ml[s];
+                const float wgt = __builtin_amdgcn_exp2f(e.x - mx);
+                den = fmaf(wgt, e.y, den);
+                num = fmaf(wgt, pd[(int64_t)s * D], num);
+            }
         }
         out = num / den * v_scale;
     }
     if (o != nullptr) o[(int64_t)rh * D + d] = out;
-    const float gt = to_f32(gate[(int64_t)r * gate_ld + h * D + d]);
     y[(int64_t)rh * D + d] = from_f32<TY>(out / (1.0f + expf(-gt)));
 }
 
