@@ -131,6 +131,18 @@ def test_gqa_decode_parity(which):
     check(case, y, o, kc, vc, y_dtype)
 
 
+@pytest.mark.parametrize("hq,hkv,rd,fp8", [(4, 2, 64, False), (6, 2, 32, False), (8, 2, 128, True),
+                                          (5, 1, 64, False), (7, 1, 2, True)])
+def test_gqa_decode_head_ratios(hq, hkv, rd, fp8):
+    """The query heads per key/value head the kernel is built for beside 1, 6
+    and 8 (2, 3, 4, 5, 7), each with the new token alone in its run (513) and
+    at a page's first position (17), on a bf16 or an e4m3 cache."""
+    kw = dict(cache_dtype=FP8, k_scale=0.5, v_scale=2.0) if fp8 else {}
+    case = make_gqa_case(100 + hq * 8 + hkv, [513, 17, 1, 300], 16, dims=GqaDims(hq, hkv, 256, rd), **kw)
+    y, o, kc, vc = run_gpu(case)
+    check(case, y, o, kc, vc)
+
+
 def test_gqa_skipped_request_and_slack_context_bound():
     """A request whose length is 0 is skipped (zero rows, cache untouched) and
     max_context_len may exceed every length (extra runs of positions exit)."""
