@@ -295,6 +295,10 @@ def check_state_slots(case, got, ref, tol):
 def fused_case(which):
     if which == "decode_r64":
         return decode_r64(), torch.bfloat16
+    if which == "d32_g2":
+        # d = 32 (4 lanes a state row), 2 value heads per key head, bf16
+        return make_gdn_case(33, GdnDims(3, 6, 32, 32, 4), [1] * 13, num_slots=20, permute_slots=True,
+                             state_std=0.02, hist_std=1.0, gamma_std=0.1), torch.bfloat16
     if which == "tiny_f32":
         c = make_gdn_case(31, TINY_DIMS, [1] * 9, num_slots=14, permute_slots=True,
                           act_dtype=torch.float32, state_std=0.02, hist_std=1.0, gamma_std=0.1)
@@ -305,7 +309,7 @@ def fused_case(which):
     return c, torch.bfloat16
 
 
-@pytest.mark.parametrize("which", ["decode_r64", "tiny_f32", "d64_g4"])
+@pytest.mark.parametrize("which", ["decode_r64", "tiny_f32", "d64_g4", "d32_g2"])
 def test_decode_fused_parity(which):
     """One-launch decode step against the fp64 oracle chain: o (fp32 copy) and
     states to fp32 accuracy, y within one rounding, history bit-exact, unused

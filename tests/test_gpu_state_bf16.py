@@ -58,10 +58,16 @@ def check_untouched(case, got_state, got_pool, used):
         np.testing.assert_array_equal(bits(got_pool)[rest], bits(case.conv_pool)[rest])
 
 
-@pytest.mark.parametrize("which", ["decode_r64", "tiny_f32"])
+@pytest.mark.parametrize("which", ["decode_r64", "tiny_f32", "d64_g4", "d32_g2"])
 def test_decode_fused_bf16_state(which):
     if which == "decode_r64":
         case, ydt = bf16_case(decode_r64()), torch.bfloat16
+    elif which in ("d64_g4", "d32_g2"):
+        # d = 64 with 4 value heads per key head, d = 32 with 2 (8 and 4 lanes a row)
+        dims = GdnDims(2, 8, 64, 64, 4) if which == "d64_g4" else GdnDims(3, 6, 32, 32, 4)
+        case = make_gdn_case(52 if which == "d64_g4" else 53, dims, [1] * 11, num_slots=17,
+                             permute_slots=True, state_std=0.02, hist_std=1.0, gamma_std=0.1)
+        case, ydt = bf16_case(case), torch.bfloat16
     else:
         case = make_gdn_case(51, TINY_DIMS, [1] * 9, num_slots=14, permute_slots=True,
                              act_dtype=torch.float32, state_std=0.02, hist_std=1.0, gamma_std=0.1)
