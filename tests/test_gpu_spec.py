@@ -24,6 +24,8 @@ def small_case(which):
     every third request."""
     if which == "tiny_f32":
         dims, lens, maxn, act, ydt, seed = TINY_DIMS, [3, 1, 8, 0, 5, 2, 7, 4], 8, torch.float32, torch.float32, 41
+    elif which == "d32_g2":
+        dims, lens, maxn, act, ydt, seed = GdnDims(3, 6, 32, 32, 4), [5, 1, 3, 0, 5, 2], 5, torch.bfloat16, torch.bfloat16, 43
     else:
         dims, lens, maxn, act, ydt, seed = GdnDims(2, 8, 64, 64, 4), [2, 4, 1, 3, 4, 0, 4], 4, torch.bfloat16, torch.bfloat16, 42
     nreq = len(lens)
@@ -91,7 +93,7 @@ def check(case, spec, ydt, y, o, pool, state, tol_state=FP32_TOL):
     np.testing.assert_array_equal(bits(state)[rest], bits(case.state_pool)[rest])
 
 
-@pytest.mark.parametrize("which", ["tiny_f32", "d64_g4"])
+@pytest.mark.parametrize("which", ["tiny_f32", "d64_g4", "d32_g2"])
 def test_spec_verify_parity(which):
     case, spec, ydt = small_case(which)
     assert gdn.gdn_validate_spec_metadata(case.qsl, case.slot_ids, spec, case.num_tokens,
