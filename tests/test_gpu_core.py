@@ -451,7 +451,7 @@ def run_prefill_fused_gpu(case, y_dtype=torch.bfloat16, x_pad=0):
 
 
 @pytest.mark.parametrize("which", ["d128_split_rows", "d128_whole_heads", "d128_group_f32y", "d32_seq",
-                                   "d128_unaligned_rows", "d128_many_requests", "d128_f32x_rows",
+                                   "d64_seq", "d128_unaligned_rows", "d128_many_requests", "d128_f32x_rows",
                                    "d128_f32x_heads"])
 def test_prefill_fused_parity(which):
     """One prefill step through gdn_prefill_fused against the fp64 oracle chain:
@@ -488,6 +488,8 @@ def test_prefill_fused_parity(which):
         rng = np.random.default_rng(45)
         lens = [int(x) for x in rng.integers(0, 70, 100)]
         case = varlen_case(45, lengths=lens, num_slots=104)
+    elif which == "d64_seq":
+        case = varlen_case(48, D=64, Hk=2, Hv=8, lengths=(5, 66, 0, 31, 2), num_slots=7)
     else:
         case = varlen_case(43, D=32, Hk=2, Hv=4, lengths=(3, 40, 1, 77), num_slots=6)
     y, pool, state = run_prefill_fused_gpu(case, y_dtype=y_dtype, x_pad=x_pad)
@@ -535,7 +537,7 @@ def check_states(case, got_state, ref_state, tol):
     return used
 
 
-@pytest.mark.parametrize("which", ["tiny", "varlen_d128", "varlen_d32", "group_blocks",
+@pytest.mark.parametrize("which", ["tiny", "varlen_d128", "varlen_d32", "varlen_d64", "group_blocks",
                                    "whole_head_blocks", "many_requests"])
 def test_prefill_chain_parity(which):
     """The prefill entry point on each chain shape: 32-row blocks (few heads x
@@ -557,6 +559,8 @@ def test_prefill_chain_parity(which):
     elif which == "many_requests":
         rng = np.random.default_rng(28)
         case = varlen_case(28, lengths=[int(x) for x in rng.integers(0, 70, 100)], num_slots=104)
+    elif which == "varlen_d64":
+        case = varlen_case(29, D=64, Hk=2, Hv=8, lengths=(33, 1, 0, 64, 100), num_slots=7)
     else:
         case = varlen_case(22, D=32, Hk=2, Hv=4, lengths=(70, 1, 0, 129), num_slots=6)
     q, k, v, pool = run_conv_gpu(case)
